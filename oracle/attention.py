@@ -87,6 +87,8 @@ def allowed(mask_type, window_left, window_right, len_q, len_k, rows=None, cols=
 def _softmax_rows(s, ok):
     """Row softmax of s over the allowed entries; returns (P, LSE).  A row with no allowed
     entry has P = 0 and LSE = -inf."""
+    if s.shape[1] == 0:  # no keys at all: every row is empty
+        return np.zeros(s.shape), np.full(s.shape[0], -np.inf)
     s = np.where(ok, s, -np.inf)
     m = s.max(axis=1)
     finite = np.isfinite(m)

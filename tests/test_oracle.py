@@ -281,6 +281,19 @@ def test_empty_rows_and_segments():
     dq, dk, dv = A.backward(q, k, v, do, scale=1.0, mask_type=BR)
     np.testing.assert_array_equal(dq[0, :4], 0)
     assert np.all(np.isfinite(dk)) and np.all(np.isfinite(dv))
+    # a segment with no keys at all: every row is empty
+    lq, lk = [2, 3], [0, 4]
+    sq = np.array([0, 2, 5], np.int32)
+    sk = np.array([0, 0, 4], np.int32)
+    q, k, v, do = _rand(5, 2, 4), _rand(4, 1, 4), _rand(4, 1, 4), _rand(5, 2, 4)
+    o, lse = A.forward(q, k, v, scale=1.0, seqstart_q=sq, seqstart_k=sk)
+    assert np.all(np.isneginf(lse[:, :2])) and np.all(np.isfinite(lse[:, 2:]))
+    np.testing.assert_array_equal(o[:2], 0)
+    dq, dk, dv = A.backward(q, k, v, do, scale=1.0, seqstart_q=sq, seqstart_k=sk)
+    np.testing.assert_array_equal(dq[:2], 0)
+    dq1, dk1, dv1 = A.backward(q[None, 2:], k[None], v[None], do[None, 2:], scale=1.0)
+    np.testing.assert_allclose(dq[2:], dq1[0], atol=1e-14)
+    np.testing.assert_allclose(dk, dk1[0], atol=1e-14)
     # a window that excludes everything beyond the diagonal key
     assert A.allowed(WIN, 0, 0, 4, 4).sum() == 4
 
