@@ -1,1 +1,134 @@
-"""MI355X (gfx950) fused multi-head attention backward."""
+"""MI355X (gfx950) fused multi-head attention backward.
+
+Thin Python surface over the C ABI of ``include/fmha_bwd.h``: every step of the computation
+runs in the library's HIP kernels; torch tensors only carry device memory and the stream.
+
+    dq, dk, dv = attention_backward_fmha_amd.bwd(q, k, v, o, lse, do, mask_type=1)
+
+Batch (BSHD) tensors are [B, S, H, d] with LSE [B, Hq, Sq]; group (THD, ragged) tensors are
+[T, H, d] with LSE [Hq, T] and ``cu_seqlens_q``/``cu_seqlens_k`` offsets (B+1 int32).
+"""
+
+import numpy as np
+
+from . import _lib
+from ._lib import (  # noqa: F401
+    MASK_NONE, MASK_CAUSAL_TOP_LEFT, MASK_CAUSAL_BOTTOM_RIGHT, MASK_WINDOW,
+    STAGE_DOT, STAGE_MAIN, STAGE_REDUCE, STAGE_ALL,
+    Args, PlanInfo, FmhaError, status_string, workspace_size, plan_query,
+)
+
+
+class BwdCall:
+    """An argument struct plus the Python objects whose memory it points at."""
+
+    def __init__(self, args, keep):
+        self.args = args
+        self.keep = keep
+
+    def workspace_size(self):
+        return _lib.workspace_size(self.args)
+
+    def plan(self):
+        return _lib.plan_query(self.args)
+
+    def prepare(self, ws, stream):
+        _lib.prepare_workspace(self.args, ws.data_ptr(), ws.numel() * ws.element_size(), stream)
+
+    def run(self, ws, stream, stages=STAGE_ALL):
+        _lib.run(self.args, ws.data_ptr(), ws.numel() * ws.element_size(), stream, stages)
+
+
+def _strides(t, group):
+    if t is None:
+        return (0, 0, 0)
+    st = t.stride()
+    if st[-1] != 1:
+        raise ValueError("the head dimension must be contiguous")
+    if group:
+        return (0, st[0], st[1])
+    return (st[0], st[1], st[2])
+
+
+def _ptr(t):
+    return 0 if t is None else t.data_ptr()
+
+
+def make_call(q, k, v, o, lse, do, dq, dk, dv, *, scale=None, mask_type=MASK_NONE,
+              window=(-1, -1), deterministic=True, cu_seqlens_q=None, cu_seqlens_k=None,
+              cu_seqlens_q_host=None, cu_seqlens_k_host=None, max_seqlen_q=None,
+              max_seqlen_k=None):
+    """Fill the C argument struct from tensors (no device work)."""
+    group = cu_seqlens_q is not None
+    d_qk = q.shape[-1]
+    d_v = v.shape[-1]
+    keep = [q, k, v, o, lse, do, dq, dk, dv]
+    a = Args()
+    if group:
+        if cu_seqlens_q_host is None:
+            cu_seqlens_q_host = cu_seqlens_q.cpu().numpy()
+        if cu_seqlens_k_host is None:
+            cu_seqlens_k_host = cu_seqlens_k.cpu().numpy()
+        hq_ = np.ascontiguousarray(cu_seqlens_q_host, dtype=np.int32)
+        hk_ = np.ascontiguousarray(cu_seqlens_k_host, dtype=np.int32)
+        keep += [hq_, hk_, cu_seqlens_q, cu_seqlens_k]
+        B = len(hq_) - 1
+        lq = np.diff(hq_)
+        lk = np.diff(hk_)
+        a.B = B
+        a.Sq = int(max_seqlen_q if max_seqlen_q is not None else (lq.max() if B else 0))
+        a.Sk = int(max_seqlen_k if max_seqlen_k is not None else (lk.max() if B else 0))
+        a.seqstart_q_host = hq_.ctypes.data
+        a.seqstart_k_host = hk_.ctypes.data
+        a.seqstart_q_dev = cu_seqlens_q.data_ptr()
+        a.seqstart_k_dev = cu_seqlens_k.data_ptr()
+        a.Hq, a.Hkv = q.shape[1], k.shape[1]
+        a.lse_stride[0] = 0
+        a.lse_stride[1] = lse.stride(0)
+    else:
+        a.B, a.Sq, a.Hq = q.shape[0], q.shape[1], q.shape[2]
+        a.Sk, a.Hkv = k.shape[1], k.shape[2]
+        a.lse_stride[0] = lse.stride(0)
+        a.lse_stride[1] = lse.stride(1)
+    a.d_qk, a.d_v = d_qk, d_v
+    a.scale = float(scale if scale is not None else 1.0 / np.sqrt(d_qk))
+    a.mask_type = int(mask_type)
+    a.window_left, a.window_right = (int(window[0]), int(window[1]))
+    a.deterministic = 1 if deterministic else 0
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", do), ("lse", lse),
+                    ("dq", dq), ("dk", dk), ("dv", dv)):
+        setattr(a, name, _ptr(t))
+    for name, t in (("q_stride", q), ("k_stride", k), ("v_stride", v), ("o_stride", o),
+                    ("do_stride", do), ("dq_stride", dq), ("dk_stride", dk), ("dv_stride", dv)):
+        s = _strides(t, group)
+        arr = getattr(a, name)
+        arr[0], arr[1], arr[2] = s
+    return BwdCall(a, keep)
+
+
+def bwd(q, k, v, o, lse, do, *, scale=None, mask_type=MASK_NONE, window=(-1, -1),
+        deterministic=True, cu_seqlens_q=None, cu_seqlens_k=None, cu_seqlens_q_host=None,
+        cu_seqlens_k_host=None, max_seqlen_q=None, max_seqlen_k=None, workspace=None):
+    """Gradients (dq, dk, dv) of softmax attention; see the module docstring for layouts."""
+    import torch
+
+    for t in (q, k, v, o, do):
+        if t.dtype != torch.bfloat16 or not t.is_cuda:
+            raise TypeError("q, k, v, o and do must be bfloat16 CUDA tensors")
+    if lse.dtype != torch.float32:
+        raise TypeError("lse must be float32")
+    dq = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    dk = torch.empty(k.shape, dtype=torch.bfloat16, device=k.device)
+    dv = torch.empty(v.shape, dtype=torch.bfloat16, device=v.device)
+    call = make_call(q, k, v, o, lse, do, dq, dk, dv, scale=scale, mask_type=mask_type,
+                     window=window, deterministic=deterministic, cu_seqlens_q=cu_seqlens_q,
+                     cu_seqlens_k=cu_seqlens_k, cu_seqlens_q_host=cu_seqlens_q_host,
+                     cu_seqlens_k_host=cu_seqlens_k_host, max_seqlen_q=max_seqlen_q,
+                     max_seqlen_k=max_seqlen_k)
+    nbytes = call.workspace_size()
+    if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    call.prepare(workspace, stream)
+    call.run(workspace, stream)
+    return dq, dk, dv

@@ -1,0 +1,44 @@
+// kernels.h -- parameters and launchers of the device stages (implemented in kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "plan.h"
+
+namespace fmha {
+
+// Everything a kernel needs, passed by value as the kernel argument.
+struct KParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dout;
+  const float* lse;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* dsum;    // workspace: D = rowsum(dO * O), [Hq][rows_q]
+  float* dq_acc;  // workspace: fp32 dQ partials, [nsplits][Hq][rows_q][d_qk]
+  const int32_t* seqstart_q;  // device offsets, null in batch mode
+  const int32_t* seqstart_k;
+  int64_t q_s[3], k_s[3], v_s[3], o_s[3], do_s[3], dq_s[3], dk_s[3], dv_s[3];
+  int64_t lse_s[2];
+  int64_t split_stride;  // elements
+  int64_t head_stride;   // elements
+  int64_t rows_q;
+  int B, Hq, Hkv, group_size, Sq, Sk;
+  int mask_type, window_left, window_right;
+  int deterministic;
+  int n_kv_tiles, n_q_blocks;
+  float scale;
+  float scale_log2;  // scale * log2(e)
+};
+
+hipError_t launch_dot(const Plan& plan, const KParams& kp, hipStream_t stream);
+hipError_t launch_main(const Plan& plan, const KParams& kp, hipStream_t stream);
+hipError_t launch_reduce(const Plan& plan, const KParams& kp, hipStream_t stream);
+hipError_t launch_zero(float* ptr, int64_t count, hipStream_t stream);
+
+}  // namespace fmha

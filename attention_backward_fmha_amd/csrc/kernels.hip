@@ -1,0 +1,485 @@
+// kernels.hip -- the three device stages of the attention backward on gfx950 (CDNA4).
+//
+// Stage 1 (k_dot):     D[h][row] = sum_c dO[row,h,c] * O[row,h,c]                 HBM bound
+// Stage 2 (k_bwd_main): one work item per (segment b, K/V head g, key tile j):
+//     for every query head h of g's group and every query block i the mask lets tile j see:
+//       S = Q_i K_j^T, P = exp(scale*S - LSE_i) (0 where masked), dP = dO_i V_j^T,
+//       dS = P * (dP - D_i), dV_j += P^T dO_i, dK_j += dS^T Q_i, dQ_i += dS K_j
+//     dK_j (scaled) and dV_j are written once at the end; the tile's dS K_j goes to the fp32
+//     accumulator: split j (deterministic) or an fp32 atomic add into split 0.      MFMA bound
+// Stage 3 (k_dq_reduce): dQ = bf16(scale * sum_{splits that wrote the block} acc), the fp32
+//     sum in ascending split order.                                                HBM bound
+//
+// Matrix products use v_mfma_f32_32x32x16_bf16 (bf16 operands, fp32 accumulation).  Its lane
+// layout (checked on the device): lane l holds row (l % 32) of A and column (l % 32) of B with
+// the 8 reduction-index values 8*(l/32) .. 8*(l/32)+7; result element (i, j) sits in lane
+// j + 32*((i/4)%2), register 4*(i/8) + i%4.  A sum over the reduction index does not depend on
+// the order of its terms, so any assignment of reduction indices to (lane half, slot) works as
+// long as A and B use the same one; the kernels use that to feed P and dS straight from the
+// result registers of S and dP into the next products.
+//
+// Operands whose reduction index runs along LDS rows (dO and Q in dV/dK, dS^T and K in dQ) are
+// read with ds_read_b64_tr_b16: in each 16-lane group, lane s points at 4 consecutive elements
+// of row (s/4), columns 4*(s%4)..4*(s%4)+3 of a 4x16 block, and lane i receives column i of the
+// block (4 values, one per row).  So every tile is stored row-major in LDS exactly once.
+#include "kernels.h"
+#include "tiling.h"
+
+namespace fmha {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct Seg {
+  int64_t q_row0;   // first tensor row of the segment (0 in batch mode)
+  int64_t k_row0;
+  int64_t lq, lk;   // segment lengths
+  int64_t ws_row0;  // first workspace row (b*Sq in batch mode)
+};
+
+__device__ __forceinline__ Seg seg_of(const KParams& p, int b) {
+  Seg s;
+  if (p.seqstart_q != nullptr) {
+    s.q_row0 = p.seqstart_q[b];
+    s.lq = (int64_t)p.seqstart_q[b + 1] - s.q_row0;
+    s.k_row0 = p.seqstart_k[b];
+    s.lk = (int64_t)p.seqstart_k[b + 1] - s.k_row0;
+    s.ws_row0 = s.q_row0;
+  } else {
+    s.q_row0 = 0;
+    s.k_row0 = 0;
+    s.lq = p.Sq;
+    s.lk = p.Sk;
+    s.ws_row0 = (int64_t)b * p.Sq;
+  }
+  return s;
+}
+
+// Element offset of (segment b, tensor row `row`, head h, column 0).
+__device__ __forceinline__ int64_t elem_off(const int64_t s[3], bool group, int b, int64_t row,
+                                            int h) {
+  return (group ? 0 : (int64_t)b * s[0]) + row * s[1] + (int64_t)h * s[2];
+}
+
+__device__ __forceinline__ bf16x8 tr_read(const uint16_t* p0, const uint16_t* p1) {
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p1));
+  const s16x8 c = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, c);
+}
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint16_t to_bf16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+// ------------------------------------------------------------------------------------------
+// Stage 1: D = rowsum(dO * O).  DV/8 lanes per row, 16 bytes per lane per tensor.
+// ------------------------------------------------------------------------------------------
+template <int DV>
+__global__ __launch_bounds__(256) void k_dot(const KParams p) {
+  constexpr int LPR = DV / 8;
+  constexpr int RPB = 256 / LPR;
+  const int tid = threadIdx.x;
+  const int64_t r = (int64_t)blockIdx.x * RPB + tid / LPR;  // r = row*Hq + h
+  const int c8 = tid % LPR;
+  const bool group = p.seqstart_q != nullptr;
+  const bool valid = r < p.rows_q * p.Hq;
+  float acc = 0.f;
+  int64_t row = 0;
+  int h = 0;
+  if (valid) {
+    row = r / p.Hq;
+    h = (int)(r - row * p.Hq);
+    int b = 0;
+    int64_t trow = row;
+    if (!group) {
+      b = (int)(row / p.Sq);
+      trow = row - (int64_t)b * p.Sq;
+    }
+    const bf16x8 a = *(const bf16x8*)(p.dout + elem_off(p.do_s, group, b, trow, h) + c8 * 8);
+    const bf16x8 o = *(const bf16x8*)(p.o + elem_off(p.o_s, group, b, trow, h) + c8 * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += (float)a[e] * (float)o[e];
+  }
+#pragma unroll
+  for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, LPR);
+  if (valid && c8 == 0) p.dsum[(int64_t)h * p.rows_q + row] = acc;
+}
+
+// ------------------------------------------------------------------------------------------
+// Stage 2: the main kernel.  256 threads = 4 waves; wave w owns keys 32w..32w+31 of the tile.
+// ------------------------------------------------------------------------------------------
+template <int DQK, int DV>
+__global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
+  constexpr int TM = 64;   // query rows per block
+  constexpr int TN = 128;  // keys per tile
+  constexpr int QS = DQK + 8;  // LDS row strides in elements (16-byte pad)
+  constexpr int OS = DV + 8;
+  constexpr int KS = DQK + 8;
+  constexpr int SS = TM + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[TN * KS];   // K_j, row-major
+  __shared__ __attribute__((aligned(16))) uint16_t q_lds[TM * QS];   // Q_i
+  __shared__ __attribute__((aligned(16))) uint16_t o_lds[TM * OS];   // dO_i
+  __shared__ __attribute__((aligned(16))) uint16_t st_lds[TN * SS];  // dS^T (key-major)
+  __shared__ __attribute__((aligned(16))) float lse_lds[TM];        // LSE_i * log2(e)
+  __shared__ __attribute__((aligned(16))) float dd_lds[TM];         // D_i
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  const int g16 = lane >> 4;
+  const int i16 = lane & 15;
+
+  const int nbh = p.Hkv * p.B;
+  const int j = blockIdx.x / nbh;
+  const int rem = blockIdx.x - j * nbh;
+  const int g = rem % p.Hkv;
+  const int b = rem / p.Hkv;
+  const bool group = p.seqstart_q != nullptr;
+  const Seg sg = seg_of(p, b);
+  const int64_t key0 = (int64_t)j * TN;
+  if (key0 >= sg.lk) return;  // whole work item beyond this segment (uniform)
+  const int nk = (int)min((int64_t)TN, sg.lk - key0);
+  const MaskGeom mg = mask_geom(p.mask_type, p.window_left, p.window_right, sg.lq, sg.lk);
+  int64_t qb_lo, qb_hi;
+  qblocks_for_tile(mg, sg.lq, sg.lk, j, TM, TN, &qb_lo, &qb_hi);
+  // allowed  <=>  lo_d <= key - row <= hi_d (and both inside the segment)
+  int64_t lo64 = mg.left >= 0 ? mg.delta - mg.left : INT64_MIN / 2;
+  int64_t hi64 = mg.right >= 0 ? mg.delta + mg.right : INT64_MAX / 2;
+  const int lo_d = (int)max(lo64, (int64_t)INT32_MIN);
+  const int hi_d = (int)min(hi64, (int64_t)INT32_MAX);
+
+  // This lane's key (B-operand column of S and dP) and the wave's K/V rows in registers.
+  const int key_l = wave * 32 + l32;
+  bf16x8 kw[DQK / 16];
+  bf16x8 vw[DV / 16];
+  {
+    const bool ok = key_l < nk;
+    const int64_t krow = sg.k_row0 + key0 + key_l;
+    const uint16_t* kp = p.k + elem_off(p.k_s, group, b, krow, g);
+    const uint16_t* vp = p.v + elem_off(p.v_s, group, b, krow, g);
+#pragma unroll
+    for (int kk = 0; kk < DQK / 16; ++kk) {
+      kw[kk] = ok ? *(const bf16x8*)(kp + 16 * kk + 8 * hi) : bf16x8{};
+      *(bf16x8*)&k_lds[key_l * KS + 16 * kk + 8 * hi] = kw[kk];
+    }
+#pragma unroll
+    for (int kk = 0; kk < DV / 16; ++kk) vw[kk] = ok ? *(const bf16x8*)(vp + 16 * kk + 8 * hi) : bf16x8{};
+  }
+
+  f32x16 dk_acc[DQK / 32];
+  f32x16 dv_acc[DV / 32];
+#pragma unroll
+  for (int n = 0; n < DQK / 32; ++n) dk_acc[n] = f32x16{};
+#pragma unroll
+  for (int n = 0; n < DV / 32; ++n) dv_acc[n] = f32x16{};
+
+  const int tr_row = i16 >> 2;                        // row inside a 4-row transpose block
+  const int tr_col = 16 * (g16 & 1) + 4 * (i16 & 3);  // column offset inside a 32-wide tile
+
+  for (int hh = 0; hh < p.group_size; ++hh) {
+    const int h = g * p.group_size + hh;
+    for (int64_t qb = qb_lo; qb <= qb_hi; ++qb) {
+      const int64_t q0 = qb * TM;
+      const int nq = (int)min((int64_t)TM, sg.lq - q0);
+
+      // ---- stage Q_i, dO_i, LSE_i, D_i in LDS (rows past the segment end are zero) ----
+      for (int c = tid; c < TM * DQK / 8; c += 256) {
+        const int r = c / (DQK / 8);
+        const int c8 = c - r * (DQK / 8);
+        bf16x8 val{};
+        if (r < nq) val = *(const bf16x8*)(p.q + elem_off(p.q_s, group, b, sg.q_row0 + q0 + r, h) + c8 * 8);
+        *(bf16x8*)&q_lds[r * QS + c8 * 8] = val;
+      }
+      for (int c = tid; c < TM * DV / 8; c += 256) {
+        const int r = c / (DV / 8);
+        const int c8 = c - r * (DV / 8);
+        bf16x8 val{};
+        if (r < nq) val = *(const bf16x8*)(p.dout + elem_off(p.do_s, group, b, sg.q_row0 + q0 + r, h) + c8 * 8);
+        *(bf16x8*)&o_lds[r * OS + c8 * 8] = val;
+      }
+      if (tid < TM) {
+        float l2 = 0.f, dd = 0.f;
+        if (tid < nq) {
+          const int64_t row = sg.q_row0 + q0 + tid;
+          const int64_t lo = (group ? 0 : (int64_t)b * p.lse_s[0]) + (int64_t)h * p.lse_s[1] + row;
+          l2 = p.lse[lo] * kLog2e;
+          dd = p.dsum[(int64_t)h * p.rows_q + sg.ws_row0 + q0 + tid];
+        }
+        lse_lds[tid] = l2;
+        dd_lds[tid] = dd;
+      }
+      __syncthreads();
+
+      // ---- S = Q_i K_w^T and dP = dO_i V_w^T (2 row tiles of 32 queries) ----
+      f32x16 s_acc[2] = {f32x16{}, f32x16{}};
+      f32x16 dp_acc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int kk = 0; kk < DQK / 16; ++kk) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const bf16x8 a = *(const bf16x8*)&q_lds[(32 * m + l32) * QS + 16 * kk + 8 * hi];
+          s_acc[m] = mfma(a, kw[kk], s_acc[m]);
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < DV / 16; ++kk) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const bf16x8 a = *(const bf16x8*)&o_lds[(32 * m + l32) * OS + 16 * kk + 8 * hi];
+          dp_acc[m] = mfma(a, vw[kk], dp_acc[m]);
+        }
+      }
+
+      // ---- P, dS (fp32), rounded to bf16 as MFMA operands ----
+      // result register r of row tile m is query 32m + 8(r/4) + 4*hi + r%4, key key_l
+      const bool full = block_full(mg, sg.lq, sg.lk, q0, q0 + TM - 1, key0 + 32 * wave,
+                                   key0 + 32 * wave + 31);
+      const int base_d = (int)(key0 - q0) + key_l;
+      bf16x8 pa[2][2];
+      bf16x8 sa[2][2];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int qr = 32 * m + 8 * c + 4 * hi;
+          const f32x4 l4 = *(const f32x4*)&lse_lds[qr];
+          const f32x4 d4 = *(const f32x4*)&dd_lds[qr];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * c + e;
+            float pv = __builtin_amdgcn_exp2f(s_acc[m][r] * p.scale_log2 - l4[e]);
+            if (!full) {
+              const int dlt = base_d - (qr + e);
+              const bool ok = (dlt >= lo_d) && (dlt <= hi_d) && (qr + e < nq) && (key_l < nk);
+              pv = ok ? pv : 0.f;
+            }
+            const float dsv = pv * (dp_acc[m][r] - d4[e]);
+            pa[m][c >> 1][(c & 1) * 4 + e] = (__bf16)pv;
+            sa[m][c >> 1][(c & 1) * 4 + e] = (__bf16)dsv;
+          }
+        }
+      }
+
+      // ---- dV += P^T dO_i ; dK += dS^T Q_i  (reduction over the block's queries) ----
+      // slot s of lane half hi, step (m, t): query 32m + 16t + 8(s/4) + 4hi + s%4
+#pragma unroll
+      for (int n = 0; n < DV / 32; ++n) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const int kb = 32 * m + 16 * t + 4 * hi + tr_row;
+            const int col = 32 * n + tr_col;
+            const bf16x8 bo = tr_read(&o_lds[kb * OS + col], &o_lds[(kb + 8) * OS + col]);
+            dv_acc[n] = mfma(pa[m][t], bo, dv_acc[n]);
+          }
+        }
+      }
+#pragma unroll
+      for (int n = 0; n < DQK / 32; ++n) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const int kb = 32 * m + 16 * t + 4 * hi + tr_row;
+            const int col = 32 * n + tr_col;
+            const bf16x8 bq = tr_read(&q_lds[kb * QS + col], &q_lds[(kb + 8) * QS + col]);
+            dk_acc[n] = mfma(sa[m][t], bq, dk_acc[n]);
+          }
+        }
+      }
+
+      // ---- dS^T to LDS: 4 consecutive queries per 8-byte store ----
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const bf16x8 v = sa[m][c >> 1];
+          const bf16x4 v4 = (c & 1) ? __builtin_shufflevector(v, v, 4, 5, 6, 7)
+                                    : __builtin_shufflevector(v, v, 0, 1, 2, 3);
+          *(bf16x4*)&st_lds[key_l * SS + 32 * m + 8 * c + 4 * hi] = v4;
+        }
+      }
+      __syncthreads();
+
+      // ---- dQ_i partial = dS K_j  (reduction over the tile's 128 keys) ----
+      constexpr int NT = (TM / 32) * (DQK / 32);
+      for (int ti = wave; ti < NT; ti += 4) {
+        const int mq = ti / (DQK / 32);
+        const int nd = ti - mq * (DQK / 32);
+        f32x16 acc = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < TN / 16; ++kk) {
+          const int kb = 16 * kk + 8 * hi + tr_row;
+          const bf16x8 a = tr_read(&st_lds[kb * SS + 32 * mq + tr_col], &st_lds[(kb + 4) * SS + 32 * mq + tr_col]);
+          const bf16x8 bk = tr_read(&k_lds[kb * KS + 32 * nd + tr_col], &k_lds[(kb + 4) * KS + 32 * nd + tr_col]);
+          acc = mfma(a, bk, acc);
+        }
+        float* dst = p.dq_acc + (p.deterministic ? (int64_t)j * p.split_stride : 0) +
+                     (int64_t)h * p.head_stride + (sg.ws_row0 + q0) * DQK + 32 * nd + l32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int ql = 32 * mq + 8 * (r >> 2) + 4 * hi + (r & 3);
+          if (ql < nq) {
+            if (p.deterministic) {
+              dst[(int64_t)ql * DQK] = acc[r];
+            } else {
+              unsafeAtomicAdd(&dst[(int64_t)ql * DQK], acc[r]);
+            }
+          }
+        }
+      }
+    }
+  }
+
+  // ---- epilogue: dK = scale * dK_acc, dV = dV_acc as bf16 ----
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int kl = wave * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+    if (kl < nk) {
+      const int64_t krow = sg.k_row0 + key0 + kl;
+      uint16_t* dkp = p.dk + elem_off(p.dk_s, group, b, krow, g) + l32;
+      uint16_t* dvp = p.dv + elem_off(p.dv_s, group, b, krow, g) + l32;
+#pragma unroll
+      for (int n = 0; n < DQK / 32; ++n) dkp[32 * n] = to_bf16_bits(dk_acc[n][r] * p.scale);
+#pragma unroll
+      for (int n = 0; n < DV / 32; ++n) dvp[32 * n] = to_bf16_bits(dv_acc[n][r]);
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Stage 3: dQ = bf16(scale * sum of the partials), one block of TM rows per work group.
+// ------------------------------------------------------------------------------------------
+template <int DQK>
+__global__ __launch_bounds__(256) void k_dq_reduce(const KParams p) {
+  constexpr int TM = 64, TN = 128;
+  constexpr int C4 = DQK / 4;           // float4 chunks per row
+  constexpr int PER = TM * C4 / 256;    // chunks per thread
+  const int qb = blockIdx.x;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const bool group = p.seqstart_q != nullptr;
+  const Seg sg = seg_of(p, b);
+  const int64_t q0 = (int64_t)qb * TM;
+  if (q0 >= sg.lq) return;
+  const int nq = (int)min((int64_t)TM, sg.lq - q0);
+  const MaskGeom mg = mask_geom(p.mask_type, p.window_left, p.window_right, sg.lq, sg.lk);
+  const int ntiles = (int)((sg.lk + TN - 1) / TN);
+  const int tid = threadIdx.x;
+  f32x4 acc[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const float* base = p.dq_acc + (int64_t)h * p.head_stride + (sg.ws_row0 + q0) * DQK;
+  if (p.deterministic) {
+    for (int jt = 0; jt < ntiles; ++jt) {  // ascending split order
+      int64_t lo, hi;
+      qblocks_for_tile(mg, sg.lq, sg.lk, jt, TM, TN, &lo, &hi);
+      if (qb < lo || qb > hi) continue;
+      const float* src = base + (int64_t)jt * p.split_stride;
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int c = tid + 256 * u;
+        const int r = c / C4;
+        if (r < nq) {
+          const f32x4 x = *(const f32x4*)(src + (int64_t)r * DQK + (c - r * C4) * 4);
+          acc[u] += x;
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int c = tid + 256 * u;
+      const int r = c / C4;
+      if (r < nq) acc[u] += *(const f32x4*)(base + (int64_t)r * DQK + (c - r * C4) * 4);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int c = tid + 256 * u;
+    const int r = c / C4;
+    if (r < nq) {
+      const f32x4 y = acc[u] * p.scale;
+      bf16x4 o;
+      o[0] = (__bf16)y[0];
+      o[1] = (__bf16)y[1];
+      o[2] = (__bf16)y[2];
+      o[3] = (__bf16)y[3];
+      *(bf16x4*)(p.dq + elem_off(p.dq_s, group, b, sg.q_row0 + q0 + r, h) + (c - r * C4) * 4) = o;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_zero(float* ptr, int64_t n4) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride)
+    ((f32x4*)ptr)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+}  // namespace
+
+hipError_t launch_dot(const Plan& plan, const KParams& kp, hipStream_t stream) {
+  const int64_t rows = plan.rows_q * plan.Hq;
+  if (rows == 0) return hipSuccess;
+  const int rpb = 256 / (plan.d_v / 8);
+  const int64_t blocks = (rows + rpb - 1) / rpb;
+  if (plan.d_v == 64) {
+    hipLaunchKernelGGL(k_dot<64>, dim3((unsigned)blocks), dim3(256), 0, stream, kp);
+  } else {
+    hipLaunchKernelGGL(k_dot<128>, dim3((unsigned)blocks), dim3(256), 0, stream, kp);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_main(const Plan& plan, const KParams& kp, hipStream_t stream) {
+  const int64_t items = (int64_t)plan.n_kv_tiles * plan.Hkv * plan.B;
+  if (items == 0) return hipSuccess;
+  const dim3 grid((unsigned)items);
+  if (plan.d_qk == 64) {
+    hipLaunchKernelGGL((k_bwd_main<64, 64>), grid, dim3(256), 0, stream, kp);
+  } else if (plan.d_qk == 128) {
+    hipLaunchKernelGGL((k_bwd_main<128, 128>), grid, dim3(256), 0, stream, kp);
+  } else {
+    hipLaunchKernelGGL((k_bwd_main<192, 128>), grid, dim3(256), 0, stream, kp);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce(const Plan& plan, const KParams& kp, hipStream_t stream) {
+  if (plan.n_q_blocks == 0 || plan.B == 0) return hipSuccess;
+  const dim3 grid((unsigned)plan.n_q_blocks, (unsigned)plan.Hq, (unsigned)plan.B);
+  if (plan.d_qk == 64) {
+    hipLaunchKernelGGL(k_dq_reduce<64>, grid, dim3(256), 0, stream, kp);
+  } else if (plan.d_qk == 128) {
+    hipLaunchKernelGGL(k_dq_reduce<128>, grid, dim3(256), 0, stream, kp);
+  } else {
+    hipLaunchKernelGGL(k_dq_reduce<192>, grid, dim3(256), 0, stream, kp);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_zero(float* ptr, int64_t count, hipStream_t stream) {
+  if (count == 0) return hipSuccess;
+  const int64_t n4 = count / 4;  // the accumulator is a multiple of 4 floats (d_qk % 4 == 0)
+  int64_t blocks = (n4 + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(k_zero, dim3((unsigned)blocks), dim3(256), 0, stream, ptr, n4);
+  return hipGetLastError();
+}
+
+}  // namespace fmha

@@ -1,0 +1,173 @@
+// plan.cpp -- argument validation and workspace layout (host only).
+//
+// Workspace layout (byte offsets 256-aligned):
+//   D       fp32 [Hq][rows_q]                     rowsum(dO * O) from the first stage
+//   dq_acc  fp32 [nsplits][Hq][rows_q][d_qk]      dQ partials (deterministic: split = key tile
+//                                                 index of the segment; atomic: one split)
+// One layout serves batch and group mode: row = b*Sq + i in batch mode and seqstart_q[b] + i
+// in group mode (the physical token), so a ragged segment never aliases another one's rows --
+// unlike the layout mix-up in "[ROCm] Fix THD/ragged dQ backward on the bf16 dq_shuffle path
+// (gfx950)", Root cause, where ragged segments after the first landed on slot 0.
+#include "plan.h"
+
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "tiling.h"
+
+namespace fmha {
+namespace {
+
+int fail(int status, char* err, size_t len, const char* msg) {
+  if (err && len) {
+    snprintf(err, len, "%s", msg);
+  }
+  return status;
+}
+
+int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// The kernels move 8 bf16 (16 bytes) per lane access along the head dimension.
+bool strides_ok(const int64_t s[3], bool group) {
+  for (int i = group ? 1 : 0; i < 3; ++i) {
+    if (s[i] < 0 || (s[i] & 7) != 0) return false;
+  }
+  return true;
+}
+
+}  // namespace
+
+int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t el) {
+  if (!a || !p) return fail(FMHA_ERR_INVALID_ARG, err, el, "null argument");
+  if (a->struct_size != sizeof(fmha_bwd_args))
+    return fail(FMHA_ERR_INVALID_ARG, err, el, "struct_size does not match this library");
+  if (a->abi_version != FMHA_BWD_ABI_VERSION)
+    return fail(FMHA_ERR_INVALID_ARG, err, el, "abi_version does not match this library");
+  memset(p, 0, sizeof(*p));
+  const bool group = a->seqstart_q_host != nullptr;
+  p->group_mode = group;
+  if (a->B < 0 || a->Sq < 0 || a->Sk < 0)
+    return fail(FMHA_ERR_INVALID_ARG, err, el, "B, Sq and Sk must be non-negative");
+  if (a->Hq <= 0 || a->Hkv <= 0 || a->Hq % a->Hkv != 0)
+    return fail(FMHA_ERR_INVALID_ARG, err, el, "Hq and Hkv must be positive with Hq % Hkv == 0");
+  const bool dims_ok = (a->d_qk == 64 && a->d_v == 64) || (a->d_qk == 128 && a->d_v == 128) ||
+                       (a->d_qk == 192 && a->d_v == 128);
+  if (!dims_ok)
+    return fail(FMHA_ERR_UNSUPPORTED, err, el,
+                "head dims (d_qk, d_v) must be (64,64), (128,128) or (192,128)");
+  if (!isfinite(a->scale)) return fail(FMHA_ERR_INVALID_ARG, err, el, "scale is not finite");
+  if (a->mask_type < FMHA_MASK_NONE || a->mask_type > FMHA_MASK_WINDOW)
+    return fail(FMHA_ERR_INVALID_ARG, err, el, "unknown mask_type");
+  if (a->mask_type != FMHA_MASK_WINDOW && (a->window_left != -1 || a->window_right != -1))
+    return fail(FMHA_ERR_INVALID_ARG, err, el,
+                "window_left/window_right must be -1 unless mask_type is FMHA_MASK_WINDOW");
+  if (a->window_left < -1 || a->window_right < -1)
+    return fail(FMHA_ERR_INVALID_ARG, err, el, "window bounds must be >= -1");
+  if (a->deterministic != 0 && a->deterministic != 1)
+    return fail(FMHA_ERR_INVALID_ARG, err, el, "deterministic must be 0 or 1");
+
+  p->B = a->B;
+  p->Hq = a->Hq;
+  p->Hkv = a->Hkv;
+  p->group_size = a->Hq / a->Hkv;
+  p->Sq = a->Sq;
+  p->Sk = a->Sk;
+  p->d_qk = a->d_qk;
+  p->d_v = a->d_v;
+  p->tile_m = 64;
+  p->tile_n = 128;
+  p->deterministic = a->deterministic == 1;
+
+  int64_t max_lq = a->Sq, max_lk = a->Sk;
+  if (group) {
+    if (!a->seqstart_k_host || !a->seqstart_q_dev || !a->seqstart_k_dev)
+      return fail(FMHA_ERR_INVALID_ARG, err, el,
+                  "group mode needs host and device seqstart arrays for both q and k");
+    const int32_t* sq = a->seqstart_q_host;
+    const int32_t* sk = a->seqstart_k_host;
+    if (sq[0] < 0 || sk[0] < 0)
+      return fail(FMHA_ERR_INVALID_ARG, err, el, "seqstart offsets must be non-negative");
+    max_lq = 0;
+    max_lk = 0;
+    for (int b = 0; b < a->B; ++b) {
+      const int64_t lq = (int64_t)sq[b + 1] - sq[b];
+      const int64_t lk = (int64_t)sk[b + 1] - sk[b];
+      if (lq < 0 || lk < 0)
+        return fail(FMHA_ERR_INVALID_ARG, err, el, "seqstart offsets must be non-decreasing");
+      if (lq > a->Sq || lk > a->Sk)
+        return fail(FMHA_ERR_INVALID_ARG, err, el,
+                    "a segment is longer than Sq/Sk (the maximum segment lengths)");
+      if (lq > max_lq) max_lq = lq;
+      if (lk > max_lk) max_lk = lk;
+    }
+    p->rows_q = a->B > 0 ? sq[a->B] : 0;
+  } else {
+    if (a->seqstart_k_host || a->seqstart_q_dev || a->seqstart_k_dev)
+      return fail(FMHA_ERR_INVALID_ARG, err, el,
+                  "seqstart arrays must be all null (batch mode) or all set (group mode)");
+    p->rows_q = (int64_t)a->B * a->Sq;
+  }
+
+  // pointers and strides (only when there is data to touch)
+  const bool any_q = p->rows_q > 0;
+  const bool any_k = group ? (a->B > 0 && a->seqstart_k_host[a->B] > 0) : ((int64_t)a->B * a->Sk > 0);
+  if (any_q) {
+    if (!a->q || !a->o || !a->dout || !a->dq || !a->lse)
+      return fail(FMHA_ERR_INVALID_ARG, err, el, "q, o, dout, dq and lse must be set");
+    if (!aligned16(a->q) || !aligned16(a->o) || !aligned16(a->dout) || !aligned16(a->dq))
+      return fail(FMHA_ERR_UNSUPPORTED, err, el, "bf16 tensors must be 16-byte aligned");
+    if (((uintptr_t)a->lse & 3u) != 0)
+      return fail(FMHA_ERR_INVALID_ARG, err, el, "lse must be 4-byte aligned");
+    if (!strides_ok(a->q_stride, group) || !strides_ok(a->o_stride, group) ||
+        !strides_ok(a->do_stride, group) || !strides_ok(a->dq_stride, group))
+      return fail(FMHA_ERR_UNSUPPORTED, err, el,
+                  "q/o/dout/dq strides must be non-negative multiples of 8 elements");
+    if ((!group && a->lse_stride[0] < 0) || a->lse_stride[1] < 0)
+      return fail(FMHA_ERR_INVALID_ARG, err, el, "lse strides must be non-negative");
+  }
+  if (any_k) {
+    if (!a->k || !a->v || !a->dk || !a->dv)
+      return fail(FMHA_ERR_INVALID_ARG, err, el, "k, v, dk and dv must be set");
+    if (!aligned16(a->k) || !aligned16(a->v) || !aligned16(a->dk) || !aligned16(a->dv))
+      return fail(FMHA_ERR_UNSUPPORTED, err, el, "bf16 tensors must be 16-byte aligned");
+    if (!strides_ok(a->k_stride, group) || !strides_ok(a->v_stride, group) ||
+        !strides_ok(a->dk_stride, group) || !strides_ok(a->dv_stride, group))
+      return fail(FMHA_ERR_UNSUPPORTED, err, el,
+                  "k/v/dk/dv strides must be non-negative multiples of 8 elements");
+  }
+
+  p->n_kv_tiles = (int)((max_lk + p->tile_n - 1) / p->tile_n);
+  p->n_q_blocks = (int)((max_lq + p->tile_m - 1) / p->tile_m);
+  p->nsplits = p->deterministic ? (p->n_kv_tiles > 0 ? p->n_kv_tiles : 1) : 1;
+  p->needs_zero = !p->deterministic;
+  p->max_rows_q = p->rows_q;
+
+  p->head_stride = p->rows_q * p->d_qk;
+  p->split_stride = (int64_t)p->Hq * p->head_stride;
+  p->d_offset = 0;
+  p->d_bytes = (int64_t)p->Hq * p->rows_q * 4;
+  p->dq_acc_offset = align_up(p->d_bytes, 256);
+  p->dq_acc_bytes = (int64_t)p->nsplits * p->split_stride * 4;
+  p->workspace_bytes = align_up(p->dq_acc_offset + p->dq_acc_bytes, 256);
+  if (p->workspace_bytes == 0) p->workspace_bytes = 256;
+  return FMHA_OK;
+}
+
+int64_t count_pairs(const fmha_bwd_args* a) {
+  const bool group = a->seqstart_q_host != nullptr;
+  int64_t pairs = 0;
+  for (int b = 0; b < (group ? a->B : (a->B > 0 ? 1 : 0)); ++b) {
+    const int64_t lq = group ? (int64_t)a->seqstart_q_host[b + 1] - a->seqstart_q_host[b] : a->Sq;
+    const int64_t lk = group ? (int64_t)a->seqstart_k_host[b + 1] - a->seqstart_k_host[b] : a->Sk;
+    const MaskGeom g = mask_geom(a->mask_type, a->window_left, a->window_right, lq, lk);
+    int64_t seg = 0;
+    for (int64_t i = 0; i < lq; ++i) seg += keys_of_row(g, i, lk);
+    pairs += group ? seg : seg * a->B;
+  }
+  return pairs * a->Hq;
+}
+
+}  // namespace fmha

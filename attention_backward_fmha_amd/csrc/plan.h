@@ -1,0 +1,42 @@
+// plan.h -- the single host-side derivation of every size, offset and launch shape.
+//
+// fmha_bwd_workspace_size, fmha_bwd_prepare_workspace and fmha_bwd_run all call make_plan on
+// the same arguments; nothing else computes a workspace quantity.  Host only (no HIP calls),
+// so it runs and is tested on machines without a GPU.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "fmha_bwd.h"
+
+namespace fmha {
+
+struct Plan {
+  bool group_mode;
+  int B, Hq, Hkv, group_size;
+  int Sq, Sk;            // batch: lengths; group: maximum segment lengths
+  int d_qk, d_v;
+  int tile_m, tile_n;    // query rows per block, keys per tile
+  int n_kv_tiles;        // key tiles of the longest segment (grid extent)
+  int n_q_blocks;        // query blocks of the longest segment (grid extent)
+  int nsplits;           // accumulator depth
+  bool needs_zero;       // prepare zeroes the accumulator (atomic mode)
+  bool deterministic;
+  int64_t rows_q;        // accumulator / D rows: B*Sq or seqstart_q[B]
+  int64_t d_offset, d_bytes;
+  int64_t dq_acc_offset, dq_acc_bytes;
+  int64_t split_stride;  // elements between consecutive splits: Hq*rows_q*d_qk
+  int64_t head_stride;   // elements between heads inside a split: rows_q*d_qk
+  int64_t workspace_bytes;
+  int64_t max_rows_q;    // for the D stage grid: rows_q
+};
+
+// Validates `a` and fills `p`.  Returns FMHA_OK or a negative status; on failure `err`
+// (if not null) receives a message.
+int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t err_len);
+
+// Allowed (query, key) pairs over all heads and segments (FLOP accounting).
+int64_t count_pairs(const fmha_bwd_args* a);
+
+}  // namespace fmha

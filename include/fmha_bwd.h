@@ -1,0 +1,174 @@
+/*
+ * fmha_bwd.h -- C ABI of the MI355X (gfx950) fused multi-head attention backward.
+ *
+ * Computes dQ, dK, dV of softmax attention O = softmax(scale * Q K^T + mask) V from Q, K, V,
+ * the forward output O, its gradient dO and the forward log-sum-exp.  Three device stages run
+ * on the caller's stream:
+ *   1. D = rowsum(dO * O) into the workspace                                   (HBM bound)
+ *   2. the main kernel: per (segment, K/V head, key tile) it recomputes P = exp(S - LSE),
+ *      accumulates dV += P^T dO and dK += dS^T Q in registers and emits the tile's fp32
+ *      contribution dS K to the dQ accumulator                                   (MFMA bound)
+ *   3. dQ = bf16(scale * sum over splits of the accumulator)                   (HBM bound)
+ *
+ * The workspace protocol follows "[CK_TILE] FMHA BWD Use Persistent Kernels in Deterministic
+ * Mode" (aiter PR 2216), commit messages: the launcher reports a workspace size, the caller
+ * allocates it, a prepare call initialises it, then the run call uses it.  As there, only the
+ * atomic accumulation needs a zeroed accumulator; group mode without sequence offsets is
+ * rejected; a workspace that is too small is an error, never a silent truncation.
+ * Deterministic mode writes one fp32 dQ partial per key tile into an nsplits-deep workspace
+ * and reduces it in a fixed order (the split/convert scheme of that page's Motivation).
+ *
+ * One pure host function (the plan) derives every size, offset and launch shape from the
+ * arguments; fmha_bwd_workspace_size, fmha_bwd_prepare_workspace and fmha_bwd_run all call
+ * it, so the sizing pass and the run pass cannot disagree -- the failure class described in
+ * "[ROCm] Fix THD/ragged dQ backward on the bf16 dq_shuffle path (gfx950)", Root cause.
+ *
+ * Conventions
+ *   - bf16 tensors (q, k, v, o, dout, dq, dk, dv) have the head dimension contiguous and
+ *     element strides {batch, sequence, head}.  Batch mode (BSHD): element (b, s, h, c) is at
+ *     b*stride[0] + s*stride[1] + h*stride[2] + c.  Group mode (THD, ragged): stride[0] is
+ *     ignored and token t (a physical row given by the seqstart offsets) is at
+ *     t*stride[1] + h*stride[2] + c.
+ *   - lse is fp32, natural logarithm, as written by the forward: batch mode
+ *     lse[b*lse_stride[0] + h*lse_stride[1] + s]; group mode lse[h*lse_stride[1] + t].
+ *     A row with no allowed key carries -inf.
+ *   - Grouped-query attention: query head h uses K/V head h / (Hq / Hkv).
+ *   - Masks (numbering mirrors the mask-type table in the review of
+ *     "Update AITER subcommit and refactor internal AITER/CK FA API usage", TransformerEngine
+ *     PR 446): with Lq, Lk the lengths of a segment, key j is allowed for query i iff
+ *     j < Lk and
+ *       FMHA_MASK_NONE                 always
+ *       FMHA_MASK_CAUSAL_TOP_LEFT      j <= i
+ *       FMHA_MASK_CAUSAL_BOTTOM_RIGHT  j <= i + (Lk - Lq)
+ *       FMHA_MASK_WINDOW               (left < 0 or j >= i + Lk - Lq - left) and
+ *                                      (right < 0 or j <= i + Lk - Lq + right)
+ *     window_left/window_right must be -1 for the first three types.
+ *   - Rows with no allowed key get dQ = 0 and contribute nothing to dK and dV.
+ *
+ * Ownership: the caller owns every tensor and the workspace; the library allocates no device
+ * memory and keeps no state between calls.  Host seqstart arrays are read during the call
+ * only.  Device pointers must stay valid until the stream work completes.  One workspace must
+ * not serve two runs in flight at the same time, and fmha_bwd_prepare_workspace must precede
+ * every fmha_bwd_run (in atomic mode it zeroes the accumulator each time).
+ *
+ * Errors: every function returns FMHA_OK or a negative fmha_status and never aborts.  Set
+ * FMHA_BWD_LOG=1 in the environment to have the reason printed to stderr.
+ */
+#ifndef FMHA_BWD_H
+#define FMHA_BWD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FMHA_BWD_ABI_VERSION 1u
+
+#if defined(__GNUC__)
+#define FMHA_BWD_API __attribute__((visibility("default")))
+#else
+#define FMHA_BWD_API
+#endif
+
+enum fmha_mask_type {
+  FMHA_MASK_NONE = 0,
+  FMHA_MASK_CAUSAL_TOP_LEFT = 1,
+  FMHA_MASK_CAUSAL_BOTTOM_RIGHT = 2,
+  FMHA_MASK_WINDOW = 3
+};
+
+enum fmha_status {
+  FMHA_OK = 0,
+  FMHA_ERR_INVALID_ARG = -1,          /* bad shape, pointer, stride, mask or seqstart */
+  FMHA_ERR_UNSUPPORTED = -2,          /* valid but not built: head dims, alignment */
+  FMHA_ERR_WORKSPACE_TOO_SMALL = -3,  /* workspace_bytes below fmha_bwd_workspace_size */
+  FMHA_ERR_HIP = -5                   /* a HIP runtime call or kernel launch failed */
+};
+
+typedef struct fmha_bwd_args {
+  uint32_t struct_size;  /* sizeof(fmha_bwd_args), checked against the library's */
+  uint32_t abi_version;  /* FMHA_BWD_ABI_VERSION */
+  int32_t B;             /* batch size (batch mode) or number of segments (group mode) */
+  int32_t Hq, Hkv;       /* query heads, K/V heads; Hq % Hkv == 0 */
+  int32_t Sq, Sk;        /* sequence lengths (batch mode) or maximum segment lengths (group) */
+  int32_t d_qk, d_v;     /* head dims; supported pairs: (64,64), (128,128), (192,128) */
+  float scale;           /* softmax scale, usually 1/sqrt(d_qk) */
+  int32_t mask_type;     /* enum fmha_mask_type */
+  int32_t window_left;   /* FMHA_MASK_WINDOW only; -1 = unbounded */
+  int32_t window_right;  /* FMHA_MASK_WINDOW only; -1 = unbounded */
+  int32_t deterministic; /* 1: per-key-tile fp32 partials + ordered reduction, bit-reproducible;
+                            0: fp32 atomic accumulation of dQ */
+  /* Group (THD) mode iff seqstart_q_host != NULL.  Then all four arrays are required and hold
+     the same B+1 non-decreasing physical token offsets (host copies for planning, device
+     copies for the kernels); segment b covers tokens [seqstart[b], seqstart[b+1]). */
+  const int32_t* seqstart_q_host;
+  const int32_t* seqstart_k_host;
+  const int32_t* seqstart_q_dev;
+  const int32_t* seqstart_k_dev;
+  const void* q;     /* bf16 [.., Sq|T_q, Hq, d_qk] */
+  const void* k;     /* bf16 [.., Sk|T_k, Hkv, d_qk] */
+  const void* v;     /* bf16 [.., Sk|T_k, Hkv, d_v] */
+  const void* o;     /* bf16 [.., Sq|T_q, Hq, d_v] forward output */
+  const void* dout;  /* bf16 [.., Sq|T_q, Hq, d_v] gradient of o */
+  const float* lse;  /* fp32 forward log-sum-exp, see conventions */
+  void* dq;          /* bf16 [.., Sq|T_q, Hq, d_qk], fully overwritten */
+  void* dk;          /* bf16 [.., Sk|T_k, Hkv, d_qk], fully overwritten */
+  void* dv;          /* bf16 [.., Sk|T_k, Hkv, d_v], fully overwritten */
+  int64_t q_stride[3], k_stride[3], v_stride[3], o_stride[3], do_stride[3];
+  int64_t dq_stride[3], dk_stride[3], dv_stride[3];
+  int64_t lse_stride[2]; /* {batch, head}; the sequence stride is 1 */
+} fmha_bwd_args;
+
+/* Workspace bytes that prepare/run need for these arguments.  Host only: no GPU call, no
+   allocation, no synchronisation; device pointers are not dereferenced. */
+FMHA_BWD_API int fmha_bwd_workspace_size(const fmha_bwd_args* args, size_t* bytes);
+
+/* Initialise the workspace on `stream` (a hipStream_t; NULL = the default stream).  Atomic
+   mode zeroes the dQ accumulator; deterministic mode needs no initialisation (every partial
+   the reduction reads is written by the run).  Asynchronous. */
+FMHA_BWD_API int fmha_bwd_prepare_workspace(const fmha_bwd_args* args, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* Enqueue the three stages on `stream`.  Asynchronous; returns after the launches. */
+FMHA_BWD_API int fmha_bwd_run(const fmha_bwd_args* args, void* workspace, size_t workspace_bytes,
+                 void* stream);
+
+/* Static string naming a status code. */
+FMHA_BWD_API const char* fmha_bwd_status_string(int status);
+
+/* ---- test and measurement hooks -------------------------------------------------------- */
+
+/* What the plan decided for these arguments (host only, like fmha_bwd_workspace_size). */
+typedef struct fmha_bwd_plan_info {
+  int32_t group_mode;      /* 1 for THD */
+  int32_t tile_m;          /* query rows per block in the main kernel */
+  int32_t tile_n;          /* keys per tile (one work item) */
+  int32_t n_kv_tiles;      /* key tiles of the longest segment */
+  int32_t n_q_blocks;      /* query blocks of the longest segment */
+  int32_t nsplits;         /* depth of the dQ accumulator (n_kv_tiles, or 1 in atomic mode) */
+  int32_t needs_zero;      /* prepare zeroes the accumulator */
+  int32_t reserved;
+  int64_t rows_q;          /* T_q: B*Sq (batch) or seqstart_q[B] (group) */
+  int64_t d_offset;        /* byte offset of D = rowsum(dO*O), fp32 [Hq][rows_q] */
+  int64_t dq_acc_offset;   /* byte offset of the fp32 accumulator [nsplits][Hq][rows_q][d_qk] */
+  int64_t dq_acc_bytes;
+  int64_t workspace_bytes; /* == fmha_bwd_workspace_size */
+  int64_t pairs;           /* allowed (query, key) pairs summed over heads and segments */
+  double flops;            /* 2*(3*d_qk + 2*d_v) * pairs: the five contractions */
+} fmha_bwd_plan_info;
+
+FMHA_BWD_API int fmha_bwd_plan_query(const fmha_bwd_args* args, fmha_bwd_plan_info* info);
+
+/* Run a subset of the stages of fmha_bwd_run (bit mask of fmha_bwd_stage), for unit tests
+   of one kernel and per-kernel timing.  Same contract as fmha_bwd_run. */
+enum fmha_bwd_stage { FMHA_STAGE_DOT = 1, FMHA_STAGE_MAIN = 2, FMHA_STAGE_REDUCE = 4 };
+FMHA_BWD_API int fmha_bwd_run_stages(const fmha_bwd_args* args, void* workspace, size_t workspace_bytes,
+                        int stages, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FMHA_BWD_H */

@@ -1,0 +1,106 @@
+"""Shared pieces of the GPU parity tests: seeded inputs, the oracle side, the HIP side and the
+comparison at the tolerance the target sets (max |err| <= 2e-2 * max |ref| and cosine >= 0.9999,
+per tensor and per ragged segment)."""
+
+import numpy as np
+
+from attention_backward_fmha_amd import inputs as I
+
+TOL_MAX = 2e-2
+TOL_COS = 0.9999
+
+
+def seq_offsets(lengths):
+    return I.seqstart(lengths)
+
+
+def make_inputs(seed, *, B=None, Sq=None, Sk=None, lens_q=None, lens_k=None, Hq, Hkv, d_qk, d_v,
+                sigmas=(1, 1, 1, 1)):
+    """Batch mode when lens_q is None.  Returns dict of float32 bf16-representable arrays."""
+    if lens_q is None:
+        shapes = [(B, Sq, Hq, d_qk), (B, Sk, Hkv, d_qk), (B, Sk, Hkv, d_v), (B, Sq, Hq, d_v)]
+    else:
+        tq, tk = int(sum(lens_q)), int(sum(lens_k))
+        shapes = [(tq, Hq, d_qk), (tk, Hkv, d_qk), (tk, Hkv, d_v), (tq, Hq, d_v)]
+    return I.draw(seed, shapes, sigmas)
+
+
+def oracle_forward(x, *, scale, mask, window=(-1, -1), sq=None, sk=None):
+    import oracle
+    o, lse = oracle.forward(x["q"], x["k"], x["v"], scale=scale, mask_type=mask,
+                            window_left=window[0], window_right=window[1], seqstart_q=sq,
+                            seqstart_k=sk)
+    return o, lse
+
+
+def oracle_backward(x, *, scale, mask, window=(-1, -1), sq=None, sk=None):
+    import oracle
+    return oracle.backward(x["q"], x["k"], x["v"], x["do"], scale=scale, mask_type=mask,
+                           window_left=window[0], window_right=window[1], seqstart_q=sq,
+                           seqstart_k=sk)
+
+
+def to_dev_bf16(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(torch.bfloat16).cuda()
+
+
+def to_dev_f32(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
+
+
+def run_gpu(x, o, lse, *, scale, mask, window=(-1, -1), sq=None, sk=None, deterministic=True):
+    """Round O to bf16 and LSE to fp32 as the forward would store them, run the library."""
+    import torch
+    import attention_backward_fmha_amd as F
+    q, k, v, do = (to_dev_bf16(x[n]) for n in ("q", "k", "v", "do"))
+    od = to_dev_bf16(I.round_bf16(o.astype(np.float32)))
+    ld = to_dev_f32(lse.astype(np.float32))
+    kw = {}
+    if sq is not None:
+        kw = dict(cu_seqlens_q=torch.from_numpy(np.asarray(sq, np.int32)).cuda(),
+                  cu_seqlens_k=torch.from_numpy(np.asarray(sk, np.int32)).cuda(),
+                  cu_seqlens_q_host=np.asarray(sq, np.int32),
+                  cu_seqlens_k_host=np.asarray(sk, np.int32))
+    dq, dk, dv = F.bwd(q, k, v, od, ld, do, scale=scale, mask_type=mask, window=window,
+                       deterministic=deterministic, **kw)
+    torch.cuda.synchronize()
+    return tuple(t.float().cpu().numpy().astype(np.float64) for t in (dq, dk, dv))
+
+
+def metrics(got, ref):
+    got = np.asarray(got, np.float64).ravel()
+    ref = np.asarray(ref, np.float64).ravel()
+    mref = float(np.abs(ref).max()) if ref.size else 0.0
+    err = float(np.abs(got - ref).max()) if ref.size else 0.0
+    ng, nr = np.linalg.norm(got), np.linalg.norm(ref)
+    if nr == 0.0 and ng == 0.0:
+        cos = 1.0
+    elif nr == 0.0 or ng == 0.0:
+        cos = 0.0
+    else:
+        cos = float(got @ ref / (ng * nr))
+    return err, mref, cos
+
+
+def assert_close(name, got, ref):
+    assert np.all(np.isfinite(got)), "%s has non-finite values" % name
+    err, mref, cos = metrics(got, ref)
+    if mref == 0.0:
+        assert err == 0.0, "%s: reference is zero but max|got| = %g" % (name, err)
+        return
+    assert err <= TOL_MAX * mref, "%s: max|err| %.3g > %.3g * max|ref| (%.3g)" % (name, err, TOL_MAX, mref)
+    assert cos >= TOL_COS, "%s: cosine %.6f < %.4f" % (name, cos, TOL_COS)
+
+
+def assert_grads_close(got, ref, sq=None, sk=None, label=""):
+    names = ("dq", "dk", "dv")
+    for n, g, r in zip(names, got, ref):
+        assert_close(label + n, g, r)
+    if sq is not None:
+        for b in range(len(sq) - 1):
+            for n, g, r, s in zip(names, got, ref, (sq, sk, sk)):
+                a0, a1 = int(s[b]), int(s[b + 1])
+                if a1 > a0:
+                    assert_close("%s%s[segment %d]" % (label, n, b), g[a0:a1], r[a0:a1])
