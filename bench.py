@@ -1,0 +1,214 @@
+#!/usr/bin/env python3
+"""Throughput of the attention backward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--mode atomic|deterministic]
+                    [--workload headline_2x32x4096_causal] [--no-cpu-baseline]
+
+A step is one full backward (prepare_workspace + the dot, main and reduce kernels) over one
+batch of seeded synthetic input already resident in HBM.  Prints one JSON line.
+
+Workload: B=2, Hq=Hkv=32, S=4096, d=128, causal (top-left), BSHD, bf16 -- the B*H*S*d =
+2*32*4096*128 causal shape the throughput target is quoted on.  Q, K, V, dO are N(0,1) draws
+rounded to bf16; O and LSE (the forward's outputs, inputs of the backward) are prepared once,
+untimed, with fp32 torch matrix products on the GPU.
+
+FLOPs are counted as 2*(3*d_qk + 2*d_v) per allowed (query, key) pair (exact causal pair count),
+i.e. 2.5 * 4 * B*H*S^2*d, halved for causal, up to the diagonal.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--mode", choices=["atomic", "deterministic"], default="atomic")
+    ap.add_argument("--workload", default="headline_2x32x4096_causal")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def prepare_inputs(w, device):
+    """Seeded Q, K, V, dO (bf16) plus O, LSE of the forward computed on the GPU in fp32."""
+    import torch
+    from attention_backward_fmha_amd import inputs as I
+
+    B, Hq, Hkv, Sq, Sk, dqk, dv = (w[k] for k in ("B", "Hq", "Hkv", "Sq", "Sk", "d_qk", "d_v"))
+    x = I.draw(w["seed"], [(B, Sq, Hq, dqk), (B, Sk, Hkv, dqk), (B, Sk, Hkv, dv), (B, Sq, Hq, dv)],
+               w["sigmas"])
+    dev = {n: torch.from_numpy(x[n]).to(torch.bfloat16).to(device) for n in x}
+    scale = 1.0 / math.sqrt(dqk)
+    o = torch.empty((B, Sq, Hq, dv), dtype=torch.bfloat16, device=device)
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=device)
+    grp = Hq // Hkv
+    mask = w["mask"]
+    wl, wr = w.get("window", (-1, -1))
+    delta = Sk - Sq if mask in (2, 3) else 0
+    left, right = (-1, -1) if mask == 0 else ((-1, 0) if mask in (1, 2) else (wl, wr))
+    i = torch.arange(Sq, device=device)[:, None]
+    j = torch.arange(Sk, device=device)[None, :]
+    allowed = torch.ones((Sq, Sk), dtype=torch.bool, device=device)
+    if left >= 0:
+        allowed &= j >= i + delta - left
+    if right >= 0:
+        allowed &= j <= i + delta + right
+    for b in range(B):
+        for h in range(Hq):
+            qf = dev["q"][b, :, h, :].float().contiguous()
+            kf = dev["k"][b, :, h // grp, :].float().contiguous()
+            vf = dev["v"][b, :, h // grp, :].float().contiguous()
+            s = (qf @ kf.t().contiguous()) * scale
+            s = s.masked_fill(~allowed, float("-inf"))
+            l = torch.logsumexp(s, dim=-1)
+            p = torch.exp(s - l[:, None])
+            p = torch.nan_to_num(p, nan=0.0)
+            o[b, :, h, :] = (p @ vf).to(torch.bfloat16)
+            lse[b, h, :] = l
+    torch.cuda.synchronize()
+    return dev["q"], dev["k"], dev["v"], o, lse, dev["do"], scale
+
+
+def cpu_baseline(w, budget_s):
+    """The fp64 oracle on the host cores, on a bounded sample of the workload: single
+    (batch, query head) problems of the same shape and mask, as many as fit the time budget."""
+    import oracle
+    from attention_backward_fmha_amd import inputs as I
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    Sq, Sk, dqk, dv = w["Sq"], w["Sk"], w["d_qk"], w["d_v"]
+    x = I.draw(w["seed"] + 100, [(1, Sq, 1, dqk), (1, Sk, 1, dqk), (1, Sk, 1, dv), (1, Sq, 1, dv)],
+               w["sigmas"])
+    wl, wr = w.get("window", (-1, -1))
+    pairs = int(oracle.allowed(w["mask"], wl, wr, Sq, Sk).sum())
+    flops_per = 2.0 * (3 * dqk + 2 * dv) * pairs
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.backward(x["q"], x["k"], x["v"], x["do"], scale=1.0 / math.sqrt(dqk),
+                        mask_type=w["mask"], window_left=wl, window_right=wr)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {
+        "value": flops_per * done / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": "%d of %d (batch, head) problems (Sq=%d, Sk=%d, d=%d, same mask), fp64 numpy, %.1f s"
+                  % (done, w["B"] * w["Hq"], Sq, Sk, dqk, dt),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (each GPU would run "
+              "its own share of heads/segments independently); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import attention_backward_fmha_amd as F
+    from attention_backward_fmha_amd import inputs as I
+
+    w = I.WORKLOADS[args.workload]
+    device = torch.device("cuda:0")
+    torch.cuda.set_device(device)
+    q, k, v, o, lse, do, scale = prepare_inputs(w, device)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    det = args.mode == "deterministic"
+    call = F.make_call(q, k, v, o, lse, do, dq, dk, dv, scale=scale, mask_type=w["mask"],
+                       window=w.get("window", (-1, -1)), deterministic=det)
+    plan = call.plan()
+    ws = torch.empty(call.workspace_size(), dtype=torch.uint8, device=device)
+    stream = torch.cuda.current_stream(device)
+    sh = stream.cuda_stream
+
+    def step(evs=None):
+        call.prepare(ws, sh)
+        call.run(ws, sh, F.STAGE_DOT)
+        if evs is not None:
+            evs[0].record(stream)
+        call.run(ws, sh, F.STAGE_MAIN)
+        if evs is not None:
+            evs[1].record(stream)
+        call.run(ws, sh, F.STAGE_REDUCE)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for s in range(args.steps):
+        step(kev[s])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    ms = total_ms / args.steps
+    main_ms = sum(a.elapsed_time(b) for a, b in kev) / args.steps
+    flops = plan.flops
+    tflops = flops / (ms * 1e-3) / 1e12
+    main_tflops = flops / (main_ms * 1e-3) / 1e12
+
+    out = {
+        "metric": "FMHA bwd TFLOP/s and % of bf16 MFMA peak, B*H*S*d=2*32*4096*128 causal",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload,
+            "B": w["B"], "Hq": w["Hq"], "Hkv": w["Hkv"], "Sq": w["Sq"], "Sk": w["Sk"],
+            "d_qk": w["d_qk"], "d_v": w["d_v"], "mask": w["mask"], "layout": "bshd",
+            "dq_accumulation": args.mode, "nsplits": plan.nsplits,
+            "flops_per_step": flops, "pct_of_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        },
+        "roofline": {
+            "kernel": "k_bwd_main",
+            "bound": "mfma",
+            "achieved": round(main_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(main_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "avg_launch_ms": round(main_ms, 4),
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()
