@@ -119,15 +119,58 @@ __global__ __launch_bounds__(256) void k_dot(const KParams p) {
 
 // ------------------------------------------------------------------------------------------
 // Stage 2: the main kernel.  256 threads = 4 waves; wave w owns keys 32w..32w+31 of the tile.
+// The (query head, query block) steps of a work item form one flat loop; while step n is being
+// computed, the global loads of step n+1 are in flight into registers and land in LDS after
+// the step's second barrier, so HBM latency hides behind the step's MFMA work.
 // ------------------------------------------------------------------------------------------
 template <int DQK, int DV>
+struct MainTile {
+  static constexpr int TM = 64;        // query rows per block
+  static constexpr int TN = 128;       // keys per tile
+  static constexpr int QS = DQK + 8;   // LDS row strides in elements (16-byte pad)
+  static constexpr int OS = DV + 8;
+  static constexpr int KS = DQK + 8;
+  static constexpr int SS = TM + 8;
+  static constexpr int QCH = TM * DQK / 8 / 256;  // 16-byte chunks of Q per thread
+  static constexpr int OCH = TM * DV / 8 / 256;   // 16-byte chunks of dO per thread
+};
+
+// P and dS of one step.  Result register r of row tile m holds query 32m + 8(r/4) + 4*hi + r%4
+// and this lane's key; P and dS come out already packed as bf16 MFMA operands.
+template <bool MASKED>
+__device__ __forceinline__ void probs_and_grads(const f32x16 (&s)[2], const f32x16 (&dp)[2],
+                                                const float* lse_lds, const float* dd_lds,
+                                                float scale_log2, int hi, int base_d, int lo_d,
+                                                int hi_d, int nq, bool key_ok,
+                                                bf16x8 (&pa)[2][2], bf16x8 (&sa)[2][2]) {
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int qr = 32 * m + 8 * c + 4 * hi;
+      const f32x4 l4 = *(const f32x4*)&lse_lds[qr];
+      const f32x4 d4 = *(const f32x4*)&dd_lds[qr];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * c + e;
+        float pv = __builtin_amdgcn_exp2f(s[m][r] * scale_log2 - l4[e]);
+        if (MASKED) {
+          const int dlt = base_d - (qr + e);
+          const bool ok = (dlt >= lo_d) & (dlt <= hi_d) & (qr + e < nq) & key_ok;
+          pv = ok ? pv : 0.f;
+        }
+        const float dsv = pv * (dp[m][r] - d4[e]);
+        pa[m][c >> 1][(c & 1) * 4 + e] = (__bf16)pv;
+        sa[m][c >> 1][(c & 1) * 4 + e] = (__bf16)dsv;
+      }
+    }
+  }
+}
+
+template <int DQK, int DV>
 __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
-  constexpr int TM = 64;   // query rows per block
-  constexpr int TN = 128;  // keys per tile
-  constexpr int QS = DQK + 8;  // LDS row strides in elements (16-byte pad)
-  constexpr int OS = DV + 8;
-  constexpr int KS = DQK + 8;
-  constexpr int SS = TM + 8;
+  using T = MainTile<DQK, DV>;
+  constexpr int TM = T::TM, TN = T::TN, QS = T::QS, OS = T::OS, KS = T::KS, SS = T::SS;
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[TN * KS];   // K_j, row-major
   __shared__ __attribute__((aligned(16))) uint16_t q_lds[TM * QS];   // Q_i
   __shared__ __attribute__((aligned(16))) uint16_t o_lds[TM * OS];   // dO_i
@@ -156,28 +199,33 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
   const MaskGeom mg = mask_geom(p.mask_type, p.window_left, p.window_right, sg.lq, sg.lk);
   int64_t qb_lo, qb_hi;
   qblocks_for_tile(mg, sg.lq, sg.lk, j, TM, TN, &qb_lo, &qb_hi);
+  const int nblk = qb_hi >= qb_lo ? (int)(qb_hi - qb_lo + 1) : 0;
+  const int nsteps = nblk * p.group_size;
   // allowed  <=>  lo_d <= key - row <= hi_d (and both inside the segment)
-  int64_t lo64 = mg.left >= 0 ? mg.delta - mg.left : INT64_MIN / 2;
-  int64_t hi64 = mg.right >= 0 ? mg.delta + mg.right : INT64_MAX / 2;
+  const int64_t lo64 = mg.left >= 0 ? mg.delta - mg.left : INT64_MIN / 2;
+  const int64_t hi64 = mg.right >= 0 ? mg.delta + mg.right : INT64_MAX / 2;
   const int lo_d = (int)max(lo64, (int64_t)INT32_MIN);
   const int hi_d = (int)min(hi64, (int64_t)INT32_MAX);
 
-  // This lane's key (B-operand column of S and dP) and the wave's K/V rows in registers.
+  // This lane's key (B-operand column of S and dP).  The K tile lives in LDS (it is the B
+  // operand of both S and dQ); the wave's V rows stay in registers.
   const int key_l = wave * 32 + l32;
-  bf16x8 kw[DQK / 16];
+  const bool key_ok = key_l < nk;
   bf16x8 vw[DV / 16];
   {
-    const bool ok = key_l < nk;
-    const int64_t krow = sg.k_row0 + key0 + key_l;
+    const int64_t krow = sg.k_row0 + key0 + (key_ok ? key_l : 0);
     const uint16_t* kp = p.k + elem_off(p.k_s, group, b, krow, g);
     const uint16_t* vp = p.v + elem_off(p.v_s, group, b, krow, g);
 #pragma unroll
     for (int kk = 0; kk < DQK / 16; ++kk) {
-      kw[kk] = ok ? *(const bf16x8*)(kp + 16 * kk + 8 * hi) : bf16x8{};
-      *(bf16x8*)&k_lds[key_l * KS + 16 * kk + 8 * hi] = kw[kk];
+      const bf16x8 x = *(const bf16x8*)(kp + 16 * kk + 8 * hi);
+      *(bf16x8*)&k_lds[key_l * KS + 16 * kk + 8 * hi] = key_ok ? x : bf16x8{};
     }
 #pragma unroll
-    for (int kk = 0; kk < DV / 16; ++kk) vw[kk] = ok ? *(const bf16x8*)(vp + 16 * kk + 8 * hi) : bf16x8{};
+    for (int kk = 0; kk < DV / 16; ++kk) {
+      const bf16x8 x = *(const bf16x8*)(vp + 16 * kk + 8 * hi);
+      vw[kk] = key_ok ? x : bf16x8{};
+    }
   }
 
   f32x16 dk_acc[DQK / 32];
@@ -190,160 +238,180 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
   const int tr_row = i16 >> 2;                        // row inside a 4-row transpose block
   const int tr_col = 16 * (g16 & 1) + 4 * (i16 & 3);  // column offset inside a 32-wide tile
 
-  for (int hh = 0; hh < p.group_size; ++hh) {
-    const int h = g * p.group_size + hh;
-    for (int64_t qb = qb_lo; qb <= qb_hi; ++qb) {
-      const int64_t q0 = qb * TM;
-      const int nq = (int)min((int64_t)TM, sg.lq - q0);
+  // ---- prefetch registers for one step: Q, dO rows (zero past the segment end), LSE, D ----
+  bf16x8 qpre[T::QCH];
+  bf16x8 opre[T::OCH];
+  float lpre = 0.f, dpre = 0.f;
+  auto load_step = [&](int n) {
+    const int h = g * p.group_size + n / nblk;
+    const int64_t q0 = (qb_lo + n % nblk) * TM;
+    const int nq = (int)min((int64_t)TM, sg.lq - q0);
+#pragma unroll
+    for (int u = 0; u < T::QCH; ++u) {
+      const int c = tid + 256 * u;
+      const int r = c / (DQK / 8);
+      const int c8 = c - r * (DQK / 8);
+      const int rr = r < nq ? r : nq - 1;
+      const bf16x8 x = *(const bf16x8*)(p.q + elem_off(p.q_s, group, b, sg.q_row0 + q0 + rr, h) + c8 * 8);
+      qpre[u] = r < nq ? x : bf16x8{};
+    }
+#pragma unroll
+    for (int u = 0; u < T::OCH; ++u) {
+      const int c = tid + 256 * u;
+      const int r = c / (DV / 8);
+      const int c8 = c - r * (DV / 8);
+      const int rr = r < nq ? r : nq - 1;
+      const bf16x8 x = *(const bf16x8*)(p.dout + elem_off(p.do_s, group, b, sg.q_row0 + q0 + rr, h) + c8 * 8);
+      opre[u] = r < nq ? x : bf16x8{};
+    }
+    if (tid < TM) {
+      const int rr = tid < nq ? tid : nq - 1;
+      const int64_t row = sg.q_row0 + q0 + rr;
+      const float l = p.lse[(group ? 0 : (int64_t)b * p.lse_s[0]) + (int64_t)h * p.lse_s[1] + row];
+      const float d = p.dsum[(int64_t)h * p.rows_q + sg.ws_row0 + q0 + rr];
+      lpre = tid < nq ? l * kLog2e : 0.f;
+      dpre = tid < nq ? d : 0.f;
+    }
+  };
+  auto store_step = [&]() {
+#pragma unroll
+    for (int u = 0; u < T::QCH; ++u) {
+      const int c = tid + 256 * u;
+      const int r = c / (DQK / 8);
+      *(bf16x8*)&q_lds[r * QS + (c - r * (DQK / 8)) * 8] = qpre[u];
+    }
+#pragma unroll
+    for (int u = 0; u < T::OCH; ++u) {
+      const int c = tid + 256 * u;
+      const int r = c / (DV / 8);
+      *(bf16x8*)&o_lds[r * OS + (c - r * (DV / 8)) * 8] = opre[u];
+    }
+    if (tid < TM) {
+      lse_lds[tid] = lpre;
+      dd_lds[tid] = dpre;
+    }
+  };
 
-      // ---- stage Q_i, dO_i, LSE_i, D_i in LDS (rows past the segment end are zero) ----
-      for (int c = tid; c < TM * DQK / 8; c += 256) {
-        const int r = c / (DQK / 8);
-        const int c8 = c - r * (DQK / 8);
-        bf16x8 val{};
-        if (r < nq) val = *(const bf16x8*)(p.q + elem_off(p.q_s, group, b, sg.q_row0 + q0 + r, h) + c8 * 8);
-        *(bf16x8*)&q_lds[r * QS + c8 * 8] = val;
-      }
-      for (int c = tid; c < TM * DV / 8; c += 256) {
-        const int r = c / (DV / 8);
-        const int c8 = c - r * (DV / 8);
-        bf16x8 val{};
-        if (r < nq) val = *(const bf16x8*)(p.dout + elem_off(p.do_s, group, b, sg.q_row0 + q0 + r, h) + c8 * 8);
-        *(bf16x8*)&o_lds[r * OS + c8 * 8] = val;
-      }
-      if (tid < TM) {
-        float l2 = 0.f, dd = 0.f;
-        if (tid < nq) {
-          const int64_t row = sg.q_row0 + q0 + tid;
-          const int64_t lo = (group ? 0 : (int64_t)b * p.lse_s[0]) + (int64_t)h * p.lse_s[1] + row;
-          l2 = p.lse[lo] * kLog2e;
-          dd = p.dsum[(int64_t)h * p.rows_q + sg.ws_row0 + q0 + tid];
-        }
-        lse_lds[tid] = l2;
-        dd_lds[tid] = dd;
-      }
-      __syncthreads();
+  if (nsteps > 0) {
+    load_step(0);
+    store_step();
+  }
 
-      // ---- S = Q_i K_w^T and dP = dO_i V_w^T (2 row tiles of 32 queries) ----
-      f32x16 s_acc[2] = {f32x16{}, f32x16{}};
-      f32x16 dp_acc[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-      for (int kk = 0; kk < DQK / 16; ++kk) {
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          const bf16x8 a = *(const bf16x8*)&q_lds[(32 * m + l32) * QS + 16 * kk + 8 * hi];
-          s_acc[m] = mfma(a, kw[kk], s_acc[m]);
-        }
-      }
-#pragma unroll
-      for (int kk = 0; kk < DV / 16; ++kk) {
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          const bf16x8 a = *(const bf16x8*)&o_lds[(32 * m + l32) * OS + 16 * kk + 8 * hi];
-          dp_acc[m] = mfma(a, vw[kk], dp_acc[m]);
-        }
-      }
+  for (int n = 0; n < nsteps; ++n) {
+    const int h = g * p.group_size + n / nblk;
+    const int64_t q0 = (qb_lo + n % nblk) * TM;
+    const int nq = (int)min((int64_t)TM, sg.lq - q0);
+    __syncthreads();  // LDS holds step n; every wave is done with step n-1's dS^T
+    if (n + 1 < nsteps) load_step(n + 1);
 
-      // ---- P, dS (fp32), rounded to bf16 as MFMA operands ----
-      // result register r of row tile m is query 32m + 8(r/4) + 4*hi + r%4, key key_l
-      const bool full = block_full(mg, sg.lq, sg.lk, q0, q0 + TM - 1, key0 + 32 * wave,
-                                   key0 + 32 * wave + 31);
-      const int base_d = (int)(key0 - q0) + key_l;
-      bf16x8 pa[2][2];
-      bf16x8 sa[2][2];
+    // ---- S = Q_i K_w^T and dP = dO_i V_w^T (2 row tiles of 32 queries) ----
+    f32x16 s_acc[2] = {f32x16{}, f32x16{}};
+    f32x16 dp_acc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int kk = 0; kk < DQK / 16; ++kk) {
+      const bf16x8 kb = *(const bf16x8*)&k_lds[key_l * KS + 16 * kk + 8 * hi];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const bf16x8 a = *(const bf16x8*)&q_lds[(32 * m + l32) * QS + 16 * kk + 8 * hi];
+        s_acc[m] = mfma(a, kb, s_acc[m]);
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < DV / 16; ++kk) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const bf16x8 a = *(const bf16x8*)&o_lds[(32 * m + l32) * OS + 16 * kk + 8 * hi];
+        dp_acc[m] = mfma(a, vw[kk], dp_acc[m]);
+      }
+    }
+
+    // ---- P, dS ----
+    const bool full = block_full(mg, sg.lq, sg.lk, q0, q0 + TM - 1, key0 + 32 * wave,
+                                 key0 + 32 * wave + 31);
+    const int base_d = (int)(key0 - q0) + key_l;
+    bf16x8 pa[2][2];
+    bf16x8 sa[2][2];
+    if (full) {
+      probs_and_grads<false>(s_acc, dp_acc, lse_lds, dd_lds, p.scale_log2, hi, base_d, lo_d, hi_d,
+                             nq, key_ok, pa, sa);
+    } else {
+      probs_and_grads<true>(s_acc, dp_acc, lse_lds, dd_lds, p.scale_log2, hi, base_d, lo_d, hi_d,
+                            nq, key_ok, pa, sa);
+    }
+
+    // ---- dV += P^T dO_i ; dK += dS^T Q_i  (reduction over the block's queries) ----
+    // slot s of lane half hi, step (m, t): query 32m + 16t + 8(s/4) + 4hi + s%4
+#pragma unroll
+    for (int n2 = 0; n2 < DV / 32; ++n2) {
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int qr = 32 * m + 8 * c + 4 * hi;
-          const f32x4 l4 = *(const f32x4*)&lse_lds[qr];
-          const f32x4 d4 = *(const f32x4*)&dd_lds[qr];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * c + e;
-            float pv = __builtin_amdgcn_exp2f(s_acc[m][r] * p.scale_log2 - l4[e]);
-            if (!full) {
-              const int dlt = base_d - (qr + e);
-              const bool ok = (dlt >= lo_d) && (dlt <= hi_d) && (qr + e < nq) && (key_l < nk);
-              pv = ok ? pv : 0.f;
-            }
-            const float dsv = pv * (dp_acc[m][r] - d4[e]);
-            pa[m][c >> 1][(c & 1) * 4 + e] = (__bf16)pv;
-            sa[m][c >> 1][(c & 1) * 4 + e] = (__bf16)dsv;
-          }
+        for (int t = 0; t < 2; ++t) {
+          const int kb = 32 * m + 16 * t + 4 * hi + tr_row;
+          const int col = 32 * n2 + tr_col;
+          const bf16x8 bo = tr_read(&o_lds[kb * OS + col], &o_lds[(kb + 8) * OS + col]);
+          dv_acc[n2] = mfma(pa[m][t], bo, dv_acc[n2]);
         }
       }
-
-      // ---- dV += P^T dO_i ; dK += dS^T Q_i  (reduction over the block's queries) ----
-      // slot s of lane half hi, step (m, t): query 32m + 16t + 8(s/4) + 4hi + s%4
+    }
 #pragma unroll
-      for (int n = 0; n < DV / 32; ++n) {
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const int kb = 32 * m + 16 * t + 4 * hi + tr_row;
-            const int col = 32 * n + tr_col;
-            const bf16x8 bo = tr_read(&o_lds[kb * OS + col], &o_lds[(kb + 8) * OS + col]);
-            dv_acc[n] = mfma(pa[m][t], bo, dv_acc[n]);
-          }
-        }
-      }
-#pragma unroll
-      for (int n = 0; n < DQK / 32; ++n) {
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const int kb = 32 * m + 16 * t + 4 * hi + tr_row;
-            const int col = 32 * n + tr_col;
-            const bf16x8 bq = tr_read(&q_lds[kb * QS + col], &q_lds[(kb + 8) * QS + col]);
-            dk_acc[n] = mfma(sa[m][t], bq, dk_acc[n]);
-          }
-        }
-      }
-
-      // ---- dS^T to LDS: 4 consecutive queries per 8-byte store ----
+    for (int n2 = 0; n2 < DQK / 32; ++n2) {
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const bf16x8 v = sa[m][c >> 1];
-          const bf16x4 v4 = (c & 1) ? __builtin_shufflevector(v, v, 4, 5, 6, 7)
-                                    : __builtin_shufflevector(v, v, 0, 1, 2, 3);
-          *(bf16x4*)&st_lds[key_l * SS + 32 * m + 8 * c + 4 * hi] = v4;
+        for (int t = 0; t < 2; ++t) {
+          const int kb = 32 * m + 16 * t + 4 * hi + tr_row;
+          const int col = 32 * n2 + tr_col;
+          const bf16x8 bq = tr_read(&q_lds[kb * QS + col], &q_lds[(kb + 8) * QS + col]);
+          dk_acc[n2] = mfma(sa[m][t], bq, dk_acc[n2]);
         }
       }
-      __syncthreads();
+    }
 
-      // ---- dQ_i partial = dS K_j  (reduction over the tile's 128 keys) ----
-      constexpr int NT = (TM / 32) * (DQK / 32);
-      for (int ti = wave; ti < NT; ti += 4) {
-        const int mq = ti / (DQK / 32);
-        const int nd = ti - mq * (DQK / 32);
-        f32x16 acc = f32x16{};
+    // ---- dS^T to LDS: 4 consecutive queries per 8-byte store ----
 #pragma unroll
-        for (int kk = 0; kk < TN / 16; ++kk) {
-          const int kb = 16 * kk + 8 * hi + tr_row;
-          const bf16x8 a = tr_read(&st_lds[kb * SS + 32 * mq + tr_col], &st_lds[(kb + 4) * SS + 32 * mq + tr_col]);
-          const bf16x8 bk = tr_read(&k_lds[kb * KS + 32 * nd + tr_col], &k_lds[(kb + 4) * KS + 32 * nd + tr_col]);
-          acc = mfma(a, bk, acc);
-        }
-        float* dst = p.dq_acc + (p.deterministic ? (int64_t)j * p.split_stride : 0) +
-                     (int64_t)h * p.head_stride + (sg.ws_row0 + q0) * DQK + 32 * nd + l32;
+    for (int m = 0; m < 2; ++m) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int ql = 32 * mq + 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (ql < nq) {
-            if (p.deterministic) {
-              dst[(int64_t)ql * DQK] = acc[r];
-            } else {
-              unsafeAtomicAdd(&dst[(int64_t)ql * DQK], acc[r]);
-            }
+      for (int c = 0; c < 4; ++c) {
+        const bf16x8 v = sa[m][c >> 1];
+        const bf16x4 v4 = (c & 1) ? __builtin_shufflevector(v, v, 4, 5, 6, 7)
+                                  : __builtin_shufflevector(v, v, 0, 1, 2, 3);
+        *(bf16x4*)&st_lds[key_l * SS + 32 * m + 8 * c + 4 * hi] = v4;
+      }
+    }
+    __syncthreads();  // dS^T complete; every wave is done reading Q_i, dO_i
+
+    // ---- dQ_i partial = dS K_j  (reduction over the tile's 128 keys) ----
+    constexpr int NT = (TM / 32) * (DQK / 32);
+    float* dst_base = p.dq_acc + (p.deterministic ? (int64_t)j * p.split_stride : 0) +
+                      (int64_t)h * p.head_stride + (sg.ws_row0 + q0) * DQK + l32;
+#pragma unroll
+    for (int tt = 0; tt < NT / 4; ++tt) {
+      const int ti = wave + 4 * tt;
+      const int mq = ti / (DQK / 32);
+      const int nd = ti - mq * (DQK / 32);
+      f32x16 acc = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < TN / 16; ++kk) {
+        const int kb = 16 * kk + 8 * hi + tr_row;
+        const bf16x8 a = tr_read(&st_lds[kb * SS + 32 * mq + tr_col], &st_lds[(kb + 4) * SS + 32 * mq + tr_col]);
+        const bf16x8 bk = tr_read(&k_lds[kb * KS + 32 * nd + tr_col], &k_lds[(kb + 4) * KS + 32 * nd + tr_col]);
+        acc = mfma(a, bk, acc);
+      }
+      float* dst = dst_base + 32 * nd;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int ql = 32 * mq + 8 * (r >> 2) + 4 * hi + (r & 3);
+        if (ql < nq) {
+          if (p.deterministic) {
+            dst[(int64_t)ql * DQK] = acc[r];
+          } else {
+            unsafeAtomicAdd(&dst[(int64_t)ql * DQK], acc[r]);
           }
         }
       }
     }
+    if (n + 1 < nsteps) store_step();  // Q_i, dO_i, LSE, D are dead: stage step n+1
   }
 
   // ---- epilogue: dK = scale * dK_acc, dV = dV_acc as bf16 ----
