@@ -119,21 +119,38 @@ __global__ __launch_bounds__(256) void k_dot(const KParams p) {
 
 // ------------------------------------------------------------------------------------------
 // Stage 2: the main kernel.  256 threads = 4 waves; wave w owns keys 32w..32w+31 of the tile.
-// The (query head, query block) steps of a work item form one flat loop; while step n is being
-// computed, the global loads of step n+1 are in flight into registers and land in LDS after
-// the step's second barrier, so HBM latency hides behind the step's MFMA work.
+//
+// The (query head, query block) steps of a work item form one flat loop.  While step n is
+// computed, the global loads of step n+1 are in flight into registers; after the step's second
+// barrier they are written to LDS twice: row-major (the A operand of S and dP) and transposed
+// with the block's queries along the row (the B operand of dV and dK).  The transposed copies
+// store queries in the order the P/dS result registers feed the reduction slots, so every
+// operand of S, dP, dV and dK is a plain 16-byte LDS read.  LDS measurements on gfx950 put
+// 16-byte reads at ~121 B/clk per CU and every 8-byte access (transposing reads included) at
+// ~40 B/clk, hence the copies.
 // ------------------------------------------------------------------------------------------
 template <int DQK, int DV>
 struct MainTile {
   static constexpr int TM = 64;        // query rows per block
   static constexpr int TN = 128;       // keys per tile
-  static constexpr int QS = DQK + 8;   // LDS row strides in elements (16-byte pad)
+  static constexpr int QS = DQK + 8;   // row-major strides in elements (16-byte pad)
   static constexpr int OS = DV + 8;
   static constexpr int KS = DQK + 8;
-  static constexpr int SS = TM + 8;
-  static constexpr int QCH = TM * DQK / 8 / 256;  // 16-byte chunks of Q per thread
-  static constexpr int OCH = TM * DV / 8 / 256;   // 16-byte chunks of dO per thread
+  static constexpr int SS = TM + 8;    // dS^T rows (one per key)
+  static constexpr int TS = TM + 8;    // transposed copies: one row per head-dim column
+  static constexpr int QBLK = (TM / 4) * (DQK / 8);  // 4x8 staging blocks of Q
+  static constexpr int OBLK = (TM / 4) * (DV / 8);
+  static constexpr int QU = (QBLK + 255) / 256;      // blocks per thread
+  static constexpr int OU = (OBLK + 255) / 256;
+  static constexpr bool KT_REGS = (DQK == 64 || DQK == 128);  // dQ's K operand in registers
 };
+
+// Position of query q (0 <= q < TM) inside a transposed row: bits 2 and 3 of q swapped, so
+// that slots 0..7 of lane half h in reduction step ks are the 8 consecutive positions
+// 16ks + 8h .. 16ks + 8h + 7.
+__device__ __forceinline__ int tpos(int q) {
+  return (q & ~12) | ((q & 4) << 1) | ((q & 8) >> 1);
+}
 
 // P and dS of one step.  Result register r of row tile m holds query 32m + 8(r/4) + 4*hi + r%4
 // and this lane's key; P and dS come out already packed as bf16 MFMA operands.
@@ -167,16 +184,42 @@ __device__ __forceinline__ void probs_and_grads(const f32x16 (&s)[2], const f32x
   }
 }
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// Write a 4-query x 8-column block (rows r0..r0+3 of `x`, column chunk c8) into a row-major
+// tile and into the transposed copy.
+template <int RS, int TSS>
+__device__ __forceinline__ void stage_block(uint16_t* rm, uint16_t* tr, const u32x4 (&x)[4],
+                                            int r0, int c8) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) *(u32x4*)&rm[(r0 + u) * RS + c8 * 8] = x[u];
+  const int pos = tpos(r0);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    // columns 2k (low halves) and 2k+1 (high halves) of the 4 rows
+    const unsigned lo01 = __builtin_amdgcn_perm(x[1][k], x[0][k], 0x05040100u);
+    const unsigned lo23 = __builtin_amdgcn_perm(x[3][k], x[2][k], 0x05040100u);
+    const unsigned hi01 = __builtin_amdgcn_perm(x[1][k], x[0][k], 0x07060302u);
+    const unsigned hi23 = __builtin_amdgcn_perm(x[3][k], x[2][k], 0x07060302u);
+    *(u32x2*)&tr[(c8 * 8 + 2 * k) * TSS + pos] = u32x2{lo01, lo23};
+    *(u32x2*)&tr[(c8 * 8 + 2 * k + 1) * TSS + pos] = u32x2{hi01, hi23};
+  }
+}
+
 template <int DQK, int DV>
 __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
   using T = MainTile<DQK, DV>;
-  constexpr int TM = T::TM, TN = T::TN, QS = T::QS, OS = T::OS, KS = T::KS, SS = T::SS;
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[TN * KS];   // K_j, row-major
-  __shared__ __attribute__((aligned(16))) uint16_t q_lds[TM * QS];   // Q_i
-  __shared__ __attribute__((aligned(16))) uint16_t o_lds[TM * OS];   // dO_i
-  __shared__ __attribute__((aligned(16))) uint16_t st_lds[TN * SS];  // dS^T (key-major)
-  __shared__ __attribute__((aligned(16))) float lse_lds[TM];        // LSE_i * log2(e)
-  __shared__ __attribute__((aligned(16))) float dd_lds[TM];         // D_i
+  constexpr int TM = T::TM, TN = T::TN, QS = T::QS, OS = T::OS, KS = T::KS, SS = T::SS,
+                TS = T::TS;
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[TN * KS];    // K_j, row-major
+  __shared__ __attribute__((aligned(16))) uint16_t q_lds[TM * QS];    // Q_i, row-major
+  __shared__ __attribute__((aligned(16))) uint16_t o_lds[TM * OS];    // dO_i, row-major
+  __shared__ __attribute__((aligned(16))) uint16_t qt_lds[DQK * TS];  // Q_i transposed
+  __shared__ __attribute__((aligned(16))) uint16_t ot_lds[DV * TS];   // dO_i transposed
+  __shared__ __attribute__((aligned(16))) uint16_t st_lds[TN * SS];   // dS^T (key-major)
+  __shared__ __attribute__((aligned(16))) float lse_lds[TM];         // LSE_i * log2(e)
+  __shared__ __attribute__((aligned(16))) float dd_lds[TM];          // D_i
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -207,8 +250,10 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
   const int lo_d = (int)max(lo64, (int64_t)INT32_MIN);
   const int hi_d = (int)min(hi64, (int64_t)INT32_MAX);
 
-  // This lane's key (B-operand column of S and dP).  The K tile lives in LDS (it is the B
-  // operand of both S and dQ); the wave's V rows stay in registers.
+  const int tr_row = i16 >> 2;                        // row inside a 4-row transpose block
+  const int tr_col = 16 * (g16 & 1) + 4 * (i16 & 3);  // column offset inside a 32-wide tile
+
+  // K tile -> LDS (row-major); the wave's V rows -> registers (B operand of dP).
   const int key_l = wave * 32 + l32;
   const bool key_ok = key_l < nk;
   bf16x8 vw[DV / 16];
@@ -227,6 +272,21 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
       vw[kk] = key_ok ? x : bf16x8{};
     }
   }
+  __syncthreads();
+
+  // dQ work of this wave: tiles ti = wave + 4*tt of the (TM/32) x (DQK/32) grid.  With
+  // KT_REGS, every tile of the wave uses the same 32 head-dim columns, whose K operand
+  // (reduction over the tile's keys) is read once here.
+  constexpr int NT = (TM / 32) * (DQK / 32);
+  bf16x8 kt[T::KT_REGS ? TN / 16 : 1];
+  if (T::KT_REGS) {
+    const int nd = wave % (DQK / 32);
+#pragma unroll
+    for (int kk = 0; kk < TN / 16; ++kk) {
+      const int kb = 16 * kk + 8 * hi + tr_row;
+      kt[kk] = tr_read(&k_lds[kb * KS + 32 * nd + tr_col], &k_lds[(kb + 4) * KS + 32 * nd + tr_col]);
+    }
+  }
 
   f32x16 dk_acc[DQK / 32];
   f32x16 dv_acc[DV / 32];
@@ -235,34 +295,44 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
 #pragma unroll
   for (int n = 0; n < DV / 32; ++n) dv_acc[n] = f32x16{};
 
-  const int tr_row = i16 >> 2;                        // row inside a 4-row transpose block
-  const int tr_col = 16 * (g16 & 1) + 4 * (i16 & 3);  // column offset inside a 32-wide tile
-
-  // ---- prefetch registers for one step: Q, dO rows (zero past the segment end), LSE, D ----
-  bf16x8 qpre[T::QCH];
-  bf16x8 opre[T::OCH];
+  // ---- prefetch registers for one step: 4-row x 8-column blocks of Q and dO, LSE, D ----
+  // block id = tid + 256u; query group qg = id % 16 (rows 4qg..4qg+3), column chunk id / 16
+  u32x4 qpre[T::QU][4];
+  u32x4 opre[T::OU][4];
   float lpre = 0.f, dpre = 0.f;
   auto load_step = [&](int n) {
     const int h = g * p.group_size + n / nblk;
     const int64_t q0 = (qb_lo + n % nblk) * TM;
     const int nq = (int)min((int64_t)TM, sg.lq - q0);
 #pragma unroll
-    for (int u = 0; u < T::QCH; ++u) {
-      const int c = tid + 256 * u;
-      const int r = c / (DQK / 8);
-      const int c8 = c - r * (DQK / 8);
-      const int rr = r < nq ? r : nq - 1;
-      const bf16x8 x = *(const bf16x8*)(p.q + elem_off(p.q_s, group, b, sg.q_row0 + q0 + rr, h) + c8 * 8);
-      qpre[u] = r < nq ? x : bf16x8{};
+    for (int v = 0; v < T::QU; ++v) {
+      const int id = tid + 256 * v;
+      const int r0 = 4 * (id & 15);
+      const int c8 = id >> 4;
+      if (T::QBLK % 256 == 0 || id < T::QBLK) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r = r0 + u;
+          const int rr = r < nq ? r : nq - 1;
+          const u32x4 x = *(const u32x4*)(p.q + elem_off(p.q_s, group, b, sg.q_row0 + q0 + rr, h) + c8 * 8);
+          qpre[v][u] = r < nq ? x : u32x4{0u, 0u, 0u, 0u};
+        }
+      }
     }
 #pragma unroll
-    for (int u = 0; u < T::OCH; ++u) {
-      const int c = tid + 256 * u;
-      const int r = c / (DV / 8);
-      const int c8 = c - r * (DV / 8);
-      const int rr = r < nq ? r : nq - 1;
-      const bf16x8 x = *(const bf16x8*)(p.dout + elem_off(p.do_s, group, b, sg.q_row0 + q0 + rr, h) + c8 * 8);
-      opre[u] = r < nq ? x : bf16x8{};
+    for (int v = 0; v < T::OU; ++v) {
+      const int id = tid + 256 * v;
+      const int r0 = 4 * (id & 15);
+      const int c8 = id >> 4;
+      if (T::OBLK % 256 == 0 || id < T::OBLK) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r = r0 + u;
+          const int rr = r < nq ? r : nq - 1;
+          const u32x4 x = *(const u32x4*)(p.dout + elem_off(p.do_s, group, b, sg.q_row0 + q0 + rr, h) + c8 * 8);
+          opre[v][u] = r < nq ? x : u32x4{0u, 0u, 0u, 0u};
+        }
+      }
     }
     if (tid < TM) {
       const int rr = tid < nq ? tid : nq - 1;
@@ -275,16 +345,16 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
   };
   auto store_step = [&]() {
 #pragma unroll
-    for (int u = 0; u < T::QCH; ++u) {
-      const int c = tid + 256 * u;
-      const int r = c / (DQK / 8);
-      *(bf16x8*)&q_lds[r * QS + (c - r * (DQK / 8)) * 8] = qpre[u];
+    for (int v = 0; v < T::QU; ++v) {
+      const int id = tid + 256 * v;
+      if (T::QBLK % 256 == 0 || id < T::QBLK)
+        stage_block<QS, TS>(q_lds, qt_lds, qpre[v], 4 * (id & 15), id >> 4);
     }
 #pragma unroll
-    for (int u = 0; u < T::OCH; ++u) {
-      const int c = tid + 256 * u;
-      const int r = c / (DV / 8);
-      *(bf16x8*)&o_lds[r * OS + (c - r * (DV / 8)) * 8] = opre[u];
+    for (int v = 0; v < T::OU; ++v) {
+      const int id = tid + 256 * v;
+      if (T::OBLK % 256 == 0 || id < T::OBLK)
+        stage_block<OS, TS>(o_lds, ot_lds, opre[v], 4 * (id & 15), id >> 4);
     }
     if (tid < TM) {
       lse_lds[tid] = lpre;
@@ -340,31 +410,21 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
     }
 
     // ---- dV += P^T dO_i ; dK += dS^T Q_i  (reduction over the block's queries) ----
-    // slot s of lane half hi, step (m, t): query 32m + 16t + 8(s/4) + 4hi + s%4
+    // step ks = 2m + t covers transposed positions 16ks .. 16ks + 15
 #pragma unroll
     for (int n2 = 0; n2 < DV / 32; ++n2) {
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int kb = 32 * m + 16 * t + 4 * hi + tr_row;
-          const int col = 32 * n2 + tr_col;
-          const bf16x8 bo = tr_read(&o_lds[kb * OS + col], &o_lds[(kb + 8) * OS + col]);
-          dv_acc[n2] = mfma(pa[m][t], bo, dv_acc[n2]);
-        }
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 bo = *(const bf16x8*)&ot_lds[(32 * n2 + l32) * TS + 16 * ks + 8 * hi];
+        dv_acc[n2] = mfma(pa[ks >> 1][ks & 1], bo, dv_acc[n2]);
       }
     }
 #pragma unroll
     for (int n2 = 0; n2 < DQK / 32; ++n2) {
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int kb = 32 * m + 16 * t + 4 * hi + tr_row;
-          const int col = 32 * n2 + tr_col;
-          const bf16x8 bq = tr_read(&q_lds[kb * QS + col], &q_lds[(kb + 8) * QS + col]);
-          dk_acc[n2] = mfma(sa[m][t], bq, dk_acc[n2]);
-        }
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 bq = *(const bf16x8*)&qt_lds[(32 * n2 + l32) * TS + 16 * ks + 8 * hi];
+        dk_acc[n2] = mfma(sa[ks >> 1][ks & 1], bq, dk_acc[n2]);
       }
     }
 
@@ -379,12 +439,11 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
         *(bf16x4*)&st_lds[key_l * SS + 32 * m + 8 * c + 4 * hi] = v4;
       }
     }
-    __syncthreads();  // dS^T complete; every wave is done reading Q_i, dO_i
+    __syncthreads();  // dS^T complete; every wave is done reading this step's Q, dO tiles
 
     // ---- dQ_i partial = dS K_j  (reduction over the tile's 128 keys) ----
-    constexpr int NT = (TM / 32) * (DQK / 32);
     float* dst_base = p.dq_acc + (p.deterministic ? (int64_t)j * p.split_stride : 0) +
-                      (int64_t)h * p.head_stride + (sg.ws_row0 + q0) * DQK + l32;
+                      (int64_t)h * p.head_stride + (sg.ws_row0 + q0) * DQK;
 #pragma unroll
     for (int tt = 0; tt < NT / 4; ++tt) {
       const int ti = wave + 4 * tt;
@@ -395,23 +454,39 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
       for (int kk = 0; kk < TN / 16; ++kk) {
         const int kb = 16 * kk + 8 * hi + tr_row;
         const bf16x8 a = tr_read(&st_lds[kb * SS + 32 * mq + tr_col], &st_lds[(kb + 4) * SS + 32 * mq + tr_col]);
-        const bf16x8 bk = tr_read(&k_lds[kb * KS + 32 * nd + tr_col], &k_lds[(kb + 4) * KS + 32 * nd + tr_col]);
+        bf16x8 bk;
+        if (T::KT_REGS) {
+          bk = kt[kk];
+        } else {
+          bk = tr_read(&k_lds[kb * KS + 32 * nd + tr_col], &k_lds[(kb + 4) * KS + 32 * nd + tr_col]);
+        }
         acc = mfma(a, bk, acc);
       }
-      float* dst = dst_base + 32 * nd;
+      // result register r: query 32mq + 8(r/4) + 4hi + r%4, column 32nd + l32
+      const int off0 = (32 * mq + 4 * hi) * DQK + 32 * nd + l32;
+      if (nq == TM) {
+        if (p.deterministic) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int ql = 32 * mq + 8 * (r >> 2) + 4 * hi + (r & 3);
-        if (ql < nq) {
-          if (p.deterministic) {
-            dst[(int64_t)ql * DQK] = acc[r];
-          } else {
-            unsafeAtomicAdd(&dst[(int64_t)ql * DQK], acc[r]);
+          for (int r = 0; r < 16; ++r) dst_base[off0 + (8 * (r >> 2) + (r & 3)) * DQK] = acc[r];
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) unsafeAtomicAdd(&dst_base[off0 + (8 * (r >> 2) + (r & 3)) * DQK], acc[r]);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int ql = 32 * mq + 8 * (r >> 2) + 4 * hi + (r & 3);
+          if (ql < nq) {
+            if (p.deterministic) {
+              dst_base[off0 + (8 * (r >> 2) + (r & 3)) * DQK] = acc[r];
+            } else {
+              unsafeAtomicAdd(&dst_base[off0 + (8 * (r >> 2) + (r & 3)) * DQK], acc[r]);
+            }
           }
         }
       }
     }
-    if (n + 1 < nsteps) store_step();  // Q_i, dO_i, LSE, D are dead: stage step n+1
+    if (n + 1 < nsteps) store_step();  // this step's tiles are dead: stage step n+1
   }
 
   // ---- epilogue: dK = scale * dK_acc, dV = dV_acc as bf16 ----

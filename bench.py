@@ -41,7 +41,22 @@ def parse():
     ap.add_argument("--workload", default="headline_2x32x4096_causal")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB (steps times), "
+                         "the reference kernel for scaling HBM byte counters")
     return ap.parse_args()
+
+
+def copy_probe(mib, steps):
+    import torch
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_mib": mib, "bytes_read_per_copy": n * 4,
+                      "bytes_written_per_copy": n * 4, "copies": steps}))
 
 
 def prepare_inputs(w, device):
@@ -125,6 +140,9 @@ def main():
         print("bench.py measures one GPU: this build has no multi-GPU path (each GPU would run "
               "its own share of heads/segments independently); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib, args.steps)
+        return
     import torch
     import attention_backward_fmha_amd as F
     from attention_backward_fmha_amd import inputs as I
