@@ -51,6 +51,7 @@ fmha::KParams make_params(const fmha_bwd_args* a, const fmha::Plan& p, void* ws)
   k.dk = (uint16_t*)a->dk;
   k.dv = (uint16_t*)a->dv;
   k.dsum = (float*)((char*)ws + p.d_offset);
+  k.lse2 = (float*)((char*)ws + p.lse2_offset);
   k.dq_acc = (float*)((char*)ws + p.dq_acc_offset);
   k.seqstart_q = p.group_mode ? a->seqstart_q_dev : nullptr;
   k.seqstart_k = p.group_mode ? a->seqstart_k_dev : nullptr;

@@ -20,6 +20,7 @@ struct KParams {
   uint16_t* dk;
   uint16_t* dv;
   float* dsum;    // workspace: D = rowsum(dO * O), [Hq][rows_q]
+  float* lse2;    // workspace: LSE * log2(e), [Hq][rows_q]
   float* dq_acc;  // workspace: fp32 dQ partials, [nsplits][Hq][rows_q][d_qk]
   const int32_t* seqstart_q;  // device offsets, null in batch mode
   const int32_t* seqstart_k;

@@ -1,6 +1,6 @@
 // kernels.hip -- the three device stages of the attention backward on gfx950 (CDNA4).
 //
-// Stage 1 (k_dot):     D[h][row] = sum_c dO[row,h,c] * O[row,h,c]                 HBM bound
+// Stage 1 (k_dot):     D[h][row] = sum_c dO[row,h,c] * O[row,h,c] and LSE*log2(e)  HBM bound
 // Stage 2 (k_bwd_main): one work item per (segment b, K/V head g, key tile j):
 //     for every query head h of g's group and every query block i the mask lets tile j see:
 //       S = Q_i K_j^T, P = exp(scale*S - LSE_i) (0 where masked), dP = dO_i V_j^T,
@@ -96,6 +96,7 @@ __global__ __launch_bounds__(256) void k_dot(const KParams p) {
   const bool group = p.seqstart_q != nullptr;
   const bool valid = r < p.rows_q * p.Hq;
   float acc = 0.f;
+  float l2 = 0.f;
   int64_t row = 0;
   int h = 0;
   if (valid) {
@@ -107,6 +108,8 @@ __global__ __launch_bounds__(256) void k_dot(const KParams p) {
       b = (int)(row / p.Sq);
       trow = row - (int64_t)b * p.Sq;
     }
+    if (c8 == 0)
+      l2 = p.lse[(group ? 0 : (int64_t)b * p.lse_s[0]) + (int64_t)h * p.lse_s[1] + trow] * kLog2e;
     const bf16x8 a = *(const bf16x8*)(p.dout + elem_off(p.do_s, group, b, trow, h) + c8 * 8);
     const bf16x8 o = *(const bf16x8*)(p.o + elem_off(p.o_s, group, b, trow, h) + c8 * 8);
 #pragma unroll
@@ -114,7 +117,10 @@ __global__ __launch_bounds__(256) void k_dot(const KParams p) {
   }
 #pragma unroll
   for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, LPR);
-  if (valid && c8 == 0) p.dsum[(int64_t)h * p.rows_q + row] = acc;
+  if (valid && c8 == 0) {
+    p.dsum[(int64_t)h * p.rows_q + row] = acc;
+    p.lse2[(int64_t)h * p.rows_q + row] = l2;
+  }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -129,9 +135,10 @@ __global__ __launch_bounds__(256) void k_dot(const KParams p) {
 // 16-byte reads at ~121 B/clk per CU and every 8-byte access (transposing reads included) at
 // ~40 B/clk, hence the copies.
 // ------------------------------------------------------------------------------------------
-template <int DQK, int DV>
+template <int DQK, int DV, int TM_>
 struct MainTile {
-  static constexpr int TM = 64;        // query rows per block
+  static constexpr int TM = TM_;       // query rows per block (32 or 64)
+  static constexpr int MT = TM / 32;   // 32-row MFMA tiles per block
   static constexpr int TN = 128;       // keys per tile
   static constexpr int QS = DQK + 8;   // row-major strides in elements (16-byte pad)
   static constexpr int OS = DV + 8;
@@ -139,10 +146,13 @@ struct MainTile {
   static constexpr int SS = TM + 8;    // dS^T rows (one per key)
   static constexpr int TS = TM + 8;    // transposed copies: one row per head-dim column
   static constexpr int QBLK = (TM / 4) * (DQK / 8);  // 4x8 staging blocks of Q
-  static constexpr int OBLK = (TM / 4) * (DV / 8);
-  static constexpr int QU = (QBLK + 255) / 256;      // blocks per thread
-  static constexpr int OU = (OBLK + 255) / 256;
-  static constexpr bool KT_REGS = (DQK == 64 || DQK == 128);  // dQ's K operand in registers
+  static constexpr int OBLK = (TM / 4) * (DV / 8);   // ... of dO (ids after Q's)
+  static constexpr int NV = (QBLK + OBLK + 255) / 256;  // blocks per thread
+  static constexpr int NT = MT * (DQK / 32);            // 32x32 tiles of a dQ block
+  static constexpr int NTW = (NT + 3) / 4;              // dQ tiles per wave
+  // every dQ tile of a wave uses the same 32 head-dim columns: their K operand is kept in
+  // registers for the whole work item
+  static constexpr bool KT_REGS = (DQK / 32) % 4 == 0 || NT <= 4;
 };
 
 // Position of query q (0 <= q < TM) inside a transposed row: bits 2 and 3 of q swapped, so
@@ -154,14 +164,14 @@ __device__ __forceinline__ int tpos(int q) {
 
 // P and dS of one step.  Result register r of row tile m holds query 32m + 8(r/4) + 4*hi + r%4
 // and this lane's key; P and dS come out already packed as bf16 MFMA operands.
-template <bool MASKED>
-__device__ __forceinline__ void probs_and_grads(const f32x16 (&s)[2], const f32x16 (&dp)[2],
+template <bool MASKED, int MT>
+__device__ __forceinline__ void probs_and_grads(const f32x16 (&s)[MT], const f32x16 (&dp)[MT],
                                                 const float* lse_lds, const float* dd_lds,
                                                 float scale_log2, int hi, int base_d, int lo_d,
                                                 int hi_d, int nq, bool key_ok,
-                                                bf16x8 (&pa)[2][2], bf16x8 (&sa)[2][2]) {
+                                                bf16x8 (&pa)[MT][2], bf16x8 (&sa)[MT][2]) {
 #pragma unroll
-  for (int m = 0; m < 2; ++m) {
+  for (int m = 0; m < MT; ++m) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int qr = 32 * m + 8 * c + 4 * hi;
@@ -207,11 +217,11 @@ __device__ __forceinline__ void stage_block(uint16_t* rm, uint16_t* tr, const u3
   }
 }
 
-template <int DQK, int DV>
+template <int DQK, int DV, int TM_>
 __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
-  using T = MainTile<DQK, DV>;
-  constexpr int TM = T::TM, TN = T::TN, QS = T::QS, OS = T::OS, KS = T::KS, SS = T::SS,
-                TS = T::TS;
+  using T = MainTile<DQK, DV, TM_>;
+  constexpr int TM = T::TM, MT = T::MT, TN = T::TN, QS = T::QS, OS = T::OS, KS = T::KS,
+                SS = T::SS, TS = T::TS, NT = T::NT;
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[TN * KS];    // K_j, row-major
   __shared__ __attribute__((aligned(16))) uint16_t q_lds[TM * QS];    // Q_i, row-major
   __shared__ __attribute__((aligned(16))) uint16_t o_lds[TM * OS];    // dO_i, row-major
@@ -274,10 +284,8 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
   }
   __syncthreads();
 
-  // dQ work of this wave: tiles ti = wave + 4*tt of the (TM/32) x (DQK/32) grid.  With
-  // KT_REGS, every tile of the wave uses the same 32 head-dim columns, whose K operand
-  // (reduction over the tile's keys) is read once here.
-  constexpr int NT = (TM / 32) * (DQK / 32);
+  // dQ work of this wave: tiles ti = wave + 4*tt (tt < NTW) of the MT x (DQK/32) grid.  With
+  // KT_REGS the wave's K operand (its 32 head-dim columns over the tile's keys) is read once.
   bf16x8 kt[T::KT_REGS ? TN / 16 : 1];
   if (T::KT_REGS) {
     const int nd = wave % (DQK / 32);
@@ -295,66 +303,65 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
 #pragma unroll
   for (int n = 0; n < DV / 32; ++n) dv_acc[n] = f32x16{};
 
-  // ---- prefetch registers for one step: 4-row x 8-column blocks of Q and dO, LSE, D ----
-  // block id = tid + 256u; query group qg = id % 16 (rows 4qg..4qg+3), column chunk id / 16
-  u32x4 qpre[T::QU][4];
-  u32x4 opre[T::OU][4];
+  // ---- prefetch registers for one step: 4-row x 8-column blocks of Q and dO, LSE2, D ----
+  // Block ids tid + 256v: ids below QBLK are Q blocks, the next OBLK are dO blocks; block id
+  // covers rows 4*(id % (TM/4)) .. +3 and column chunk id / (TM/4).  The loads land in
+  // registers untouched (rows past the segment end re-read its last row); zeroing happens
+  // when the registers are written to LDS, so nothing waits for them until then.  Offsets
+  // inside a block are 32-bit (the plan bounds the sequence strides).
+  u32x4 pre[T::NV][4];
   float lpre = 0.f, dpre = 0.f;
+  const int qs1 = (int)p.q_s[1];
+  const int os1 = (int)p.do_s[1];
   auto load_step = [&](int n) {
     const int h = g * p.group_size + n / nblk;
     const int64_t q0 = (qb_lo + n % nblk) * TM;
     const int nq = (int)min((int64_t)TM, sg.lq - q0);
+    const uint16_t* qb = p.q + elem_off(p.q_s, group, b, sg.q_row0 + q0, h);
+    const uint16_t* ob = p.dout + elem_off(p.do_s, group, b, sg.q_row0 + q0, h);
 #pragma unroll
-    for (int v = 0; v < T::QU; ++v) {
-      const int id = tid + 256 * v;
-      const int r0 = 4 * (id & 15);
-      const int c8 = id >> 4;
-      if (T::QBLK % 256 == 0 || id < T::QBLK) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int r = r0 + u;
-          const int rr = r < nq ? r : nq - 1;
-          const u32x4 x = *(const u32x4*)(p.q + elem_off(p.q_s, group, b, sg.q_row0 + q0 + rr, h) + c8 * 8);
-          qpre[v][u] = r < nq ? x : u32x4{0u, 0u, 0u, 0u};
-        }
-      }
-    }
-#pragma unroll
-    for (int v = 0; v < T::OU; ++v) {
-      const int id = tid + 256 * v;
-      const int r0 = 4 * (id & 15);
-      const int c8 = id >> 4;
-      if (T::OBLK % 256 == 0 || id < T::OBLK) {
+    for (int v = 0; v < T::NV; ++v) {
+      const int id0 = tid + 256 * v;
+      if ((T::QBLK + T::OBLK) % 256 == 0 || id0 < T::QBLK + T::OBLK) {
+        const bool isq = id0 < T::QBLK;
+        const int id = isq ? id0 : id0 - T::QBLK;
+        const int r0 = 4 * (id % (TM / 4));
+        const int c8 = id / (TM / 4);
+        const uint16_t* base = isq ? qb : ob;
+        const int s1 = isq ? qs1 : os1;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const int r = r0 + u;
-          const int rr = r < nq ? r : nq - 1;
-          const u32x4 x = *(const u32x4*)(p.dout + elem_off(p.do_s, group, b, sg.q_row0 + q0 + rr, h) + c8 * 8);
-          opre[v][u] = r < nq ? x : u32x4{0u, 0u, 0u, 0u};
+          const int rr = min(r0 + u, nq - 1);
+          pre[v][u] = *(const u32x4*)(base + (rr * s1 + c8 * 8));
         }
       }
     }
     if (tid < TM) {
-      const int rr = tid < nq ? tid : nq - 1;
-      const int64_t row = sg.q_row0 + q0 + rr;
-      const float l = p.lse[(group ? 0 : (int64_t)b * p.lse_s[0]) + (int64_t)h * p.lse_s[1] + row];
-      const float d = p.dsum[(int64_t)h * p.rows_q + sg.ws_row0 + q0 + rr];
-      lpre = tid < nq ? l * kLog2e : 0.f;
-      dpre = tid < nq ? d : 0.f;
+      const int64_t row = (int64_t)h * p.rows_q + sg.ws_row0 + q0 + min(tid, nq - 1);
+      lpre = p.lse2[row];
+      dpre = p.dsum[row];
     }
   };
-  auto store_step = [&]() {
+  auto store_step = [&](int n) {
+    const int64_t q0 = (qb_lo + n % nblk) * TM;
+    const int nq = (int)min((int64_t)TM, sg.lq - q0);
 #pragma unroll
-    for (int v = 0; v < T::QU; ++v) {
-      const int id = tid + 256 * v;
-      if (T::QBLK % 256 == 0 || id < T::QBLK)
-        stage_block<QS, TS>(q_lds, qt_lds, qpre[v], 4 * (id & 15), id >> 4);
-    }
+    for (int v = 0; v < T::NV; ++v) {
+      const int id0 = tid + 256 * v;
+      if ((T::QBLK + T::OBLK) % 256 == 0 || id0 < T::QBLK + T::OBLK) {
+        const bool isq = id0 < T::QBLK;
+        const int id = isq ? id0 : id0 - T::QBLK;
+        const int r0 = 4 * (id % (TM / 4));
+        const int c8 = id / (TM / 4);
+        u32x4 x[4];
 #pragma unroll
-    for (int v = 0; v < T::OU; ++v) {
-      const int id = tid + 256 * v;
-      if (T::OBLK % 256 == 0 || id < T::OBLK)
-        stage_block<OS, TS>(o_lds, ot_lds, opre[v], 4 * (id & 15), id >> 4);
+        for (int u = 0; u < 4; ++u) x[u] = r0 + u < nq ? pre[v][u] : u32x4{0u, 0u, 0u, 0u};
+        if (isq) {
+          stage_block<QS, TS>(q_lds, qt_lds, x, r0, c8);
+        } else {
+          stage_block<OS, TS>(o_lds, ot_lds, x, r0, c8);
+        }
+      }
     }
     if (tid < TM) {
       lse_lds[tid] = lpre;
@@ -364,7 +371,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
 
   if (nsteps > 0) {
     load_step(0);
-    store_step();
+    store_step(0);
   }
 
   for (int n = 0; n < nsteps; ++n) {
@@ -374,14 +381,19 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
     __syncthreads();  // LDS holds step n; every wave is done with step n-1's dS^T
     if (n + 1 < nsteps) load_step(n + 1);
 
-    // ---- S = Q_i K_w^T and dP = dO_i V_w^T (2 row tiles of 32 queries) ----
-    f32x16 s_acc[2] = {f32x16{}, f32x16{}};
-    f32x16 dp_acc[2] = {f32x16{}, f32x16{}};
+    // ---- S = Q_i K_w^T and dP = dO_i V_w^T (MT row tiles of 32 queries) ----
+    f32x16 s_acc[MT];
+    f32x16 dp_acc[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      s_acc[m] = f32x16{};
+      dp_acc[m] = f32x16{};
+    }
 #pragma unroll
     for (int kk = 0; kk < DQK / 16; ++kk) {
       const bf16x8 kb = *(const bf16x8*)&k_lds[key_l * KS + 16 * kk + 8 * hi];
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
+      for (int m = 0; m < MT; ++m) {
         const bf16x8 a = *(const bf16x8*)&q_lds[(32 * m + l32) * QS + 16 * kk + 8 * hi];
         s_acc[m] = mfma(a, kb, s_acc[m]);
       }
@@ -389,7 +401,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
 #pragma unroll
     for (int kk = 0; kk < DV / 16; ++kk) {
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
+      for (int m = 0; m < MT; ++m) {
         const bf16x8 a = *(const bf16x8*)&o_lds[(32 * m + l32) * OS + 16 * kk + 8 * hi];
         dp_acc[m] = mfma(a, vw[kk], dp_acc[m]);
       }
@@ -399,14 +411,14 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
     const bool full = block_full(mg, sg.lq, sg.lk, q0, q0 + TM - 1, key0 + 32 * wave,
                                  key0 + 32 * wave + 31);
     const int base_d = (int)(key0 - q0) + key_l;
-    bf16x8 pa[2][2];
-    bf16x8 sa[2][2];
+    bf16x8 pa[MT][2];
+    bf16x8 sa[MT][2];
     if (full) {
-      probs_and_grads<false>(s_acc, dp_acc, lse_lds, dd_lds, p.scale_log2, hi, base_d, lo_d, hi_d,
-                             nq, key_ok, pa, sa);
+      probs_and_grads<false, MT>(s_acc, dp_acc, lse_lds, dd_lds, p.scale_log2, hi, base_d, lo_d,
+                                 hi_d, nq, key_ok, pa, sa);
     } else {
-      probs_and_grads<true>(s_acc, dp_acc, lse_lds, dd_lds, p.scale_log2, hi, base_d, lo_d, hi_d,
-                            nq, key_ok, pa, sa);
+      probs_and_grads<true, MT>(s_acc, dp_acc, lse_lds, dd_lds, p.scale_log2, hi, base_d, lo_d,
+                                hi_d, nq, key_ok, pa, sa);
     }
 
     // ---- dV += P^T dO_i ; dK += dS^T Q_i  (reduction over the block's queries) ----
@@ -414,7 +426,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
 #pragma unroll
     for (int n2 = 0; n2 < DV / 32; ++n2) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
+      for (int ks = 0; ks < 2 * MT; ++ks) {
         const bf16x8 bo = *(const bf16x8*)&ot_lds[(32 * n2 + l32) * TS + 16 * ks + 8 * hi];
         dv_acc[n2] = mfma(pa[ks >> 1][ks & 1], bo, dv_acc[n2]);
       }
@@ -422,7 +434,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
 #pragma unroll
     for (int n2 = 0; n2 < DQK / 32; ++n2) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
+      for (int ks = 0; ks < 2 * MT; ++ks) {
         const bf16x8 bq = *(const bf16x8*)&qt_lds[(32 * n2 + l32) * TS + 16 * ks + 8 * hi];
         dk_acc[n2] = mfma(sa[ks >> 1][ks & 1], bq, dk_acc[n2]);
       }
@@ -430,7 +442,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
 
     // ---- dS^T to LDS: 4 consecutive queries per 8-byte store ----
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
+    for (int m = 0; m < MT; ++m) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const bf16x8 v = sa[m][c >> 1];
@@ -445,48 +457,51 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
     float* dst_base = p.dq_acc + (p.deterministic ? (int64_t)j * p.split_stride : 0) +
                       (int64_t)h * p.head_stride + (sg.ws_row0 + q0) * DQK;
 #pragma unroll
-    for (int tt = 0; tt < NT / 4; ++tt) {
+    for (int tt = 0; tt < T::NTW; ++tt) {
       const int ti = wave + 4 * tt;
-      const int mq = ti / (DQK / 32);
-      const int nd = ti - mq * (DQK / 32);
-      f32x16 acc = f32x16{};
+      if (NT % 4 == 0 || ti < NT) {
+        const int mq = ti / (DQK / 32);
+        const int nd = ti - mq * (DQK / 32);
+        f32x16 acc = f32x16{};
 #pragma unroll
-      for (int kk = 0; kk < TN / 16; ++kk) {
-        const int kb = 16 * kk + 8 * hi + tr_row;
-        const bf16x8 a = tr_read(&st_lds[kb * SS + 32 * mq + tr_col], &st_lds[(kb + 4) * SS + 32 * mq + tr_col]);
-        bf16x8 bk;
-        if (T::KT_REGS) {
-          bk = kt[kk];
-        } else {
-          bk = tr_read(&k_lds[kb * KS + 32 * nd + tr_col], &k_lds[(kb + 4) * KS + 32 * nd + tr_col]);
+        for (int kk = 0; kk < TN / 16; ++kk) {
+          const int kb = 16 * kk + 8 * hi + tr_row;
+          const bf16x8 a = tr_read(&st_lds[kb * SS + 32 * mq + tr_col], &st_lds[(kb + 4) * SS + 32 * mq + tr_col]);
+          bf16x8 bk;
+          if (T::KT_REGS) {
+            bk = kt[kk];
+          } else {
+            bk = tr_read(&k_lds[kb * KS + 32 * nd + tr_col], &k_lds[(kb + 4) * KS + 32 * nd + tr_col]);
+          }
+          acc = mfma(a, bk, acc);
         }
-        acc = mfma(a, bk, acc);
-      }
-      // result register r: query 32mq + 8(r/4) + 4hi + r%4, column 32nd + l32
-      const int off0 = (32 * mq + 4 * hi) * DQK + 32 * nd + l32;
-      if (nq == TM) {
-        if (p.deterministic) {
+        // result register r: query 32mq + 8(r/4) + 4hi + r%4, column 32nd + l32
+        const int off0 = (32 * mq + 4 * hi) * DQK + 32 * nd + l32;
+        if (nq == TM) {
+          if (p.deterministic) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) dst_base[off0 + (8 * (r >> 2) + (r & 3)) * DQK] = acc[r];
-        } else {
+            for (int r = 0; r < 16; ++r) dst_base[off0 + (8 * (r >> 2) + (r & 3)) * DQK] = acc[r];
+          } else {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) unsafeAtomicAdd(&dst_base[off0 + (8 * (r >> 2) + (r & 3)) * DQK], acc[r]);
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int ql = 32 * mq + 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (ql < nq) {
-            if (p.deterministic) {
-              dst_base[off0 + (8 * (r >> 2) + (r & 3)) * DQK] = acc[r];
-            } else {
+            for (int r = 0; r < 16; ++r)
               unsafeAtomicAdd(&dst_base[off0 + (8 * (r >> 2) + (r & 3)) * DQK], acc[r]);
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int ql = 32 * mq + 8 * (r >> 2) + 4 * hi + (r & 3);
+            if (ql < nq) {
+              if (p.deterministic) {
+                dst_base[off0 + (8 * (r >> 2) + (r & 3)) * DQK] = acc[r];
+              } else {
+                unsafeAtomicAdd(&dst_base[off0 + (8 * (r >> 2) + (r & 3)) * DQK], acc[r]);
+              }
             }
           }
         }
       }
     }
-    if (n + 1 < nsteps) store_step();  // this step's tiles are dead: stage step n+1
+    if (n + 1 < nsteps) store_step(n + 1);  // this step's tiles are dead: stage step n+1
   }
 
   // ---- epilogue: dK = scale * dK_acc, dV = dV_acc as bf16 ----
@@ -508,11 +523,11 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
 // ------------------------------------------------------------------------------------------
 // Stage 3: dQ = bf16(scale * sum of the partials), one block of TM rows per work group.
 // ------------------------------------------------------------------------------------------
-template <int DQK>
+template <int DQK, int TM>
 __global__ __launch_bounds__(256) void k_dq_reduce(const KParams p) {
-  constexpr int TM = 64, TN = 128;
-  constexpr int C4 = DQK / 4;           // float4 chunks per row
-  constexpr int PER = TM * C4 / 256;    // chunks per thread
+  constexpr int TN = 128;
+  constexpr int C4 = DQK / 4;                   // float4 chunks per row
+  constexpr int PER = (TM * C4 + 255) / 256;    // chunks per thread
   const int qb = blockIdx.x;
   const int h = blockIdx.y;
   const int b = blockIdx.z;
@@ -594,11 +609,15 @@ hipError_t launch_main(const Plan& plan, const KParams& kp, hipStream_t stream) 
   if (items == 0) return hipSuccess;
   const dim3 grid((unsigned)items);
   if (plan.d_qk == 64) {
-    hipLaunchKernelGGL((k_bwd_main<64, 64>), grid, dim3(256), 0, stream, kp);
+    hipLaunchKernelGGL((k_bwd_main<64, 64, 64>), grid, dim3(256), 0, stream, kp);
   } else if (plan.d_qk == 128) {
-    hipLaunchKernelGGL((k_bwd_main<128, 128>), grid, dim3(256), 0, stream, kp);
+    if (plan.tile_m == 32) {
+      hipLaunchKernelGGL((k_bwd_main<128, 128, 32>), grid, dim3(256), 0, stream, kp);
+    } else {
+      hipLaunchKernelGGL((k_bwd_main<128, 128, 64>), grid, dim3(256), 0, stream, kp);
+    }
   } else {
-    hipLaunchKernelGGL((k_bwd_main<192, 128>), grid, dim3(256), 0, stream, kp);
+    hipLaunchKernelGGL((k_bwd_main<192, 128, 32>), grid, dim3(256), 0, stream, kp);
   }
   return hipGetLastError();
 }
@@ -607,11 +626,15 @@ hipError_t launch_reduce(const Plan& plan, const KParams& kp, hipStream_t stream
   if (plan.n_q_blocks == 0 || plan.B == 0) return hipSuccess;
   const dim3 grid((unsigned)plan.n_q_blocks, (unsigned)plan.Hq, (unsigned)plan.B);
   if (plan.d_qk == 64) {
-    hipLaunchKernelGGL(k_dq_reduce<64>, grid, dim3(256), 0, stream, kp);
+    hipLaunchKernelGGL((k_dq_reduce<64, 64>), grid, dim3(256), 0, stream, kp);
   } else if (plan.d_qk == 128) {
-    hipLaunchKernelGGL(k_dq_reduce<128>, grid, dim3(256), 0, stream, kp);
+    if (plan.tile_m == 32) {
+      hipLaunchKernelGGL((k_dq_reduce<128, 32>), grid, dim3(256), 0, stream, kp);
+    } else {
+      hipLaunchKernelGGL((k_dq_reduce<128, 64>), grid, dim3(256), 0, stream, kp);
+    }
   } else {
-    hipLaunchKernelGGL(k_dq_reduce<192>, grid, dim3(256), 0, stream, kp);
+    hipLaunchKernelGGL((k_dq_reduce<192, 32>), grid, dim3(256), 0, stream, kp);
   }
   return hipGetLastError();
 }

@@ -2,6 +2,7 @@
 //
 // Workspace layout (byte offsets 256-aligned):
 //   D       fp32 [Hq][rows_q]                     rowsum(dO * O) from the first stage
+//   L       fp32 [Hq][rows_q]                     LSE * log2(e), also from the first stage
 //   dq_acc  fp32 [nsplits][Hq][rows_q][d_qk]      dQ partials (deterministic: split = key tile
 //                                                 index of the segment; atomic: one split)
 // One layout serves batch and group mode: row = b*Sq + i in batch mode and seqstart_q[b] + i
@@ -12,6 +13,7 @@
 
 #include <math.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "tiling.h"
@@ -30,12 +32,13 @@ int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-// The kernels move 8 bf16 (16 bytes) per lane access along the head dimension.
+// The kernels move 8 bf16 (16 bytes) per lane access along the head dimension, and address
+// rows inside one tile with 32-bit offsets (sequence stride < 2^24 elements).
 bool strides_ok(const int64_t s[3], bool group) {
   for (int i = group ? 1 : 0; i < 3; ++i) {
     if (s[i] < 0 || (s[i] & 7) != 0) return false;
   }
-  return true;
+  return s[1] < (int64_t(1) << 24);
 }
 
 }  // namespace
@@ -77,7 +80,11 @@ int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t el) {
   p->Sk = a->Sk;
   p->d_qk = a->d_qk;
   p->d_v = a->d_v;
-  p->tile_m = 64;
+  // query rows per main-kernel block: 64, or 32 for d_qk = 192 (register and LDS budget)
+  p->tile_m = a->d_qk == 192 ? 32 : 64;
+  if (const char* e = getenv("FMHA_BWD_TILE_M")) {  // tuning knob: 32 or 64 for d_qk = 128
+    if (a->d_qk == 128 && (atoi(e) == 32 || atoi(e) == 64)) p->tile_m = atoi(e);
+  }
   p->tile_n = 128;
   p->deterministic = a->deterministic == 1;
 
@@ -124,7 +131,7 @@ int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t el) {
     if (!strides_ok(a->q_stride, group) || !strides_ok(a->o_stride, group) ||
         !strides_ok(a->do_stride, group) || !strides_ok(a->dq_stride, group))
       return fail(FMHA_ERR_UNSUPPORTED, err, el,
-                  "q/o/dout/dq strides must be non-negative multiples of 8 elements");
+                  "q/o/dout/dq strides must be non-negative multiples of 8 elements (sequence stride < 2^24)");
     if ((!group && a->lse_stride[0] < 0) || a->lse_stride[1] < 0)
       return fail(FMHA_ERR_INVALID_ARG, err, el, "lse strides must be non-negative");
   }
@@ -136,7 +143,7 @@ int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t el) {
     if (!strides_ok(a->k_stride, group) || !strides_ok(a->v_stride, group) ||
         !strides_ok(a->dk_stride, group) || !strides_ok(a->dv_stride, group))
       return fail(FMHA_ERR_UNSUPPORTED, err, el,
-                  "k/v/dk/dv strides must be non-negative multiples of 8 elements");
+                  "k/v/dk/dv strides must be non-negative multiples of 8 elements (sequence stride < 2^24)");
   }
 
   p->n_kv_tiles = (int)((max_lk + p->tile_n - 1) / p->tile_n);
@@ -149,7 +156,8 @@ int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t el) {
   p->split_stride = (int64_t)p->Hq * p->head_stride;
   p->d_offset = 0;
   p->d_bytes = (int64_t)p->Hq * p->rows_q * 4;
-  p->dq_acc_offset = align_up(p->d_bytes, 256);
+  p->lse2_offset = align_up(p->d_bytes, 256);
+  p->dq_acc_offset = align_up(p->lse2_offset + p->d_bytes, 256);
   p->dq_acc_bytes = (int64_t)p->nsplits * p->split_stride * 4;
   p->workspace_bytes = align_up(p->dq_acc_offset + p->dq_acc_bytes, 256);
   if (p->workspace_bytes == 0) p->workspace_bytes = 256;

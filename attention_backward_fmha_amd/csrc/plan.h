@@ -25,6 +25,7 @@ struct Plan {
   bool deterministic;
   int64_t rows_q;        // accumulator / D rows: B*Sq or seqstart_q[B]
   int64_t d_offset, d_bytes;
+  int64_t lse2_offset;   // LSE * log2(e), same shape as D
   int64_t dq_acc_offset, dq_acc_bytes;
   int64_t split_stride;  // elements between consecutive splits: Hq*rows_q*d_qk
   int64_t head_stride;   // elements between heads inside a split: rows_q*d_qk
