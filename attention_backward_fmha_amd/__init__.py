@@ -42,7 +42,12 @@ class BwdCall:
 def _strides(t, group):
     if t is None:
         return (0, 0, 0)
-    st = t.stride()
+    if t.numel() == 0:  # nothing is addressed; report dense strides
+        st = [1] * t.dim()
+        for i in range(t.dim() - 2, -1, -1):
+            st[i] = st[i + 1] * max(1, t.shape[i + 1])
+    else:
+        st = t.stride()
     if st[-1] != 1:
         raise ValueError("the head dimension must be contiguous")
     if group:

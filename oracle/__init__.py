@@ -25,4 +25,5 @@ from .attention import (  # noqa: F401
     dq_rows,
     dkdv_rows,
     dq_split_reduce,
+    rowsum_product,
 )

@@ -290,6 +290,11 @@ def dkdv_rows(q, k, v, do, *, scale, segment, kv_head, rows, stats, mask_type=MA
     return dk, dv
 
 
+def rowsum_product(a, b):
+    """D_i = sum_c a_ic b_ic in fp64 over the last axis (D = rowsum(dO * O) for the given O)."""
+    return (np.asarray(a, np.float64) * np.asarray(b, np.float64)).sum(axis=-1)
+
+
 # ---------------------------------------------------------------------------------------
 # Deterministic split reduction (aiter PR 2216, Motivation: dQ is "split, stored, and
 # converted back"; TransformerEngine PR 671, Root cause: the fp32 convert post-kernel).

@@ -1,0 +1,244 @@
+"""CPU tests of the C ABI: the library loads and exports every declared entry point, and the
+host-only entry points (workspace sizing, plan query) validate arguments and agree with each
+other.  No compute call is made (there may be no GPU here)."""
+
+import ctypes
+import json
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from attention_backward_fmha_amd import _lib
+from attention_backward_fmha_amd._lib import Args
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fmha_bwd.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+FAKE = 1 << 20  # a 16-byte aligned non-null address (never dereferenced by host entry points)
+
+
+@pytest.fixture(scope="session", autouse=True)
+def built_library():
+    if not os.path.exists(_lib.LIB_PATH):
+        from attention_backward_fmha_amd import build
+        build.build()
+    return _lib.lib()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"FMHA_BWD_API\s+[\w\s\*]+?\b(fmha_bwd_\w+)\s*\(", src)))
+
+
+def test_header_declarations_are_exported():
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    for n in names:
+        assert n in exported, n
+    # nothing but the C ABI leaks out of the library
+    ours = {e for e in exported if "fmha" in e}
+    assert ours == set(names)
+
+
+def test_struct_layout_matches_header():
+    """Offsets of the ctypes mirror against a C compile of the header."""
+    src = """
+#include <stddef.h>
+#include <stdio.h>
+#include "fmha_bwd.h"
+#define F(m) printf("\\"%s\\": %zu,\\n", #m, offsetof(fmha_bwd_args, m));
+#define G(m) printf("\\"%s\\": %zu,\\n", #m, offsetof(fmha_bwd_plan_info, m));
+int main(void) {
+  printf("{\\n");
+  F(B) F(scale) F(deterministic) F(seqstart_q_host) F(seqstart_k_dev) F(q) F(lse) F(dv)
+  F(q_stride) F(dv_stride) F(lse_stride)
+  G(nsplits) G(rows_q) G(workspace_bytes) G(flops)
+  printf("\\"size_args\\": %zu, \\"size_info\\": %zu}\\n", sizeof(fmha_bwd_args), sizeof(fmha_bwd_plan_info));
+  return 0;
+}
+"""
+    import tempfile
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "t.c")
+        exe = os.path.join(d, "t")
+        open(c, "w").write(src)
+        subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), c, "-o", exe], check=True)
+        ref = json.loads(subprocess.run([exe], capture_output=True, text=True, check=True).stdout)
+    assert ref["size_args"] == ctypes.sizeof(Args)
+    assert ref["size_info"] == ctypes.sizeof(_lib.PlanInfo)
+    for k, v in ref.items():
+        if k.startswith("size"):
+            continue
+        cls = _lib.PlanInfo if k in ("nsplits", "rows_q", "workspace_bytes", "flops") else Args
+        assert getattr(cls, k).offset == v, k
+
+
+def test_mask_numbering_matches_pages():
+    """Mask numbering from the mask-type table of the TransformerEngine PR 446 review."""
+    table = json.load(open(os.path.join(GOLDEN, "mask_encoding.json")))
+    src = open(HEADER).read()
+    for name, value in table["numbering"].items():
+        assert re.search(r"\b%s\s*=\s*%d\b" % (name, value), src), name
+        assert getattr(_lib, name.replace("FMHA_", "")) == value
+
+
+def batch_args(B=2, Hq=4, Hkv=2, Sq=200, Sk=333, d_qk=128, d_v=128, mask=0, window=(-1, -1),
+               deterministic=1):
+    a = Args(B=B, Hq=Hq, Hkv=Hkv, Sq=Sq, Sk=Sk, d_qk=d_qk, d_v=d_v, scale=1.0 / np.sqrt(d_qk),
+             mask_type=mask, window_left=window[0], window_right=window[1],
+             deterministic=deterministic)
+    for n in ("q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv"):
+        setattr(a, n, FAKE)
+    for n, H, d, S in (("q_stride", Hq, d_qk, Sq), ("k_stride", Hkv, d_qk, Sk), ("v_stride", Hkv, d_v, Sk),
+                       ("o_stride", Hq, d_v, Sq), ("do_stride", Hq, d_v, Sq), ("dq_stride", Hq, d_qk, Sq),
+                       ("dk_stride", Hkv, d_qk, Sk), ("dv_stride", Hkv, d_v, Sk)):
+        arr = getattr(a, n)
+        arr[0], arr[1], arr[2] = S * H * d, H * d, d
+    a.lse_stride[0] = Hq * Sq
+    a.lse_stride[1] = Sq
+    return a
+
+
+def group_args(lens_q, lens_k, Hq=4, Hkv=2, d=128, mask=1, deterministic=1):
+    sq = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32)
+    sk = np.concatenate([[0], np.cumsum(lens_k)]).astype(np.int32)
+    a = batch_args(B=len(lens_q), Hq=Hq, Hkv=Hkv, Sq=max(lens_q), Sk=max(lens_k), d_qk=d, d_v=d,
+                   mask=mask, deterministic=deterministic)
+    a.seqstart_q_host = sq.ctypes.data
+    a.seqstart_k_host = sk.ctypes.data
+    a.seqstart_q_dev = FAKE
+    a.seqstart_k_dev = FAKE
+    a._keep = (sq, sk)
+    return a
+
+
+def status_of(a):
+    n = ctypes.c_size_t(0)
+    return _lib.lib().fmha_bwd_workspace_size(ctypes.byref(a), ctypes.byref(n))
+
+
+def test_workspace_size_and_plan_agree():
+    for det in (0, 1):
+        a = batch_args(deterministic=det)
+        info = _lib.plan_query(a)
+        assert _lib.workspace_size(a) == info.workspace_bytes
+        rows = 2 * 200
+        assert info.rows_q == rows
+        assert info.nsplits == (3 if det else 1)  # ceil(333 / 128) key tiles
+        assert info.needs_zero == (0 if det else 1)
+        assert info.dq_acc_bytes == info.nsplits * 4 * rows * 128 * 4
+        assert info.dq_acc_offset % 256 == 0 and info.workspace_bytes % 256 == 0
+        assert info.dq_acc_offset + info.dq_acc_bytes <= info.workspace_bytes
+        # nsplits never exceeds ceil(max Sk / 16)
+        assert info.nsplits <= -(-333 // 16)
+
+
+def test_group_mode_uses_physical_rows():
+    lens = [100, 80, 76]
+    a = group_args(lens, lens)
+    info = _lib.plan_query(a)
+    assert info.group_mode == 1
+    assert info.rows_q == 256
+    assert info.nsplits == 1  # longest segment has 100 keys: one 128-key tile
+    # empty segments are fine and contribute no rows
+    b = group_args([5, 0, 7], [0, 3, 9])
+    assert _lib.plan_query(b).rows_q == 12
+
+
+def test_flop_count_matches_pair_count():
+    a = batch_args(B=2, Hq=16, Hkv=16, Sq=2048, Sk=2048, mask=1)
+    info = _lib.plan_query(a)
+    pairs = 2 * 16 * 2048 * 2049 // 2
+    assert info.pairs == pairs
+    assert info.flops == 2.0 * (3 * 128 + 2 * 128) * pairs
+    w = batch_args(B=1, Hq=1, Hkv=1, Sq=16384, Sk=16384, mask=3, window=(4096, 0))
+    assert _lib.plan_query(w).pairs == 58734592  # 4097 keys per row, fewer near the start
+
+
+@pytest.mark.parametrize("mutate,expected", [
+    (lambda a: setattr(a, "struct_size", 8), _lib.ERR_INVALID_ARG),
+    (lambda a: setattr(a, "abi_version", 99), _lib.ERR_INVALID_ARG),
+    (lambda a: setattr(a, "Hkv", 3), _lib.ERR_INVALID_ARG),
+    (lambda a: setattr(a, "d_qk", 96), _lib.ERR_UNSUPPORTED),
+    (lambda a: (setattr(a, "d_qk", 128), setattr(a, "d_v", 64)), _lib.ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "mask_type", 7), _lib.ERR_INVALID_ARG),
+    (lambda a: setattr(a, "window_left", 5), _lib.ERR_INVALID_ARG),  # NONE with a window
+    (lambda a: setattr(a, "scale", float("nan")), _lib.ERR_INVALID_ARG),
+    (lambda a: setattr(a, "q", 0), _lib.ERR_INVALID_ARG),
+    (lambda a: setattr(a, "q", FAKE + 8), _lib.ERR_UNSUPPORTED),
+    (lambda a: a.q_stride.__setitem__(1, 4 * 128 + 4), _lib.ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "deterministic", 2), _lib.ERR_INVALID_ARG),
+    (lambda a: setattr(a, "B", -1), _lib.ERR_INVALID_ARG),
+    (lambda a: setattr(a, "seqstart_k_host", FAKE), _lib.ERR_INVALID_ARG),  # half group mode
+])
+def test_invalid_arguments_are_rejected(mutate, expected):
+    a = batch_args()
+    assert status_of(a) == _lib.OK
+    mutate(a)
+    assert status_of(a) == expected
+
+
+def test_group_mode_errors():
+    a = group_args([5, 7], [5, 7])
+    assert status_of(a) == _lib.OK
+    a.seqstart_q_dev = 0  # device offsets missing
+    assert status_of(a) == _lib.ERR_INVALID_ARG
+    bad = group_args([5, 7], [5, 7])
+    bad._keep[0][2] = 3  # non-monotone
+    assert status_of(bad) == _lib.ERR_INVALID_ARG
+    long = group_args([5, 7], [5, 7])
+    long.Sq = 6  # a segment longer than the declared maximum
+    assert status_of(long) == _lib.ERR_INVALID_ARG
+
+
+def test_window_masks_need_window_type():
+    assert status_of(batch_args(mask=3, window=(10, 0))) == _lib.OK
+    assert status_of(batch_args(mask=1, window=(10, 0))) == _lib.ERR_INVALID_ARG
+    assert status_of(batch_args(mask=3, window=(-2, 0))) == _lib.ERR_INVALID_ARG
+
+
+def test_workspace_too_small_is_reported_before_any_device_work():
+    a = batch_args()
+    n = _lib.workspace_size(a)
+    L = _lib.lib()
+    st = L.fmha_bwd_run(ctypes.byref(a), ctypes.c_void_p(FAKE), n - 1, None)
+    assert st == _lib.ERR_WORKSPACE_TOO_SMALL
+    st = L.fmha_bwd_prepare_workspace(ctypes.byref(a), ctypes.c_void_p(FAKE), n - 1, None)
+    assert st == _lib.ERR_WORKSPACE_TOO_SMALL
+    st = L.fmha_bwd_run_stages(ctypes.byref(a), ctypes.c_void_p(FAKE), n, 8, None)
+    assert st == _lib.ERR_INVALID_ARG
+    assert _lib.status_string(_lib.ERR_WORKSPACE_TOO_SMALL) == "FMHA_ERR_WORKSPACE_TOO_SMALL"
+
+
+def test_sizing_is_a_pure_function_of_the_arguments():
+    """The same arguments always give the same plan, and only the fields that define the
+    problem change it (pointer values do not)."""
+    rng = np.random.default_rng(5)
+    for _ in range(200):
+        nseg = int(rng.integers(1, 6))
+        lq = rng.integers(0, 700, nseg)
+        lk = rng.integers(0, 700, nseg)
+        if lq.sum() == 0 or lk.sum() == 0:
+            continue
+        d = int(rng.choice([64, 128, 192]))
+        det = int(rng.integers(0, 2))
+        a = group_args(list(lq), list(lk), Hq=4, Hkv=int(rng.choice([1, 2, 4])), d=d, mask=int(rng.integers(0, 3)),
+                       deterministic=det)
+        if d == 192:
+            a.d_v = 128
+        i1 = _lib.plan_query(a).as_dict()
+        a.q = FAKE * 3
+        a.dq = FAKE * 5
+        i2 = _lib.plan_query(a).as_dict()
+        assert i1 == i2
+        assert i1["workspace_bytes"] == _lib.workspace_size(a)
+        nt = -(-int(lk.max()) // i1["tile_n"])
+        assert i1["n_kv_tiles"] == nt
+        assert i1["nsplits"] == (max(nt, 1) if det else 1)
+        assert i1["rows_q"] == int(lq.sum())

@@ -435,3 +435,13 @@ def test_checker_catches_the_ragged_slot_zero_bug():
         y = dq[sq[b]:sq[b + 1]].ravel()
         cos.append(float(x @ y / np.linalg.norm(x) / np.linalg.norm(y)))
     assert cos[0] > 0.9999 and cos[1] < 0.5 and cos[2] < 0.5
+
+
+def test_rowsum_product_is_the_row_dot():
+    a, b = _rand(3, 5, 7), _rand(3, 5, 7)
+    np.testing.assert_allclose(A.rowsum_product(a, b), np.einsum("ijk,ijk->ij", a, b), rtol=1e-14)
+    # D equals <dO, O> with O from the forward, the identity the backward relies on
+    q, k, v, do = _rand(1, 6, 2, 4), _rand(1, 6, 1, 4), _rand(1, 6, 1, 4), _rand(1, 6, 2, 4)
+    o, _ = A.forward(q, k, v, scale=0.5)
+    _, _, dv = A.backward(q, k, v, do, scale=0.5)
+    np.testing.assert_allclose((dv * v).sum(), A.rowsum_product(do, o).sum(), rtol=1e-12)
