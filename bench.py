@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--mode", choices=["atomic", "deterministic"], default="atomic")
     ap.add_argument("--workload", default="headline_2x32x4096_causal")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-mode", action="store_true",
+                    help="time only --mode (profiling runs); by default both modes are timed")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (steps times), "
@@ -99,6 +101,25 @@ def prepare_inputs(w, device):
     return dev["q"], dev["k"], dev["v"], o, lse, dev["do"], scale
 
 
+def measured_traffic(workload, mode):
+    """HBM bytes per launch of the main kernel from the committed rocprofv3 counter summary,
+    or None when there is none or the kernel source changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "k_bwd_main_%s_%s_traffic.txt" % (workload, mode))
+    src = os.path.join(ROOT, "attention_backward_fmha_amd", "csrc", "kernels.hip")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k_, v_ = line.split(":", 1)
+            fields[k_.strip()] = v_.strip()
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if fields.get("kernel_source_sha256") != sha:
+        return None
+    return int(float(fields["read_bytes_per_launch"]) + float(fields["write_bytes_per_launch"]))
+
+
 def cpu_baseline(w, budget_s):
     """The fp64 oracle on the host cores, on a bounded sample of the workload: single
     (batch, query head) problems of the same shape and mask, as many as fit the time budget."""
@@ -129,8 +150,9 @@ def cpu_baseline(w, budget_s):
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": "%d of %d (batch, head) problems (Sq=%d, Sk=%d, d=%d, same mask), fp64 numpy, %.1f s"
-                  % (done, w["B"] * w["Hq"], Sq, Sk, dqk, dt),
+        "sample": "%d repetitions of one (batch, head) problem of the workload (Sq=%d, Sk=%d, d=%d, "
+                  "same mask; the workload has %d such problems), fp64 numpy, %.1f s"
+                  % (done, Sq, Sk, dqk, w["B"] * w["Hq"], dt),
     }
 
 
@@ -154,43 +176,57 @@ def main():
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
-    det = args.mode == "deterministic"
-    call = F.make_call(q, k, v, o, lse, do, dq, dk, dv, scale=scale, mask_type=w["mask"],
-                       window=w.get("window", (-1, -1)), deterministic=det)
-    plan = call.plan()
-    ws = torch.empty(call.workspace_size(), dtype=torch.uint8, device=device)
     stream = torch.cuda.current_stream(device)
     sh = stream.cuda_stream
 
-    def step(evs=None):
-        call.prepare(ws, sh)
-        call.run(ws, sh, F.STAGE_DOT)
-        if evs is not None:
-            evs[0].record(stream)
-        call.run(ws, sh, F.STAGE_MAIN)
-        if evs is not None:
-            evs[1].record(stream)
-        call.run(ws, sh, F.STAGE_REDUCE)
+    def time_mode(det):
+        call = F.make_call(q, k, v, o, lse, do, dq, dk, dv, scale=scale, mask_type=w["mask"],
+                           window=w.get("window", (-1, -1)), deterministic=det)
+        plan = call.plan()
+        ws = torch.empty(call.workspace_size(), dtype=torch.uint8, device=device)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record(stream)
-    for s in range(args.steps):
-        step(kev[s])
-    t1.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t0.elapsed_time(t1)
-    ms = total_ms / args.steps
-    main_ms = sum(a.elapsed_time(b) for a, b in kev) / args.steps
+        def step(evs=None):
+            call.prepare(ws, sh)
+            call.run(ws, sh, F.STAGE_DOT)
+            if evs is not None:
+                evs[0].record(stream)
+            call.run(ws, sh, F.STAGE_MAIN)
+            if evs is not None:
+                evs[1].record(stream)
+            call.run(ws, sh, F.STAGE_REDUCE)
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for s_ in range(args.steps):
+            step(kev[s_])
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / args.steps
+        main_ms = sum(a_.elapsed_time(b_) for a_, b_ in kev) / args.steps
+        del ws
+        torch.cuda.empty_cache()
+        return ms, main_ms, plan
+
+    primary_det = args.mode == "deterministic"
+    ms, main_ms, plan = time_mode(primary_det)
+    runs = [(primary_det, ms, main_ms, plan)]
+    if not args.only_mode:
+        runs.append((not primary_det,) + time_mode(not primary_det))
     flops = plan.flops
     tflops = flops / (ms * 1e-3) / 1e12
     main_tflops = flops / (main_ms * 1e-3) / 1e12
+    modes = {}
+    for det, m_ms, m_main, m_plan in runs:
+        modes["deterministic" if det else "atomic"] = {
+            "value": round(flops / (m_ms * 1e-3) / 1e12, 2), "ms_per_step": round(m_ms, 4),
+            "main_kernel_ms": round(m_main, 4), "nsplits": m_plan.nsplits}
 
     out = {
         "metric": "FMHA bwd TFLOP/s and % of bf16 MFMA peak, B*H*S*d=2*32*4096*128 causal",
@@ -211,6 +247,7 @@ def main():
             "d_qk": w["d_qk"], "d_v": w["d_v"], "mask": w["mask"], "layout": "bshd",
             "dq_accumulation": args.mode, "nsplits": plan.nsplits,
             "flops_per_step": flops, "pct_of_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+            "modes": modes,
         },
         "roofline": {
             "kernel": "k_bwd_main",
@@ -219,7 +256,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(main_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(args.workload, args.mode),
             "avg_launch_ms": round(main_ms, 4),
         },
     }
