@@ -44,13 +44,19 @@ struct Seg {
   int64_t ws_row0;  // first workspace row (b*Sq in batch mode)
 };
 
+// Segment bounds; b is uniform across the work group and readfirstlane keeps the loaded
+// offsets in scalar registers, so everything derived from them stays wave-uniform.
 __device__ __forceinline__ Seg seg_of(const KParams& p, int b) {
   Seg s;
   if (p.seqstart_q != nullptr) {
-    s.q_row0 = p.seqstart_q[b];
-    s.lq = (int64_t)p.seqstart_q[b + 1] - s.q_row0;
-    s.k_row0 = p.seqstart_k[b];
-    s.lk = (int64_t)p.seqstart_k[b + 1] - s.k_row0;
+    const int q0 = __builtin_amdgcn_readfirstlane(p.seqstart_q[b]);
+    const int q1 = __builtin_amdgcn_readfirstlane(p.seqstart_q[b + 1]);
+    const int k0 = __builtin_amdgcn_readfirstlane(p.seqstart_k[b]);
+    const int k1 = __builtin_amdgcn_readfirstlane(p.seqstart_k[b + 1]);
+    s.q_row0 = q0;
+    s.lq = (int64_t)q1 - q0;
+    s.k_row0 = k0;
+    s.lk = (int64_t)k1 - k0;
     s.ws_row0 = s.q_row0;
   } else {
     s.q_row0 = 0;
@@ -73,6 +79,13 @@ __device__ __forceinline__ bf16x8 tr_read(const uint16_t* p0, const uint16_t* p1
   const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p1));
   const s16x8 c = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8, c);
+}
+
+// Raw buffer resource over [base, base + bytes): loads past the end return 0 and stores or
+// atomics past the end are dropped by the hardware range check.  Callers pass every offset in
+// the per-lane offset operand and 0 as the scalar offset.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -153,6 +166,8 @@ struct MainTile {
   // every dQ tile of a wave uses the same 32 head-dim columns: their K operand is kept in
   // registers for the whole work item
   static constexpr bool KT_REGS = (DQK / 32) % 4 == 0 || NT <= 4;
+  // a wave's staging blocks are all Q or all dO, so the choice of buffer is wave-uniform
+  static_assert(QBLK % 64 == 0, "staging blocks of Q must fill whole waves");
 };
 
 // Position of query q (0 <= q < TM) inside a transposed row: bits 2 and 3 of q swapped, so
@@ -217,7 +232,7 @@ __device__ __forceinline__ void stage_block(uint16_t* rm, uint16_t* tr, const u3
   }
 }
 
-template <int DQK, int DV, int TM_>
+template <int DQK, int DV, int TM_, bool DET>
 __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
   using T = MainTile<DQK, DV, TM_>;
   constexpr int TM = T::TM, MT = T::MT, TN = T::TN, QS = T::QS, OS = T::OS, KS = T::KS,
@@ -305,61 +320,58 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
 
   // ---- prefetch registers for one step: 4-row x 8-column blocks of Q and dO, LSE2, D ----
   // Block ids tid + 256v: ids below QBLK are Q blocks, the next OBLK are dO blocks; block id
-  // covers rows 4*(id % (TM/4)) .. +3 and column chunk id / (TM/4).  The loads land in
-  // registers untouched (rows past the segment end re-read its last row); zeroing happens
-  // when the registers are written to LDS, so nothing waits for them until then.  Offsets
-  // inside a block are 32-bit (the plan bounds the sequence strides).
+  // covers rows 4*(id % (TM/4)) .. +3 and column chunk id / (TM/4).  Buffer loads over the
+  // block's valid rows return zeros for rows past the segment end.  The registers are not
+  // touched until they are written to LDS, so nothing waits for the loads before then.
+  // Offsets inside a block are 32-bit (the plan bounds the sequence strides).
   u32x4 pre[T::NV][4];
   float lpre = 0.f, dpre = 0.f;
   const int qs1 = (int)p.q_s[1];
   const int os1 = (int)p.do_s[1];
-  auto load_step = [&](int n) {
-    const int h = g * p.group_size + n / nblk;
-    const int64_t q0 = (qb_lo + n % nblk) * TM;
+  auto load_step = [&](int h, int64_t q0) {
     const int nq = (int)min((int64_t)TM, sg.lq - q0);
-    const uint16_t* qb = p.q + elem_off(p.q_s, group, b, sg.q_row0 + q0, h);
-    const uint16_t* ob = p.dout + elem_off(p.do_s, group, b, sg.q_row0 + q0, h);
+    const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(
+        p.q + elem_off(p.q_s, group, b, sg.q_row0 + q0, h), (uint32_t)((nq - 1) * qs1 + DQK) * 2u);
+    const __amdgpu_buffer_rsrc_t ro = buffer_rsrc(
+        p.dout + elem_off(p.do_s, group, b, sg.q_row0 + q0, h), (uint32_t)((nq - 1) * os1 + DV) * 2u);
 #pragma unroll
     for (int v = 0; v < T::NV; ++v) {
       const int id0 = tid + 256 * v;
       if ((T::QBLK + T::OBLK) % 256 == 0 || id0 < T::QBLK + T::OBLK) {
-        const bool isq = id0 < T::QBLK;
+        const bool isq = __builtin_amdgcn_readfirstlane(id0) < T::QBLK;  // wave-uniform
         const int id = isq ? id0 : id0 - T::QBLK;
         const int r0 = 4 * (id % (TM / 4));
         const int c8 = id / (TM / 4);
-        const uint16_t* base = isq ? qb : ob;
-        const int s1 = isq ? qs1 : os1;
+        if (isq) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int rr = min(r0 + u, nq - 1);
-          pre[v][u] = *(const u32x4*)(base + (rr * s1 + c8 * 8));
+          for (int u = 0; u < 4; ++u)
+            pre[v][u] = __builtin_amdgcn_raw_buffer_load_b128(rq, ((r0 + u) * qs1 + c8 * 8) * 2, 0, 0);
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            pre[v][u] = __builtin_amdgcn_raw_buffer_load_b128(ro, ((r0 + u) * os1 + c8 * 8) * 2, 0, 0);
         }
       }
     }
     if (tid < TM) {
-      const int64_t row = (int64_t)h * p.rows_q + sg.ws_row0 + q0 + min(tid, nq - 1);
-      lpre = p.lse2[row];
-      dpre = p.dsum[row];
+      const int64_t row0 = (int64_t)h * p.rows_q + sg.ws_row0 + q0;
+      lpre = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(p.lse2 + row0, (uint32_t)nq * 4u), tid * 4, 0, 0));
+      dpre = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(p.dsum + row0, (uint32_t)nq * 4u), tid * 4, 0, 0));
     }
   };
-  auto store_step = [&](int n) {
-    const int64_t q0 = (qb_lo + n % nblk) * TM;
-    const int nq = (int)min((int64_t)TM, sg.lq - q0);
+  auto store_step = [&]() {
 #pragma unroll
     for (int v = 0; v < T::NV; ++v) {
       const int id0 = tid + 256 * v;
       if ((T::QBLK + T::OBLK) % 256 == 0 || id0 < T::QBLK + T::OBLK) {
-        const bool isq = id0 < T::QBLK;
+        const bool isq = __builtin_amdgcn_readfirstlane(id0) < T::QBLK;  // wave-uniform
         const int id = isq ? id0 : id0 - T::QBLK;
         const int r0 = 4 * (id % (TM / 4));
         const int c8 = id / (TM / 4);
-        u32x4 x[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) x[u] = r0 + u < nq ? pre[v][u] : u32x4{0u, 0u, 0u, 0u};
         if (isq) {
-          stage_block<QS, TS>(q_lds, qt_lds, x, r0, c8);
+          stage_block<QS, TS>(q_lds, qt_lds, pre[v], r0, c8);
         } else {
-          stage_block<OS, TS>(o_lds, ot_lds, x, r0, c8);
+          stage_block<OS, TS>(o_lds, ot_lds, pre[v], r0, c8);
         }
       }
     }
@@ -369,17 +381,24 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
     }
   };
 
+  // step n covers query head h = g*group_size + n / nblk and query block qb_lo + n % nblk
+  int h = g * p.group_size;
+  int64_t q0 = qb_lo * TM;
   if (nsteps > 0) {
-    load_step(0);
-    store_step(0);
+    load_step(h, q0);
+    store_step();
   }
 
   for (int n = 0; n < nsteps; ++n) {
-    const int h = g * p.group_size + n / nblk;
-    const int64_t q0 = (qb_lo + n % nblk) * TM;
     const int nq = (int)min((int64_t)TM, sg.lq - q0);
+    int h_next = h;
+    int64_t q0_next = q0 + TM;
+    if (q0_next > qb_hi * TM) {
+      q0_next = qb_lo * TM;
+      ++h_next;
+    }
     __syncthreads();  // LDS holds step n; every wave is done with step n-1's dS^T
-    if (n + 1 < nsteps) load_step(n + 1);
+    if (n + 1 < nsteps) load_step(h_next, q0_next);
 
     // ---- S = Q_i K_w^T and dP = dO_i V_w^T (MT row tiles of 32 queries) ----
     f32x16 s_acc[MT];
@@ -454,54 +473,55 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
     __syncthreads();  // dS^T complete; every wave is done reading this step's Q, dO tiles
 
     // ---- dQ_i partial = dS K_j  (reduction over the tile's 128 keys) ----
-    float* dst_base = p.dq_acc + (p.deterministic ? (int64_t)j * p.split_stride : 0) +
-                      (int64_t)h * p.head_stride + (sg.ws_row0 + q0) * DQK;
+    // Buffer stores/atomics over the block's valid rows drop the rows past the segment end.
+    const __amdgpu_buffer_rsrc_t rdq = buffer_rsrc(
+        p.dq_acc + (DET ? (int64_t)j * p.split_stride : 0) + (int64_t)h * p.head_stride +
+            (sg.ws_row0 + q0) * DQK,
+        (uint32_t)nq * DQK * 4u);
 #pragma unroll
     for (int tt = 0; tt < T::NTW; ++tt) {
       const int ti = wave + 4 * tt;
       if (NT % 4 == 0 || ti < NT) {
         const int mq = ti / (DQK / 32);
         const int nd = ti - mq * (DQK / 32);
+        // all dS operands of the tile first, so the reads overlap each other
+        bf16x8 da[TN / 16];
+#pragma unroll
+        for (int kk = 0; kk < TN / 16; ++kk) {
+          const int kb = 16 * kk + 8 * hi + tr_row;
+          da[kk] = tr_read(&st_lds[kb * SS + 32 * mq + tr_col], &st_lds[(kb + 4) * SS + 32 * mq + tr_col]);
+        }
         f32x16 acc = f32x16{};
 #pragma unroll
         for (int kk = 0; kk < TN / 16; ++kk) {
           const int kb = 16 * kk + 8 * hi + tr_row;
-          const bf16x8 a = tr_read(&st_lds[kb * SS + 32 * mq + tr_col], &st_lds[(kb + 4) * SS + 32 * mq + tr_col]);
           bf16x8 bk;
           if (T::KT_REGS) {
             bk = kt[kk];
           } else {
             bk = tr_read(&k_lds[kb * KS + 32 * nd + tr_col], &k_lds[(kb + 4) * KS + 32 * nd + tr_col]);
           }
-          acc = mfma(a, bk, acc);
+          acc = mfma(da[kk], bk, acc);
         }
-        // result register r: query 32mq + 8(r/4) + 4hi + r%4, column 32nd + l32
-        const int off0 = (32 * mq + 4 * hi) * DQK + 32 * nd + l32;
-        if (nq == TM) {
-          if (p.deterministic) {
+        // Register r holds query row 32mq + 8(r/4) + 4hi + r%4, column 32nd + l%32: each store
+        // or atomic covers two 128-byte row segments.  Offsets go entirely in the per-lane
+        // operand (the scalar offset is outside the hardware range check), so rows at or past
+        // nq fall outside the resource.
+        const int voff = ((32 * mq + 4 * hi) * DQK + 32 * nd + l32) * 4;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) dst_base[off0 + (8 * (r >> 2) + (r & 3)) * DQK] = acc[r];
+        for (int r = 0; r < 16; ++r) {
+          const int off = voff + (8 * (r >> 2) + (r & 3)) * DQK * 4;
+          if (DET) {
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[r]), rdq, off, 0, 0);
           } else {
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-              unsafeAtomicAdd(&dst_base[off0 + (8 * (r >> 2) + (r & 3)) * DQK], acc[r]);
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int ql = 32 * mq + 8 * (r >> 2) + 4 * hi + (r & 3);
-            if (ql < nq) {
-              if (p.deterministic) {
-                dst_base[off0 + (8 * (r >> 2) + (r & 3)) * DQK] = acc[r];
-              } else {
-                unsafeAtomicAdd(&dst_base[off0 + (8 * (r >> 2) + (r & 3)) * DQK], acc[r]);
-              }
-            }
+            __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[r], rdq, off, 0, 0);
           }
         }
       }
     }
-    if (n + 1 < nsteps) store_step(n + 1);  // this step's tiles are dead: stage step n+1
+    if (n + 1 < nsteps) store_step();  // this step's tiles are dead: stage step n+1
+    h = h_next;
+    q0 = q0_next;
   }
 
   // ---- epilogue: dK = scale * dK_acc, dV = dV_acc as bf16 ----
@@ -604,20 +624,29 @@ hipError_t launch_dot(const Plan& plan, const KParams& kp, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int DQK, int DV, int TM>
+static void launch_main_t(const Plan& plan, const KParams& kp, dim3 grid, hipStream_t stream) {
+  if (plan.deterministic) {
+    hipLaunchKernelGGL((k_bwd_main<DQK, DV, TM, true>), grid, dim3(256), 0, stream, kp);
+  } else {
+    hipLaunchKernelGGL((k_bwd_main<DQK, DV, TM, false>), grid, dim3(256), 0, stream, kp);
+  }
+}
+
 hipError_t launch_main(const Plan& plan, const KParams& kp, hipStream_t stream) {
   const int64_t items = (int64_t)plan.n_kv_tiles * plan.Hkv * plan.B;
   if (items == 0) return hipSuccess;
   const dim3 grid((unsigned)items);
   if (plan.d_qk == 64) {
-    hipLaunchKernelGGL((k_bwd_main<64, 64, 64>), grid, dim3(256), 0, stream, kp);
+    launch_main_t<64, 64, 64>(plan, kp, grid, stream);
   } else if (plan.d_qk == 128) {
     if (plan.tile_m == 32) {
-      hipLaunchKernelGGL((k_bwd_main<128, 128, 32>), grid, dim3(256), 0, stream, kp);
+      launch_main_t<128, 128, 32>(plan, kp, grid, stream);
     } else {
-      hipLaunchKernelGGL((k_bwd_main<128, 128, 64>), grid, dim3(256), 0, stream, kp);
+      launch_main_t<128, 128, 64>(plan, kp, grid, stream);
     }
   } else {
-    hipLaunchKernelGGL((k_bwd_main<192, 128, 32>), grid, dim3(256), 0, stream, kp);
+    launch_main_t<192, 128, 32>(plan, kp, grid, stream);
   }
   return hipGetLastError();
 }
