@@ -104,6 +104,7 @@ class PlanInfo(ctypes.Structure):
         ("workspace_bytes", ctypes.c_int64),
         ("pairs", ctypes.c_int64),
         ("flops", ctypes.c_double),
+        ("acc_rows", ctypes.c_int64),
     ]
 
     def as_dict(self):

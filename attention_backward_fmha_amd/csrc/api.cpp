@@ -70,6 +70,7 @@ fmha::KParams make_params(const fmha_bwd_args* a, const fmha::Plan& p, void* ws)
   k.split_stride = p.split_stride;
   k.head_stride = p.head_stride;
   k.rows_q = p.rows_q;
+  k.acc_pad = p.acc_pad;
   k.B = p.B;
   k.Hq = p.Hq;
   k.Hkv = p.Hkv;
@@ -185,6 +186,7 @@ int fmha_bwd_plan_query(const fmha_bwd_args* args, fmha_bwd_plan_info* info) {
   info->nsplits = p.nsplits;
   info->needs_zero = p.needs_zero ? 1 : 0;
   info->rows_q = p.rows_q;
+  info->acc_rows = p.acc_rows;
   info->d_offset = p.d_offset;
   info->dq_acc_offset = p.dq_acc_offset;
   info->dq_acc_bytes = p.dq_acc_bytes;

@@ -21,7 +21,7 @@ struct KParams {
   uint16_t* dv;
   float* dsum;    // workspace: D = rowsum(dO * O), [Hq][rows_q]
   float* lse2;    // workspace: LSE * log2(e), [Hq][rows_q]
-  float* dq_acc;  // workspace: fp32 dQ partials, [nsplits][Hq][rows_q][d_qk]
+  float* dq_acc;  // workspace: fp32 dQ partials, [nsplits][Hq][acc_rows][d_qk]
   const int32_t* seqstart_q;  // device offsets, null in batch mode
   const int32_t* seqstart_k;
   int64_t q_s[3], k_s[3], v_s[3], o_s[3], do_s[3], dq_s[3], dk_s[3], dv_s[3];
@@ -29,6 +29,7 @@ struct KParams {
   int64_t split_stride;  // elements
   int64_t head_stride;   // elements
   int64_t rows_q;
+  int acc_pad;           // accumulator rows of padding per segment (0 or tile_m)
   int B, Hq, Hkv, group_size, Sq, Sk;
   int mask_type, window_left, window_right;
   int deterministic;

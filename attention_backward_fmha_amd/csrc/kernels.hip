@@ -18,10 +18,10 @@
 // long as A and B use the same one; the kernels use that to feed P and dS straight from the
 // result registers of S and dP into the next products.
 //
-// Operands whose reduction index runs along LDS rows (dO and Q in dV/dK, dS^T and K in dQ) are
-// read with ds_read_b64_tr_b16: in each 16-lane group, lane s points at 4 consecutive elements
-// of row (s/4), columns 4*(s%4)..4*(s%4)+3 of a 4x16 block, and lane i receives column i of the
-// block (4 values, one per row).  So every tile is stored row-major in LDS exactly once.
+// The K operand of dQ (reduction over keys, which run along the K tile's rows) is read once
+// per work item with ds_read_b64_tr_b16: in each 16-lane group, lane s points at 4 consecutive
+// elements of row (s/4), columns 4*(s%4)..4*(s%4)+3 of a 4x16 block, and lane i receives
+// column i of the block (4 values, one per row).
 #include "kernels.h"
 #include "tiling.h"
 
@@ -41,7 +41,8 @@ struct Seg {
   int64_t q_row0;   // first tensor row of the segment (0 in batch mode)
   int64_t k_row0;
   int64_t lq, lk;   // segment lengths
-  int64_t ws_row0;  // first workspace row (b*Sq in batch mode)
+  int64_t ws_row0;  // first workspace row of D and LSE2 (b*Sq in batch mode)
+  int64_t acc_row0; // first accumulator row: ws_row0 + b*acc_pad
 };
 
 // Segment bounds; b is uniform across the work group and readfirstlane keeps the loaded
@@ -65,6 +66,7 @@ __device__ __forceinline__ Seg seg_of(const KParams& p, int b) {
     s.lk = p.Sk;
     s.ws_row0 = (int64_t)b * p.Sq;
   }
+  s.acc_row0 = s.ws_row0 + (int64_t)b * p.acc_pad;
   return s;
 }
 
@@ -137,16 +139,19 @@ __global__ __launch_bounds__(256) void k_dot(const KParams p) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Stage 2: the main kernel.  256 threads = 4 waves; wave w owns keys 32w..32w+31 of the tile.
+// Stage 2: the main kernel.  256 threads = 4 waves; wave w owns 32 keys of the tile (keys
+// 32w .. 32w+31, spread over its lanes by kmap below).
 //
 // The (query head, query block) steps of a work item form one flat loop.  While step n is
 // computed, the global loads of step n+1 are in flight into registers; after the step's second
 // barrier they are written to LDS twice: row-major (the A operand of S and dP) and transposed
 // with the block's queries along the row (the B operand of dV and dK).  The transposed copies
 // store queries in the order the P/dS result registers feed the reduction slots, so every
-// operand of S, dP, dV and dK is a plain 16-byte LDS read.  LDS measurements on gfx950 put
-// 16-byte reads at ~121 B/clk per CU and every 8-byte access (transposing reads included) at
-// ~40 B/clk, hence the copies.
+// operand of S, dP, dV and dK is a plain 16-byte LDS read.  dS goes to LDS row-major (one row
+// per query) after an exchange between lanes that gives every lane 8 consecutive keys of one
+// query, so the A operand of dQ = dS K is a 16-byte read as well.  LDS measurements on gfx950
+// put 16-byte accesses at ~121 B/clk per CU and every 8-byte access (transposing reads
+// included) at ~40 B/clk.
 // ------------------------------------------------------------------------------------------
 template <int DQK, int DV, int TM_>
 struct MainTile {
@@ -156,10 +161,13 @@ struct MainTile {
   static constexpr int QS = DQK + 8;   // row-major strides in elements (16-byte pad)
   static constexpr int OS = DV + 8;
   static constexpr int KS = DQK + 8;
-  static constexpr int SS = TM + 8;    // dS^T rows (one per key)
+  static constexpr int SR = TN + 8;    // dS rows (one per query)
   static constexpr int TS = TM + 8;    // transposed copies: one row per head-dim column
-  static constexpr int QBLK = (TM / 4) * (DQK / 8);  // 4x8 staging blocks of Q
-  static constexpr int OBLK = (TM / 4) * (DV / 8);   // ... of dO (ids after Q's)
+  // staging blocks of RB query rows x 8 columns, one per thread and step; 8-row blocks give
+  // 16-byte transposed writes and are used whenever the Q blocks fill whole waves
+  static constexpr int RB = ((TM / 8) * (DQK / 8)) % 64 == 0 ? 8 : 4;
+  static constexpr int QBLK = (TM / RB) * (DQK / 8);  // staging blocks of Q
+  static constexpr int OBLK = (TM / RB) * (DV / 8);   // ... of dO (ids after Q's)
   static constexpr int NV = (QBLK + OBLK + 255) / 256;  // blocks per thread
   static constexpr int NT = MT * (DQK / 32);            // 32x32 tiles of a dQ block
   static constexpr int NTW = (NT + 3) / 4;              // dQ tiles per wave
@@ -177,58 +185,109 @@ __device__ __forceinline__ int tpos(int q) {
   return (q & ~12) | ((q & 4) << 1) | ((q & 8) >> 1);
 }
 
-// P and dS of one step.  Result register r of row tile m holds query 32m + 8(r/4) + 4*hi + r%4
-// and this lane's key; P and dS come out already packed as bf16 MFMA operands.
-template <bool MASKED, int MT>
-__device__ __forceinline__ void probs_and_grads(const f32x16 (&s)[MT], const f32x16 (&dp)[MT],
-                                                const float* lse_lds, const float* dd_lds,
-                                                float scale_log2, int hi, int base_d, int lo_d,
-                                                int hi_d, int nq, bool key_ok,
-                                                bf16x8 (&pa)[MT][2], bf16x8 (&sa)[MT][2]) {
-#pragma unroll
-  for (int m = 0; m < MT; ++m) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int qr = 32 * m + 8 * c + 4 * hi;
-      const f32x4 l4 = *(const f32x4*)&lse_lds[qr];
-      const f32x4 d4 = *(const f32x4*)&dd_lds[qr];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * c + e;
-        float pv = __builtin_amdgcn_exp2f(s[m][r] * scale_log2 - l4[e]);
-        if (MASKED) {
-          const int dlt = base_d - (qr + e);
-          const bool ok = (dlt >= lo_d) & (dlt <= hi_d) & (qr + e < nq) & key_ok;
-          pv = ok ? pv : 0.f;
-        }
-        const float dsv = pv * (dp[m][r] - d4[e]);
-        pa[m][c >> 1][(c & 1) * 4 + e] = (__bf16)pv;
-        sa[m][c >> 1][(c & 1) * 4 + e] = (__bf16)dsv;
-      }
-    }
-  }
+// Key (inside the wave's 32) held by lane l32: bit 4 of the lane is bit 0 of the key and lane
+// bits 0..3 are key bits 1..4.  With it the dS exchange below ends with lane bits 2, 3 naming
+// an aligned group of 8 keys and the exchanged register bits naming the key inside the group.
+__device__ __forceinline__ int kmap(int l) {
+  return ((l >> 4) & 1) | ((l & 15) << 1);
 }
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// Write a 4-query x 8-column block (rows r0..r0+3 of `x`, column chunk c8) into a row-major
-// tile and into the transposed copy.
-template <int RS, int TSS>
-__device__ __forceinline__ void stage_block(uint16_t* rm, uint16_t* tr, const u32x4 (&x)[4],
-                                            int r0, int c8) {
+__device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
+  return __builtin_bit_cast(unsigned, bf16x2{(__bf16)lo, (__bf16)hi});
+}
+
+// Value of lane (l ^ 1) and of lane (l ^ 2) (DPP quad permutations).
+__device__ __forceinline__ unsigned xor1(unsigned v) {
+  return (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);
+}
+__device__ __forceinline__ unsigned xor2(unsigned v) {
+  return (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);
+}
+
+// dS of one 32-query tile to LDS, one row per query.  On entry d[4c + e] is dS(query
+// 8c + 4*hi + e of the tile, this lane's key).  Three exchanges move key bits into registers
+// and query bits into lanes: lane bit 4 <-> e bit 0 (permlane16 swap, on fp32 values), then
+// on bf16 pairs lane bit 0 <-> e bit 1 and lane bit 1 <-> c bit 0 (DPP).  Afterwards the lane
+// holds, for c bit 1 = u, 8 consecutive keys 8*(lane bits 2,3) + 0..7 of query
+// 16u + 8*(lane bit 1) + 4*hi + 2*(lane bit 0) + (lane bit 4), as one 16-byte row segment.
+template <int SR>
+__device__ __forceinline__ void write_ds_tile(uint16_t* ds_lds, const float (&d)[16], int row0,
+                                              int col0, int lane) {
+  unsigned w[4][2];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) *(u32x4*)&rm[(r0 + u) * RS + c8 * 8] = x[u];
-  const int pos = tpos(r0);
+  for (int c = 0; c < 4; ++c) {
+#pragma unroll
+    for (int e1 = 0; e1 < 2; ++e1) {
+      const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(d[4 * c + 2 * e1]),
+                                                      __float_as_uint(d[4 * c + 2 * e1 + 1]),
+                                                      false, false);
+      w[c][e1] = pack_bf16(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    }
+  }
+  const bool x0 = (lane & 1) != 0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const unsigned t0 = xor1(w[c][0]);
+    const unsigned t1 = xor1(w[c][1]);
+    const unsigned n0 = x0 ? t1 : w[c][0];
+    const unsigned n1 = x0 ? w[c][1] : t0;
+    w[c][0] = n0;
+    w[c][1] = n1;
+  }
+  const bool x1 = (lane & 2) != 0;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const unsigned a = w[2 * u][s];
+      const unsigned b = w[2 * u + 1][s];
+      const unsigned ta = xor2(a);
+      const unsigned tb = xor2(b);
+      w[2 * u][s] = x1 ? tb : a;
+      w[2 * u + 1][s] = x1 ? b : ta;
+    }
+  }
+  const int row = row0 + 8 * ((lane >> 1) & 1) + 4 * (lane >> 5) + 2 * (lane & 1) + ((lane >> 4) & 1);
+  const int col = col0 + 8 * ((lane >> 2) & 3);
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+    *(u32x4*)&ds_lds[(row + 16 * u) * SR + col] = u32x4{w[2 * u][0], w[2 * u][1], w[2 * u + 1][0], w[2 * u + 1][1]};
+}
+
+// Query row of register u of a staging block whose first row is r0.  8-row blocks hold rows
+// r0 + {0..3, 8..11} (r0 = 16a + 4b), which are 8 consecutive transposed positions.
+template <int RB>
+__device__ __forceinline__ int block_row(int r0, int u) {
+  return RB == 8 ? r0 + (u & 3) + 8 * (u >> 2) : r0 + u;
+}
+
+// Write one staging block (RB rows of x, column chunk c8) into a row-major tile and into the
+// transposed copy, where its rows occupy positions pos0 .. pos0 + RB - 1.
+template <int RB, int TSS>
+__device__ __forceinline__ void stage_block(uint16_t* rm, uint16_t* tr, int RS,
+                                            const u32x4 (&x)[RB], int r0, int pos0, int c8) {
+#pragma unroll
+  for (int u = 0; u < RB; ++u) *(u32x4*)&rm[block_row<RB>(r0, u) * RS + c8 * 8] = x[u];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    // columns 2k (low halves) and 2k+1 (high halves) of the 4 rows
-    const unsigned lo01 = __builtin_amdgcn_perm(x[1][k], x[0][k], 0x05040100u);
-    const unsigned lo23 = __builtin_amdgcn_perm(x[3][k], x[2][k], 0x05040100u);
-    const unsigned hi01 = __builtin_amdgcn_perm(x[1][k], x[0][k], 0x07060302u);
-    const unsigned hi23 = __builtin_amdgcn_perm(x[3][k], x[2][k], 0x07060302u);
-    *(u32x2*)&tr[(c8 * 8 + 2 * k) * TSS + pos] = u32x2{lo01, lo23};
-    *(u32x2*)&tr[(c8 * 8 + 2 * k + 1) * TSS + pos] = u32x2{hi01, hi23};
+    // columns 2k (low halves) and 2k+1 (high halves), rows in position order
+    unsigned lo[RB / 2], hi[RB / 2];
+#pragma unroll
+    for (int t = 0; t < RB / 2; ++t) {
+      lo[t] = __builtin_amdgcn_perm(x[2 * t + 1][k], x[2 * t][k], 0x05040100u);
+      hi[t] = __builtin_amdgcn_perm(x[2 * t + 1][k], x[2 * t][k], 0x07060302u);
+    }
+    if constexpr (RB == 8) {
+      *(u32x4*)&tr[(c8 * 8 + 2 * k) * TSS + pos0] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+      *(u32x4*)&tr[(c8 * 8 + 2 * k + 1) * TSS + pos0] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+    } else {
+      *(u32x2*)&tr[(c8 * 8 + 2 * k) * TSS + pos0] = u32x2{lo[0], lo[1]};
+      *(u32x2*)&tr[(c8 * 8 + 2 * k + 1) * TSS + pos0] = u32x2{hi[0], hi[1]};
+    }
   }
 }
 
@@ -236,15 +295,15 @@ template <int DQK, int DV, int TM_, bool DET>
 __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
   using T = MainTile<DQK, DV, TM_>;
   constexpr int TM = T::TM, MT = T::MT, TN = T::TN, QS = T::QS, OS = T::OS, KS = T::KS,
-                SS = T::SS, TS = T::TS, NT = T::NT;
+                SR = T::SR, TS = T::TS, NT = T::NT, RB = T::RB;
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[TN * KS];    // K_j, row-major
   __shared__ __attribute__((aligned(16))) uint16_t q_lds[TM * QS];    // Q_i, row-major
   __shared__ __attribute__((aligned(16))) uint16_t o_lds[TM * OS];    // dO_i, row-major
   __shared__ __attribute__((aligned(16))) uint16_t qt_lds[DQK * TS];  // Q_i transposed
   __shared__ __attribute__((aligned(16))) uint16_t ot_lds[DV * TS];   // dO_i transposed
-  __shared__ __attribute__((aligned(16))) uint16_t st_lds[TN * SS];   // dS^T (key-major)
-  __shared__ __attribute__((aligned(16))) float lse_lds[TM];         // LSE_i * log2(e)
-  __shared__ __attribute__((aligned(16))) float dd_lds[TM];          // D_i
+  __shared__ __attribute__((aligned(16))) uint16_t ds_lds[TM * SR];   // dS (query-major)
+  __shared__ __attribute__((aligned(16))) float lse_lds[256];        // LSE_i * log2(e)
+  __shared__ __attribute__((aligned(16))) float dd_lds[256];         // D_i
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -269,17 +328,20 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
   qblocks_for_tile(mg, sg.lq, sg.lk, j, TM, TN, &qb_lo, &qb_hi);
   const int nblk = qb_hi >= qb_lo ? (int)(qb_hi - qb_lo + 1) : 0;
   const int nsteps = nblk * p.group_size;
-  // allowed  <=>  lo_d <= key - row <= hi_d (and both inside the segment)
-  const int64_t lo64 = mg.left >= 0 ? mg.delta - mg.left : INT64_MIN / 2;
-  const int64_t hi64 = mg.right >= 0 ? mg.delta + mg.right : INT64_MAX / 2;
-  const int lo_d = (int)max(lo64, (int64_t)INT32_MIN);
-  const int hi_d = (int)min(hi64, (int64_t)INT32_MAX);
+  // allowed  <=>  lo_d <= key - row <= hi_d (and both inside the segment).  key - row always
+  // lies in [-lq, lk], so the bounds are clamped to that range and the test becomes one
+  // unsigned compare: (unsigned)(key - row - lo_d) <= span.
+  const int64_t lo64 = mg.left >= 0 ? mg.delta - mg.left : -sg.lq;
+  const int64_t hi64 = mg.right >= 0 ? mg.delta + mg.right : sg.lk;
+  const int lo_d = (int)max(lo64, -sg.lq);
+  const int hi_d = (int)min(hi64, sg.lk);
+  const unsigned span = (unsigned)(hi_d - lo_d);  // only used when some pair is allowed
 
   const int tr_row = i16 >> 2;                        // row inside a 4-row transpose block
   const int tr_col = 16 * (g16 & 1) + 4 * (i16 & 3);  // column offset inside a 32-wide tile
 
   // K tile -> LDS (row-major); the wave's V rows -> registers (B operand of dP).
-  const int key_l = wave * 32 + l32;
+  const int key_l = wave * 32 + kmap(l32);
   const bool key_ok = key_l < nk;
   bf16x8 vw[DV / 16];
   {
@@ -298,6 +360,11 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
     }
   }
   __syncthreads();
+
+  // The wave's K rows as the B operand of S, kept in registers for the whole work item.
+  bf16x8 kf[DQK / 16];
+#pragma unroll
+  for (int kk = 0; kk < DQK / 16; ++kk) kf[kk] = *(const bf16x8*)&k_lds[key_l * KS + 16 * kk + 8 * hi];
 
   // dQ work of this wave: tiles ti = wave + 4*tt (tt < NTW) of the MT x (DQK/32) grid.  With
   // KT_REGS the wave's K operand (its 32 head-dim columns over the tile's keys) is read once.
@@ -318,46 +385,56 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
 #pragma unroll
   for (int n = 0; n < DV / 32; ++n) dv_acc[n] = f32x16{};
 
-  // ---- prefetch registers for one step: 4-row x 8-column blocks of Q and dO, LSE2, D ----
+  // ---- prefetch registers for one step: RB-row x 8-column blocks of Q and dO, LSE2, D ----
   // Block ids tid + 256v: ids below QBLK are Q blocks, the next OBLK are dO blocks; block id
-  // covers rows 4*(id % (TM/4)) .. +3 and column chunk id / (TM/4).  Buffer loads over the
-  // block's valid rows return zeros for rows past the segment end.  The registers are not
-  // touched until they are written to LDS, so nothing waits for the loads before then.
-  // Offsets inside a block are 32-bit (the plan bounds the sequence strides).
-  u32x4 pre[T::NV][4];
+  // covers row group id % (TM/RB) and column chunk id / (TM/RB).  Buffer loads over the
+  // block's valid rows return zeros for rows past the segment end (and for everything when
+  // the step does not exist, whose resources are empty).  The registers are not touched until
+  // they are written to LDS, so nothing waits for the loads before then.  Offsets inside a
+  // block are 32-bit (the plan bounds the sequence strides).
+  u32x4 pre[T::NV][RB];
   float lpre = 0.f, dpre = 0.f;
   const int qs1 = (int)p.q_s[1];
   const int os1 = (int)p.do_s[1];
-  auto load_step = [&](int h, int64_t q0) {
-    const int nq = (int)min((int64_t)TM, sg.lq - q0);
+  auto blk_geom = [&](int id, int& r0, int& pos0, int& c8) {
+    const int rg = id % (TM / RB);
+    c8 = id / (TM / RB);
+    if (RB == 8) {
+      r0 = 16 * (rg >> 1) + 4 * (rg & 1);
+      pos0 = 8 * rg;
+    } else {
+      r0 = 4 * rg;
+      pos0 = tpos(r0);
+    }
+  };
+  int nq_pre = 0;  // valid rows of the prefetched step
+  auto load_step = [&](bool valid, int h, int64_t q0) {
+    const int nq = valid ? (int)min((int64_t)TM, sg.lq - q0) : 0;
+    nq_pre = nq;
     const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(
-        p.q + elem_off(p.q_s, group, b, sg.q_row0 + q0, h), (uint32_t)((nq - 1) * qs1 + DQK) * 2u);
+        p.q + (valid ? elem_off(p.q_s, group, b, sg.q_row0 + q0, h) : 0),
+        nq > 0 ? (uint32_t)((nq - 1) * qs1 + DQK) * 2u : 0u);
     const __amdgpu_buffer_rsrc_t ro = buffer_rsrc(
-        p.dout + elem_off(p.do_s, group, b, sg.q_row0 + q0, h), (uint32_t)((nq - 1) * os1 + DV) * 2u);
+        p.dout + (valid ? elem_off(p.do_s, group, b, sg.q_row0 + q0, h) : 0),
+        nq > 0 ? (uint32_t)((nq - 1) * os1 + DV) * 2u : 0u);
 #pragma unroll
     for (int v = 0; v < T::NV; ++v) {
       const int id0 = tid + 256 * v;
       if ((T::QBLK + T::OBLK) % 256 == 0 || id0 < T::QBLK + T::OBLK) {
         const bool isq = __builtin_amdgcn_readfirstlane(id0) < T::QBLK;  // wave-uniform
         const int id = isq ? id0 : id0 - T::QBLK;
-        const int r0 = 4 * (id % (TM / 4));
-        const int c8 = id / (TM / 4);
-        if (isq) {
+        const __amdgpu_buffer_rsrc_t rs = isq ? rq : ro;
+        const int st = isq ? qs1 : os1;
+        int r0, pos0, c8;
+        blk_geom(id, r0, pos0, c8);
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
-            pre[v][u] = __builtin_amdgcn_raw_buffer_load_b128(rq, ((r0 + u) * qs1 + c8 * 8) * 2, 0, 0);
-        } else {
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-            pre[v][u] = __builtin_amdgcn_raw_buffer_load_b128(ro, ((r0 + u) * os1 + c8 * 8) * 2, 0, 0);
-        }
+        for (int u = 0; u < RB; ++u)
+          pre[v][u] = __builtin_amdgcn_raw_buffer_load_b128(rs, (block_row<RB>(r0, u) * st + c8 * 8) * 2, 0, 0);
       }
     }
-    if (tid < TM) {
-      const int64_t row0 = (int64_t)h * p.rows_q + sg.ws_row0 + q0;
-      lpre = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(p.lse2 + row0, (uint32_t)nq * 4u), tid * 4, 0, 0));
-      dpre = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(p.dsum + row0, (uint32_t)nq * 4u), tid * 4, 0, 0));
-    }
+    const int64_t row0 = valid ? (int64_t)h * p.rows_q + sg.ws_row0 + q0 : 0;
+    lpre = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(p.lse2 + row0, (uint32_t)nq * 4u), tid * 4, 0, 0));
+    dpre = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(p.dsum + row0, (uint32_t)nq * 4u), tid * 4, 0, 0));
   };
   auto store_step = [&]() {
 #pragma unroll
@@ -366,18 +443,88 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
       if ((T::QBLK + T::OBLK) % 256 == 0 || id0 < T::QBLK + T::OBLK) {
         const bool isq = __builtin_amdgcn_readfirstlane(id0) < T::QBLK;  // wave-uniform
         const int id = isq ? id0 : id0 - T::QBLK;
-        const int r0 = 4 * (id % (TM / 4));
-        const int c8 = id / (TM / 4);
-        if (isq) {
-          stage_block<QS, TS>(q_lds, qt_lds, pre[v], r0, c8);
-        } else {
-          stage_block<OS, TS>(o_lds, ot_lds, pre[v], r0, c8);
-        }
+        int r0, pos0, c8;
+        blk_geom(id, r0, pos0, c8);
+        stage_block<RB, TS>(isq ? q_lds : o_lds, isq ? qt_lds : ot_lds, isq ? QS : OS, pre[v], r0,
+                            pos0, c8);
       }
     }
-    if (tid < TM) {
-      lse_lds[tid] = lpre;
-      dd_lds[tid] = dpre;
+    // rows past the segment end get LSE = +inf, so their P is exactly 0
+    lse_lds[tid] = tid < nq_pre ? lpre : __builtin_inff();
+    dd_lds[tid] = dpre;
+  };
+
+  // The arithmetic of one step between its two barriers: S, dP, then per 32-query tile P, dS,
+  // the dV/dK products and the dS tile to LDS (so the exponentials of one tile can overlap
+  // the products of the other).
+  auto compute_step = [&](int q0) {
+    f32x16 s_acc[MT];
+    f32x16 dp_acc[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      s_acc[m] = f32x16{};
+      dp_acc[m] = f32x16{};
+    }
+    // ---- S = Q_i K_w^T and dP = dO_i V_w^T (MT row tiles of 32 queries) ----
+    // all operands of a row tile are read before its products, so the reads overlap
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      bf16x8 qa[DQK / 16], oa[DV / 16];
+#pragma unroll
+      for (int kk = 0; kk < DQK / 16; ++kk)
+        qa[kk] = *(const bf16x8*)&q_lds[(32 * m + l32) * QS + 16 * kk + 8 * hi];
+#pragma unroll
+      for (int kk = 0; kk < DV / 16; ++kk)
+        oa[kk] = *(const bf16x8*)&o_lds[(32 * m + l32) * OS + 16 * kk + 8 * hi];
+#pragma unroll
+      for (int kk = 0; kk < DQK / 16; ++kk) s_acc[m] = mfma(qa[kk], kf[kk], s_acc[m]);
+#pragma unroll
+      for (int kk = 0; kk < DV / 16; ++kk) dp_acc[m] = mfma(oa[kk], vw[kk], dp_acc[m]);
+    }
+    // mask: pair (row, key) allowed iff (unsigned)(key - row - lo_d) <= span; keys past the
+    // tile end get an offset that fails for every row of the block
+    const int t0 = key_ok ? (int)(key0 - q0) + key_l - lo_d - 4 * hi : (int)span + TM + 1;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      // ---- P, dS of tile m: register r holds query 32m + 8(r/4) + 4*hi + r%4 ----
+      bf16x8 pa[2], sa[2];
+      float ds32[16];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int qr = 32 * m + 8 * c + 4 * hi;
+        const f32x4 l4 = *(const f32x4*)&lse_lds[qr];
+        const f32x4 d4 = *(const f32x4*)&dd_lds[qr];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * c + e;
+          float pv = __builtin_amdgcn_exp2f(s_acc[m][r] * p.scale_log2 - l4[e]);
+          pv = (unsigned)(t0 - (32 * m + 8 * c + e)) <= span ? pv : 0.f;
+          const float dsv = pv * (dp_acc[m][r] - d4[e]);
+          pa[c >> 1][(c & 1) * 4 + e] = (__bf16)pv;
+          sa[c >> 1][(c & 1) * 4 + e] = (__bf16)dsv;
+          ds32[r] = dsv;
+        }
+      }
+      // ---- dV += P^T dO_i ; dK += dS^T Q_i over this tile's queries ----
+      // reduction step ks = 2m + t covers transposed positions 16ks .. 16ks + 15
+      bf16x8 bo[2][DV / 32], bq[2][DQK / 32];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int n2 = 0; n2 < DV / 32; ++n2)
+          bo[t][n2] = *(const bf16x8*)&ot_lds[(32 * n2 + l32) * TS + 16 * (2 * m + t) + 8 * hi];
+#pragma unroll
+        for (int n2 = 0; n2 < DQK / 32; ++n2)
+          bq[t][n2] = *(const bf16x8*)&qt_lds[(32 * n2 + l32) * TS + 16 * (2 * m + t) + 8 * hi];
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int n2 = 0; n2 < DV / 32; ++n2) dv_acc[n2] = mfma(pa[t], bo[t][n2], dv_acc[n2]);
+#pragma unroll
+        for (int n2 = 0; n2 < DQK / 32; ++n2) dk_acc[n2] = mfma(sa[t], bq[t][n2], dk_acc[n2]);
+      }
+      write_ds_tile<SR>(ds_lds, ds32, 32 * m, 32 * wave, lane);
     }
   };
 
@@ -385,7 +532,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
   int h = g * p.group_size;
   int64_t q0 = qb_lo * TM;
   if (nsteps > 0) {
-    load_step(h, q0);
+    load_step(true, h, q0);
     store_step();
   }
 
@@ -397,137 +544,74 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
       q0_next = qb_lo * TM;
       ++h_next;
     }
-    __syncthreads();  // LDS holds step n; every wave is done with step n-1's dS^T
-    if (n + 1 < nsteps) load_step(h_next, q0_next);
+    __syncthreads();  // LDS holds step n; every wave is done with step n-1's dS
+    load_step(n + 1 < nsteps, h_next, q0_next);
 
-    // ---- S = Q_i K_w^T and dP = dO_i V_w^T (MT row tiles of 32 queries) ----
-    f32x16 s_acc[MT];
-    f32x16 dp_acc[MT];
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      s_acc[m] = f32x16{};
-      dp_acc[m] = f32x16{};
-    }
-#pragma unroll
-    for (int kk = 0; kk < DQK / 16; ++kk) {
-      const bf16x8 kb = *(const bf16x8*)&k_lds[key_l * KS + 16 * kk + 8 * hi];
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        const bf16x8 a = *(const bf16x8*)&q_lds[(32 * m + l32) * QS + 16 * kk + 8 * hi];
-        s_acc[m] = mfma(a, kb, s_acc[m]);
-      }
-    }
-#pragma unroll
-    for (int kk = 0; kk < DV / 16; ++kk) {
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        const bf16x8 a = *(const bf16x8*)&o_lds[(32 * m + l32) * OS + 16 * kk + 8 * hi];
-        dp_acc[m] = mfma(a, vw[kk], dp_acc[m]);
-      }
-    }
-
-    // ---- P, dS ----
-    const bool full = block_full(mg, sg.lq, sg.lk, q0, q0 + TM - 1, key0 + 32 * wave,
-                                 key0 + 32 * wave + 31);
-    const int base_d = (int)(key0 - q0) + key_l;
-    bf16x8 pa[MT][2];
-    bf16x8 sa[MT][2];
-    if (full) {
-      probs_and_grads<false, MT>(s_acc, dp_acc, lse_lds, dd_lds, p.scale_log2, hi, base_d, lo_d,
-                                 hi_d, nq, key_ok, pa, sa);
-    } else {
-      probs_and_grads<true, MT>(s_acc, dp_acc, lse_lds, dd_lds, p.scale_log2, hi, base_d, lo_d,
-                                hi_d, nq, key_ok, pa, sa);
-    }
-
-    // ---- dV += P^T dO_i ; dK += dS^T Q_i  (reduction over the block's queries) ----
-    // step ks = 2m + t covers transposed positions 16ks .. 16ks + 15
-#pragma unroll
-    for (int n2 = 0; n2 < DV / 32; ++n2) {
-#pragma unroll
-      for (int ks = 0; ks < 2 * MT; ++ks) {
-        const bf16x8 bo = *(const bf16x8*)&ot_lds[(32 * n2 + l32) * TS + 16 * ks + 8 * hi];
-        dv_acc[n2] = mfma(pa[ks >> 1][ks & 1], bo, dv_acc[n2]);
-      }
-    }
-#pragma unroll
-    for (int n2 = 0; n2 < DQK / 32; ++n2) {
-#pragma unroll
-      for (int ks = 0; ks < 2 * MT; ++ks) {
-        const bf16x8 bq = *(const bf16x8*)&qt_lds[(32 * n2 + l32) * TS + 16 * ks + 8 * hi];
-        dk_acc[n2] = mfma(sa[ks >> 1][ks & 1], bq, dk_acc[n2]);
-      }
-    }
-
-    // ---- dS^T to LDS: 4 consecutive queries per 8-byte store ----
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const bf16x8 v = sa[m][c >> 1];
-        const bf16x4 v4 = (c & 1) ? __builtin_shufflevector(v, v, 4, 5, 6, 7)
-                                  : __builtin_shufflevector(v, v, 0, 1, 2, 3);
-        *(bf16x4*)&st_lds[key_l * SS + 32 * m + 8 * c + 4 * hi] = v4;
-      }
-    }
-    __syncthreads();  // dS^T complete; every wave is done reading this step's Q, dO tiles
+    compute_step((int)q0);
+    __syncthreads();  // dS complete; every wave is done reading this step's Q, dO tiles
 
     // ---- dQ_i partial = dS K_j  (reduction over the tile's 128 keys) ----
-    // Buffer stores/atomics over the block's valid rows drop the rows past the segment end.
-    const __amdgpu_buffer_rsrc_t rdq = buffer_rsrc(
-        p.dq_acc + (DET ? (int64_t)j * p.split_stride : 0) + (int64_t)h * p.head_stride +
-            (sg.ws_row0 + q0) * DQK,
-        (uint32_t)nq * DQK * 4u);
+    // Deterministic: split j's block of this step (its own rows, padding included), stored
+    // lane by lane per 32x32 tile.  Atomic: fp32 adds into the row-major accumulator; the
+    // resource covers the block's valid rows, so rows past the segment end are dropped
+    // (offsets go entirely in the per-lane operand: the scalar offset is outside the range
+    // check).
+    const __amdgpu_buffer_rsrc_t rdq = DET
+        ? buffer_rsrc(p.dq_acc + (int64_t)j * p.split_stride + (int64_t)h * p.head_stride +
+                          (sg.acc_row0 + q0) * DQK, (uint32_t)TM * DQK * 4u)
+        : buffer_rsrc(p.dq_acc + (int64_t)h * p.head_stride + (sg.acc_row0 + q0) * DQK,
+                      (uint32_t)nq * DQK * 4u);
 #pragma unroll
     for (int tt = 0; tt < T::NTW; ++tt) {
       const int ti = wave + 4 * tt;
       if (NT % 4 == 0 || ti < NT) {
         const int mq = ti / (DQK / 32);
         const int nd = ti - mq * (DQK / 32);
-        // all dS operands of the tile first, so the reads overlap each other
         bf16x8 da[TN / 16];
 #pragma unroll
-        for (int kk = 0; kk < TN / 16; ++kk) {
-          const int kb = 16 * kk + 8 * hi + tr_row;
-          da[kk] = tr_read(&st_lds[kb * SS + 32 * mq + tr_col], &st_lds[(kb + 4) * SS + 32 * mq + tr_col]);
-        }
+        for (int kk = 0; kk < TN / 16; ++kk)
+          da[kk] = *(const bf16x8*)&ds_lds[(32 * mq + l32) * SR + 16 * kk + 8 * hi];
         f32x16 acc = f32x16{};
 #pragma unroll
         for (int kk = 0; kk < TN / 16; ++kk) {
-          const int kb = 16 * kk + 8 * hi + tr_row;
           bf16x8 bk;
           if (T::KT_REGS) {
             bk = kt[kk];
           } else {
+            const int kb = 16 * kk + 8 * hi + tr_row;
             bk = tr_read(&k_lds[kb * KS + 32 * nd + tr_col], &k_lds[(kb + 4) * KS + 32 * nd + tr_col]);
           }
           acc = mfma(da[kk], bk, acc);
         }
-        // Register r holds query row 32mq + 8(r/4) + 4hi + r%4, column 32nd + l%32: each store
-        // or atomic covers two 128-byte row segments.  Offsets go entirely in the per-lane
-        // operand (the scalar offset is outside the hardware range check), so rows at or past
-        // nq fall outside the resource.
-        const int voff = ((32 * mq + 4 * hi) * DQK + 32 * nd + l32) * 4;
+        if (DET) {
+          const int voff = (ti * 1024 + lane * 16) * 4;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int off = voff + (8 * (r >> 2) + (r & 3)) * DQK * 4;
-          if (DET) {
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[r]), rdq, off, 0, 0);
-          } else {
-            __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[r], rdq, off, 0, 0);
-          }
+          for (int u = 0; u < 4; ++u)
+            __builtin_amdgcn_raw_buffer_store_b128(
+                u32x4{__float_as_uint(acc[4 * u]), __float_as_uint(acc[4 * u + 1]),
+                      __float_as_uint(acc[4 * u + 2]), __float_as_uint(acc[4 * u + 3])},
+                rdq, voff + 16 * u, 0, 0);
+        } else {
+          // register r holds query row 32mq + 8(r/4) + 4hi + r%4, column 32nd + l%32: each
+          // atomic covers two 128-byte row segments
+          const int voff = ((32 * mq + 4 * hi) * DQK + 32 * nd + l32) * 4;
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(
+                acc[r], rdq, voff + (8 * (r >> 2) + (r & 3)) * DQK * 4, 0, 0);
         }
       }
     }
-    if (n + 1 < nsteps) store_step();  // this step's tiles are dead: stage step n+1
+    store_step();  // this step's tiles are dead: stage step n+1 (zeros after the last step)
     h = h_next;
     q0 = q0_next;
   }
 
   // ---- epilogue: dK = scale * dK_acc, dV = dV_acc as bf16 ----
+  // result row i of dK/dV is the key of lane i, 32*wave + kmap(i)
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const int kl = wave * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+    const int kl = wave * 32 + kmap(8 * (r >> 2) + 4 * hi + (r & 3));
     if (kl < nk) {
       const int64_t krow = sg.k_row0 + key0 + kl;
       uint16_t* dkp = p.dk + elem_off(p.dk_s, group, b, krow, g) + l32;
@@ -542,12 +626,110 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
 
 // ------------------------------------------------------------------------------------------
 // Stage 3: dQ = bf16(scale * sum of the partials), one block of TM rows per work group.
+// Deterministic mode sums, in ascending split order, exactly the key tiles whose rows meet the
+// block (qblocks_for_tile, as the main kernel) -- a contiguous range of tiles, since both ends
+// of a tile's query range move monotonically with its keys; the next split's loads are in
+// flight while the current one is added.
 // ------------------------------------------------------------------------------------------
 template <int DQK, int TM>
-__global__ __launch_bounds__(256) void k_dq_reduce(const KParams p) {
+__device__ __forceinline__ void reduce_tiles(const KParams& p, const Seg& sg, bool group, int b,
+                                             int h, int qb, int nq) {
   constexpr int TN = 128;
+  constexpr int NT = (TM / 32) * (DQK / 32);   // 32x32 tiles per block
+  constexpr int PPT = (NT * 64 + 255) / 256;   // (tile, lane) pairs per thread
+  const int tid = threadIdx.x;
+  const MaskGeom mg = mask_geom(p.mask_type, p.window_left, p.window_right, sg.lq, sg.lk);
+  const int ntiles = (int)((sg.lk + TN - 1) / TN);
+  int jlo = 0, jhi = -1;
+  for (int jt = 0; jt < ntiles; ++jt) {
+    int64_t lo, hi;
+    qblocks_for_tile(mg, sg.lq, sg.lk, jt, TM, TN, &lo, &hi);
+    const bool in = qb >= lo && qb <= hi;
+    if (in) {
+      if (jhi < 0) jlo = jt;
+      jhi = jt;
+    } else if (jhi >= 0) {
+      break;
+    }
+  }
+  const float* base = p.dq_acc + (int64_t)h * p.head_stride + (sg.acc_row0 + (int64_t)qb * TM) * DQK;
+  f32x4 acc[PPT][4];
+  f32x4 cur[PPT][4];
+#pragma unroll
+  for (int pr = 0; pr < PPT; ++pr)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[pr][u] = cur[pr][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto load = [&](int jt, f32x4 (&x)[PPT][4]) {
+    const float* src = base + (int64_t)jt * p.split_stride;
+#pragma unroll
+    for (int pr = 0; pr < PPT; ++pr) {
+      const int pair = tid + 256 * pr;
+      if ((NT * 64) % 256 == 0 || pair < NT * 64) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) x[pr][u] = *(const f32x4*)(src + pair * 16 + 4 * u);
+      }
+    }
+  };
+  if (jhi >= jlo) {
+    load(jlo, cur);
+    for (int jt = jlo; jt <= jhi; ++jt) {  // ascending split order
+      f32x4 nxt[PPT][4];
+      if (jt < jhi) load(jt + 1, nxt);
+#pragma unroll
+      for (int pr = 0; pr < PPT; ++pr)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc[pr][u] += cur[pr][u];
+      if (jt < jhi) {
+#pragma unroll
+        for (int pr = 0; pr < PPT; ++pr)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) cur[pr][u] = nxt[pr][u];
+      }
+    }
+  }
+  const int64_t q0 = (int64_t)qb * TM;
+#pragma unroll
+  for (int pr = 0; pr < PPT; ++pr) {
+    const int pair = tid + 256 * pr;
+    if ((NT * 64) % 256 == 0 || pair < NT * 64) {
+      const int ti = pair >> 6, ln = pair & 63;
+      const int mq = ti / (DQK / 32), nd = ti % (DQK / 32);
+      uint16_t* dst = p.dq + elem_off(p.dq_s, group, b, sg.q_row0 + q0, h) + 32 * nd + (ln & 31);
+#pragma unroll
+      for (int sl = 0; sl < 16; ++sl) {
+        const int row = 32 * mq + 8 * (sl >> 2) + 4 * (ln >> 5) + (sl & 3);
+        if (row < nq) dst[(int64_t)row * p.dq_s[1]] = to_bf16_bits(acc[pr][sl >> 2][sl & 3] * p.scale);
+      }
+    }
+  }
+}
+
+template <int DQK, int TM>
+__device__ __forceinline__ void reduce_rows(const KParams& p, const Seg& sg, bool group, int b,
+                                            int h, int qb, int nq) {
   constexpr int C4 = DQK / 4;                   // float4 chunks per row
   constexpr int PER = (TM * C4 + 255) / 256;    // chunks per thread
+  const int tid = threadIdx.x;
+  const int64_t q0 = (int64_t)qb * TM;
+  const float* base = p.dq_acc + (int64_t)h * p.head_stride + (sg.acc_row0 + q0) * DQK;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int c = tid + 256 * u;
+    const int r = c / C4;
+    if (r < nq) {
+      const f32x4 y = *(const f32x4*)(base + (int64_t)r * DQK + (c - r * C4) * 4) * p.scale;
+      bf16x4 o;
+      o[0] = (__bf16)y[0];
+      o[1] = (__bf16)y[1];
+      o[2] = (__bf16)y[2];
+      o[3] = (__bf16)y[3];
+      *(bf16x4*)(p.dq + elem_off(p.dq_s, group, b, sg.q_row0 + q0 + r, h) + (c - r * C4) * 4) = o;
+    }
+  }
+}
+
+template <int DQK, int TM>
+__global__ __launch_bounds__(256) void k_dq_reduce(const KParams p) {
   const int qb = blockIdx.x;
   const int h = blockIdx.y;
   const int b = blockIdx.z;
@@ -556,50 +738,10 @@ __global__ __launch_bounds__(256) void k_dq_reduce(const KParams p) {
   const int64_t q0 = (int64_t)qb * TM;
   if (q0 >= sg.lq) return;
   const int nq = (int)min((int64_t)TM, sg.lq - q0);
-  const MaskGeom mg = mask_geom(p.mask_type, p.window_left, p.window_right, sg.lq, sg.lk);
-  const int ntiles = (int)((sg.lk + TN - 1) / TN);
-  const int tid = threadIdx.x;
-  f32x4 acc[PER];
-#pragma unroll
-  for (int u = 0; u < PER; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const float* base = p.dq_acc + (int64_t)h * p.head_stride + (sg.ws_row0 + q0) * DQK;
   if (p.deterministic) {
-    for (int jt = 0; jt < ntiles; ++jt) {  // ascending split order
-      int64_t lo, hi;
-      qblocks_for_tile(mg, sg.lq, sg.lk, jt, TM, TN, &lo, &hi);
-      if (qb < lo || qb > hi) continue;
-      const float* src = base + (int64_t)jt * p.split_stride;
-#pragma unroll
-      for (int u = 0; u < PER; ++u) {
-        const int c = tid + 256 * u;
-        const int r = c / C4;
-        if (r < nq) {
-          const f32x4 x = *(const f32x4*)(src + (int64_t)r * DQK + (c - r * C4) * 4);
-          acc[u] += x;
-        }
-      }
-    }
+    reduce_tiles<DQK, TM>(p, sg, group, b, h, qb, nq);
   } else {
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int c = tid + 256 * u;
-      const int r = c / C4;
-      if (r < nq) acc[u] += *(const f32x4*)(base + (int64_t)r * DQK + (c - r * C4) * 4);
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    const int c = tid + 256 * u;
-    const int r = c / C4;
-    if (r < nq) {
-      const f32x4 y = acc[u] * p.scale;
-      bf16x4 o;
-      o[0] = (__bf16)y[0];
-      o[1] = (__bf16)y[1];
-      o[2] = (__bf16)y[2];
-      o[3] = (__bf16)y[3];
-      *(bf16x4*)(p.dq + elem_off(p.dq_s, group, b, sg.q_row0 + q0 + r, h) + (c - r * C4) * 4) = o;
-    }
+    reduce_rows<DQK, TM>(p, sg, group, b, h, qb, nq);
   }
 }
 

@@ -3,8 +3,11 @@
 // Workspace layout (byte offsets 256-aligned):
 //   D       fp32 [Hq][rows_q]                     rowsum(dO * O) from the first stage
 //   L       fp32 [Hq][rows_q]                     LSE * log2(e), also from the first stage
-//   dq_acc  fp32 [nsplits][Hq][rows_q][d_qk]      dQ partials (deterministic: split = key tile
-//                                                 index of the segment; atomic: one split)
+//   dq_acc  fp32 [nsplits][Hq][acc_rows][d_qk]    dQ partials (deterministic: split = key tile
+//                                                 index of the segment, blocks of tile_m rows
+//                                                 in matrix-core tile order, tile_m rows of
+//                                                 padding per segment; atomic: one split,
+//                                                 row-major, acc_rows = rows_q)
 // One layout serves batch and group mode: row = b*Sq + i in batch mode and seqstart_q[b] + i
 // in group mode (the physical token), so a ragged segment never aliases another one's rows --
 // unlike the layout mix-up in "[ROCm] Fix THD/ragged dQ backward on the bf16 dq_shuffle path
@@ -152,7 +155,9 @@ int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t el) {
   p->needs_zero = !p->deterministic;
   p->max_rows_q = p->rows_q;
 
-  p->head_stride = p->rows_q * p->d_qk;
+  p->acc_pad = p->deterministic ? p->tile_m : 0;
+  p->acc_rows = p->rows_q + (int64_t)p->B * p->acc_pad;
+  p->head_stride = p->acc_rows * p->d_qk;
   p->split_stride = (int64_t)p->Hq * p->head_stride;
   p->d_offset = 0;
   p->d_bytes = (int64_t)p->Hq * p->rows_q * 4;

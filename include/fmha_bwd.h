@@ -152,12 +152,21 @@ typedef struct fmha_bwd_plan_info {
   int32_t reserved;
   int64_t rows_q;          /* T_q: B*Sq (batch) or seqstart_q[B] (group) */
   int64_t d_offset;        /* byte offset of D = rowsum(dO*O), fp32 [Hq][rows_q] */
-  int64_t dq_acc_offset;   /* byte offset of the fp32 accumulator [nsplits][Hq][rows_q][d_qk] */
+  int64_t dq_acc_offset;   /* byte offset of the fp32 accumulator [nsplits][Hq][acc_rows][d_qk] */
   int64_t dq_acc_bytes;
   int64_t workspace_bytes; /* == fmha_bwd_workspace_size */
   int64_t pairs;           /* allowed (query, key) pairs summed over heads and segments */
   double flops;            /* 2*(3*d_qk + 2*d_v) * pairs: the five contractions */
+  int64_t acc_rows;        /* accumulator rows per head and split (see below) */
 } fmha_bwd_plan_info;
+/* Accumulator layout.  Atomic mode: one split, rows_q rows, row-major ([row][d_qk]), row of
+   a query = its D/LSE row.  Deterministic mode: split j holds key tile j's partial;
+   acc_rows = rows_q + B*tile_m and query block i of segment b (rows b_0 + i*tile_m ..) is
+   the tile_m*d_qk values starting at row a_b + i*tile_m, a_b = (first D row of segment b) +
+   b*tile_m, so blocks of different segments never share rows.  Inside a block the values
+   are grouped in 32x32 tiles, tile t = (r/32)*(d_qk/32) + c/32 at offset 1024*t, and tile
+   element (r, c) (r, c < 32) at 16*(c + 32*((r/4)%2)) + 4*(r/8) + r%4: the result layout of
+   a 32x32 matrix-core product, stored lane by lane. */
 
 FMHA_BWD_API int fmha_bwd_plan_query(const fmha_bwd_args* args, fmha_bwd_plan_info* info);
 

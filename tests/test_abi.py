@@ -58,7 +58,7 @@ int main(void) {
   printf("{\\n");
   F(B) F(scale) F(deterministic) F(seqstart_q_host) F(seqstart_k_dev) F(q) F(lse) F(dv)
   F(q_stride) F(dv_stride) F(lse_stride)
-  G(nsplits) G(rows_q) G(workspace_bytes) G(flops)
+  G(nsplits) G(rows_q) G(workspace_bytes) G(flops) G(acc_rows)
   printf("\\"size_args\\": %zu, \\"size_info\\": %zu}\\n", sizeof(fmha_bwd_args), sizeof(fmha_bwd_plan_info));
   return 0;
 }
@@ -75,7 +75,7 @@ int main(void) {
     for k, v in ref.items():
         if k.startswith("size"):
             continue
-        cls = _lib.PlanInfo if k in ("nsplits", "rows_q", "workspace_bytes", "flops") else Args
+        cls = _lib.PlanInfo if k in ("nsplits", "rows_q", "workspace_bytes", "flops", "acc_rows") else Args
         assert getattr(cls, k).offset == v, k
 
 
@@ -132,7 +132,9 @@ def test_workspace_size_and_plan_agree():
         assert info.rows_q == rows
         assert info.nsplits == (3 if det else 1)  # ceil(333 / 128) key tiles
         assert info.needs_zero == (0 if det else 1)
-        assert info.dq_acc_bytes == info.nsplits * 4 * rows * 128 * 4
+        # deterministic blocks get tile_m rows of padding per segment
+        assert info.acc_rows == rows + (2 * info.tile_m if det else 0)
+        assert info.dq_acc_bytes == info.nsplits * 4 * info.acc_rows * 128 * 4
         assert info.dq_acc_offset % 256 == 0 and info.workspace_bytes % 256 == 0
         assert info.dq_acc_offset + info.dq_acc_bytes <= info.workspace_bytes
         # nsplits never exceeds ceil(max Sk / 16)

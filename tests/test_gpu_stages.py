@@ -57,10 +57,22 @@ def _touch(mask, window, lq, lk, tm, tn):
             if ok[i * tm:(i + 1) * tm, j * tn:(j + 1) * tn].any()}
 
 
+def _block_offsets(tm, d):
+    """Offset of element (r, c) inside a deterministic accumulator block, as documented with
+    fmha_bwd_plan_info: 32x32 tiles t = (r/32)*(d/32) + c/32 at 1024*t, element (r, c) of a
+    tile at 16*(c + 32*((r/4)%2)) + 4*(r/8) + r%4."""
+    r = np.arange(tm)[:, None]
+    c = np.arange(d)[None, :]
+    t = (r // 32) * (d // 32) + c // 32
+    rr, cc = r % 32, c % 32
+    return 1024 * t + 16 * (cc + 32 * ((rr // 4) % 2)) + 4 * (rr // 8) + rr % 4
+
+
 @pytest.mark.parametrize("mask,window", [(NONE, (-1, -1)), (TL, (-1, -1)), (WIN, (100, 0))])
 def test_reduce_stage_is_bit_exact(mask, window):
-    """Partials placed in the accumulator by hand; untouched splits hold NaN, so reading one
-    would show.  Expected bits from the oracle's ascending fp32 split sum and RNE rounding."""
+    """Partials placed in the accumulator by hand; untouched splits and the padding rows past
+    each segment hold NaN, so reading one would show.  Expected bits from the oracle's
+    ascending fp32 split sum and RNE rounding."""
     import torch
     import attention_backward_fmha_amd as F
     lens = [300, 77, 512]
@@ -72,25 +84,27 @@ def test_reduce_stage_is_bit_exact(mask, window):
     call, ws, t = _setup(x, o, lse, scale=0.125, mask=mask, window=window, sq=sq, sk=sq)
     info = call.plan()
     rows = info.rows_q
+    tm, tn = info.tile_m, info.tile_n
+    assert info.acc_rows == rows + len(lens) * tm
     acc = ws[info.dq_acc_offset:info.dq_acc_offset + info.dq_acc_bytes].view(torch.float32)
-    acc = acc.view(info.nsplits, hq, rows, d)
     rng = np.random.default_rng(9)
     parts = (rng.standard_normal((info.nsplits, hq, rows, d)) * 10).astype(np.float32)
-    parts_dev = parts.copy()
+    dev = np.full((info.nsplits, hq, info.acc_rows * d), np.nan, np.float32)
+    offs = _block_offsets(tm, d)
     expect = np.zeros((rows, hq, d), np.uint16)
-    tm, tn = info.tile_m, info.tile_n
     for b in range(len(lens)):
         r0 = int(sq[b])
         touched = _touch(mask, window, lens[b], lens[b], tm, tn)
         for i in range(-(-lens[b] // tm)):
-            rs = slice(r0 + i * tm, r0 + min(lens[b], (i + 1) * tm))
+            nr = min(lens[b], (i + 1) * tm) - i * tm
+            rs = slice(r0 + i * tm, r0 + i * tm + nr)
             used = sorted(j for (ii, j) in touched if ii == i)
-            for j in range(info.nsplits):
-                if j not in used:
-                    parts_dev[j, :, rs, :] = np.nan
-            sel = parts[used][:, :, rs, :] if used else np.zeros((0, hq, rs.stop - rs.start, d), np.float32)
+            base = (r0 + b * tm + i * tm) * d
+            for j in used:
+                dev[j, :, base + offs[:nr].ravel()] = parts[j, :, rs, :].reshape(hq, -1).T
+            sel = parts[used][:, :, rs, :] if used else np.zeros((0, hq, nr, d), np.float32)
             expect[rs] = oracle.dq_split_reduce(sel, 0.125).transpose(1, 0, 2)
-    acc.copy_(torch.from_numpy(parts_dev))
+    acc.copy_(torch.from_numpy(dev.ravel()))
     stream = torch.cuda.current_stream().cuda_stream
     call.run(ws, stream, F.STAGE_REDUCE)
     torch.cuda.synchronize()
