@@ -185,6 +185,15 @@ __device__ __forceinline__ int tpos(int q) {
   return (q & ~12) | ((q & 4) << 1) | ((q & 8) >> 1);
 }
 
+// LDS row swizzles.  Row-major Q/dO copies keep row r at qrow(r) = r ^ ((r >> 4) & 3): the 8
+// lanes of a staging write then hit 8 different 16-byte bank groups (plain rows 16 apart share
+// one), and reads of 8 consecutive rows still do.  The dS tile keeps query row r at
+// dsrow(r) = r ^ ((r & 8) >> 1), which does the same for the rows the dS exchange writes
+// together (r, r+2, r+8, r+10) and for the dQ operand reads.  Both permute rows inside each
+// aligned group of 16.
+__device__ __forceinline__ int qrow(int r) { return r ^ ((r >> 4) & 3); }
+__device__ __forceinline__ int dsrow(int r) { return r ^ ((r & 8) >> 1); }
+
 // Key (inside the wave's 32) held by lane l32: bit 4 of the lane is bit 0 of the key and lane
 // bits 0..3 are key bits 1..4.  With it the dS exchange below ends with lane bits 2, 3 naming
 // an aligned group of 8 keys and the exchanged register bits naming the key inside the group.
@@ -255,7 +264,7 @@ __device__ __forceinline__ void write_ds_tile(uint16_t* ds_lds, const float (&d)
   const int col = col0 + 8 * ((lane >> 2) & 3);
 #pragma unroll
   for (int u = 0; u < 2; ++u)
-    *(u32x4*)&ds_lds[(row + 16 * u) * SR + col] = u32x4{w[2 * u][0], w[2 * u][1], w[2 * u + 1][0], w[2 * u + 1][1]};
+    *(u32x4*)&ds_lds[dsrow(row + 16 * u) * SR + col] = u32x4{w[2 * u][0], w[2 * u][1], w[2 * u + 1][0], w[2 * u + 1][1]};
 }
 
 // Query row of register u of a staging block whose first row is r0.  8-row blocks hold rows
@@ -271,7 +280,7 @@ template <int RB, int TSS>
 __device__ __forceinline__ void stage_block(uint16_t* rm, uint16_t* tr, int RS,
                                             const u32x4 (&x)[RB], int r0, int pos0, int c8) {
 #pragma unroll
-  for (int u = 0; u < RB; ++u) *(u32x4*)&rm[block_row<RB>(r0, u) * RS + c8 * 8] = x[u];
+  for (int u = 0; u < RB; ++u) *(u32x4*)&rm[qrow(block_row<RB>(r0, u)) * RS + c8 * 8] = x[u];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     // columns 2k (low halves) and 2k+1 (high halves), rows in position order
@@ -472,10 +481,10 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
       bf16x8 qa[DQK / 16], oa[DV / 16];
 #pragma unroll
       for (int kk = 0; kk < DQK / 16; ++kk)
-        qa[kk] = *(const bf16x8*)&q_lds[(32 * m + l32) * QS + 16 * kk + 8 * hi];
+        qa[kk] = *(const bf16x8*)&q_lds[qrow(32 * m + l32) * QS + 16 * kk + 8 * hi];
 #pragma unroll
       for (int kk = 0; kk < DV / 16; ++kk)
-        oa[kk] = *(const bf16x8*)&o_lds[(32 * m + l32) * OS + 16 * kk + 8 * hi];
+        oa[kk] = *(const bf16x8*)&o_lds[qrow(32 * m + l32) * OS + 16 * kk + 8 * hi];
 #pragma unroll
       for (int kk = 0; kk < DQK / 16; ++kk) s_acc[m] = mfma(qa[kk], kf[kk], s_acc[m]);
 #pragma unroll
@@ -570,7 +579,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
         bf16x8 da[TN / 16];
 #pragma unroll
         for (int kk = 0; kk < TN / 16; ++kk)
-          da[kk] = *(const bf16x8*)&ds_lds[(32 * mq + l32) * SR + 16 * kk + 8 * hi];
+          da[kk] = *(const bf16x8*)&ds_lds[dsrow(32 * mq + l32) * SR + 16 * kk + 8 * hi];
         f32x16 acc = f32x16{};
 #pragma unroll
         for (int kk = 0; kk < TN / 16; ++kk) {
@@ -633,11 +642,11 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
 // ------------------------------------------------------------------------------------------
 template <int DQK, int TM>
 __device__ __forceinline__ void reduce_tiles(const KParams& p, const Seg& sg, bool group, int b,
-                                             int h, int qb, int nq) {
+                                             int h, int qb, int nq, int part) {
   constexpr int TN = 128;
   constexpr int NT = (TM / 32) * (DQK / 32);   // 32x32 tiles per block
-  constexpr int PPT = (NT * 64 + 255) / 256;   // (tile, lane) pairs per thread
-  const int tid = threadIdx.x;
+  constexpr int PPT = 1;                        // (tile, lane) pairs per thread
+  const int tid = threadIdx.x + 256 * part;     // the block's pairs are split over work groups
   const MaskGeom mg = mask_geom(p.mask_type, p.window_left, p.window_right, sg.lq, sg.lk);
   const int ntiles = (int)((sg.lk + TN - 1) / TN);
   int jlo = 0, jhi = -1;
@@ -670,22 +679,33 @@ __device__ __forceinline__ void reduce_tiles(const KParams& p, const Seg& sg, bo
       }
     }
   };
-  if (jhi >= jlo) {
-    load(jlo, cur);
-    for (int jt = jlo; jt <= jhi; ++jt) {  // ascending split order
-      f32x4 nxt[PPT][4];
-      if (jt < jhi) load(jt + 1, nxt);
+  // two splits per iteration, the next two in flight
+  auto add = [&](const f32x4 (&x)[PPT][4]) {
 #pragma unroll
-      for (int pr = 0; pr < PPT; ++pr)
+    for (int pr = 0; pr < PPT; ++pr)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) acc[pr][u] += cur[pr][u];
-      if (jt < jhi) {
+      for (int u = 0; u < 4; ++u) acc[pr][u] += x[pr][u];
+  };
+  f32x4 nxt[PPT][4];
 #pragma unroll
-        for (int pr = 0; pr < PPT; ++pr)
+  for (int pr = 0; pr < PPT; ++pr)
 #pragma unroll
-          for (int u = 0; u < 4; ++u) cur[pr][u] = nxt[pr][u];
+    for (int u = 0; u < 4; ++u) nxt[pr][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (jhi >= jlo) load(jlo, cur);
+  if (jhi >= jlo + 1) load(jlo + 1, nxt);
+  for (int jt = jlo; jt <= jhi; jt += 2) {  // ascending split order
+    f32x4 c2[PPT][4] = {}, n2[PPT][4] = {};
+    if (jt + 2 <= jhi) load(jt + 2, c2);
+    if (jt + 3 <= jhi) load(jt + 3, n2);
+    add(cur);
+    if (jt + 1 <= jhi) add(nxt);
+#pragma unroll
+    for (int pr = 0; pr < PPT; ++pr)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        cur[pr][u] = c2[pr][u];
+        nxt[pr][u] = n2[pr][u];
       }
-    }
   }
   const int64_t q0 = (int64_t)qb * TM;
 #pragma unroll
@@ -728,9 +748,15 @@ __device__ __forceinline__ void reduce_rows(const KParams& p, const Seg& sg, boo
   }
 }
 
+// Work groups per query block in deterministic mode: one per 256 (tile, lane) pairs.
+template <int DQK, int TM>
+constexpr int reduce_parts() { return ((TM / 32) * (DQK / 32) * 64 + 255) / 256; }
+
 template <int DQK, int TM>
 __global__ __launch_bounds__(256) void k_dq_reduce(const KParams p) {
-  const int qb = blockIdx.x;
+  constexpr int PARTS = reduce_parts<DQK, TM>();
+  const int part = p.deterministic ? (int)blockIdx.x % PARTS : 0;
+  const int qb = p.deterministic ? (int)blockIdx.x / PARTS : (int)blockIdx.x;
   const int h = blockIdx.y;
   const int b = blockIdx.z;
   const bool group = p.seqstart_q != nullptr;
@@ -739,7 +765,7 @@ __global__ __launch_bounds__(256) void k_dq_reduce(const KParams p) {
   if (q0 >= sg.lq) return;
   const int nq = (int)min((int64_t)TM, sg.lq - q0);
   if (p.deterministic) {
-    reduce_tiles<DQK, TM>(p, sg, group, b, h, qb, nq);
+    reduce_tiles<DQK, TM>(p, sg, group, b, h, qb, nq, part);
   } else {
     reduce_rows<DQK, TM>(p, sg, group, b, h, qb, nq);
   }
@@ -793,19 +819,25 @@ hipError_t launch_main(const Plan& plan, const KParams& kp, hipStream_t stream) 
   return hipGetLastError();
 }
 
+template <int DQK, int TM>
+static void launch_reduce_t(const Plan& plan, const KParams& kp, hipStream_t stream) {
+  const int parts = plan.deterministic ? reduce_parts<DQK, TM>() : 1;
+  const dim3 grid((unsigned)(plan.n_q_blocks * parts), (unsigned)plan.Hq, (unsigned)plan.B);
+  hipLaunchKernelGGL((k_dq_reduce<DQK, TM>), grid, dim3(256), 0, stream, kp);
+}
+
 hipError_t launch_reduce(const Plan& plan, const KParams& kp, hipStream_t stream) {
   if (plan.n_q_blocks == 0 || plan.B == 0) return hipSuccess;
-  const dim3 grid((unsigned)plan.n_q_blocks, (unsigned)plan.Hq, (unsigned)plan.B);
   if (plan.d_qk == 64) {
-    hipLaunchKernelGGL((k_dq_reduce<64, 64>), grid, dim3(256), 0, stream, kp);
+    launch_reduce_t<64, 64>(plan, kp, stream);
   } else if (plan.d_qk == 128) {
     if (plan.tile_m == 32) {
-      hipLaunchKernelGGL((k_dq_reduce<128, 32>), grid, dim3(256), 0, stream, kp);
+      launch_reduce_t<128, 32>(plan, kp, stream);
     } else {
-      hipLaunchKernelGGL((k_dq_reduce<128, 64>), grid, dim3(256), 0, stream, kp);
+      launch_reduce_t<128, 64>(plan, kp, stream);
     }
   } else {
-    hipLaunchKernelGGL((k_dq_reduce<192, 32>), grid, dim3(256), 0, stream, kp);
+    launch_reduce_t<192, 32>(plan, kp, stream);
   }
   return hipGetLastError();
 }
