@@ -37,7 +37,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--mode", choices=["atomic", "deterministic"], default="atomic")
+    ap.add_argument("--mode", choices=["atomic", "deterministic"], default="deterministic")
     ap.add_argument("--workload", default="headline_2x32x4096_causal")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-mode", action="store_true",
