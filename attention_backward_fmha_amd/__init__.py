@@ -6,7 +6,9 @@ runs in the library's HIP kernels; torch tensors only carry device memory and th
     dq, dk, dv = attention_backward_fmha_amd.bwd(q, k, v, o, lse, do, mask_type=1)
 
 Batch (BSHD) tensors are [B, S, H, d] with LSE [B, Hq, Sq]; group (THD, ragged) tensors are
-[T, H, d] with LSE [Hq, T] and ``cu_seqlens_q``/``cu_seqlens_k`` offsets (B+1 int32).
+[T, H, d] with LSE [Hq, T] and ``cu_seqlens_q``/``cu_seqlens_k`` offsets (B+1 int32).  Padded
+THD adds ``cu_seqlens_q_padded``/``cu_seqlens_k_padded``: segment b's rows start at physical
+row padded[b] and the rest of its slot (up to padded[b+1]) is padding, left untouched.
 """
 
 import numpy as np
@@ -62,7 +64,8 @@ def _ptr(t):
 def make_call(q, k, v, o, lse, do, dq, dk, dv, *, scale=None, mask_type=MASK_NONE,
               window=(-1, -1), deterministic=True, cu_seqlens_q=None, cu_seqlens_k=None,
               cu_seqlens_q_host=None, cu_seqlens_k_host=None, max_seqlen_q=None,
-              max_seqlen_k=None):
+              max_seqlen_k=None, cu_seqlens_q_padded=None, cu_seqlens_k_padded=None,
+              cu_seqlens_q_padded_host=None, cu_seqlens_k_padded_host=None):
     """Fill the C argument struct from tensors (no device work)."""
     group = cu_seqlens_q is not None
     d_qk = q.shape[-1]
@@ -90,6 +93,16 @@ def make_call(q, k, v, o, lse, do, dq, dk, dv, *, scale=None, mask_type=MASK_NON
         a.Hq, a.Hkv = q.shape[1], k.shape[1]
         a.lse_stride[0] = 0
         a.lse_stride[1] = lse.stride(0)
+        for side, dev_t, host in (("q", cu_seqlens_q_padded, cu_seqlens_q_padded_host),
+                                  ("k", cu_seqlens_k_padded, cu_seqlens_k_padded_host)):
+            if dev_t is None:
+                continue
+            if host is None:
+                host = dev_t.cpu().numpy()
+            h_ = np.ascontiguousarray(host, dtype=np.int32)
+            keep += [h_, dev_t]
+            setattr(a, "seqstart_%s_padded_host" % side, h_.ctypes.data)
+            setattr(a, "seqstart_%s_padded_dev" % side, dev_t.data_ptr())
     else:
         a.B, a.Sq, a.Hq = q.shape[0], q.shape[1], q.shape[2]
         a.Sk, a.Hkv = k.shape[1], k.shape[2]
@@ -113,7 +126,9 @@ def make_call(q, k, v, o, lse, do, dq, dk, dv, *, scale=None, mask_type=MASK_NON
 
 def bwd(q, k, v, o, lse, do, *, scale=None, mask_type=MASK_NONE, window=(-1, -1),
         deterministic=True, cu_seqlens_q=None, cu_seqlens_k=None, cu_seqlens_q_host=None,
-        cu_seqlens_k_host=None, max_seqlen_q=None, max_seqlen_k=None, workspace=None):
+        cu_seqlens_k_host=None, max_seqlen_q=None, max_seqlen_k=None, cu_seqlens_q_padded=None,
+        cu_seqlens_k_padded=None, cu_seqlens_q_padded_host=None, cu_seqlens_k_padded_host=None,
+        workspace=None, out=None):
     """Gradients (dq, dk, dv) of softmax attention; see the module docstring for layouts."""
     import torch
 
@@ -122,14 +137,20 @@ def bwd(q, k, v, o, lse, do, *, scale=None, mask_type=MASK_NONE, window=(-1, -1)
             raise TypeError("q, k, v, o and do must be bfloat16 CUDA tensors")
     if lse.dtype != torch.float32:
         raise TypeError("lse must be float32")
-    dq = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
-    dk = torch.empty(k.shape, dtype=torch.bfloat16, device=k.device)
-    dv = torch.empty(v.shape, dtype=torch.bfloat16, device=v.device)
+    if out is not None:  # caller-provided (dq, dk, dv), e.g. to keep padding rows
+        dq, dk, dv = out
+    else:
+        dq = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+        dk = torch.empty(k.shape, dtype=torch.bfloat16, device=k.device)
+        dv = torch.empty(v.shape, dtype=torch.bfloat16, device=v.device)
     call = make_call(q, k, v, o, lse, do, dq, dk, dv, scale=scale, mask_type=mask_type,
                      window=window, deterministic=deterministic, cu_seqlens_q=cu_seqlens_q,
                      cu_seqlens_k=cu_seqlens_k, cu_seqlens_q_host=cu_seqlens_q_host,
                      cu_seqlens_k_host=cu_seqlens_k_host, max_seqlen_q=max_seqlen_q,
-                     max_seqlen_k=max_seqlen_k)
+                     max_seqlen_k=max_seqlen_k, cu_seqlens_q_padded=cu_seqlens_q_padded,
+                     cu_seqlens_k_padded=cu_seqlens_k_padded,
+                     cu_seqlens_q_padded_host=cu_seqlens_q_padded_host,
+                     cu_seqlens_k_padded_host=cu_seqlens_k_padded_host)
     nbytes = call.workspace_size()
     if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)

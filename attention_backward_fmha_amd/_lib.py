@@ -6,7 +6,7 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libfmha_bwd.so")
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 MASK_NONE = 0
 MASK_CAUSAL_TOP_LEFT = 1
@@ -74,6 +74,10 @@ class Args(ctypes.Structure):
         ("dk_stride", _i64x3),
         ("dv_stride", _i64x3),
         ("lse_stride", ctypes.c_int64 * 2),
+        ("seqstart_q_padded_host", ctypes.c_void_p),
+        ("seqstart_k_padded_host", ctypes.c_void_p),
+        ("seqstart_q_padded_dev", ctypes.c_void_p),
+        ("seqstart_k_padded_dev", ctypes.c_void_p),
     ]
 
     def __init__(self, **kw):

@@ -55,6 +55,8 @@ fmha::KParams make_params(const fmha_bwd_args* a, const fmha::Plan& p, void* ws)
   k.dq_acc = (float*)((char*)ws + p.dq_acc_offset);
   k.seqstart_q = p.group_mode ? a->seqstart_q_dev : nullptr;
   k.seqstart_k = p.group_mode ? a->seqstart_k_dev : nullptr;
+  k.slot_q = p.group_mode ? a->seqstart_q_padded_dev : nullptr;
+  k.slot_k = p.group_mode ? a->seqstart_k_padded_dev : nullptr;
   for (int i = 0; i < 3; ++i) {
     k.q_s[i] = a->q_stride[i];
     k.k_s[i] = a->k_stride[i];

@@ -22,8 +22,10 @@ struct KParams {
   float* dsum;    // workspace: D = rowsum(dO * O), [Hq][rows_q]
   float* lse2;    // workspace: LSE * log2(e), [Hq][rows_q]
   float* dq_acc;  // workspace: fp32 dQ partials, [nsplits][Hq][acc_rows][d_qk]
-  const int32_t* seqstart_q;  // device offsets, null in batch mode
+  const int32_t* seqstart_q;  // device offsets, null in batch mode (segment lengths)
   const int32_t* seqstart_k;
+  const int32_t* slot_q;      // device offsets of the padded slots (first physical row), or
+  const int32_t* slot_k;      // null: the slots are the segments
   int64_t q_s[3], k_s[3], v_s[3], o_s[3], do_s[3], dq_s[3], dk_s[3], dv_s[3];
   int64_t lse_s[2];
   int64_t split_stride;  // elements

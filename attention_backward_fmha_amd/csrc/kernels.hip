@@ -54,9 +54,9 @@ __device__ __forceinline__ Seg seg_of(const KParams& p, int b) {
     const int q1 = __builtin_amdgcn_readfirstlane(p.seqstart_q[b + 1]);
     const int k0 = __builtin_amdgcn_readfirstlane(p.seqstart_k[b]);
     const int k1 = __builtin_amdgcn_readfirstlane(p.seqstart_k[b + 1]);
-    s.q_row0 = q0;
+    s.q_row0 = p.slot_q ? __builtin_amdgcn_readfirstlane(p.slot_q[b]) : q0;
     s.lq = (int64_t)q1 - q0;
-    s.k_row0 = k0;
+    s.k_row0 = p.slot_k ? __builtin_amdgcn_readfirstlane(p.slot_k[b]) : k0;
     s.lk = (int64_t)k1 - k0;
     s.ws_row0 = s.q_row0;
   } else {

@@ -98,7 +98,13 @@ int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t el) {
                   "group mode needs host and device seqstart arrays for both q and k");
     const int32_t* sq = a->seqstart_q_host;
     const int32_t* sk = a->seqstart_k_host;
-    if (sq[0] < 0 || sk[0] < 0)
+    const int32_t* pq = a->seqstart_q_padded_host;
+    const int32_t* pk = a->seqstart_k_padded_host;
+    if ((pq == nullptr) != (a->seqstart_q_padded_dev == nullptr) ||
+        (pk == nullptr) != (a->seqstart_k_padded_dev == nullptr))
+      return fail(FMHA_ERR_INVALID_ARG, err, el,
+                  "padded seqstart arrays come in host/device pairs");
+    if (sq[0] < 0 || sk[0] < 0 || (pq && pq[0] < 0) || (pk && pk[0] < 0))
       return fail(FMHA_ERR_INVALID_ARG, err, el, "seqstart offsets must be non-negative");
     max_lq = 0;
     max_lk = 0;
@@ -112,12 +118,18 @@ int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t el) {
                     "a segment is longer than Sq/Sk (the maximum segment lengths)");
       if (lq > max_lq) max_lq = lq;
       if (lk > max_lk) max_lk = lk;
+      if ((pq && (int64_t)pq[b] + lq > pq[b + 1]) || (pk && (int64_t)pk[b] + lk > pk[b + 1]))
+        return fail(FMHA_ERR_INVALID_ARG, err, el,
+                    "a segment does not fit its padded slot (padded[b] + length > padded[b+1])");
     }
-    p->rows_q = a->B > 0 ? sq[a->B] : 0;
+    p->rows_q = a->B > 0 ? (pq ? pq[a->B] : sq[a->B]) : 0;
   } else {
     if (a->seqstart_k_host || a->seqstart_q_dev || a->seqstart_k_dev)
       return fail(FMHA_ERR_INVALID_ARG, err, el,
                   "seqstart arrays must be all null (batch mode) or all set (group mode)");
+    if (a->seqstart_q_padded_host || a->seqstart_k_padded_host || a->seqstart_q_padded_dev ||
+        a->seqstart_k_padded_dev)
+      return fail(FMHA_ERR_INVALID_ARG, err, el, "padded seqstart arrays need group mode");
     p->rows_q = (int64_t)a->B * a->Sq;
   }
 

@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define FMHA_BWD_ABI_VERSION 1u
+#define FMHA_BWD_ABI_VERSION 2u
 
 #if defined(__GNUC__)
 #define FMHA_BWD_API __attribute__((visibility("default")))
@@ -113,12 +113,24 @@ typedef struct fmha_bwd_args {
   const void* o;     /* bf16 [.., Sq|T_q, Hq, d_v] forward output */
   const void* dout;  /* bf16 [.., Sq|T_q, Hq, d_v] gradient of o */
   const float* lse;  /* fp32 forward log-sum-exp, see conventions */
-  void* dq;          /* bf16 [.., Sq|T_q, Hq, d_qk], fully overwritten */
-  void* dk;          /* bf16 [.., Sk|T_k, Hkv, d_qk], fully overwritten */
-  void* dv;          /* bf16 [.., Sk|T_k, Hkv, d_v], fully overwritten */
+  void* dq;          /* bf16 [.., Sq|T_q, Hq, d_qk], every segment row overwritten */
+  void* dk;          /* bf16 [.., Sk|T_k, Hkv, d_qk], every segment row overwritten */
+  void* dv;          /* bf16 [.., Sk|T_k, Hkv, d_v], every segment row overwritten */
   int64_t q_stride[3], k_stride[3], v_stride[3], o_stride[3], do_stride[3];
   int64_t dq_stride[3], dk_stride[3], dv_stride[3];
   int64_t lse_stride[2]; /* {batch, head}; the sequence stride is 1 */
+  /* Padded THD (group mode, optional; the cu_seqlens_padded arrays next to cu_seqlens in
+     "Update AITER subcommit and refactor internal AITER/CK FA API usage", review): the tensors
+     hold segment b in a slot of physical rows [padded[b], padded[b+1]) that may be longer than
+     its length seqstart[b+1] - seqstart[b].  Its rows are the first ones of the slot; the rest
+     of the slot is never read, and dq/dk/dv rows there are left as they are.  lse is indexed
+     by physical row.  For q and for k independently: both the host and the device array
+     (B+1 non-decreasing offsets with padded[b] + length_b <= padded[b+1]), or neither (the
+     slots are then the segments themselves). */
+  const int32_t* seqstart_q_padded_host;
+  const int32_t* seqstart_k_padded_host;
+  const int32_t* seqstart_q_padded_dev;
+  const int32_t* seqstart_k_padded_dev;
 } fmha_bwd_args;
 
 /* Workspace bytes that prepare/run need for these arguments.  Host only: no GPU call, no
@@ -150,7 +162,8 @@ typedef struct fmha_bwd_plan_info {
   int32_t nsplits;         /* depth of the dQ accumulator (n_kv_tiles, or 1 in atomic mode) */
   int32_t needs_zero;      /* prepare zeroes the accumulator */
   int32_t reserved;
-  int64_t rows_q;          /* T_q: B*Sq (batch) or seqstart_q[B] (group) */
+  int64_t rows_q;          /* T_q: B*Sq (batch), seqstart_q[B] (group) or the padded q
+                              offsets' last entry (padded group) */
   int64_t d_offset;        /* byte offset of D = rowsum(dO*O), fp32 [Hq][rows_q] */
   int64_t dq_acc_offset;   /* byte offset of the fp32 accumulator [nsplits][Hq][acc_rows][d_qk] */
   int64_t dq_acc_bytes;

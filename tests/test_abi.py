@@ -57,7 +57,7 @@ def test_struct_layout_matches_header():
 int main(void) {
   printf("{\\n");
   F(B) F(scale) F(deterministic) F(seqstart_q_host) F(seqstart_k_dev) F(q) F(lse) F(dv)
-  F(q_stride) F(dv_stride) F(lse_stride)
+  F(q_stride) F(dv_stride) F(lse_stride) F(seqstart_q_padded_host) F(seqstart_k_padded_dev)
   G(nsplits) G(rows_q) G(workspace_bytes) G(flops) G(acc_rows)
   printf("\\"size_args\\": %zu, \\"size_info\\": %zu}\\n", sizeof(fmha_bwd_args), sizeof(fmha_bwd_plan_info));
   return 0;
@@ -151,6 +151,35 @@ def test_group_mode_uses_physical_rows():
     # empty segments are fine and contribute no rows
     b = group_args([5, 0, 7], [0, 3, 9])
     assert _lib.plan_query(b).rows_q == 12
+
+
+def test_padded_thd_plan():
+    """Padded slots: the physical row count comes from the padded q offsets; a segment that
+    does not fit its slot, a host array without its device twin, or padding in batch mode
+    are argument errors."""
+    lens = [103, 77, 61]
+    a = group_args(lens, lens)
+    pq = np.array([0, 112, 192, 256], np.int32)
+    a.seqstart_q_padded_host = pq.ctypes.data
+    a.seqstart_q_padded_dev = FAKE
+    a.seqstart_k_padded_host = pq.ctypes.data
+    a.seqstart_k_padded_dev = FAKE
+    a._keep2 = pq
+    info = _lib.plan_query(a)
+    assert info.rows_q == 256
+    assert info.pairs == sum(n * (n + 1) // 2 for n in lens) * 4  # logical lengths, causal, 4 heads
+    bad = np.array([0, 100, 192, 256], np.int32)  # 103 rows do not fit a 100-row slot
+    a.seqstart_q_padded_host = bad.ctypes.data
+    a._keep3 = bad
+    assert status_of(a) == _lib.ERR_INVALID_ARG
+    a.seqstart_q_padded_host = pq.ctypes.data
+    a.seqstart_q_padded_dev = None
+    assert status_of(a) == _lib.ERR_INVALID_ARG
+    b = batch_args()
+    b.seqstart_q_padded_host = pq.ctypes.data
+    b.seqstart_q_padded_dev = FAKE
+    b._keep = pq
+    assert status_of(b) == _lib.ERR_INVALID_ARG
 
 
 def test_flop_count_matches_pair_count():
