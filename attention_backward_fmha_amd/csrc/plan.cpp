@@ -65,6 +65,7 @@ int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t el) {
     return fail(FMHA_ERR_UNSUPPORTED, err, el,
                 "head dims (d_qk, d_v) must be (64,64), (128,128) or (192,128)");
   if (!isfinite(a->scale)) return fail(FMHA_ERR_INVALID_ARG, err, el, "scale is not finite");
+  if (!(a->scale > 0.f)) return fail(FMHA_ERR_UNSUPPORTED, err, el, "scale must be positive");
   if (a->mask_type < FMHA_MASK_NONE || a->mask_type > FMHA_MASK_WINDOW)
     return fail(FMHA_ERR_INVALID_ARG, err, el, "unknown mask_type");
   if (a->mask_type != FMHA_MASK_WINDOW && (a->window_left != -1 || a->window_right != -1))

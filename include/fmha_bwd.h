@@ -94,7 +94,7 @@ typedef struct fmha_bwd_args {
   int32_t Hq, Hkv;       /* query heads, K/V heads; Hq % Hkv == 0 */
   int32_t Sq, Sk;        /* sequence lengths (batch mode) or maximum segment lengths (group) */
   int32_t d_qk, d_v;     /* head dims; supported pairs: (64,64), (128,128), (192,128) */
-  float scale;           /* softmax scale, usually 1/sqrt(d_qk) */
+  float scale;           /* softmax scale, > 0, usually 1/sqrt(d_qk) */
   int32_t mask_type;     /* enum fmha_mask_type */
   int32_t window_left;   /* FMHA_MASK_WINDOW only; -1 = unbounded */
   int32_t window_right;  /* FMHA_MASK_WINDOW only; -1 = unbounded */

@@ -153,6 +153,16 @@ def test_group_mode_uses_physical_rows():
     assert _lib.plan_query(b).rows_q == 12
 
 
+def test_scale_must_be_positive():
+    for sc in (0.0, -0.125):
+        a = batch_args()
+        a.scale = sc
+        assert status_of(a) == _lib.ERR_UNSUPPORTED
+    a = batch_args()
+    a.scale = float("nan")
+    assert status_of(a) == _lib.ERR_INVALID_ARG
+
+
 def test_padded_thd_plan():
     """Padded slots: the physical row count comes from the padded q offsets; a segment that
     does not fit its slot, a host array without its device twin, or padding in batch mode
