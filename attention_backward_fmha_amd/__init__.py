@@ -158,3 +158,30 @@ def bwd(q, k, v, o, lse, do, *, scale=None, mask_type=MASK_NONE, window=(-1, -1)
     call.prepare(workspace, stream)
     call.run(workspace, stream)
     return dq, dk, dv
+
+
+def fwd(q, k, v, *, scale=None, mask_type=MASK_NONE, window=(-1, -1), cu_seqlens_q=None,
+        cu_seqlens_k=None, cu_seqlens_q_host=None, cu_seqlens_k_host=None, max_seqlen_q=None,
+        max_seqlen_k=None, cu_seqlens_q_padded=None, cu_seqlens_k_padded=None,
+        cu_seqlens_q_padded_host=None, cu_seqlens_k_padded_host=None):
+    """Forward (o, lse) on the device, in the layouts ``bwd`` takes: o like q with d_v columns,
+    lse [B, Hq, Sq] (batch) or [Hq, T] (group)."""
+    import torch
+
+    for t in (q, k, v):
+        if t.dtype != torch.bfloat16 or not t.is_cuda:
+            raise TypeError("q, k and v must be bfloat16 CUDA tensors")
+    o = torch.empty(q.shape[:-1] + (v.shape[-1],), dtype=torch.bfloat16, device=q.device)
+    if cu_seqlens_q is not None:
+        lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
+    else:
+        lse = torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32, device=q.device)
+    call = make_call(q, k, v, o, lse, None, None, None, None, scale=scale, mask_type=mask_type,
+                     window=window, cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k,
+                     cu_seqlens_q_host=cu_seqlens_q_host, cu_seqlens_k_host=cu_seqlens_k_host,
+                     max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k,
+                     cu_seqlens_q_padded=cu_seqlens_q_padded, cu_seqlens_k_padded=cu_seqlens_k_padded,
+                     cu_seqlens_q_padded_host=cu_seqlens_q_padded_host,
+                     cu_seqlens_k_padded_host=cu_seqlens_k_padded_host)
+    _lib.fwd_run(call.args, torch.cuda.current_stream(q.device).cuda_stream)
+    return o, lse

@@ -31,6 +31,7 @@ EXPORTS = (
     "fmha_bwd_status_string",
     "fmha_bwd_plan_query",
     "fmha_bwd_run_stages",
+    "fmha_fwd_run",
 )
 
 _i64x3 = ctypes.c_int64 * 3
@@ -140,6 +141,7 @@ def lib():
         L.fmha_bwd_run_stages.argtypes = [ap, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
                                           ctypes.c_void_p]
         L.fmha_bwd_plan_query.argtypes = [ap, ctypes.POINTER(PlanInfo)]
+        L.fmha_fwd_run.argtypes = [ap, ctypes.c_void_p]
         L.fmha_bwd_status_string.argtypes = [ctypes.c_int]
         L.fmha_bwd_status_string.restype = ctypes.c_char_p
         for name in EXPORTS:
@@ -185,3 +187,9 @@ def run(args, ws_ptr, ws_bytes, stream, stages=STAGE_ALL):
                                        int(stages), ctypes.c_void_p(stream))
     if st != OK:
         raise FmhaError(st, "fmha_bwd_run")
+
+
+def fwd_run(args, stream):
+    st = lib().fmha_fwd_run(ctypes.byref(args), ctypes.c_void_p(stream))
+    if st != OK:
+        raise FmhaError(st, "fmha_fwd_run")

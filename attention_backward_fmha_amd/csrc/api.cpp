@@ -21,9 +21,9 @@ int report(int status, const char* where, const char* msg) {
   return status;
 }
 
-int plan_or_fail(const fmha_bwd_args* a, fmha::Plan* p, const char* where) {
+int plan_or_fail(const fmha_bwd_args* a, fmha::Plan* p, const char* where, bool forward = false) {
   char err[256] = {0};
-  const int st = fmha::make_plan(a, p, err, sizeof err);
+  const int st = fmha::make_plan(a, p, err, sizeof err, forward);
   return report(st, where, err);
 }
 
@@ -47,12 +47,16 @@ fmha::KParams make_params(const fmha_bwd_args* a, const fmha::Plan& p, void* ws)
   k.o = (const uint16_t*)a->o;
   k.dout = (const uint16_t*)a->dout;
   k.lse = a->lse;
+  k.o_out = (uint16_t*)a->o;
+  k.lse_out = (float*)a->lse;
   k.dq = (uint16_t*)a->dq;
   k.dk = (uint16_t*)a->dk;
   k.dv = (uint16_t*)a->dv;
-  k.dsum = (float*)((char*)ws + p.d_offset);
-  k.lse2 = (float*)((char*)ws + p.lse2_offset);
-  k.dq_acc = (float*)((char*)ws + p.dq_acc_offset);
+  if (ws != nullptr) {
+    k.dsum = (float*)((char*)ws + p.d_offset);
+    k.lse2 = (float*)((char*)ws + p.lse2_offset);
+    k.dq_acc = (float*)((char*)ws + p.dq_acc_offset);
+  }
   k.seqstart_q = p.group_mode ? a->seqstart_q_dev : nullptr;
   k.seqstart_k = p.group_mode ? a->seqstart_k_dev : nullptr;
   k.slot_q = p.group_mode ? a->seqstart_q_padded_dev : nullptr;
@@ -161,6 +165,15 @@ int fmha_bwd_run_stages(const fmha_bwd_args* args, void* ws, size_t bytes, int s
 int fmha_bwd_run(const fmha_bwd_args* args, void* ws, size_t bytes, void* stream) {
   return fmha_bwd_run_stages(args, ws, bytes, FMHA_STAGE_DOT | FMHA_STAGE_MAIN | FMHA_STAGE_REDUCE,
                              stream);
+}
+
+int fmha_fwd_run(const fmha_bwd_args* args, void* stream) {
+  fmha::Plan p;
+  int st = plan_or_fail(args, &p, "fwd", true);
+  if (st != FMHA_OK) return st;
+  log_plan(p, "fwd");
+  const fmha::KParams kp = make_params(args, p, nullptr);
+  return hip_status(fmha::launch_fwd(p, kp, (hipStream_t)stream), "fwd");
 }
 
 const char* fmha_bwd_status_string(int status) {

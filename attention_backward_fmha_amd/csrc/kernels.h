@@ -16,6 +16,8 @@ struct KParams {
   const uint16_t* o;
   const uint16_t* dout;
   const float* lse;
+  uint16_t* o_out;  // forward outputs (the same tensors as o and lse)
+  float* lse_out;
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
@@ -41,6 +43,7 @@ struct KParams {
 };
 
 hipError_t launch_dot(const Plan& plan, const KParams& kp, hipStream_t stream);
+hipError_t launch_fwd(const Plan& plan, const KParams& kp, hipStream_t stream);
 hipError_t launch_main(const Plan& plan, const KParams& kp, hipStream_t stream);
 hipError_t launch_reduce(const Plan& plan, const KParams& kp, hipStream_t stream);
 hipError_t launch_zero(float* ptr, int64_t count, hipStream_t stream);

@@ -771,6 +771,246 @@ __global__ __launch_bounds__(256) void k_dq_reduce(const KParams p) {
   }
 }
 
+// ------------------------------------------------------------------------------------------
+// Forward: O = softmax(scale * Q K^T + mask) V and LSE.  One work group per (block of 128
+// queries, query head, segment); wave w owns queries 32w .. 32w+31 of the block.
+//
+// S^T = K Q^T puts one query per lane (lane l%32, in both lane halves) and, per 32-key block,
+// 16 keys in the result registers, so the online softmax keeps its running max and sum per
+// lane; the two lane halves hold different keys of the same query and agree on the max with
+// one exchange.  P^T goes from the result registers straight into O^T += V^T P^T (V^T staged
+// with keys in the order the registers feed the reduction slots, as the backward stages Q^T).
+// Q stays in registers for the whole item; K (row-major) and V^T pass through LDS per 64-key
+// tile, with the next tile's global loads in flight during the current one.
+// ------------------------------------------------------------------------------------------
+template <int DQK, int DV>
+struct FwdTile {
+  static constexpr int TQ = 128;                      // queries per block
+  static constexpr int TK = 64;                       // keys per tile
+  static constexpr int KS = DQK + 8;                  // K row-major stride (elements)
+  static constexpr int VS = TK + 8;                   // V^T stride (one row per head-dim column)
+  static constexpr int KBLK = (TK / 8) * (DQK / 8);   // 8x8 staging blocks of K
+  static constexpr int VBLK = (TK / 8) * (DV / 8);    // ... of V (ids after K's)
+  static constexpr int NV = (KBLK + VBLK + 255) / 256;
+  static_assert(KBLK % 64 == 0, "staging blocks of K must fill whole waves");
+};
+
+template <int DQK, int DV>
+__global__ __launch_bounds__(256, DQK <= 128 ? 2 : 1) void k_fwd(const KParams p) {
+  using T = FwdTile<DQK, DV>;
+  constexpr int TQ = T::TQ, TK = T::TK, KS = T::KS, VS = T::VS;
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[TK * KS];  // K tile, row-major
+  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[DV * VS];  // V tile, transposed
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int g = h / p.group_size;
+  const bool group = p.seqstart_q != nullptr;
+  const Seg sg = seg_of(p, b);
+  // last query blocks first: under a causal mask they see the most keys
+  const int64_t q0 = ((int64_t)gridDim.x - 1 - blockIdx.x) * TQ;
+  if (q0 >= sg.lq) return;  // uniform
+  const int nq = (int)min((int64_t)TQ, sg.lq - q0);
+  const MaskGeom mg = mask_geom(p.mask_type, p.window_left, p.window_right, sg.lq, sg.lk);
+
+  // keys any row of the block may see: [k_lo, k_hi]
+  int64_t k_lo = 0, k_hi = sg.lk - 1;
+  if (mg.left >= 0) k_lo = max(k_lo, q0 + mg.delta - mg.left);
+  if (mg.right >= 0) k_hi = min(k_hi, q0 + nq - 1 + mg.delta + mg.right);
+  const int t_lo = (int)(k_lo / TK);
+  const int ntiles = k_hi >= k_lo ? (int)(k_hi / TK) - t_lo + 1 : 0;
+
+  // this lane's query and its allowed key offsets: lo_l <= key - row <= hi_l
+  const int row = (int)q0 + 32 * wave + l32;  // inside the segment; may be >= lq (not stored)
+  int64_t lo_l = -(int64_t)row, hi_l = sg.lk - 1 - row;
+  if (mg.left >= 0) lo_l = max(lo_l, mg.delta - mg.left);
+  if (mg.right >= 0) hi_l = min(hi_l, mg.delta + mg.right);
+  const bool lane_ok = hi_l >= lo_l && row < sg.lq;
+  const unsigned span = lane_ok ? (unsigned)(hi_l - lo_l) : 0u;
+
+  // Q rows of this wave as the B operand of S^T (rows past the segment end read as zeros)
+  bf16x8 qf[DQK / 16];
+  {
+    const int qs1 = (int)p.q_s[1];
+    const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(
+        p.q + elem_off(p.q_s, group, b, sg.q_row0 + q0, h), (uint32_t)((nq - 1) * qs1 + DQK) * 2u);
+#pragma unroll
+    for (int kk = 0; kk < DQK / 16; ++kk)
+      qf[kk] = __builtin_bit_cast(
+          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                      rq, ((unsigned)(32 * wave + l32) * (unsigned)qs1 + 16u * kk + 8u * hi) * 2u, 0, 0));
+  }
+
+  // ---- staging: 8-row x 8-column blocks of K (row-major copy) and V (transposed copy) ----
+  // K block id: column chunk fastest, so the 8 lanes of an LDS write group cover 8 chunks of
+  // one row; V block id: row group fastest (8 consecutive transposed positions per lane group).
+  u32x4 pre[T::NV][8];
+  const int ks1 = (int)p.k_s[1];
+  const int vs1 = (int)p.v_s[1];
+  auto load_tile = [&](bool valid, int64_t kt0) {
+    const int nk = valid ? (int)min((int64_t)TK, sg.lk - kt0) : 0;
+    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(
+        p.k + (valid ? elem_off(p.k_s, group, b, sg.k_row0 + kt0, g) : 0),
+        nk > 0 ? (uint32_t)((nk - 1) * ks1 + DQK) * 2u : 0u);
+    const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(
+        p.v + (valid ? elem_off(p.v_s, group, b, sg.k_row0 + kt0, g) : 0),
+        nk > 0 ? (uint32_t)((nk - 1) * vs1 + DV) * 2u : 0u);
+#pragma unroll
+    for (int v = 0; v < T::NV; ++v) {
+      const int id0 = tid + 256 * v;
+      if ((T::KBLK + T::VBLK) % 256 == 0 || id0 < T::KBLK + T::VBLK) {
+        const bool isk = __builtin_amdgcn_readfirstlane(id0) < T::KBLK;  // wave-uniform
+        if (isk) {
+          const int c8 = id0 % (DQK / 8), r0 = 8 * (id0 / (DQK / 8));
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            pre[v][u] = __builtin_amdgcn_raw_buffer_load_b128(rk, ((r0 + u) * ks1 + c8 * 8) * 2, 0, 0);
+        } else {
+          const int id = id0 - T::KBLK;
+          const int rg = id % (TK / 8), c8 = id / (TK / 8);
+          const int r0 = 16 * (rg >> 1) + 4 * (rg & 1);
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            pre[v][u] = __builtin_amdgcn_raw_buffer_load_b128(
+                rv, ((block_row<8>(r0, u)) * vs1 + c8 * 8) * 2, 0, 0);
+        }
+      }
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int v = 0; v < T::NV; ++v) {
+      const int id0 = tid + 256 * v;
+      if ((T::KBLK + T::VBLK) % 256 == 0 || id0 < T::KBLK + T::VBLK) {
+        const bool isk = __builtin_amdgcn_readfirstlane(id0) < T::KBLK;
+        if (isk) {
+          const int c8 = id0 % (DQK / 8), r0 = 8 * (id0 / (DQK / 8));
+#pragma unroll
+          for (int u = 0; u < 8; ++u) *(u32x4*)&k_lds[(r0 + u) * KS + c8 * 8] = pre[v][u];
+        } else {
+          const int id = id0 - T::KBLK;
+          const int rg = id % (TK / 8), c8 = id / (TK / 8);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            unsigned lo[4], hi2[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              lo[t] = __builtin_amdgcn_perm(pre[v][2 * t + 1][k], pre[v][2 * t][k], 0x05040100u);
+              hi2[t] = __builtin_amdgcn_perm(pre[v][2 * t + 1][k], pre[v][2 * t][k], 0x07060302u);
+            }
+            *(u32x4*)&vt_lds[(c8 * 8 + 2 * k) * VS + 8 * rg] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+            *(u32x4*)&vt_lds[(c8 * 8 + 2 * k + 1) * VS + 8 * rg] = u32x4{hi2[0], hi2[1], hi2[2], hi2[3]};
+          }
+        }
+      }
+    }
+  };
+
+  // ---- online softmax state (log2 units) and the O^T accumulator ----
+  float m_run = -__builtin_inff();
+  float l_run = 0.f;
+  f32x16 o_acc[DV / 32];
+#pragma unroll
+  for (int n = 0; n < DV / 32; ++n) o_acc[n] = f32x16{};
+
+  if (ntiles > 0) {
+    load_tile(true, (int64_t)t_lo * TK);
+    store_tile();
+  }
+  for (int it = 0; it < ntiles; ++it) {
+    const int64_t kt0 = (int64_t)(t_lo + it) * TK;
+    __syncthreads();  // LDS holds tile it
+    load_tile(it + 1 < ntiles, kt0 + TK);
+
+    // S^T for the tile's two 32-key blocks: register r of block kb holds key
+    // kt0 + 32kb + 8(r/4) + 4hi + r%4 of this lane's query
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      bf16x8 ka[DQK / 16];
+#pragma unroll
+      for (int kk = 0; kk < DQK / 16; ++kk)
+        ka[kk] = *(const bf16x8*)&k_lds[(32 * kb + l32) * KS + 16 * kk + 8 * hi];
+      s[kb] = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < DQK / 16; ++kk) s[kb] = mfma(ka[kk], qf[kk], s[kb]);
+    }
+    // mask and running max
+    const int t0 = lane_ok ? (int)(kt0 - row - lo_l) + 4 * hi : (1 << 30);
+    float mt = -__builtin_inff();
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int ko = 32 * kb + 8 * (r >> 2) + (r & 3);
+        const float x = s[kb][r] * p.scale_log2;
+        s[kb][r] = (unsigned)(t0 + ko) <= span ? x : -__builtin_inff();
+        mt = fmaxf(mt, s[kb][r]);
+      }
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float m_new = fmaxf(m_run, mt);
+    const float m_use = m_new == -__builtin_inff() ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    m_run = m_new;
+    // P (bf16, laid out as the B operand of O^T) and the running sum
+    bf16x8 pb[2][2];
+    float ls = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float pv = __builtin_amdgcn_exp2f(s[kb][4 * c + e] - m_use);
+          ls += pv;
+          pb[kb][c >> 1][(c & 1) * 4 + e] = (__bf16)pv;
+        }
+    l_run = l_run * alpha + ls;
+    // O^T = alpha * O^T + V^T P^T (reduction step ks = 2kb + t covers transposed positions
+    // 16ks .. 16ks + 15)
+    bf16x8 va[4][DV / 32];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int n = 0; n < DV / 32; ++n)
+        va[ks][n] = *(const bf16x8*)&vt_lds[(32 * n + l32) * VS + 16 * ks + 8 * hi];
+#pragma unroll
+    for (int n = 0; n < DV / 32; ++n) {
+      o_acc[n] *= alpha;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) o_acc[n] = mfma(va[ks][n], pb[ks >> 1][ks & 1], o_acc[n]);
+    }
+    __syncthreads();  // every wave is done with tile it
+    store_tile();     // tile it+1 (zeros after the last one)
+  }
+
+  // ---- finish: the lane halves' sums, O = O^T / l, LSE = (m + log2 l) * ln 2 ----
+  const float l_all = l_run + __shfl_xor(l_run, 32);
+  const float inv = l_all > 0.f ? 1.f / l_all : 0.f;
+  if (row < sg.lq) {
+    uint16_t* orow = p.o_out + elem_off(p.o_s, group, b, sg.q_row0 + row, h);
+#pragma unroll
+    for (int n = 0; n < DV / 32; ++n)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        bf16x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(o_acc[n][4 * c + e] * inv);
+        *(bf16x4*)&orow[32 * n + 8 * c + 4 * hi] = v4;
+      }
+    if (hi == 0) {
+      const float lse = l_all > 0.f ? (m_run + __builtin_log2f(l_all)) * 0.6931471805599453f
+                                    : -__builtin_inff();
+      p.lse_out[(group ? 0 : (int64_t)b * p.lse_s[0]) + (int64_t)h * p.lse_s[1] + sg.q_row0 + row] = lse;
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void k_zero(float* ptr, int64_t n4) {
   const int64_t stride = (int64_t)gridDim.x * 256;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride)
@@ -788,6 +1028,20 @@ hipError_t launch_dot(const Plan& plan, const KParams& kp, hipStream_t stream) {
     hipLaunchKernelGGL(k_dot<64>, dim3((unsigned)blocks), dim3(256), 0, stream, kp);
   } else {
     hipLaunchKernelGGL(k_dot<128>, dim3((unsigned)blocks), dim3(256), 0, stream, kp);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd(const Plan& plan, const KParams& kp, hipStream_t stream) {
+  if (plan.B == 0 || plan.n_q_blocks == 0) return hipSuccess;
+  const int64_t rows = (int64_t)plan.n_q_blocks * plan.tile_m;  // >= the longest segment
+  const dim3 grid((unsigned)((rows + 127) / 128), (unsigned)plan.Hq, (unsigned)plan.B);
+  if (plan.d_qk == 64) {
+    hipLaunchKernelGGL((k_fwd<64, 64>), grid, dim3(256), 0, stream, kp);
+  } else if (plan.d_qk == 128) {
+    hipLaunchKernelGGL((k_fwd<128, 128>), grid, dim3(256), 0, stream, kp);
+  } else {
+    hipLaunchKernelGGL((k_fwd<192, 128>), grid, dim3(256), 0, stream, kp);
   }
   return hipGetLastError();
 }

@@ -46,7 +46,7 @@ bool strides_ok(const int64_t s[3], bool group) {
 
 }  // namespace
 
-int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t el) {
+int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t el, bool forward) {
   if (!a || !p) return fail(FMHA_ERR_INVALID_ARG, err, el, "null argument");
   if (a->struct_size != sizeof(fmha_bwd_args))
     return fail(FMHA_ERR_INVALID_ARG, err, el, "struct_size does not match this library");
@@ -138,26 +138,30 @@ int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t el) {
   const bool any_q = p->rows_q > 0;
   const bool any_k = group ? (a->B > 0 && a->seqstart_k_host[a->B] > 0) : ((int64_t)a->B * a->Sk > 0);
   if (any_q) {
-    if (!a->q || !a->o || !a->dout || !a->dq || !a->lse)
-      return fail(FMHA_ERR_INVALID_ARG, err, el, "q, o, dout, dq and lse must be set");
-    if (!aligned16(a->q) || !aligned16(a->o) || !aligned16(a->dout) || !aligned16(a->dq))
+    if (!a->q || !a->o || !a->lse || (!forward && (!a->dout || !a->dq)))
+      return fail(FMHA_ERR_INVALID_ARG, err, el,
+                  forward ? "q, o and lse must be set" : "q, o, dout, dq and lse must be set");
+    if (!aligned16(a->q) || !aligned16(a->o) ||
+        (!forward && (!aligned16(a->dout) || !aligned16(a->dq))))
       return fail(FMHA_ERR_UNSUPPORTED, err, el, "bf16 tensors must be 16-byte aligned");
     if (((uintptr_t)a->lse & 3u) != 0)
       return fail(FMHA_ERR_INVALID_ARG, err, el, "lse must be 4-byte aligned");
     if (!strides_ok(a->q_stride, group) || !strides_ok(a->o_stride, group) ||
-        !strides_ok(a->do_stride, group) || !strides_ok(a->dq_stride, group))
+        (!forward && (!strides_ok(a->do_stride, group) || !strides_ok(a->dq_stride, group))))
       return fail(FMHA_ERR_UNSUPPORTED, err, el,
                   "q/o/dout/dq strides must be non-negative multiples of 8 elements (sequence stride < 2^24)");
     if ((!group && a->lse_stride[0] < 0) || a->lse_stride[1] < 0)
       return fail(FMHA_ERR_INVALID_ARG, err, el, "lse strides must be non-negative");
   }
   if (any_k) {
-    if (!a->k || !a->v || !a->dk || !a->dv)
-      return fail(FMHA_ERR_INVALID_ARG, err, el, "k, v, dk and dv must be set");
-    if (!aligned16(a->k) || !aligned16(a->v) || !aligned16(a->dk) || !aligned16(a->dv))
+    if (!a->k || !a->v || (!forward && (!a->dk || !a->dv)))
+      return fail(FMHA_ERR_INVALID_ARG, err, el,
+                  forward ? "k and v must be set" : "k, v, dk and dv must be set");
+    if (!aligned16(a->k) || !aligned16(a->v) ||
+        (!forward && (!aligned16(a->dk) || !aligned16(a->dv))))
       return fail(FMHA_ERR_UNSUPPORTED, err, el, "bf16 tensors must be 16-byte aligned");
     if (!strides_ok(a->k_stride, group) || !strides_ok(a->v_stride, group) ||
-        !strides_ok(a->dk_stride, group) || !strides_ok(a->dv_stride, group))
+        (!forward && (!strides_ok(a->dk_stride, group) || !strides_ok(a->dv_stride, group))))
       return fail(FMHA_ERR_UNSUPPORTED, err, el,
                   "k/v/dk/dv strides must be non-negative multiples of 8 elements (sequence stride < 2^24)");
   }

@@ -37,7 +37,9 @@ struct Plan {
 
 // Validates `a` and fills `p`.  Returns FMHA_OK or a negative status; on failure `err`
 // (if not null) receives a message.
-int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t err_len);
+// forward = true checks the arguments of fmha_fwd_run instead: q, k, v in; o, lse out;
+// dout, dq, dk, dv unused.
+int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t err_len, bool forward = false);
 
 // Allowed (query, key) pairs over all heads and segments (FLOP accounting).
 int64_t count_pairs(const fmha_bwd_args* a);

@@ -214,6 +214,28 @@ def main():
         torch.cuda.empty_cache()
         return ms, main_ms, plan
 
+    def time_forward(bwd_flops):
+        """The device forward (fmha_fwd_run) on the same inputs, into scratch outputs."""
+        o2 = torch.empty_like(o)
+        lse2 = torch.empty_like(lse)
+        call = F.make_call(q, k, v, o2, lse2, None, None, None, None, scale=scale,
+                           mask_type=w["mask"], window=w.get("window", (-1, -1)))
+        for _ in range(args.warmup):
+            F._lib.fwd_run(call.args, sh)
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for _ in range(args.steps):
+            F._lib.fwd_run(call.args, sh)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        f_ms = t0.elapsed_time(t1) / args.steps
+        # forward FLOPs: S and P.V, 2*(d_qk + d_v) per allowed pair
+        f_flops = bwd_flops * (w["d_qk"] + w["d_v"]) / (3 * w["d_qk"] + 2 * w["d_v"])
+        return {"ms_per_call": round(f_ms, 4), "tflops": round(f_flops / (f_ms * 1e-3) / 1e12, 2),
+                "pct_of_bf16_peak": round(100.0 * f_flops / (f_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+
     primary_det = args.mode == "deterministic"
     ms, main_ms, plan = time_mode(primary_det)
     runs = [(primary_det, ms, main_ms, plan)]
@@ -248,6 +270,7 @@ def main():
             "dq_accumulation": args.mode, "nsplits": plan.nsplits,
             "flops_per_step": flops, "pct_of_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
             "modes": modes,
+            "forward": time_forward(flops),
         },
         "roofline": {
             "kernel": "k_bwd_main",

@@ -147,6 +147,15 @@ FMHA_BWD_API int fmha_bwd_prepare_workspace(const fmha_bwd_args* args, void* wor
 FMHA_BWD_API int fmha_bwd_run(const fmha_bwd_args* args, void* workspace, size_t workspace_bytes,
                  void* stream);
 
+/* Forward pass with the same argument struct: reads q, k, v (and the masks, seqstart and
+   padded-slot arrays, scale) and writes o = softmax(scale * q k^T + mask) v (bf16, layout of
+   dout in the backward, strides o_stride) and lse (fp32 natural-log log-sum-exp, the layout
+   the backward reads; -inf for a row with no allowed key, whose o row is 0).  dout, dq, dk and
+   dv are not used.  No workspace; asynchronous on `stream`.  The forward computation is the
+   one the backward differentiates (the plain definition, fp32 softmax statistics, bf16 P in
+   the P.V product). */
+FMHA_BWD_API int fmha_fwd_run(const fmha_bwd_args* args, void* stream);
+
 /* Static string naming a status code. */
 FMHA_BWD_API const char* fmha_bwd_status_string(int status);
 

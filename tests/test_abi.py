@@ -30,7 +30,7 @@ def built_library():
 
 def declared_functions():
     src = open(HEADER).read()
-    return sorted(set(re.findall(r"FMHA_BWD_API\s+[\w\s\*]+?\b(fmha_bwd_\w+)\s*\(", src)))
+    return sorted(set(re.findall(r"FMHA_BWD_API\s+[\w\s\*]+?\b(fmha_(?:bwd|fwd)_\w+)\s*\(", src)))
 
 
 def test_header_declarations_are_exported():
@@ -151,6 +151,25 @@ def test_group_mode_uses_physical_rows():
     # empty segments are fine and contribute no rows
     b = group_args([5, 0, 7], [0, 3, 9])
     assert _lib.plan_query(b).rows_q == 12
+
+
+def test_forward_argument_errors():
+    """fmha_fwd_run checks its arguments before any device work: o and lse are required, the
+    backward-only tensors are not (a missing one is no error, so the call reaches the launch,
+    which needs a GPU and is not made here)."""
+    L = _lib.lib()
+    a = batch_args()
+    a.o = None
+    assert L.fmha_fwd_run(ctypes.byref(a), None) == _lib.ERR_INVALID_ARG
+    a = batch_args()
+    a.lse = None
+    assert L.fmha_fwd_run(ctypes.byref(a), None) == _lib.ERR_INVALID_ARG
+    a = batch_args()
+    a.q = FAKE + 8
+    assert L.fmha_fwd_run(ctypes.byref(a), None) == _lib.ERR_UNSUPPORTED
+    a = batch_args()
+    a.scale = 0.0
+    assert L.fmha_fwd_run(ctypes.byref(a), None) == _lib.ERR_UNSUPPORTED
 
 
 def test_scale_must_be_positive():
