@@ -101,7 +101,7 @@ class PlanInfo(ctypes.Structure):
         ("n_q_blocks", ctypes.c_int32),
         ("nsplits", ctypes.c_int32),
         ("needs_zero", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("tiles_per_item", ctypes.c_int32),
         ("rows_q", ctypes.c_int64),
         ("d_offset", ctypes.c_int64),
         ("dq_acc_offset", ctypes.c_int64),

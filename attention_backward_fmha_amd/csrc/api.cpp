@@ -88,6 +88,7 @@ fmha::KParams make_params(const fmha_bwd_args* a, const fmha::Plan& p, void* ws)
   k.window_right = a->window_right;
   k.deterministic = p.deterministic ? 1 : 0;
   k.n_kv_tiles = p.n_kv_tiles;
+  k.tiles_per_item = p.tiles_per_item;
   k.n_q_blocks = p.n_q_blocks;
   k.scale = a->scale;
   k.scale_log2 = a->scale * 1.4426950408889634f;
@@ -197,6 +198,7 @@ int fmha_bwd_plan_query(const fmha_bwd_args* args, fmha_bwd_plan_info* info) {
   info->tile_m = p.tile_m;
   info->tile_n = p.tile_n;
   info->n_kv_tiles = p.n_kv_tiles;
+  info->tiles_per_item = p.tiles_per_item;
   info->n_q_blocks = p.n_q_blocks;
   info->nsplits = p.nsplits;
   info->needs_zero = p.needs_zero ? 1 : 0;

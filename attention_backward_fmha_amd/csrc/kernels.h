@@ -38,6 +38,7 @@ struct KParams {
   int mask_type, window_left, window_right;
   int deterministic;
   int n_kv_tiles, n_q_blocks;
+  int tiles_per_item;    // key tiles per main-kernel work item (deterministic mode: one split each)
   float scale;
   float scale_log2;  // scale * log2(e)
 };

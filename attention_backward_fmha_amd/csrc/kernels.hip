@@ -323,16 +323,25 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
   const int i16 = lane & 15;
 
   const int nbh = p.Hkv * p.B;
-  const int j = blockIdx.x / nbh;
-  const int rem = blockIdx.x - j * nbh;
+  const int item = blockIdx.x / nbh;  // key tiles item*T .. item*T + T - 1; split `item`
+  const int rem = blockIdx.x - item * nbh;
   const int g = rem % p.Hkv;
   const int b = rem / p.Hkv;
   const bool group = p.seqstart_q != nullptr;
   const Seg sg = seg_of(p, b);
-  const int64_t key0 = (int64_t)j * TN;
-  if (key0 >= sg.lk) return;  // whole work item beyond this segment (uniform)
-  const int nk = (int)min((int64_t)TN, sg.lk - key0);
   const MaskGeom mg = mask_geom(p.mask_type, p.window_left, p.window_right, sg.lq, sg.lk);
+  // query blocks whose partial this item has already written into its split (a contiguous
+  // range: consecutive tiles touch overlapping or adjacent ranges)
+  int64_t w_lo = 1, w_hi = 0;
+  for (int tsub = 0; tsub < p.tiles_per_item; ++tsub) {
+  const int j = item * p.tiles_per_item + tsub;
+  const int64_t key0 = (int64_t)j * TN;
+  if (key0 >= sg.lk) break;  // the rest of the item is beyond this segment (uniform)
+  if (tsub > 0) {
+    __builtin_amdgcn_s_waitcnt(0);  // the previous tile's partial stores have completed
+    __syncthreads();                // every wave is done with the previous tile's LDS
+  }
+  const int nk = (int)min((int64_t)TN, sg.lk - key0);
   int64_t qb_lo, qb_hi;
   qblocks_for_tile(mg, sg.lq, sg.lk, j, TM, TN, &qb_lo, &qb_hi);
   const int nblk = qb_hi >= qb_lo ? (int)(qb_hi - qb_lo + 1) : 0;
@@ -402,6 +411,9 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
   // they are written to LDS, so nothing waits for the loads before then.  Offsets inside a
   // block are 32-bit (the plan bounds the sequence strides).
   u32x4 pre[T::NV][RB];
+  // deterministic mode, later tiles of an item: the item's partial of the step's query block
+  // (written by an earlier tile) is read back during the step and added before the store
+  u32x4 prev[T::NTW][4];
   float lpre = 0.f, dpre = 0.f;
   const int qs1 = (int)p.q_s[1];
   const int os1 = (int)p.do_s[1];
@@ -555,21 +567,35 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
     }
     __syncthreads();  // LDS holds step n; every wave is done with step n-1's dS
     load_step(n + 1 < nsteps, h_next, q0_next);
-
-    compute_step((int)q0);
-    __syncthreads();  // dS complete; every wave is done reading this step's Q, dO tiles
-
-    // ---- dQ_i partial = dS K_j  (reduction over the tile's 128 keys) ----
-    // Deterministic: split j's block of this step (its own rows, padding included), stored
-    // lane by lane per 32x32 tile.  Atomic: fp32 adds into the row-major accumulator; the
-    // resource covers the block's valid rows, so rows past the segment end are dropped
-    // (offsets go entirely in the per-lane operand: the scalar offset is outside the range
-    // check).
     const __amdgpu_buffer_rsrc_t rdq = DET
-        ? buffer_rsrc(p.dq_acc + (int64_t)j * p.split_stride + (int64_t)h * p.head_stride +
+        ? buffer_rsrc(p.dq_acc + (int64_t)item * p.split_stride + (int64_t)h * p.head_stride +
                           (sg.acc_row0 + q0) * DQK, (uint32_t)TM * DQK * 4u)
         : buffer_rsrc(p.dq_acc + (int64_t)h * p.head_stride + (sg.acc_row0 + q0) * DQK,
                       (uint32_t)nq * DQK * 4u);
+    compute_step((int)q0);
+    if (DET) {  // issued late: the S/dP accumulators are dead by now
+      const int64_t qbn = q0 / TM;
+      const __amdgpu_buffer_rsrc_t rprev =
+          qbn >= w_lo && qbn <= w_hi ? rdq : buffer_rsrc(p.dq_acc, 0u);  // empty: reads 0
+#pragma unroll
+      for (int tt = 0; tt < T::NTW; ++tt) {
+        const int ti = wave + 4 * tt;
+        if (NT % 4 == 0 || ti < NT) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            prev[tt][u] = __builtin_amdgcn_raw_buffer_load_b128(rprev, (ti * 1024 + lane * 16) * 4 + 16 * u, 0, 0);
+        }
+      }
+    }
+
+    __syncthreads();  // dS complete; every wave is done reading this step's Q, dO tiles
+
+    // ---- dQ_i partial = dS K_j  (reduction over the tile's 128 keys) ----
+    // Deterministic: the item's split block of this step (its own rows, padding included),
+    // the earlier tiles' sum plus this tile's, stored lane by lane per 32x32 tile.  Atomic:
+    // fp32 adds into the row-major accumulator; the resource covers the block's valid rows,
+    // so rows past the segment end are dropped (offsets go entirely in the per-lane operand:
+    // the scalar offset is outside the range check).
 #pragma unroll
     for (int tt = 0; tt < T::NTW; ++tt) {
       const int ti = wave + 4 * tt;
@@ -597,8 +623,10 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
 #pragma unroll
           for (int u = 0; u < 4; ++u)
             __builtin_amdgcn_raw_buffer_store_b128(
-                u32x4{__float_as_uint(acc[4 * u]), __float_as_uint(acc[4 * u + 1]),
-                      __float_as_uint(acc[4 * u + 2]), __float_as_uint(acc[4 * u + 3])},
+                u32x4{__float_as_uint(__uint_as_float(prev[tt][u][0]) + acc[4 * u]),
+                      __float_as_uint(__uint_as_float(prev[tt][u][1]) + acc[4 * u + 1]),
+                      __float_as_uint(__uint_as_float(prev[tt][u][2]) + acc[4 * u + 2]),
+                      __float_as_uint(__uint_as_float(prev[tt][u][3]) + acc[4 * u + 3])},
                 rdq, voff + 16 * u, 0, 0);
         } else {
           // register r holds query row 32mq + 8(r/4) + 4hi + r%4, column 32nd + l%32: each
@@ -631,6 +659,12 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
       for (int n = 0; n < DV / 32; ++n) dvp[32 * n] = to_bf16_bits(dv_acc[n][r]);
     }
   }
+  if (nblk > 0) {
+    const bool had = w_hi >= w_lo;
+    w_lo = had ? min(w_lo, qb_lo) : qb_lo;
+    w_hi = had ? max(w_hi, qb_hi) : qb_hi;
+  }
+  }  // tiles of the item
 }
 
 // ------------------------------------------------------------------------------------------
@@ -660,6 +694,12 @@ __device__ __forceinline__ void reduce_tiles(const KParams& p, const Seg& sg, bo
     } else if (jhi >= 0) {
       break;
     }
+  }
+  // split s holds key tiles s*T .. s*T + T - 1: the tile range maps to a split range
+  const int T = p.tiles_per_item;
+  if (jhi >= jlo) {
+    jlo /= T;
+    jhi /= T;
   }
   const float* base = p.dq_acc + (int64_t)h * p.head_stride + (sg.acc_row0 + (int64_t)qb * TM) * DQK;
   f32x4 acc[PPT][4];
@@ -1056,7 +1096,8 @@ static void launch_main_t(const Plan& plan, const KParams& kp, dim3 grid, hipStr
 }
 
 hipError_t launch_main(const Plan& plan, const KParams& kp, hipStream_t stream) {
-  const int64_t items = (int64_t)plan.n_kv_tiles * plan.Hkv * plan.B;
+  const int64_t items = (int64_t)((plan.n_kv_tiles + plan.tiles_per_item - 1) / plan.tiles_per_item) *
+                        plan.Hkv * plan.B;
   if (items == 0) return hipSuccess;
   const dim3 grid((unsigned)items);
   if (plan.d_qk == 64) {

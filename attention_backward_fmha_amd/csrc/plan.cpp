@@ -3,8 +3,9 @@
 // Workspace layout (byte offsets 256-aligned):
 //   D       fp32 [Hq][rows_q]                     rowsum(dO * O) from the first stage
 //   L       fp32 [Hq][rows_q]                     LSE * log2(e), also from the first stage
-//   dq_acc  fp32 [nsplits][Hq][acc_rows][d_qk]    dQ partials (deterministic: split = key tile
-//                                                 index of the segment, blocks of tile_m rows
+//   dq_acc  fp32 [nsplits][Hq][acc_rows][d_qk]    dQ partials (deterministic: split s = key
+//                                                 tiles s*T..s*T+T-1 of the segment, T =
+//                                                 tiles_per_item, blocks of tile_m rows
 //                                                 in matrix-core tile order, tile_m rows of
 //                                                 padding per segment; atomic: one split,
 //                                                 row-major, acc_rows = rows_q)
@@ -168,7 +169,27 @@ int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t el, bool forwar
 
   p->n_kv_tiles = (int)((max_lk + p->tile_n - 1) / p->tile_n);
   p->n_q_blocks = (int)((max_lq + p->tile_m - 1) / p->tile_m);
-  p->nsplits = p->deterministic ? (p->n_kv_tiles > 0 ? p->n_kv_tiles : 1) : 1;
+  // Deterministic mode: one work item walks tiles_per_item consecutive key tiles and adds
+  // their dQ contributions into one split, so the reduction reads 1/tiles_per_item of the
+  // per-tile partials.  The largest of 4 and 2 that still leaves two work items per compute
+  // unit of an MI355X (256 CUs) is used, so that the heaviest causal items do not set the
+  // makespan.
+  p->tiles_per_item = 1;
+  if (p->deterministic) {
+    const int64_t heads = (int64_t)p->Hkv * p->B;
+    for (int t : {4, 2}) {
+      if ((int64_t)((p->n_kv_tiles + t - 1) / t) * heads >= 2 * 256) {
+        p->tiles_per_item = t;
+        break;
+      }
+    }
+  }
+  if (const char* e = getenv("FMHA_BWD_TILES_PER_ITEM")) {  // tuning knob: 1, 2 or 4
+    if (p->deterministic && (atoi(e) == 1 || atoi(e) == 2 || atoi(e) == 4))
+      p->tiles_per_item = atoi(e);
+  }
+  const int n_items = (p->n_kv_tiles + p->tiles_per_item - 1) / p->tiles_per_item;
+  p->nsplits = p->deterministic ? (n_items > 0 ? n_items : 1) : 1;
   p->needs_zero = !p->deterministic;
   p->max_rows_q = p->rows_q;
 

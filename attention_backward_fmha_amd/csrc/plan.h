@@ -18,7 +18,8 @@ struct Plan {
   int Sq, Sk;            // batch: lengths; group: maximum segment lengths
   int d_qk, d_v;
   int tile_m, tile_n;    // query rows per block, keys per tile
-  int n_kv_tiles;        // key tiles of the longest segment (grid extent)
+  int n_kv_tiles;        // key tiles of the longest segment
+  int tiles_per_item;    // key tiles per main-kernel work item; deterministic split = item
   int n_q_blocks;        // query blocks of the longest segment (grid extent)
   int nsplits;           // accumulator depth
   bool needs_zero;       // prepare zeroes the accumulator (atomic mode)

@@ -168,9 +168,10 @@ typedef struct fmha_bwd_plan_info {
   int32_t tile_n;          /* keys per tile (one work item) */
   int32_t n_kv_tiles;      /* key tiles of the longest segment */
   int32_t n_q_blocks;      /* query blocks of the longest segment */
-  int32_t nsplits;         /* depth of the dQ accumulator (n_kv_tiles, or 1 in atomic mode) */
+  int32_t nsplits;         /* depth of the dQ accumulator: ceil(n_kv_tiles / tiles_per_item),
+                              or 1 in atomic mode */
   int32_t needs_zero;      /* prepare zeroes the accumulator */
-  int32_t reserved;
+  int32_t tiles_per_item;  /* key tiles per main-kernel work item (deterministic split) */
   int64_t rows_q;          /* T_q: B*Sq (batch), seqstart_q[B] (group) or the padded q
                               offsets' last entry (padded group) */
   int64_t d_offset;        /* byte offset of D = rowsum(dO*O), fp32 [Hq][rows_q] */
@@ -182,7 +183,8 @@ typedef struct fmha_bwd_plan_info {
   int64_t acc_rows;        /* accumulator rows per head and split (see below) */
 } fmha_bwd_plan_info;
 /* Accumulator layout.  Atomic mode: one split, rows_q rows, row-major ([row][d_qk]), row of
-   a query = its D/LSE row.  Deterministic mode: split j holds key tile j's partial;
+   a query = its D/LSE row.  Deterministic mode: split s holds the sum of the partials of key
+   tiles s*T .. s*T+T-1 (T = tiles_per_item, added in ascending tile order);
    acc_rows = rows_q + B*tile_m and query block i of segment b (rows b_0 + i*tile_m ..) is
    the tile_m*d_qk values starting at row a_b + i*tile_m, a_b = (first D row of segment b) +
    b*tile_m, so blocks of different segments never share rows.  Inside a block the values

@@ -130,7 +130,9 @@ def test_workspace_size_and_plan_agree():
         assert _lib.workspace_size(a) == info.workspace_bytes
         rows = 2 * 200
         assert info.rows_q == rows
-        assert info.nsplits == (3 if det else 1)  # ceil(333 / 128) key tiles
+        # ceil(333 / 128) = 3 key tiles; 6 work items at most, so one tile per item
+        assert info.tiles_per_item == 1
+        assert info.nsplits == (3 if det else 1)
         assert info.needs_zero == (0 if det else 1)
         # deterministic blocks get tile_m rows of padding per segment
         assert info.acc_rows == rows + (2 * info.tile_m if det else 0)
@@ -170,6 +172,19 @@ def test_forward_argument_errors():
     a = batch_args()
     a.scale = 0.0
     assert L.fmha_fwd_run(ctypes.byref(a), None) == _lib.ERR_UNSUPPORTED
+
+
+def test_tiles_per_item_keeps_two_items_per_cu():
+    """Deterministic work items take 4 key tiles when that leaves >= 512 items, else 2, else 1;
+    the split count follows."""
+    for B, H, S, want in ((2, 32, 4096, 4), (1, 8, 16384, 2), (2, 16, 2048, 1)):
+        a = batch_args(B=B, Hq=H, Hkv=H, Sq=S, Sk=S, mask=1)
+        info = _lib.plan_query(a)
+        tiles = -(-S // 128)
+        assert info.tiles_per_item == want, (B, H, S)
+        assert info.nsplits == -(-tiles // want)
+    a = batch_args(B=2, Hq=32, Hkv=32, Sq=4096, Sk=4096, mask=1, deterministic=0)
+    assert _lib.plan_query(a).tiles_per_item == 1
 
 
 def test_scale_must_be_positive():
@@ -300,5 +315,7 @@ def test_sizing_is_a_pure_function_of_the_arguments():
         assert i1["workspace_bytes"] == _lib.workspace_size(a)
         nt = -(-int(lk.max()) // i1["tile_n"])
         assert i1["n_kv_tiles"] == nt
-        assert i1["nsplits"] == (max(nt, 1) if det else 1)
+        tpi = i1["tiles_per_item"]
+        assert tpi in ((1, 2, 4) if det else (1,))
+        assert i1["nsplits"] == (max(-(-nt // tpi), 1) if det else 1)
         assert i1["rows_q"] == int(lq.sum())

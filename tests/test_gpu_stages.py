@@ -98,7 +98,8 @@ def test_reduce_stage_is_bit_exact(mask, window):
         for i in range(-(-lens[b] // tm)):
             nr = min(lens[b], (i + 1) * tm) - i * tm
             rs = slice(r0 + i * tm, r0 + i * tm + nr)
-            used = sorted(j for (ii, j) in touched if ii == i)
+            # split s holds key tiles s*T .. s*T + T - 1 (T = tiles_per_item)
+            used = sorted({j // info.tiles_per_item for (ii, j) in touched if ii == i})
             base = (r0 + b * tm + i * tm) * d
             for j in used:
                 dev[j, :, base + offs[:nr].ravel()] = parts[j, :, rs, :].reshape(hq, -1).T
