@@ -6,12 +6,15 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libfmha_bwd.so")
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 MASK_NONE = 0
 MASK_CAUSAL_TOP_LEFT = 1
 MASK_CAUSAL_BOTTOM_RIGHT = 2
 MASK_WINDOW = 3
+
+DQ_ACC_FP32 = 0
+DQ_ACC_BF16 = 1
 
 OK = 0
 ERR_INVALID_ARG = -1
@@ -79,6 +82,8 @@ class Args(ctypes.Structure):
         ("seqstart_k_padded_host", ctypes.c_void_p),
         ("seqstart_q_padded_dev", ctypes.c_void_p),
         ("seqstart_k_padded_dev", ctypes.c_void_p),
+        ("dq_acc_dtype", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
     def __init__(self, **kw):
@@ -110,6 +115,8 @@ class PlanInfo(ctypes.Structure):
         ("pairs", ctypes.c_int64),
         ("flops", ctypes.c_double),
         ("acc_rows", ctypes.c_int64),
+        ("dq_acc_elem_bytes", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
     def as_dict(self):

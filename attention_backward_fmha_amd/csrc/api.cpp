@@ -30,9 +30,10 @@ int plan_or_fail(const fmha_bwd_args* a, fmha::Plan* p, const char* where, bool 
 void log_plan(const fmha::Plan& p, const char* where) {
   if (!log_enabled()) return;
   fprintf(stderr,
-          "[fmha_bwd] %s: mode=%s B=%d Hq=%d Hkv=%d Sq=%d Sk=%d d=(%d,%d) tile=(%d,%d) "
+          "[fmha_bwd] %s: mode=%s dq_acc=%s B=%d Hq=%d Hkv=%d Sq=%d Sk=%d d=(%d,%d) tile=(%d,%d) "
           "kv_tiles=%d q_blocks=%d nsplits=%d zero=%d ws=%lld (D@%lld acc@%lld+%lld)\n",
-          where, p.group_mode ? "group" : "batch", p.B, p.Hq, p.Hkv, p.Sq, p.Sk, p.d_qk, p.d_v,
+          where, p.group_mode ? "group" : "batch",
+          p.deterministic ? "split-fp32" : (p.dq_bf16 ? "atomic-bf16" : "atomic-fp32"), p.B, p.Hq, p.Hkv, p.Sq, p.Sk, p.d_qk, p.d_v,
           p.tile_m, p.tile_n, p.n_kv_tiles, p.n_q_blocks, p.nsplits, (int)p.needs_zero,
           (long long)p.workspace_bytes, (long long)p.d_offset, (long long)p.dq_acc_offset,
           (long long)p.dq_acc_bytes);
@@ -87,6 +88,7 @@ fmha::KParams make_params(const fmha_bwd_args* a, const fmha::Plan& p, void* ws)
   k.window_left = a->window_left;
   k.window_right = a->window_right;
   k.deterministic = p.deterministic ? 1 : 0;
+  k.dq_bf16 = p.dq_bf16 ? 1 : 0;
   k.n_kv_tiles = p.n_kv_tiles;
   k.tiles_per_item = p.tiles_per_item;
   k.n_q_blocks = p.n_q_blocks;
@@ -204,6 +206,7 @@ int fmha_bwd_plan_query(const fmha_bwd_args* args, fmha_bwd_plan_info* info) {
   info->needs_zero = p.needs_zero ? 1 : 0;
   info->rows_q = p.rows_q;
   info->acc_rows = p.acc_rows;
+  info->dq_acc_elem_bytes = p.dq_bf16 ? 2 : 4;
   info->d_offset = p.d_offset;
   info->dq_acc_offset = p.dq_acc_offset;
   info->dq_acc_bytes = p.dq_acc_bytes;

@@ -37,6 +37,7 @@ struct KParams {
   int B, Hq, Hkv, group_size, Sq, Sk;
   int mask_type, window_left, window_right;
   int deterministic;
+  int dq_bf16;           // dq_acc is bf16 [B][Hq][head_stride/d_qk][d_qk] (split_stride = per segment)
   int n_kv_tiles, n_q_blocks;
   int tiles_per_item;    // key tiles per main-kernel work item (deterministic mode: one split each)
   float scale;

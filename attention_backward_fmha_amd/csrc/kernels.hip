@@ -5,10 +5,11 @@
 //     for every query head h of g's group and every query block i the mask lets tile j see:
 //       S = Q_i K_j^T, P = exp(scale*S - LSE_i) (0 where masked), dP = dO_i V_j^T,
 //       dS = P * (dP - D_i), dV_j += P^T dO_i, dK_j += dS^T Q_i, dQ_i += dS K_j
-//     dK_j (scaled) and dV_j are written once at the end; the tile's dS K_j goes to the fp32
-//     accumulator: split j (deterministic) or an fp32 atomic add into split 0.      MFMA bound
+//     dK_j (scaled) and dV_j are written once at the end; the tile's dS K_j goes to the dQ
+//     accumulator: the item's split (deterministic), an fp32 atomic add into the one split,
+//     or a packed bf16 atomic add into the segment's bf16 slot.                     MFMA bound
 // Stage 3 (k_dq_reduce): dQ = bf16(scale * sum_{splits that wrote the block} acc), the fp32
-//     sum in ascending split order.                                                HBM bound
+//     sum in ascending split order (one split, fp32 or bf16, in the atomic modes).  HBM bound
 //
 // Matrix products use v_mfma_f32_32x32x16_bf16 (bf16 operands, fp32 accumulation).  Its lane
 // layout (checked on the device): lane l holds row (l % 32) of A and column (l % 32) of B with
@@ -300,8 +301,10 @@ __device__ __forceinline__ void stage_block(uint16_t* rm, uint16_t* tr, int RS,
   }
 }
 
-template <int DQK, int DV, int TM_, bool DET>
+// DQM: 0 = fp32 atomic adds, 1 = deterministic fp32 splits, 2 = packed bf16 atomic adds
+template <int DQK, int DV, int TM_, int DQM>
 __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
+  constexpr bool DET = DQM == 1;
   using T = MainTile<DQK, DV, TM_>;
   constexpr int TM = T::TM, MT = T::MT, TN = T::TN, QS = T::QS, OS = T::OS, KS = T::KS,
                 SR = T::SR, TS = T::TS, NT = T::NT, RB = T::RB;
@@ -572,6 +575,10 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
                           (sg.acc_row0 + q0) * DQK, (uint32_t)TM * DQK * 4u)
         : buffer_rsrc(p.dq_acc + (int64_t)h * p.head_stride + (sg.acc_row0 + q0) * DQK,
                       (uint32_t)nq * DQK * 4u);
+    // bf16 mode: slot (b, h) of the bf16 accumulator, rows = logical query positions
+    const __amdgpu_buffer_rsrc_t r16 =
+        buffer_rsrc((const uint16_t*)p.dq_acc + (int64_t)b * p.split_stride + (int64_t)h * p.head_stride +
+                        q0 * DQK, (uint32_t)nq * DQK * 2u);
     compute_step((int)q0);
     if (DET) {  // issued late: the S/dP accumulators are dead by now
       const int64_t qbn = q0 / TM;
@@ -628,6 +635,24 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
                       __float_as_uint(__uint_as_float(prev[tt][u][2]) + acc[4 * u + 2]),
                       __float_as_uint(__uint_as_float(prev[tt][u][3]) + acc[4 * u + 3])},
                 rdq, voff + 16 * u, 0, 0);
+        } else if (DQM == 2) {
+          // packed bf16 adds.  Each lane packs rows (k, 8+k) of its column; lanes 2c and 2c+1
+          // swap the packed words, and the even lane keeps row k of columns 2c, 2c+1, the odd
+          // lane row 8+k.  The resource covers the block's valid rows, so the hardware range
+          // check drops rows past the segment end.  (No builtin exposes the buffer form of
+          // this atomic; it is written out, without return value, so no wait depends on it.)
+          const bool odd = (lane & 1) != 0;
+          const unsigned sel = odd ? 0x03020706u : 0x05040100u;
+          const int col_off = (32 * nd + (l32 & ~1)) * 2;
+#pragma unroll
+          for (int k2 = 0; k2 < 8; ++k2) {
+            const unsigned mine = pack_bf16(acc[k2], acc[8 + k2]);
+            const unsigned other = xor1(mine);
+            const unsigned v = __builtin_amdgcn_perm(other, mine, sel);
+            const int r = odd ? 8 + k2 : k2;
+            const int voff = (32 * mq + 8 * (r >> 2) + 4 * hi + (r & 3)) * DQK * 2 + col_off;
+            asm volatile("buffer_atomic_pk_add_bf16 %0, %1, %2, 0 offen" ::"v"(v), "v"(voff), "s"(r16));
+          }
         } else {
           // register r holds query row 32mq + 8(r/4) + 4hi + r%4, column 32nd + l%32: each
           // atomic covers two 128-byte row segments
@@ -788,6 +813,30 @@ __device__ __forceinline__ void reduce_rows(const KParams& p, const Seg& sg, boo
   }
 }
 
+// bf16 accumulator: slot (b, h), row = logical query position.
+template <int DQK, int TM>
+__device__ __forceinline__ void convert_rows16(const KParams& p, const Seg& sg, bool group, int b,
+                                               int h, int qb, int nq) {
+  constexpr int C4 = DQK / 4;                   // 4-element chunks per row
+  constexpr int PER = (TM * C4 + 255) / 256;    // chunks per thread
+  const int tid = threadIdx.x;
+  const int64_t q0 = (int64_t)qb * TM;
+  const uint16_t* base = (const uint16_t*)p.dq_acc + (int64_t)b * p.split_stride +
+                         (int64_t)h * p.head_stride + q0 * DQK;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int c = tid + 256 * u;
+    const int r = c / C4;
+    if (r < nq) {
+      const bf16x4 x = *(const bf16x4*)(base + (int64_t)r * DQK + (c - r * C4) * 4);
+      bf16x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = (__bf16)((float)x[e] * p.scale);
+      *(bf16x4*)(p.dq + elem_off(p.dq_s, group, b, sg.q_row0 + q0 + r, h) + (c - r * C4) * 4) = o;
+    }
+  }
+}
+
 // Work groups per query block in deterministic mode: one per 256 (tile, lane) pairs.
 template <int DQK, int TM>
 constexpr int reduce_parts() { return ((TM / 32) * (DQK / 32) * 64 + 255) / 256; }
@@ -806,6 +855,8 @@ __global__ __launch_bounds__(256) void k_dq_reduce(const KParams p) {
   const int nq = (int)min((int64_t)TM, sg.lq - q0);
   if (p.deterministic) {
     reduce_tiles<DQK, TM>(p, sg, group, b, h, qb, nq, part);
+  } else if (p.dq_bf16) {
+    convert_rows16<DQK, TM>(p, sg, group, b, h, qb, nq);
   } else {
     reduce_rows<DQK, TM>(p, sg, group, b, h, qb, nq);
   }
@@ -1089,9 +1140,11 @@ hipError_t launch_fwd(const Plan& plan, const KParams& kp, hipStream_t stream) {
 template <int DQK, int DV, int TM>
 static void launch_main_t(const Plan& plan, const KParams& kp, dim3 grid, hipStream_t stream) {
   if (plan.deterministic) {
-    hipLaunchKernelGGL((k_bwd_main<DQK, DV, TM, true>), grid, dim3(256), 0, stream, kp);
+    hipLaunchKernelGGL((k_bwd_main<DQK, DV, TM, 1>), grid, dim3(256), 0, stream, kp);
+  } else if (plan.dq_bf16) {
+    hipLaunchKernelGGL((k_bwd_main<DQK, DV, TM, 2>), grid, dim3(256), 0, stream, kp);
   } else {
-    hipLaunchKernelGGL((k_bwd_main<DQK, DV, TM, false>), grid, dim3(256), 0, stream, kp);
+    hipLaunchKernelGGL((k_bwd_main<DQK, DV, TM, 0>), grid, dim3(256), 0, stream, kp);
   }
 }
 

@@ -9,6 +9,10 @@
 //                                                 in matrix-core tile order, tile_m rows of
 //                                                 padding per segment; atomic: one split,
 //                                                 row-major, acc_rows = rows_q)
+//           or bf16 [B][Hq][acc_rows][d_qk]       bf16 atomic mode: one slot of
+//                                                 acc_rows = pad16(longest lq) rows per
+//                                                 (segment, head), indexed by the logical
+//                                                 query position
 // One layout serves batch and group mode: row = b*Sq + i in batch mode and seqstart_q[b] + i
 // in group mode (the physical token), so a ragged segment never aliases another one's rows --
 // unlike the layout mix-up in "[ROCm] Fix THD/ragged dQ backward on the bf16 dq_shuffle path
@@ -76,6 +80,12 @@ int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t el, bool forwar
     return fail(FMHA_ERR_INVALID_ARG, err, el, "window bounds must be >= -1");
   if (a->deterministic != 0 && a->deterministic != 1)
     return fail(FMHA_ERR_INVALID_ARG, err, el, "deterministic must be 0 or 1");
+  if (a->dq_acc_dtype != FMHA_DQ_ACC_FP32 && a->dq_acc_dtype != FMHA_DQ_ACC_BF16)
+    return fail(FMHA_ERR_INVALID_ARG, err, el, "unknown dq_acc_dtype");
+  if (a->dq_acc_dtype == FMHA_DQ_ACC_BF16 && a->deterministic)
+    return fail(FMHA_ERR_INVALID_ARG, err, el,
+                "the bf16 dQ accumulator is for atomic (deterministic = 0) mode only");
+  if (a->reserved != 0) return fail(FMHA_ERR_INVALID_ARG, err, el, "reserved must be 0");
 
   p->B = a->B;
   p->Hq = a->Hq;
@@ -92,6 +102,7 @@ int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t el, bool forwar
   }
   p->tile_n = 128;
   p->deterministic = a->deterministic == 1;
+  p->dq_bf16 = a->dq_acc_dtype == FMHA_DQ_ACC_BF16;
 
   int64_t max_lq = a->Sq, max_lk = a->Sk;
   if (group) {
@@ -195,13 +206,15 @@ int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t el, bool forwar
 
   p->acc_pad = p->deterministic ? p->tile_m : 0;
   p->acc_rows = p->rows_q + (int64_t)p->B * p->acc_pad;
+  if (p->dq_bf16) p->acc_rows = align_up(max_lq, 16);  // one slot per (segment, head)
   p->head_stride = p->acc_rows * p->d_qk;
   p->split_stride = (int64_t)p->Hq * p->head_stride;
   p->d_offset = 0;
   p->d_bytes = (int64_t)p->Hq * p->rows_q * 4;
   p->lse2_offset = align_up(p->d_bytes, 256);
   p->dq_acc_offset = align_up(p->lse2_offset + p->d_bytes, 256);
-  p->dq_acc_bytes = (int64_t)p->nsplits * p->split_stride * 4;
+  p->dq_acc_bytes = p->dq_bf16 ? (int64_t)p->B * p->split_stride * 2
+                               : (int64_t)p->nsplits * p->split_stride * 4;
   p->workspace_bytes = align_up(p->dq_acc_offset + p->dq_acc_bytes, 256);
   if (p->workspace_bytes == 0) p->workspace_bytes = 256;
   return FMHA_OK;

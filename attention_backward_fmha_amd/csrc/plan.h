@@ -24,13 +24,16 @@ struct Plan {
   int nsplits;           // accumulator depth
   bool needs_zero;       // prepare zeroes the accumulator (atomic mode)
   bool deterministic;
+  bool dq_bf16;          // bf16 accumulator, packed bf16 atomic adds (non-deterministic only)
   int64_t rows_q;        // accumulator / D rows: B*Sq or seqstart_q[B]
   int64_t d_offset, d_bytes;
   int64_t lse2_offset;   // LSE * log2(e), same shape as D
   int64_t dq_acc_offset, dq_acc_bytes;
   int64_t acc_rows;      // accumulator rows per head: rows_q (atomic), rows_q + B*tile_m
+                         // (deterministic); bf16: per (segment, head), pad16(longest lq)
   int acc_pad;           // rows of padding per segment: 0 (atomic) or tile_m
-  int64_t split_stride;  // elements between consecutive splits: Hq*acc_rows*d_qk
+  int64_t split_stride;  // elements between consecutive splits: Hq*acc_rows*d_qk (bf16:
+                         // between consecutive segments' slots)
   int64_t head_stride;   // elements between heads inside a split: acc_rows*d_qk
   int64_t workspace_bytes;
   int64_t max_rows_q;    // for the D stage grid: rows_q

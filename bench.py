@@ -32,12 +32,17 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 
 
+# dQ accumulation modes: (deterministic flag, accumulator type)
+MODE_ARGS = {"deterministic": (True, "fp32"), "atomic": (False, "fp32"), "atomic16": (False, "bf16")}
+MODES = list(MODE_ARGS)
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--mode", choices=["atomic", "deterministic"], default="deterministic")
+    ap.add_argument("--mode", choices=MODES, default="deterministic")
     ap.add_argument("--workload", default="headline_2x32x4096_causal")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-mode", action="store_true",
@@ -179,9 +184,10 @@ def main():
     stream = torch.cuda.current_stream(device)
     sh = stream.cuda_stream
 
-    def time_mode(det):
+    def time_mode(mode):
+        det, acc = MODE_ARGS[mode]
         call = F.make_call(q, k, v, o, lse, do, dq, dk, dv, scale=scale, mask_type=w["mask"],
-                           window=w.get("window", (-1, -1)), deterministic=det)
+                           window=w.get("window", (-1, -1)), deterministic=det, dq_acc_dtype=acc)
         plan = call.plan()
         ws = torch.empty(call.workspace_size(), dtype=torch.uint8, device=device)
 
@@ -236,17 +242,16 @@ def main():
         return {"ms_per_call": round(f_ms, 4), "tflops": round(f_flops / (f_ms * 1e-3) / 1e12, 2),
                 "pct_of_bf16_peak": round(100.0 * f_flops / (f_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
 
-    primary_det = args.mode == "deterministic"
-    ms, main_ms, plan = time_mode(primary_det)
-    runs = [(primary_det, ms, main_ms, plan)]
+    ms, main_ms, plan = time_mode(args.mode)
+    runs = [(args.mode, ms, main_ms, plan)]
     if not args.only_mode:
-        runs.append((not primary_det,) + time_mode(not primary_det))
+        runs += [(m,) + time_mode(m) for m in MODES if m != args.mode]
     flops = plan.flops
     tflops = flops / (ms * 1e-3) / 1e12
     main_tflops = flops / (main_ms * 1e-3) / 1e12
     modes = {}
-    for det, m_ms, m_main, m_plan in runs:
-        modes["deterministic" if det else "atomic"] = {
+    for mode, m_ms, m_main, m_plan in runs:
+        modes[mode] = {
             "value": round(flops / (m_ms * 1e-3) / 1e12, 2), "ms_per_step": round(m_ms, 4),
             "main_kernel_ms": round(m_main, 4), "nsplits": m_plan.nsplits}
 

@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define FMHA_BWD_ABI_VERSION 2u
+#define FMHA_BWD_ABI_VERSION 3u
 
 #if defined(__GNUC__)
 #define FMHA_BWD_API __attribute__((visibility("default")))
@@ -77,6 +77,18 @@ enum fmha_mask_type {
   FMHA_MASK_CAUSAL_TOP_LEFT = 1,
   FMHA_MASK_CAUSAL_BOTTOM_RIGHT = 2,
   FMHA_MASK_WINDOW = 3
+};
+
+/* dQ accumulation type of the non-deterministic mode (fmha_bwd_args.dq_acc_dtype). */
+enum fmha_dq_acc_dtype {
+  FMHA_DQ_ACC_FP32 = 0, /* fp32 accumulator, fp32 atomic adds (deterministic = 0) or fp32
+                           split partials (deterministic = 1) */
+  FMHA_DQ_ACC_BF16 = 1  /* deterministic = 0 only: packed bf16 atomic adds into a bf16
+                           accumulator with one padded slot per segment, the "atomic16"
+                           accumulation of "[ROCm] Fix THD/ragged dQ backward on the bf16
+                           dq_shuffle path (gfx950)" (Root cause, Fix).  About half the
+                           atomic traffic of fp32; every add rounds the running sum to bf16,
+                           so dQ is less accurate than in the fp32 modes */
 };
 
 enum fmha_status {
@@ -131,6 +143,8 @@ typedef struct fmha_bwd_args {
   const int32_t* seqstart_k_padded_host;
   const int32_t* seqstart_q_padded_dev;
   const int32_t* seqstart_k_padded_dev;
+  int32_t dq_acc_dtype;  /* enum fmha_dq_acc_dtype; FMHA_DQ_ACC_BF16 needs deterministic = 0 */
+  int32_t reserved;      /* must be 0 */
 } fmha_bwd_args;
 
 /* Workspace bytes that prepare/run need for these arguments.  Host only: no GPU call, no
@@ -138,8 +152,8 @@ typedef struct fmha_bwd_args {
 FMHA_BWD_API int fmha_bwd_workspace_size(const fmha_bwd_args* args, size_t* bytes);
 
 /* Initialise the workspace on `stream` (a hipStream_t; NULL = the default stream).  Atomic
-   mode zeroes the dQ accumulator; deterministic mode needs no initialisation (every partial
-   the reduction reads is written by the run).  Asynchronous. */
+   modes (fp32 and bf16) zero the dQ accumulator; deterministic mode needs no initialisation
+   (every partial the reduction reads is written by the run).  Asynchronous. */
 FMHA_BWD_API int fmha_bwd_prepare_workspace(const fmha_bwd_args* args, void* workspace,
                                size_t workspace_bytes, void* stream);
 
@@ -180,7 +194,10 @@ typedef struct fmha_bwd_plan_info {
   int64_t workspace_bytes; /* == fmha_bwd_workspace_size */
   int64_t pairs;           /* allowed (query, key) pairs summed over heads and segments */
   double flops;            /* 2*(3*d_qk + 2*d_v) * pairs: the five contractions */
-  int64_t acc_rows;        /* accumulator rows per head and split (see below) */
+  int64_t acc_rows;        /* accumulator rows per head and split, or per segment and head in
+                              bf16 mode (see below) */
+  int32_t dq_acc_elem_bytes; /* 4 (fp32 accumulator) or 2 (bf16) */
+  int32_t reserved;
 } fmha_bwd_plan_info;
 /* Accumulator layout.  Atomic mode: one split, rows_q rows, row-major ([row][d_qk]), row of
    a query = its D/LSE row.  Deterministic mode: split s holds the sum of the partials of key
@@ -190,7 +207,12 @@ typedef struct fmha_bwd_plan_info {
    b*tile_m, so blocks of different segments never share rows.  Inside a block the values
    are grouped in 32x32 tiles, tile t = (r/32)*(d_qk/32) + c/32 at offset 1024*t, and tile
    element (r, c) (r, c < 32) at 16*(c + 32*((r/4)%2)) + 4*(r/8) + r%4: the result layout of
-   a 32x32 matrix-core product, stored lane by lane. */
+   a 32x32 matrix-core product, stored lane by lane.  bf16 mode (dq_acc_dtype =
+   FMHA_DQ_ACC_BF16): bf16 [B][Hq][acc_rows][d_qk], acc_rows = the longest segment's query
+   count rounded up to a multiple of 16, and query i of segment b at row i of slot (b, h):
+   the slot is indexed by the logical position, so neither the physical (padded) layout of
+   the tensors nor other segments' rows can move it.  The unscaled sum dS K is accumulated
+   there; the reduction multiplies by scale and rounds to bf16 into dq. */
 
 FMHA_BWD_API int fmha_bwd_plan_query(const fmha_bwd_args* args, fmha_bwd_plan_info* info);
 

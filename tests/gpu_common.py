@@ -50,7 +50,8 @@ def to_dev_f32(a):
     return torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
 
 
-def run_gpu(x, o, lse, *, scale, mask, window=(-1, -1), sq=None, sk=None, deterministic=True):
+def run_gpu(x, o, lse, *, scale, mask, window=(-1, -1), sq=None, sk=None, deterministic=True,
+            dq_acc_dtype="fp32"):
     """Round O to bf16 and LSE to fp32 as the forward would store them, run the library."""
     import torch
     import attention_backward_fmha_amd as F
@@ -64,7 +65,7 @@ def run_gpu(x, o, lse, *, scale, mask, window=(-1, -1), sq=None, sk=None, determ
                   cu_seqlens_q_host=np.asarray(sq, np.int32),
                   cu_seqlens_k_host=np.asarray(sk, np.int32))
     dq, dk, dv = F.bwd(q, k, v, od, ld, do, scale=scale, mask_type=mask, window=window,
-                       deterministic=deterministic, **kw)
+                       deterministic=deterministic, dq_acc_dtype=dq_acc_dtype, **kw)
     torch.cuda.synchronize()
     return tuple(t.float().cpu().numpy().astype(np.float64) for t in (dq, dk, dv))
 

@@ -58,7 +58,8 @@ int main(void) {
   printf("{\\n");
   F(B) F(scale) F(deterministic) F(seqstart_q_host) F(seqstart_k_dev) F(q) F(lse) F(dv)
   F(q_stride) F(dv_stride) F(lse_stride) F(seqstart_q_padded_host) F(seqstart_k_padded_dev)
-  G(nsplits) G(rows_q) G(workspace_bytes) G(flops) G(acc_rows)
+  F(dq_acc_dtype)
+  G(nsplits) G(rows_q) G(workspace_bytes) G(flops) G(acc_rows) G(dq_acc_elem_bytes)
   printf("\\"size_args\\": %zu, \\"size_info\\": %zu}\\n", sizeof(fmha_bwd_args), sizeof(fmha_bwd_plan_info));
   return 0;
 }
@@ -75,7 +76,8 @@ int main(void) {
     for k, v in ref.items():
         if k.startswith("size"):
             continue
-        cls = _lib.PlanInfo if k in ("nsplits", "rows_q", "workspace_bytes", "flops", "acc_rows") else Args
+        cls = _lib.PlanInfo if k in ("nsplits", "rows_q", "workspace_bytes", "flops", "acc_rows",
+                                     "dq_acc_elem_bytes") else Args
         assert getattr(cls, k).offset == v, k
 
 
@@ -174,6 +176,30 @@ def test_forward_argument_errors():
     assert L.fmha_fwd_run(ctypes.byref(a), None) == _lib.ERR_UNSUPPORTED
 
 
+def test_bf16_accumulator_plan():
+    """bf16 accumulation: one zeroed bf16 slot of pad16(longest segment) rows per (segment,
+    head), indexed by logical position, whatever the physical layout."""
+    a = batch_args(deterministic=0)
+    a.dq_acc_dtype = _lib.DQ_ACC_BF16
+    info = _lib.plan_query(a)
+    assert _lib.workspace_size(a) == info.workspace_bytes
+    assert (info.nsplits, info.needs_zero, info.dq_acc_elem_bytes) == (1, 1, 2)
+    assert info.acc_rows == 208  # Sq = 200 rounded up to 16
+    assert info.dq_acc_bytes == 2 * 4 * 208 * 128 * 2
+    lens = [103, 77, 61]
+    g = group_args(lens, lens, deterministic=0)
+    g.dq_acc_dtype = _lib.DQ_ACC_BF16
+    pq = np.array([0, 112, 192, 256], np.int32)
+    g.seqstart_q_padded_host = pq.ctypes.data
+    g.seqstart_q_padded_dev = FAKE
+    g._keep2 = pq
+    info = _lib.plan_query(g)
+    assert info.rows_q == 256 and info.acc_rows == 112  # 103 -> 112
+    assert info.dq_acc_bytes == 3 * 4 * 112 * 128 * 2
+    assert info.dq_acc_offset + info.dq_acc_bytes <= info.workspace_bytes
+    assert _lib.plan_query(batch_args(deterministic=0)).dq_acc_elem_bytes == 4
+
+
 def test_tiles_per_item_keeps_two_items_per_cu():
     """Deterministic work items take 4 key tiles when that leaves >= 512 items, else 2, else 1;
     the split count follows."""
@@ -249,6 +275,9 @@ def test_flop_count_matches_pair_count():
     (lambda a: setattr(a, "q", FAKE + 8), _lib.ERR_UNSUPPORTED),
     (lambda a: a.q_stride.__setitem__(1, 4 * 128 + 4), _lib.ERR_UNSUPPORTED),
     (lambda a: setattr(a, "deterministic", 2), _lib.ERR_INVALID_ARG),
+    (lambda a: setattr(a, "dq_acc_dtype", 1), _lib.ERR_INVALID_ARG),  # bf16 needs atomic mode
+    (lambda a: setattr(a, "dq_acc_dtype", 2), _lib.ERR_INVALID_ARG),
+    (lambda a: setattr(a, "reserved", 1), _lib.ERR_INVALID_ARG),
     (lambda a: setattr(a, "B", -1), _lib.ERR_INVALID_ARG),
     (lambda a: setattr(a, "seqstart_k_host", FAKE), _lib.ERR_INVALID_ARG),  # half group mode
 ])

@@ -23,7 +23,7 @@ def _scatter(compact, starts, slots, lens, fill):
     return out
 
 
-def _run(lens_q, lens_k, slots_q, slots_k, *, mask, hq, hkv, d, deterministic, seed):
+def _run(lens_q, lens_k, slots_q, slots_k, *, mask, hq, hkv, d, deterministic, seed, dq_acc_dtype="fp32"):
     import torch
     import attention_backward_fmha_amd as F
     sq, sk = seq_offsets(lens_q), seq_offsets(lens_k)
@@ -54,7 +54,8 @@ def _run(lens_q, lens_k, slots_q, slots_k, *, mask, hq, hkv, d, deterministic, s
                        cu_seqlens_q_host=sq, cu_seqlens_k_host=sk,
                        cu_seqlens_q_padded=torch.from_numpy(pq).cuda(),
                        cu_seqlens_k_padded=torch.from_numpy(pk).cuda(),
-                       cu_seqlens_q_padded_host=pq, cu_seqlens_k_padded_host=pk, out=tuple(outs))
+                       cu_seqlens_q_padded_host=pq, cu_seqlens_k_padded_host=pk, out=tuple(outs),
+                       dq_acc_dtype=dq_acc_dtype)
     torch.cuda.synchronize()
     bits = [t.view(torch.int16).cpu().numpy().view(np.uint16) for t in (dq, dk, dv)]
     got = [t.float().cpu().numpy().astype(np.float64) for t in (dq, dk, dv)]
@@ -90,3 +91,13 @@ def test_padded_thd_cross_lengths_no_mask():
     lens_q, lens_k = [50, 0, 30], [70, 5, 20]
     slots_q, slots_k = [0, 64, 80, 144], [0, 80, 96, 128]
     _run(lens_q, lens_k, slots_q, slots_k, mask=0, hq=2, hkv=1, d=64, deterministic=True, seed=5103)
+
+
+def test_padded_thd_pad16_causal_bf16_accumulator():
+    """The bf16 (atomic16) accumulator on the padded layout of the pages' fix: 103/77/61 tokens
+    in 112/80/64-row slots; its slots are indexed by logical position, so the tensors' padding
+    cannot move them."""
+    lens = [103, 77, 61]
+    slots = [0, 112, 192, 256]
+    _run(lens, lens, slots, slots, mask=1, hq=4, hkv=2, d=128, deterministic=False, seed=5101,
+         dq_acc_dtype="bf16")
