@@ -1,6 +1,6 @@
 """Summaries of rocprofv3 CSV output (``-f csv``) for the files kept under ``profiles/``.
 
-    python -m attention_backward_fmha_amd.rocprof_summary stats DIR
+    python -m attention_backward_fmha_amd.rocprof_summary stats DIR [--match TEXT] [--top N]
         per-kernel calls / total / average duration from DIR/*kernel_stats.csv
     python -m attention_backward_fmha_amd.rocprof_summary traffic --kernel NAME \\
         --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR --copy-mib N
@@ -48,6 +48,7 @@ def main(argv=None):
     s = sub.add_parser("stats")
     s.add_argument("dir")
     s.add_argument("--top", type=int, default=12)
+    s.add_argument("--match", default="", help="only kernels whose name contains this")
     t = sub.add_parser("traffic")
     t.add_argument("--kernel", required=True)
     t.add_argument("--fetch", required=True)
@@ -60,7 +61,8 @@ def main(argv=None):
     if a.cmd == "stats":
         print("| kernel | calls | total ms | average us | % |")
         print("|---|---:|---:|---:|---:|")
-        for name, calls, tot, avg, pct in kernel_stats(a.dir)[: a.top]:
+        rows = [r for r in kernel_stats(a.dir) if a.match in r[0]]
+        for name, calls, tot, avg, pct in rows[: a.top]:
             print("| %s | %d | %.3f | %.1f | %.1f |" % (name[:90], calls, tot / 1e6, avg / 1e3, pct))
     else:
         nbytes = a.copy_mib * (1 << 20)
