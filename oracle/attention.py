@@ -20,6 +20,13 @@ to rounding order).
   diagonal, i.e. every segment of a packed batch is an independent attention problem.
 * Grouped-query attention -- same page, Tests: query heads share K/V heads in contiguous
   groups of Hq / Hkv (reading: head h uses K/V head h // (Hq // Hkv)).
+* Additive bias -- "Update AITER subcommit and refactor internal AITER/CK FA API usage"
+  (TransformerEngine PR 446), review threads on the bias strides: a bias of shape
+  (bias_b, bias_h, Sq, Sk) with bias_b in {1, B} and bias_h in {1, H} (the shapes 11SS,
+  1HSS, B1SS, BHSS; broadcast dimensions have stride 0), batch mode only; its gradient dbias
+  has the shape of the bias and is the full (B, H, Sq, Sk) gradient summed over the
+  broadcast dimensions.  Reading: the bias is added to the scaled logits before the mask
+  and the softmax, so dbias = dS.
 * Deterministic dQ accumulation -- "[CK_TILE] FMHA BWD Use Persistent Kernels in
   Deterministic Mode" (aiter PR 2216), Motivation and commit messages: dQ is accumulated as
   fp32 partials in an nsplits-deep workspace and converted back afterwards.  The order of
@@ -27,7 +34,7 @@ to rounding order).
 
 For every (segment, query head h, K/V head g) with lengths Lq, Lk:
 
-    S   = scale * Q_h K_g^T                                  (Lq x Lk)
+    S   = scale * Q_h K_g^T (+ bias[b, h])                   (Lq x Lk)
     LSE = log sum_{allowed j} exp(S_ij)       (-inf for a row with no allowed key)
     P   = exp(S - LSE) on allowed entries, 0 elsewhere
     O   = P V_g
@@ -35,6 +42,7 @@ For every (segment, query head h, K/V head g) with lengths Lq, Lk:
     dP  = dO V_g^T
     dS  = P * (dP - D 1^T)
     dQ_h = scale * dS K_g,   dK_g += scale * dS^T Q_h,   dV_g += P^T dO_h
+    dbias[b, h] += dS   (summed over broadcast batch / head dimensions)
 
 Layouts: batch mode arrays are [B, S, H, d] and LSE is [B, Hq, Sq]; group (THD) mode arrays
 are [T, H, d] with ``seqstart`` offsets of length B+1 and LSE is [Hq, T].
@@ -114,6 +122,23 @@ def _segments(batch_mode, shape_q, shape_k, seqstart_q, seqstart_k):
                 int(seqstart_k[b]), int(seqstart_k[b + 1]))
 
 
+def _bias_plane(bias, b, h):
+    """The (Sq, Sk) plane of a (bias_b, bias_h, Sq, Sk) bias that batch b, head h reads."""
+    return bias[b if bias.shape[0] > 1 else 0, h if bias.shape[1] > 1 else 0]
+
+
+def _check_bias(bias, batch_mode, B, hq, sq, sk):
+    if bias is None:
+        return None
+    if not batch_mode:
+        raise ValueError("a bias needs batch mode")
+    bias = np.asarray(bias, np.float64)
+    if bias.ndim != 4 or bias.shape[0] not in (1, B) or bias.shape[1] not in (1, hq) or \
+            bias.shape[2:] != (sq, sk):
+        raise ValueError("bias must have shape (1|B, 1|Hq, Sq, Sk)")
+    return bias
+
+
 def _check_heads(hq, hkv):
     if hkv <= 0 or hq % hkv != 0:
         raise ValueError("Hq must be a positive multiple of Hkv")
@@ -121,15 +146,17 @@ def _check_heads(hq, hkv):
 
 
 def forward(q, k, v, *, scale, mask_type=MASK_NONE, window_left=-1, window_right=-1,
-            seqstart_q=None, seqstart_k=None):
+            seqstart_q=None, seqstart_k=None, bias=None):
     """Softmax attention forward in fp64.  Returns (O, LSE) in the layouts of the module
-    docstring."""
+    docstring.  ``bias`` (batch mode): (1|B, 1|Hq, Sq, Sk), added to the scaled logits."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
     batch_mode = seqstart_q is None
     hq, hkv = q.shape[-2], k.shape[-2]
     group = _check_heads(hq, hkv)
+    bias = _check_bias(bias, batch_mode, q.shape[0], hq, q.shape[1], k.shape[1]) if batch_mode \
+        else _check_bias(bias, False, 0, hq, 0, 0)
     o = np.zeros(q.shape[:-1] + (v.shape[-1],), np.float64)
     if batch_mode:
         lse = np.full((q.shape[0], hq, q.shape[1]), -np.inf)
@@ -144,6 +171,8 @@ def forward(q, k, v, *, scale, mask_type=MASK_NONE, window_left=-1, window_right
                 r1 = min(lq, r0 + _ROW_BLOCK)
                 ok = allowed(mask_type, window_left, window_right, lq, lk, rows=np.arange(r0, r1))
                 s = scale * (qb[r0:r1, h, :] @ kb[:, g, :].T)
+                if bias is not None:
+                    s = s + _bias_plane(bias, b, h)[r0:r1]
                 p, l = _softmax_rows(s, ok)
                 ob = p @ vb[:, g, :]
                 if batch_mode:
@@ -156,11 +185,12 @@ def forward(q, k, v, *, scale, mask_type=MASK_NONE, window_left=-1, window_right
 
 
 def backward(q, k, v, do, *, scale, mask_type=MASK_NONE, window_left=-1, window_right=-1,
-             seqstart_q=None, seqstart_k=None):
-    """Exact gradient of O = softmax(scale Q K^T + mask) V in direction dO, fp64.
+             seqstart_q=None, seqstart_k=None, bias=None):
+    """Exact gradient of O = softmax(scale Q K^T + bias + mask) V in direction dO, fp64.
 
-    Returns (dQ, dK, dV) shaped like (Q, K, V).  O, LSE and D are recomputed here from
-    Q, K, V, so the result is the gradient of the exact forward."""
+    Returns (dQ, dK, dV) shaped like (Q, K, V), and dbias (shaped like the bias) as a fourth
+    element when a bias is given.  O, LSE and D are recomputed here from Q, K, V, so the
+    result is the gradient of the exact forward."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
@@ -168,6 +198,9 @@ def backward(q, k, v, do, *, scale, mask_type=MASK_NONE, window_left=-1, window_
     batch_mode = seqstart_q is None
     hq, hkv = q.shape[-2], k.shape[-2]
     group = _check_heads(hq, hkv)
+    bias = _check_bias(bias, batch_mode, q.shape[0], hq, q.shape[1], k.shape[1]) if batch_mode \
+        else _check_bias(bias, False, 0, hq, 0, 0)
+    dbias = None if bias is None else np.zeros_like(bias)
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
@@ -185,17 +218,23 @@ def backward(q, k, v, do, *, scale, mask_type=MASK_NONE, window_left=-1, window_
                 qh = qb[r0:r1, h, :]
                 doh = dob[r0:r1, h, :]
                 s = scale * (qh @ kb[:, g, :].T)
+                if bias is not None:
+                    s = s + _bias_plane(bias, b, h)[r0:r1]
                 p, _ = _softmax_rows(s, ok)
                 o = p @ vb[:, g, :]
                 d = (doh * o).sum(axis=1)
                 dp = doh @ vb[:, g, :].T
                 ds = p * (dp - d[:, None])
+                if dbias is not None:
+                    _bias_plane(dbias, b, h)[r0:r1] += ds
                 dqb[r0:r1, h, :] = scale * (ds @ kb[:, g, :])
                 dkb[:, g, :] += scale * (ds.T @ qh)
                 dvb[:, g, :] += p.T @ doh
         dq[qs] = dqb
         dk[ks] = dkb
         dv[ks] = dvb
+    if dbias is not None:
+        return dq, dk, dv, dbias
     return dq, dk, dv
 
 
