@@ -11,6 +11,8 @@ THD adds ``cu_seqlens_q_padded``/``cu_seqlens_k_padded``: segment b's rows start
 row padded[b] and the rest of its slot (up to padded[b+1]) is padding, left untouched.
 ``dq_acc_dtype="bf16"`` (with ``deterministic=False``) accumulates dQ with packed bf16 atomic
 adds instead of fp32 ones: about half the atomic traffic, less accurate dQ.
+``bias`` (batch mode): a bf16 [1|B, 1|Hq, Sq, Sk] tensor added to the scaled logits;
+``bwd(..., bias=bias, bias_grad=True)`` also returns dbias, shaped like the bias.
 """
 
 import numpy as np
@@ -67,7 +69,8 @@ def make_call(q, k, v, o, lse, do, dq, dk, dv, *, scale=None, mask_type=MASK_NON
               window=(-1, -1), deterministic=True, cu_seqlens_q=None, cu_seqlens_k=None,
               cu_seqlens_q_host=None, cu_seqlens_k_host=None, max_seqlen_q=None,
               max_seqlen_k=None, cu_seqlens_q_padded=None, cu_seqlens_k_padded=None,
-              cu_seqlens_q_padded_host=None, cu_seqlens_k_padded_host=None, dq_acc_dtype="fp32"):
+              cu_seqlens_q_padded_host=None, cu_seqlens_k_padded_host=None, dq_acc_dtype="fp32",
+              bias=None, dbias=None):
     """Fill the C argument struct from tensors (no device work)."""
     group = cu_seqlens_q is not None
     d_qk = q.shape[-1]
@@ -118,6 +121,21 @@ def make_call(q, k, v, o, lse, do, dq, dk, dv, *, scale=None, mask_type=MASK_NON
     if dq_acc_dtype not in ("fp32", "bf16"):
         raise ValueError("dq_acc_dtype must be 'fp32' or 'bf16'")
     a.dq_acc_dtype = DQ_ACC_BF16 if dq_acc_dtype == "bf16" else DQ_ACC_FP32
+    if bias is not None:
+        if bias.dim() != 4 or bias.stride(-1) != 1:
+            raise ValueError("bias must be [1|B, 1|Hq, Sq, Sk] with contiguous columns")
+        keep.append(bias)
+        a.bias = bias.data_ptr()
+        a.bias_b, a.bias_h = bias.shape[0], bias.shape[1]
+        for i in range(3):
+            a.bias_stride[i] = bias.stride(i)
+    if dbias is not None:
+        if bias is None or dbias.shape != bias.shape or dbias.stride(-1) != 1:
+            raise ValueError("dbias must have the bias's shape, with contiguous columns")
+        keep.append(dbias)
+        a.dbias = dbias.data_ptr()
+        for i in range(3):
+            a.dbias_stride[i] = dbias.stride(i)
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", do), ("lse", lse),
                     ("dq", dq), ("dk", dk), ("dv", dv)):
         setattr(a, name, _ptr(t))
@@ -133,8 +151,9 @@ def bwd(q, k, v, o, lse, do, *, scale=None, mask_type=MASK_NONE, window=(-1, -1)
         deterministic=True, cu_seqlens_q=None, cu_seqlens_k=None, cu_seqlens_q_host=None,
         cu_seqlens_k_host=None, max_seqlen_q=None, max_seqlen_k=None, cu_seqlens_q_padded=None,
         cu_seqlens_k_padded=None, cu_seqlens_q_padded_host=None, cu_seqlens_k_padded_host=None,
-        workspace=None, out=None, dq_acc_dtype="fp32"):
-    """Gradients (dq, dk, dv) of softmax attention; see the module docstring for layouts."""
+        workspace=None, out=None, dq_acc_dtype="fp32", bias=None, bias_grad=False):
+    """Gradients (dq, dk, dv) of softmax attention, and dbias when ``bias_grad``; see the
+    module docstring for layouts."""
     import torch
 
     for t in (q, k, v, o, do):
@@ -148,6 +167,11 @@ def bwd(q, k, v, o, lse, do, *, scale=None, mask_type=MASK_NONE, window=(-1, -1)
         dq = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
         dk = torch.empty(k.shape, dtype=torch.bfloat16, device=k.device)
         dv = torch.empty(v.shape, dtype=torch.bfloat16, device=v.device)
+    dbias = None
+    if bias_grad:
+        if bias is None:
+            raise ValueError("bias_grad needs a bias")
+        dbias = torch.empty(bias.shape, dtype=torch.bfloat16, device=bias.device)
     call = make_call(q, k, v, o, lse, do, dq, dk, dv, scale=scale, mask_type=mask_type,
                      window=window, deterministic=deterministic, cu_seqlens_q=cu_seqlens_q,
                      cu_seqlens_k=cu_seqlens_k, cu_seqlens_q_host=cu_seqlens_q_host,
@@ -155,20 +179,23 @@ def bwd(q, k, v, o, lse, do, *, scale=None, mask_type=MASK_NONE, window=(-1, -1)
                      max_seqlen_k=max_seqlen_k, cu_seqlens_q_padded=cu_seqlens_q_padded,
                      cu_seqlens_k_padded=cu_seqlens_k_padded,
                      cu_seqlens_q_padded_host=cu_seqlens_q_padded_host,
-                     cu_seqlens_k_padded_host=cu_seqlens_k_padded_host, dq_acc_dtype=dq_acc_dtype)
+                     cu_seqlens_k_padded_host=cu_seqlens_k_padded_host, dq_acc_dtype=dq_acc_dtype,
+                     bias=bias, dbias=dbias)
     nbytes = call.workspace_size()
     if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     call.prepare(workspace, stream)
     call.run(workspace, stream)
+    if bias_grad:
+        return dq, dk, dv, dbias
     return dq, dk, dv
 
 
 def fwd(q, k, v, *, scale=None, mask_type=MASK_NONE, window=(-1, -1), cu_seqlens_q=None,
         cu_seqlens_k=None, cu_seqlens_q_host=None, cu_seqlens_k_host=None, max_seqlen_q=None,
         max_seqlen_k=None, cu_seqlens_q_padded=None, cu_seqlens_k_padded=None,
-        cu_seqlens_q_padded_host=None, cu_seqlens_k_padded_host=None):
+        cu_seqlens_q_padded_host=None, cu_seqlens_k_padded_host=None, bias=None):
     """Forward (o, lse) on the device, in the layouts ``bwd`` takes: o like q with d_v columns,
     lse [B, Hq, Sq] (batch) or [Hq, T] (group)."""
     import torch
@@ -187,6 +214,6 @@ def fwd(q, k, v, *, scale=None, mask_type=MASK_NONE, window=(-1, -1), cu_seqlens
                      max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k,
                      cu_seqlens_q_padded=cu_seqlens_q_padded, cu_seqlens_k_padded=cu_seqlens_k_padded,
                      cu_seqlens_q_padded_host=cu_seqlens_q_padded_host,
-                     cu_seqlens_k_padded_host=cu_seqlens_k_padded_host)
+                     cu_seqlens_k_padded_host=cu_seqlens_k_padded_host, bias=bias)
     _lib.fwd_run(call.args, torch.cuda.current_stream(q.device).cuda_stream)
     return o, lse

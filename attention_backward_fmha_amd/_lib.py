@@ -6,7 +6,7 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libfmha_bwd.so")
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 MASK_NONE = 0
 MASK_CAUSAL_TOP_LEFT = 1
@@ -84,6 +84,12 @@ class Args(ctypes.Structure):
         ("seqstart_k_padded_dev", ctypes.c_void_p),
         ("dq_acc_dtype", ctypes.c_int32),
         ("reserved", ctypes.c_int32),
+        ("bias", ctypes.c_void_p),
+        ("dbias", ctypes.c_void_p),
+        ("bias_stride", _i64x3),
+        ("dbias_stride", _i64x3),
+        ("bias_b", ctypes.c_int32),
+        ("bias_h", ctypes.c_int32),
     ]
 
     def __init__(self, **kw):
@@ -117,6 +123,8 @@ class PlanInfo(ctypes.Structure):
         ("acc_rows", ctypes.c_int64),
         ("dq_acc_elem_bytes", ctypes.c_int32),
         ("reserved", ctypes.c_int32),
+        ("dbias_acc_offset", ctypes.c_int64),
+        ("dbias_acc_bytes", ctypes.c_int64),
     ]
 
     def as_dict(self):

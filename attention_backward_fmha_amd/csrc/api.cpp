@@ -94,6 +94,21 @@ fmha::KParams make_params(const fmha_bwd_args* a, const fmha::Plan& p, void* ws)
   k.n_q_blocks = p.n_q_blocks;
   k.scale = a->scale;
   k.scale_log2 = a->scale * 1.4426950408889634f;
+  k.tile_m = p.tile_m;
+  if (p.has_bias) {
+    k.bias = (const uint16_t*)a->bias;
+    k.bias_s[0] = p.bias_b == 1 ? 0 : a->bias_stride[0];
+    k.bias_s[1] = p.bias_h == 1 ? 0 : a->bias_stride[1];
+    k.bias_s[2] = a->bias_stride[2];
+    k.bias_plane_bytes = p.bias_plane_bytes;
+    k.bias_b = p.bias_b;
+    k.bias_h = p.bias_h;
+  }
+  if (p.has_dbias) {
+    if (ws != nullptr) k.dbias_acc = (float*)((char*)ws + p.dbias_acc_offset);
+    k.dbias = (uint16_t*)a->dbias;
+    for (int i = 0; i < 3; ++i) k.dbias_s[i] = a->dbias_stride[i];
+  }
   return k;
 }
 
@@ -161,6 +176,10 @@ int fmha_bwd_run_stages(const fmha_bwd_args* args, void* ws, size_t bytes, int s
   if (stages & FMHA_STAGE_REDUCE) {
     st = hip_status(fmha::launch_reduce(p, kp, s), "run: reduce stage");
     if (st != FMHA_OK) return st;
+    if (p.has_dbias) {
+      st = hip_status(fmha::launch_dbias(p, kp, s), "run: dbias reduce");
+      if (st != FMHA_OK) return st;
+    }
   }
   return FMHA_OK;
 }
@@ -207,6 +226,8 @@ int fmha_bwd_plan_query(const fmha_bwd_args* args, fmha_bwd_plan_info* info) {
   info->rows_q = p.rows_q;
   info->acc_rows = p.acc_rows;
   info->dq_acc_elem_bytes = p.dq_bf16 ? 2 : 4;
+  info->dbias_acc_offset = p.dbias_acc_offset;
+  info->dbias_acc_bytes = p.dbias_acc_bytes;
   info->d_offset = p.d_offset;
   info->dq_acc_offset = p.dq_acc_offset;
   info->dq_acc_bytes = p.dq_acc_bytes;

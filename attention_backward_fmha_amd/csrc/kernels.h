@@ -42,12 +42,23 @@ struct KParams {
   int tiles_per_item;    // key tiles per main-kernel work item (deterministic mode: one split each)
   float scale;
   float scale_log2;  // scale * log2(e)
+  int tile_m;        // query rows per main-kernel block
+  // additive bias (batch mode): plane (b, h) at bias + b*bias_s[0] + h*bias_s[1] (strides of
+  // broadcast dimensions are 0), row stride bias_s[2]
+  const uint16_t* bias;
+  int64_t bias_s[3];
+  uint32_t bias_plane_bytes;
+  int bias_b, bias_h;
+  float* dbias_acc;  // workspace: full-shape dS, fp32 [B][Hq][Sq][Sk]; null without dbias
+  uint16_t* dbias;   // output, [bias_b][bias_h][Sq][Sk] with strides dbias_s
+  int64_t dbias_s[3];
 };
 
 hipError_t launch_dot(const Plan& plan, const KParams& kp, hipStream_t stream);
 hipError_t launch_fwd(const Plan& plan, const KParams& kp, hipStream_t stream);
 hipError_t launch_main(const Plan& plan, const KParams& kp, hipStream_t stream);
 hipError_t launch_reduce(const Plan& plan, const KParams& kp, hipStream_t stream);
+hipError_t launch_dbias(const Plan& plan, const KParams& kp, hipStream_t stream);
 hipError_t launch_zero(float* ptr, int64_t count, hipStream_t stream);
 
 }  // namespace fmha

@@ -301,8 +301,10 @@ __device__ __forceinline__ void stage_block(uint16_t* rm, uint16_t* tr, int RS,
   }
 }
 
-// DQM: 0 = fp32 atomic adds, 1 = deterministic fp32 splits, 2 = packed bf16 atomic adds
-template <int DQK, int DV, int TM_, int DQM>
+// DQM: 0 = fp32 atomic adds, 1 = deterministic fp32 splits, 2 = packed bf16 atomic adds.
+// BIAS: an additive bias joins the logits (and dS goes to the full-shape dbias scratch when
+// that is requested).
+template <int DQK, int DV, int TM_, int DQM, bool BIAS>
 __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
   constexpr bool DET = DQM == 1;
   using T = MainTile<DQK, DV, TM_>;
@@ -481,7 +483,28 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
   // The arithmetic of one step between its two barriers: S, dP, then per 32-query tile P, dS,
   // the dV/dK products and the dS tile to LDS (so the exponentials of one tile can overlap
   // the products of the other).
-  auto compute_step = [&](int q0) {
+  auto compute_step = [&](int q0, int hq) {
+    // bias of the lane's (query, key) pairs, issued before the products that hide its latency;
+    // register 16m + r pairs with the S/dP result register r of row tile m.  Rows past the
+    // plane are outside the resource (zeros); keys past the tile end are masked below.
+    float bv[BIAS ? MT * 16 : 1];
+    if constexpr (BIAS) {
+      const __amdgpu_buffer_rsrc_t rb =
+          buffer_rsrc(p.bias + (int64_t)b * p.bias_s[0] + (int64_t)hq * p.bias_s[1], p.bias_plane_bytes);
+      const int bs2 = (int)p.bias_s[2];
+      const int col = (int)key0 + key_l;
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = q0 + 32 * m + 8 * (r >> 2) + 4 * hi + (r & 3);
+          const unsigned short x = __builtin_amdgcn_raw_buffer_load_b16(rb, (row * bs2 + col) * 2, 0, 0);
+          bv[16 * m + r] = __uint_as_float((unsigned)x << 16);
+        }
+    }
+    const __amdgpu_buffer_rsrc_t rdb = buffer_rsrc(
+        BIAS && p.dbias_acc != nullptr ? p.dbias_acc + ((int64_t)b * p.Hq + hq) * p.Sq * p.Sk : nullptr,
+        BIAS && p.dbias_acc != nullptr ? (uint32_t)p.Sq * (uint32_t)p.Sk * 4u : 0u);
     f32x16 s_acc[MT];
     f32x16 dp_acc[MT];
 #pragma unroll
@@ -521,12 +544,23 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * c + e;
-          float pv = __builtin_amdgcn_exp2f(s_acc[m][r] * p.scale_log2 - l4[e]);
+          float xl = s_acc[m][r] * p.scale_log2 - l4[e];
+          if constexpr (BIAS) xl = __builtin_fmaf(bv[16 * m + r], kLog2e, xl);
+          float pv = __builtin_amdgcn_exp2f(xl);
           pv = (unsigned)(t0 - (32 * m + 8 * c + e)) <= span ? pv : 0.f;
           const float dsv = pv * (dp_acc[m][r] - d4[e]);
           pa[c >> 1][(c & 1) * 4 + e] = (__bf16)pv;
           sa[c >> 1][(c & 1) * 4 + e] = (__bf16)dsv;
           ds32[r] = dsv;
+          if constexpr (BIAS) {
+            // full-shape dS for dbias: every (row, key) of the block, masked pairs as 0; rows
+            // past the plane are dropped by the range check, keys past the tile end skipped
+            if (p.dbias_acc != nullptr && key_ok)
+              __builtin_amdgcn_raw_buffer_store_b32(
+                  __float_as_uint(dsv), rdb,
+                  ((unsigned)(q0 + 32 * m + 8 * c + 4 * hi + e) * (unsigned)p.Sk + (unsigned)(key0 + key_l)) * 4u,
+                  0, 0);
+          }
         }
       }
       // ---- dV += P^T dO_i ; dK += dS^T Q_i over this tile's queries ----
@@ -579,7 +613,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
     const __amdgpu_buffer_rsrc_t r16 =
         buffer_rsrc((const uint16_t*)p.dq_acc + (int64_t)b * p.split_stride + (int64_t)h * p.head_stride +
                         q0 * DQK, (uint32_t)nq * DQK * 2u);
-    compute_step((int)q0);
+    compute_step((int)q0, h);
     if (DET) {  // issued late: the S/dP accumulators are dead by now
       const int64_t qbn = q0 / TM;
       const __amdgpu_buffer_rsrc_t rprev =
@@ -863,6 +897,44 @@ __global__ __launch_bounds__(256) void k_dq_reduce(const KParams p) {
 }
 
 // ------------------------------------------------------------------------------------------
+// dbias = the full-shape dS summed over the bias's broadcast dimensions (ascending batch, then
+// head, fp32), rounded to bf16.  One work group per (query row, output plane, 1024 columns),
+// four columns per thread.  A (row, key) pair lies in a (query block, key tile) pair the main
+// kernel skipped (no allowed pair there) exactly when qblocks_for_tile excludes the row's
+// block; such entries were never written and count as 0, so the scratch needs no zeroing.
+// ------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_dbias_reduce(const KParams p) {
+  const int nchunk = (p.Sk + 1023) / 1024;
+  const int i = (int)blockIdx.x / nchunk;     // query row
+  const int chunk = (int)blockIdx.x - i * nchunk;
+  const int oh = blockIdx.y;                  // output head index (0 when broadcast)
+  const int ob = blockIdx.z;                  // output batch index
+  const int j0 = (chunk * 256 + (int)threadIdx.x) * 4;
+  if (j0 >= p.Sk) return;
+  const MaskGeom mg = mask_geom(p.mask_type, p.window_left, p.window_right, p.Sq, p.Sk);
+  int64_t lo, hi;
+  qblocks_for_tile(mg, p.Sq, p.Sk, j0 / 128, p.tile_m, 128, &lo, &hi);  // j0..j0+3: one tile
+  const int qb = i / p.tile_m;
+  const bool seen = qb >= lo && qb <= hi;
+  const int b0 = p.bias_b == 1 ? 0 : ob, b1 = p.bias_b == 1 ? p.B : ob + 1;
+  const int h0 = p.bias_h == 1 ? 0 : oh, h1 = p.bias_h == 1 ? p.Hq : oh + 1;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  if (seen) {
+    for (int bb = b0; bb < b1; ++bb)
+      for (int hh = h0; hh < h1; ++hh) {
+        const float* src = p.dbias_acc + (((int64_t)bb * p.Hq + hh) * p.Sq + i) * p.Sk + j0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (j0 + u < p.Sk) acc[u] += src[u];
+      }
+  }
+  uint16_t* dst = p.dbias + (int64_t)ob * p.dbias_s[0] + (int64_t)oh * p.dbias_s[1] + (int64_t)i * p.dbias_s[2] + j0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    if (j0 + u < p.Sk) dst[u] = to_bf16_bits(acc[u]);
+}
+
+// ------------------------------------------------------------------------------------------
 // Forward: O = softmax(scale * Q K^T + mask) V and LSE.  One work group per (block of 128
 // queries, query head, segment); wave w owns queries 32w .. 32w+31 of the block.
 //
@@ -886,7 +958,7 @@ struct FwdTile {
   static_assert(KBLK % 64 == 0, "staging blocks of K must fill whole waves");
 };
 
-template <int DQK, int DV>
+template <int DQK, int DV, bool BIAS>
 __global__ __launch_bounds__(256, DQK <= 128 ? 2 : 1) void k_fwd(const KParams p) {
   using T = FwdTile<DQK, DV>;
   constexpr int TQ = T::TQ, TK = T::TK, KS = T::KS, VS = T::VS;
@@ -1018,6 +1090,23 @@ __global__ __launch_bounds__(256, DQK <= 128 ? 2 : 1) void k_fwd(const KParams p
     __syncthreads();  // LDS holds tile it
     load_tile(it + 1 < ntiles, kt0 + TK);
 
+    // bias of this lane's query row for its keys of the tile, issued before the products
+    // (2-byte loads: the row stride may be any value >= Sk); rows past the plane read zeros,
+    // keys past the end are masked
+    float bz[BIAS ? 32 : 1];
+    if constexpr (BIAS) {
+      const __amdgpu_buffer_rsrc_t rb =
+          buffer_rsrc(p.bias + (int64_t)b * p.bias_s[0] + (int64_t)h * p.bias_s[1], p.bias_plane_bytes);
+      const int rowoff = row * (int)p.bias_s[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const unsigned short x = __builtin_amdgcn_raw_buffer_load_b16(
+              rb, (rowoff + (int)kt0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3)) * 2, 0, 0);
+          bz[16 * kb + r] = __uint_as_float((unsigned)x << 16);
+        }
+    }
     // S^T for the tile's two 32-key blocks: register r of block kb holds key
     // kt0 + 32kb + 8(r/4) + 4hi + r%4 of this lane's query
     f32x16 s[2];
@@ -1039,7 +1128,8 @@ __global__ __launch_bounds__(256, DQK <= 128 ? 2 : 1) void k_fwd(const KParams p
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int ko = 32 * kb + 8 * (r >> 2) + (r & 3);
-        const float x = s[kb][r] * p.scale_log2;
+        float x = s[kb][r] * p.scale_log2;
+        if constexpr (BIAS) x = __builtin_fmaf(bz[16 * kb + r], kLog2e, x);
         s[kb][r] = (unsigned)(t0 + ko) <= span ? x : -__builtin_inff();
         mt = fmaxf(mt, s[kb][r]);
       }
@@ -1128,23 +1218,34 @@ hipError_t launch_fwd(const Plan& plan, const KParams& kp, hipStream_t stream) {
   const int64_t rows = (int64_t)plan.n_q_blocks * plan.tile_m;  // >= the longest segment
   const dim3 grid((unsigned)((rows + 127) / 128), (unsigned)plan.Hq, (unsigned)plan.B);
   if (plan.d_qk == 64) {
-    hipLaunchKernelGGL((k_fwd<64, 64>), grid, dim3(256), 0, stream, kp);
+    if (plan.has_bias) hipLaunchKernelGGL((k_fwd<64, 64, true>), grid, dim3(256), 0, stream, kp);
+    else hipLaunchKernelGGL((k_fwd<64, 64, false>), grid, dim3(256), 0, stream, kp);
   } else if (plan.d_qk == 128) {
-    hipLaunchKernelGGL((k_fwd<128, 128>), grid, dim3(256), 0, stream, kp);
+    if (plan.has_bias) hipLaunchKernelGGL((k_fwd<128, 128, true>), grid, dim3(256), 0, stream, kp);
+    else hipLaunchKernelGGL((k_fwd<128, 128, false>), grid, dim3(256), 0, stream, kp);
   } else {
-    hipLaunchKernelGGL((k_fwd<192, 128>), grid, dim3(256), 0, stream, kp);
+    if (plan.has_bias) hipLaunchKernelGGL((k_fwd<192, 128, true>), grid, dim3(256), 0, stream, kp);
+    else hipLaunchKernelGGL((k_fwd<192, 128, false>), grid, dim3(256), 0, stream, kp);
   }
   return hipGetLastError();
 }
 
-template <int DQK, int DV, int TM>
+// WITH_BIAS = false for tile shapes the plan never uses with a bias (not compiled with one)
+template <int DQK, int DV, int TM, bool WITH_BIAS = true>
 static void launch_main_t(const Plan& plan, const KParams& kp, dim3 grid, hipStream_t stream) {
-  if (plan.deterministic) {
-    hipLaunchKernelGGL((k_bwd_main<DQK, DV, TM, 1>), grid, dim3(256), 0, stream, kp);
-  } else if (plan.dq_bf16) {
-    hipLaunchKernelGGL((k_bwd_main<DQK, DV, TM, 2>), grid, dim3(256), 0, stream, kp);
+  const int mode = plan.deterministic ? 1 : (plan.dq_bf16 ? 2 : 0);
+  if constexpr (!WITH_BIAS) {
+    if (mode == 1) hipLaunchKernelGGL((k_bwd_main<DQK, DV, TM, 1, false>), grid, dim3(256), 0, stream, kp);
+    else if (mode == 2) hipLaunchKernelGGL((k_bwd_main<DQK, DV, TM, 2, false>), grid, dim3(256), 0, stream, kp);
+    else hipLaunchKernelGGL((k_bwd_main<DQK, DV, TM, 0, false>), grid, dim3(256), 0, stream, kp);
+  } else if (plan.has_bias) {
+    if (mode == 1) hipLaunchKernelGGL((k_bwd_main<DQK, DV, TM, 1, true>), grid, dim3(256), 0, stream, kp);
+    else if (mode == 2) hipLaunchKernelGGL((k_bwd_main<DQK, DV, TM, 2, true>), grid, dim3(256), 0, stream, kp);
+    else hipLaunchKernelGGL((k_bwd_main<DQK, DV, TM, 0, true>), grid, dim3(256), 0, stream, kp);
   } else {
-    hipLaunchKernelGGL((k_bwd_main<DQK, DV, TM, 0>), grid, dim3(256), 0, stream, kp);
+    if (mode == 1) hipLaunchKernelGGL((k_bwd_main<DQK, DV, TM, 1, false>), grid, dim3(256), 0, stream, kp);
+    else if (mode == 2) hipLaunchKernelGGL((k_bwd_main<DQK, DV, TM, 2, false>), grid, dim3(256), 0, stream, kp);
+    else hipLaunchKernelGGL((k_bwd_main<DQK, DV, TM, 0, false>), grid, dim3(256), 0, stream, kp);
   }
 }
 
@@ -1159,7 +1260,7 @@ hipError_t launch_main(const Plan& plan, const KParams& kp, hipStream_t stream) 
     if (plan.tile_m == 32) {
       launch_main_t<128, 128, 32>(plan, kp, grid, stream);
     } else {
-      launch_main_t<128, 128, 64>(plan, kp, grid, stream);
+      launch_main_t<128, 128, 64, false>(plan, kp, grid, stream);  // bias: tile_m is 32
     }
   } else {
     launch_main_t<192, 128, 32>(plan, kp, grid, stream);
@@ -1187,6 +1288,14 @@ hipError_t launch_reduce(const Plan& plan, const KParams& kp, hipStream_t stream
   } else {
     launch_reduce_t<192, 32>(plan, kp, stream);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_dbias(const Plan& plan, const KParams& kp, hipStream_t stream) {
+  if (!plan.has_dbias || plan.B == 0 || plan.Sq == 0 || plan.Sk == 0) return hipSuccess;
+  const dim3 grid((unsigned)(((plan.Sk + 1023) / 1024) * (int64_t)plan.Sq), (unsigned)plan.bias_h,
+                  (unsigned)plan.bias_b);
+  hipLaunchKernelGGL(k_dbias_reduce, grid, dim3(256), 0, stream, kp);
   return hipGetLastError();
 }
 

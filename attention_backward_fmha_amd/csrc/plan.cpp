@@ -9,6 +9,7 @@
 //                                                 in matrix-core tile order, tile_m rows of
 //                                                 padding per segment; atomic: one split,
 //                                                 row-major, acc_rows = rows_q)
+//   dbias_acc fp32 [B][Hq][Sq][Sk]              full-shape dS when dbias is requested
 //           or bf16 [B][Hq][acc_rows][d_qk]       bf16 atomic mode: one slot of
 //                                                 acc_rows = pad16(longest lq) rows per
 //                                                 (segment, head), indexed by the logical
@@ -86,6 +87,8 @@ int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t el, bool forwar
     return fail(FMHA_ERR_INVALID_ARG, err, el,
                 "the bf16 dQ accumulator is for atomic (deterministic = 0) mode only");
   if (a->reserved != 0) return fail(FMHA_ERR_INVALID_ARG, err, el, "reserved must be 0");
+  if (a->dbias && !a->bias)
+    return fail(FMHA_ERR_INVALID_ARG, err, el, "dbias needs a bias");
 
   p->B = a->B;
   p->Hq = a->Hq;
@@ -100,6 +103,9 @@ int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t el, bool forwar
   if (const char* e = getenv("FMHA_BWD_TILE_M")) {  // tuning knob: 32 or 64 for d_qk = 128
     if (a->d_qk == 128 && (atoi(e) == 32 || atoi(e) == 64)) p->tile_m = atoi(e);
   }
+  // with a bias, d_qk = 128 takes 32-row blocks too: the bias registers of 64-row blocks do
+  // not fit beside the rest of the main kernel's registers
+  if (a->bias != nullptr && a->d_qk == 128) p->tile_m = 32;
   p->tile_n = 128;
   p->deterministic = a->deterministic == 1;
   p->dq_bf16 = a->dq_acc_dtype == FMHA_DQ_ACC_BF16;
@@ -178,6 +184,34 @@ int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t el, bool forwar
                   "k/v/dk/dv strides must be non-negative multiples of 8 elements (sequence stride < 2^24)");
   }
 
+  // additive bias (batch mode only)
+  p->has_bias = a->bias != nullptr;
+  p->has_dbias = !forward && a->dbias != nullptr;
+  p->bias_b = p->has_bias ? a->bias_b : 0;
+  p->bias_h = p->has_bias ? a->bias_h : 0;
+  p->bias_plane_bytes = 0;
+  if (p->has_bias) {
+    if (group) return fail(FMHA_ERR_UNSUPPORTED, err, el, "a bias needs batch mode");
+    if ((a->bias_b != 1 && a->bias_b != a->B) || (a->bias_h != 1 && a->bias_h != a->Hq))
+      return fail(FMHA_ERR_INVALID_ARG, err, el, "bias_b must be 1 or B and bias_h 1 or Hq");
+    const int64_t* bs = a->bias_stride;
+    if (((uintptr_t)a->bias & 1u) != 0 || bs[0] < 0 || bs[1] < 0 || bs[2] < a->Sk)
+      return fail(FMHA_ERR_UNSUPPORTED, err, el,
+                  "bias must be 2-byte aligned with non-negative strides and row stride >= Sk");
+    // row offsets inside a plane, including one block of rows past the end, stay below 2^31
+    if (((int64_t)a->Sq + 256) * bs[2] + a->Sk >= (int64_t(1) << 30))
+      return fail(FMHA_ERR_UNSUPPORTED, err, el, "bias plane too large ((Sq + 256) * row stride >= 2^30)");
+    p->bias_plane_bytes = (a->Sq > 0 && a->Sk > 0) ? (uint32_t)((((int64_t)a->Sq - 1) * bs[2] + a->Sk) * 2) : 0u;
+    if (p->has_dbias) {
+      const int64_t* ds = a->dbias_stride;
+      if (((uintptr_t)a->dbias & 1u) != 0 || ds[0] < 0 || ds[1] < 0 || ds[2] < a->Sk)
+        return fail(FMHA_ERR_UNSUPPORTED, err, el,
+                    "dbias must be 2-byte aligned with non-negative strides and row stride >= Sk");
+      if (((int64_t)a->Sq + 256) * a->Sk >= (int64_t(1) << 30))
+        return fail(FMHA_ERR_UNSUPPORTED, err, el, "dbias plane too large ((Sq + 256) * Sk >= 2^30)");
+    }
+  }
+
   p->n_kv_tiles = (int)((max_lk + p->tile_n - 1) / p->tile_n);
   p->n_q_blocks = (int)((max_lq + p->tile_m - 1) / p->tile_m);
   // Deterministic mode: one work item walks tiles_per_item consecutive key tiles and adds
@@ -215,7 +249,9 @@ int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t el, bool forwar
   p->dq_acc_offset = align_up(p->lse2_offset + p->d_bytes, 256);
   p->dq_acc_bytes = p->dq_bf16 ? (int64_t)p->B * p->split_stride * 2
                                : (int64_t)p->nsplits * p->split_stride * 4;
-  p->workspace_bytes = align_up(p->dq_acc_offset + p->dq_acc_bytes, 256);
+  p->dbias_acc_offset = align_up(p->dq_acc_offset + p->dq_acc_bytes, 256);
+  p->dbias_acc_bytes = p->has_dbias ? (int64_t)p->B * p->Hq * p->Sq * p->Sk * 4 : 0;
+  p->workspace_bytes = align_up(p->dbias_acc_offset + p->dbias_acc_bytes, 256);
   if (p->workspace_bytes == 0) p->workspace_bytes = 256;
   return FMHA_OK;
 }

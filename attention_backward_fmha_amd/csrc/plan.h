@@ -37,6 +37,10 @@ struct Plan {
   int64_t head_stride;   // elements between heads inside a split: acc_rows*d_qk
   int64_t workspace_bytes;
   int64_t max_rows_q;    // for the D stage grid: rows_q
+  bool has_bias, has_dbias;
+  int bias_b, bias_h;
+  uint32_t bias_plane_bytes;  // bytes of one (batch, head) bias plane the kernels may read
+  int64_t dbias_acc_offset, dbias_acc_bytes;  // fp32 [B][Hq][Sq][Sk] full-shape dS
 };
 
 // Validates `a` and fills `p`.  Returns FMHA_OK or a negative status; on failure `err`

@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define FMHA_BWD_ABI_VERSION 3u
+#define FMHA_BWD_ABI_VERSION 4u
 
 #if defined(__GNUC__)
 #define FMHA_BWD_API __attribute__((visibility("default")))
@@ -145,6 +145,24 @@ typedef struct fmha_bwd_args {
   const int32_t* seqstart_k_padded_dev;
   int32_t dq_acc_dtype;  /* enum fmha_dq_acc_dtype; FMHA_DQ_ACC_BF16 needs deterministic = 0 */
   int32_t reserved;      /* must be 0 */
+  /* Additive attention bias, batch mode only ("Update AITER subcommit and refactor internal
+     AITER/CK FA API usage", review threads on the bias and dbias strides).  The logits are
+     scale * q k^T + bias[b', h', i, j], b' = b if bias_b == B else 0, h' = h if bias_h == Hq
+     else 0 (the shapes 11SS, 1HSS, B1SS, BHSS), before the mask and the softmax;
+     fmha_fwd_run adds it as well, so its lse includes it.  Group mode with a bias is
+     FMHA_ERR_UNSUPPORTED. */
+  const void* bias;        /* bf16 [bias_b][bias_h][Sq][Sk], strides bias_stride (row stride
+                              >= Sk); NULL = none */
+  void* dbias;             /* bf16 gradient of bias, same shape, strides dbias_stride: the
+                              full [B][Hq][Sq][Sk] gradient (fp32 in the workspace) summed over
+                              the broadcast dimensions in ascending batch, then head order;
+                              every element is overwritten.  NULL = not computed (needs bias) */
+  int64_t bias_stride[3];  /* {batch, head, row} element strides; the column stride is 1; the
+                              batch stride is unused when bias_b == 1, the head stride when
+                              bias_h == 1 */
+  int64_t dbias_stride[3];
+  int32_t bias_b;          /* 1 or B (ignored without bias) */
+  int32_t bias_h;          /* 1 or Hq */
 } fmha_bwd_args;
 
 /* Workspace bytes that prepare/run need for these arguments.  Host only: no GPU call, no
@@ -198,6 +216,8 @@ typedef struct fmha_bwd_plan_info {
                               bf16 mode (see below) */
   int32_t dq_acc_elem_bytes; /* 4 (fp32 accumulator) or 2 (bf16) */
   int32_t reserved;
+  int64_t dbias_acc_offset;  /* byte offset of the fp32 full-shape dS [B][Hq][Sq][Sk] (dbias) */
+  int64_t dbias_acc_bytes;   /* 0 without dbias */
 } fmha_bwd_plan_info;
 /* Accumulator layout.  Atomic mode: one split, rows_q rows, row-major ([row][d_qk]), row of
    a query = its D/LSE row.  Deterministic mode: split s holds the sum of the partials of key

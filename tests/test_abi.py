@@ -58,8 +58,8 @@ int main(void) {
   printf("{\\n");
   F(B) F(scale) F(deterministic) F(seqstart_q_host) F(seqstart_k_dev) F(q) F(lse) F(dv)
   F(q_stride) F(dv_stride) F(lse_stride) F(seqstart_q_padded_host) F(seqstart_k_padded_dev)
-  F(dq_acc_dtype)
-  G(nsplits) G(rows_q) G(workspace_bytes) G(flops) G(acc_rows) G(dq_acc_elem_bytes)
+  F(dq_acc_dtype) F(bias) F(dbias_stride) F(bias_h)
+  G(nsplits) G(rows_q) G(workspace_bytes) G(flops) G(acc_rows) G(dq_acc_elem_bytes) G(dbias_acc_bytes)
   printf("\\"size_args\\": %zu, \\"size_info\\": %zu}\\n", sizeof(fmha_bwd_args), sizeof(fmha_bwd_plan_info));
   return 0;
 }
@@ -77,7 +77,7 @@ int main(void) {
         if k.startswith("size"):
             continue
         cls = _lib.PlanInfo if k in ("nsplits", "rows_q", "workspace_bytes", "flops", "acc_rows",
-                                     "dq_acc_elem_bytes") else Args
+                                     "dq_acc_elem_bytes", "dbias_acc_bytes") else Args
         assert getattr(cls, k).offset == v, k
 
 
@@ -198,6 +198,66 @@ def test_bf16_accumulator_plan():
     assert info.dq_acc_bytes == 3 * 4 * 112 * 128 * 2
     assert info.dq_acc_offset + info.dq_acc_bytes <= info.workspace_bytes
     assert _lib.plan_query(batch_args(deterministic=0)).dq_acc_elem_bytes == 4
+
+
+def _with_bias(a, bb, bh, dbias=True):
+    Sq, Sk = a.Sq, a.Sk
+    a.bias = FAKE
+    a.bias_b, a.bias_h = bb, bh
+    a.bias_stride[0], a.bias_stride[1], a.bias_stride[2] = bh * Sq * 336, Sq * 336, 336
+    if dbias:
+        a.dbias = FAKE
+        a.dbias_stride[0], a.dbias_stride[1], a.dbias_stride[2] = bh * Sq * 336, Sq * 336, 336
+    return a
+
+
+def test_bias_plan():
+    """A bias of shape (1|B, 1|Hq, Sq, Sk): dbias needs an fp32 full-shape dS region in the
+    workspace; d_qk = 128 then uses 32-row query blocks."""
+    for bb, bh in ((1, 1), (1, 4), (2, 1), (2, 4)):
+        a = _with_bias(batch_args(), bb, bh)
+        info = _lib.plan_query(a)
+        assert info.tile_m == 32
+        assert info.dbias_acc_bytes == 2 * 4 * 200 * 333 * 4
+        assert info.dbias_acc_offset % 256 == 0
+        assert info.dbias_acc_offset >= info.dq_acc_offset + info.dq_acc_bytes
+        assert info.dbias_acc_offset + info.dbias_acc_bytes <= info.workspace_bytes
+        assert _lib.workspace_size(a) == info.workspace_bytes
+    a = _with_bias(batch_args(), 1, 1, dbias=False)
+    info = _lib.plan_query(a)
+    assert info.dbias_acc_bytes == 0
+    assert _lib.plan_query(batch_args()).tile_m == 64
+
+
+@pytest.mark.parametrize("mutate,expected", [
+    (lambda a: setattr(a, "bias_b", 3), _lib.ERR_INVALID_ARG),
+    (lambda a: setattr(a, "bias_h", 2), _lib.ERR_INVALID_ARG),
+    (lambda a: setattr(a, "bias", FAKE + 1), _lib.ERR_UNSUPPORTED),  # not bf16-aligned
+    (lambda a: a.bias_stride.__setitem__(2, 332), _lib.ERR_UNSUPPORTED),  # row stride < Sk
+    (lambda a: a.dbias_stride.__setitem__(2, 332), _lib.ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "dbias", FAKE + 1), _lib.ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "bias", None), _lib.ERR_INVALID_ARG),  # dbias without a bias
+])
+def test_bias_argument_errors(mutate, expected):
+    a = _with_bias(batch_args(), 2, 4)
+    assert status_of(a) == _lib.OK
+    mutate(a)
+    assert status_of(a) == expected
+
+
+def test_bias_row_stride_may_be_any_value_at_least_sk():
+    a = _with_bias(batch_args(), 2, 4)
+    a.bias_stride[2] = 333
+    a.dbias_stride[2] = 335
+    assert status_of(a) == _lib.OK
+
+
+def test_bias_needs_batch_mode():
+    g = group_args([5, 7], [5, 7])
+    g.bias = FAKE
+    g.bias_b, g.bias_h = 1, 1
+    g.bias_stride[2] = 8
+    assert status_of(g) == _lib.ERR_UNSUPPORTED
 
 
 def test_tiles_per_item_keeps_two_items_per_cu():
