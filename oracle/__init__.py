@@ -8,8 +8,10 @@ does, and it shares no code with the HIP path.
 
 Every function is pinned by the CPU tests in ``tests/test_oracle.py`` against finite
 differences, an independent library implementation (torch fp64 SDPA + autograd) on the
-cases where it applies, closed forms and exact identities.  Nothing here is
-"parity unpinned".
+cases where it applies, closed forms and exact identities.  The dropout generator (Philox,
+written once for any word size) is pinned bit-exactly at 64-bit words against numpy's
+Philox4x64-10; the 32-bit variant the dropout uses differs only in its published constants.
+Nothing here is "parity unpinned".
 """
 
 from .attention import (  # noqa: F401

@@ -27,6 +27,15 @@ to rounding order).
   has the shape of the bias and is the full (B, H, Sq, Sk) gradient summed over the
   broadcast dimensions.  Reading: the bias is added to the scaled logits before the mask
   and the softmax, so dbias = dS.
+* Dropout -- same page, backward entry point: the random stream is a Philox generator
+  driven by a seed and an offset.  Nothing else is stated; the readings taken: the
+  generator is Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy
+  as 1, 2, 3", SC 2011); element (b, h, i, j) (segment/batch b, query head h, positions i, j
+  inside the segment) uses byte (j mod 4) of output word (i mod 4) for key (seed low 32
+  bits, seed high 32 bits) and counter (j div 4, i div 4, b*Hq + h, offset low 32 bits); it
+  is kept iff that byte is < k = round((1 - p) * 256), and kept probabilities are scaled by
+  256 / k.  Dropout acts on P in the P V product only (LSE is that of the full softmax), so
+  dV = (P Z 256/k)^T dO, dP = (dO V^T) Z 256/k and dS = P (dP - D) with D = rowsum(dO O).
 * Deterministic dQ accumulation -- "[CK_TILE] FMHA BWD Use Persistent Kernels in
   Deterministic Mode" (aiter PR 2216), Motivation and commit messages: dQ is accumulated as
   fp32 partials in an nsplits-deep workspace and converted back afterwards.  The order of
@@ -35,6 +44,7 @@ to rounding order).
 For every (segment, query head h, K/V head g) with lengths Lq, Lk:
 
     S   = scale * Q_h K_g^T (+ bias[b, h])                   (Lq x Lk)
+    (with dropout, P below is P Z 256/k in O = P V, dV and dP; Z the keep mask)
     LSE = log sum_{allowed j} exp(S_ij)       (-inf for a row with no allowed key)
     P   = exp(S - LSE) on allowed entries, 0 elsewhere
     O   = P V_g
@@ -139,6 +149,57 @@ def _check_bias(bias, batch_mode, B, hq, sq, sk):
     return bias
 
 
+# ---------------------------------------------------------------------------------------
+# Philox (Salmon et al., SC 2011): a counter-based generator.  N = 4 words of `bits` bits,
+# two multipliers and two Weyl key increments; one round multiplies words 0 and 2 by the
+# multipliers, and the output is (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1,
+# lo(M0 c0)); the key grows by the Weyl constants between rounds.
+# ---------------------------------------------------------------------------------------
+PHILOX_4X32 = dict(bits=32, M=(0xD2511F53, 0xCD9E8D57), W=(0x9E3779B9, 0xBB67AE85))
+PHILOX_4X64 = dict(bits=64, M=(0xD2E7470EE14C6C93, 0xCA5A826395121157),
+                   W=(0x9E3779B97F4A7C15, 0xBB67AE8584CAA73B))
+
+
+def philox(counter, key, *, bits, M, W, rounds=10):
+    """Philox-4x`bits`-`rounds` of a counter (4 arrays of words) under a key (2 words);
+    returns the 4 output words.  Python integers, so arrays of any shape broadcast."""
+    mask = (1 << bits) - 1
+    c = [np.asarray(x, dtype=object) for x in counter]
+    k0, k1 = int(key[0]), int(key[1])
+    for r in range(rounds):
+        if r:
+            k0 = (k0 + W[0]) & mask
+            k1 = (k1 + W[1]) & mask
+        p0 = c[0] * M[0]
+        p1 = c[2] * M[1]
+        c = [(p1 >> bits) ^ c[1] ^ k0, p1 & mask, (p0 >> bits) ^ c[3] ^ k1, p0 & mask]
+    return c
+
+
+def dropout_threshold(p):
+    """k = round((1 - p) * 256): bytes below k are kept; kept values are scaled by 256 / k."""
+    if not 0.0 <= p < 1.0:
+        raise ValueError("dropout probability must be in [0, 1)")
+    k = int(np.floor((1.0 - p) * 256.0 + 0.5))
+    if k < 1:
+        raise ValueError("dropout probability too close to 1")
+    return k
+
+
+def dropout_keep(seed, offset, b, h, hq, rows, cols, k):
+    """Keep mask Z[i, j] of segment/batch b, query head h for the given positions."""
+    ii = np.asarray(rows, dtype=np.int64)[:, None]
+    jj = np.asarray(cols, dtype=np.int64)[None, :]
+    ii, jj = np.broadcast_arrays(ii, jj)
+    out = philox((jj >> 2, ii >> 2, np.full(ii.shape, b * hq + h, dtype=np.int64),
+                  np.full(ii.shape, int(offset) & 0xFFFFFFFF, dtype=np.int64)),
+                 (int(seed) & 0xFFFFFFFF, (int(seed) >> 32) & 0xFFFFFFFF), **PHILOX_4X32)
+    words = np.stack([np.asarray(w, dtype=np.int64) for w in out])        # [4, ...]
+    word = np.take_along_axis(words, (ii & 3)[None], axis=0)[0]
+    byte = (word >> (8 * (jj & 3))) & 0xFF
+    return byte < k
+
+
 def _check_heads(hq, hkv):
     if hkv <= 0 or hq % hkv != 0:
         raise ValueError("Hq must be a positive multiple of Hkv")
@@ -146,9 +207,10 @@ def _check_heads(hq, hkv):
 
 
 def forward(q, k, v, *, scale, mask_type=MASK_NONE, window_left=-1, window_right=-1,
-            seqstart_q=None, seqstart_k=None, bias=None):
+            seqstart_q=None, seqstart_k=None, bias=None, dropout=None):
     """Softmax attention forward in fp64.  Returns (O, LSE) in the layouts of the module
-    docstring.  ``bias`` (batch mode): (1|B, 1|Hq, Sq, Sk), added to the scaled logits."""
+    docstring.  ``bias`` (batch mode): (1|B, 1|Hq, Sq, Sk), added to the scaled logits.
+    ``dropout``: (p, seed, offset), see the module docstring."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
@@ -174,6 +236,8 @@ def forward(q, k, v, *, scale, mask_type=MASK_NONE, window_left=-1, window_right
                 if bias is not None:
                     s = s + _bias_plane(bias, b, h)[r0:r1]
                 p, l = _softmax_rows(s, ok)
+                if dropout is not None:
+                    p = p * _dropout_factor(dropout, b, h, hq, np.arange(r0, r1), lk)
                 ob = p @ vb[:, g, :]
                 if batch_mode:
                     o[b, r0:r1, h, :] = ob
@@ -184,8 +248,15 @@ def forward(q, k, v, *, scale, mask_type=MASK_NONE, window_left=-1, window_right
     return o, lse
 
 
+def _dropout_factor(dropout, b, h, hq, rows, lk):
+    """Z * 256/k for the given rows of segment b, head h (all lk keys)."""
+    p_drop, seed, offset = dropout
+    k = dropout_threshold(p_drop)
+    return dropout_keep(seed, offset, b, h, hq, rows, np.arange(lk), k) * (256.0 / k)
+
+
 def backward(q, k, v, do, *, scale, mask_type=MASK_NONE, window_left=-1, window_right=-1,
-             seqstart_q=None, seqstart_k=None, bias=None):
+             seqstart_q=None, seqstart_k=None, bias=None, dropout=None):
     """Exact gradient of O = softmax(scale Q K^T + bias + mask) V in direction dO, fp64.
 
     Returns (dQ, dK, dV) shaped like (Q, K, V), and dbias (shaped like the bias) as a fourth
@@ -221,15 +292,16 @@ def backward(q, k, v, do, *, scale, mask_type=MASK_NONE, window_left=-1, window_
                 if bias is not None:
                     s = s + _bias_plane(bias, b, h)[r0:r1]
                 p, _ = _softmax_rows(s, ok)
-                o = p @ vb[:, g, :]
+                zf = 1.0 if dropout is None else _dropout_factor(dropout, b, h, hq, np.arange(r0, r1), lk)
+                o = (p * zf) @ vb[:, g, :]
                 d = (doh * o).sum(axis=1)
-                dp = doh @ vb[:, g, :].T
+                dp = (doh @ vb[:, g, :].T) * zf
                 ds = p * (dp - d[:, None])
                 if dbias is not None:
                     _bias_plane(dbias, b, h)[r0:r1] += ds
                 dqb[r0:r1, h, :] = scale * (ds @ kb[:, g, :])
                 dkb[:, g, :] += scale * (ds.T @ qh)
-                dvb[:, g, :] += p.T @ doh
+                dvb[:, g, :] += (p * zf).T @ doh
         dq[qs] = dqb
         dk[ks] = dkb
         dv[ks] = dvb

@@ -382,7 +382,7 @@ MUTATIONS = [
     ("wrong sign of D", "ds = p * (dp - d[:, None])", "ds = p * (dp + d[:, None])"),
     ("missing dQ scale", "dqb[r0:r1, h, :] = scale * (ds @ kb[:, g, :])", "dqb[r0:r1, h, :] = ds @ kb[:, g, :]"),
     ("dK from P", "dkb[:, g, :] += scale * (ds.T @ qh)", "dkb[:, g, :] += scale * (p.T @ qh)"),
-    ("dV wrong row index", "dvb[:, g, :] += p.T @ doh", "dvb[:, g, :] += p.T @ doh[::-1]"),
+    ("dV wrong row index", "dvb[:, g, :] += (p * zf).T @ doh", "dvb[:, g, :] += (p * zf).T @ doh[::-1]"),
     ("GQA index", "g = h // group", "g = h % kb.shape[1]"),
 ]
 
