@@ -13,6 +13,9 @@ row padded[b] and the rest of its slot (up to padded[b+1]) is padding, left unto
 adds instead of fp32 ones: about half the atomic traffic, less accurate dQ.
 ``bias`` (batch mode): a bf16 [1|B, 1|Hq, Sq, Sk] tensor added to the scaled logits;
 ``bwd(..., bias=bias, bias_grad=True)`` also returns dbias, shaped like the bias.
+``dropout_p``, ``philox_seed``, ``philox_offset``: dropout on the probabilities of O = P V
+(forward) and in dV, dP (backward), with the Philox keep mask of ``include/fmha_bwd.h``; the
+backward must get the forward's values.
 """
 
 import numpy as np
@@ -70,7 +73,7 @@ def make_call(q, k, v, o, lse, do, dq, dk, dv, *, scale=None, mask_type=MASK_NON
               cu_seqlens_q_host=None, cu_seqlens_k_host=None, max_seqlen_q=None,
               max_seqlen_k=None, cu_seqlens_q_padded=None, cu_seqlens_k_padded=None,
               cu_seqlens_q_padded_host=None, cu_seqlens_k_padded_host=None, dq_acc_dtype="fp32",
-              bias=None, dbias=None):
+              bias=None, dbias=None, dropout_p=0.0, philox_seed=0, philox_offset=0):
     """Fill the C argument struct from tensors (no device work)."""
     group = cu_seqlens_q is not None
     d_qk = q.shape[-1]
@@ -121,6 +124,9 @@ def make_call(q, k, v, o, lse, do, dq, dk, dv, *, scale=None, mask_type=MASK_NON
     if dq_acc_dtype not in ("fp32", "bf16"):
         raise ValueError("dq_acc_dtype must be 'fp32' or 'bf16'")
     a.dq_acc_dtype = DQ_ACC_BF16 if dq_acc_dtype == "bf16" else DQ_ACC_FP32
+    a.p_drop = float(dropout_p)
+    a.philox_seed = int(philox_seed) & (2**64 - 1)
+    a.philox_offset = int(philox_offset) & (2**64 - 1)
     if bias is not None:
         if bias.dim() != 4 or bias.stride(-1) != 1:
             raise ValueError("bias must be [1|B, 1|Hq, Sq, Sk] with contiguous columns")
@@ -151,7 +157,8 @@ def bwd(q, k, v, o, lse, do, *, scale=None, mask_type=MASK_NONE, window=(-1, -1)
         deterministic=True, cu_seqlens_q=None, cu_seqlens_k=None, cu_seqlens_q_host=None,
         cu_seqlens_k_host=None, max_seqlen_q=None, max_seqlen_k=None, cu_seqlens_q_padded=None,
         cu_seqlens_k_padded=None, cu_seqlens_q_padded_host=None, cu_seqlens_k_padded_host=None,
-        workspace=None, out=None, dq_acc_dtype="fp32", bias=None, bias_grad=False):
+        workspace=None, out=None, dq_acc_dtype="fp32", bias=None, bias_grad=False, dropout_p=0.0,
+        philox_seed=0, philox_offset=0):
     """Gradients (dq, dk, dv) of softmax attention, and dbias when ``bias_grad``; see the
     module docstring for layouts."""
     import torch
@@ -180,7 +187,8 @@ def bwd(q, k, v, o, lse, do, *, scale=None, mask_type=MASK_NONE, window=(-1, -1)
                      cu_seqlens_k_padded=cu_seqlens_k_padded,
                      cu_seqlens_q_padded_host=cu_seqlens_q_padded_host,
                      cu_seqlens_k_padded_host=cu_seqlens_k_padded_host, dq_acc_dtype=dq_acc_dtype,
-                     bias=bias, dbias=dbias)
+                     bias=bias, dbias=dbias, dropout_p=dropout_p, philox_seed=philox_seed,
+                     philox_offset=philox_offset)
     nbytes = call.workspace_size()
     if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
@@ -195,7 +203,8 @@ def bwd(q, k, v, o, lse, do, *, scale=None, mask_type=MASK_NONE, window=(-1, -1)
 def fwd(q, k, v, *, scale=None, mask_type=MASK_NONE, window=(-1, -1), cu_seqlens_q=None,
         cu_seqlens_k=None, cu_seqlens_q_host=None, cu_seqlens_k_host=None, max_seqlen_q=None,
         max_seqlen_k=None, cu_seqlens_q_padded=None, cu_seqlens_k_padded=None,
-        cu_seqlens_q_padded_host=None, cu_seqlens_k_padded_host=None, bias=None):
+        cu_seqlens_q_padded_host=None, cu_seqlens_k_padded_host=None, bias=None, dropout_p=0.0,
+        philox_seed=0, philox_offset=0):
     """Forward (o, lse) on the device, in the layouts ``bwd`` takes: o like q with d_v columns,
     lse [B, Hq, Sq] (batch) or [Hq, T] (group)."""
     import torch
@@ -214,6 +223,7 @@ def fwd(q, k, v, *, scale=None, mask_type=MASK_NONE, window=(-1, -1), cu_seqlens
                      max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k,
                      cu_seqlens_q_padded=cu_seqlens_q_padded, cu_seqlens_k_padded=cu_seqlens_k_padded,
                      cu_seqlens_q_padded_host=cu_seqlens_q_padded_host,
-                     cu_seqlens_k_padded_host=cu_seqlens_k_padded_host, bias=bias)
+                     cu_seqlens_k_padded_host=cu_seqlens_k_padded_host, bias=bias,
+                     dropout_p=dropout_p, philox_seed=philox_seed, philox_offset=philox_offset)
     _lib.fwd_run(call.args, torch.cuda.current_stream(q.device).cuda_stream)
     return o, lse

@@ -6,7 +6,7 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libfmha_bwd.so")
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 MASK_NONE = 0
 MASK_CAUSAL_TOP_LEFT = 1
@@ -90,6 +90,10 @@ class Args(ctypes.Structure):
         ("dbias_stride", _i64x3),
         ("bias_b", ctypes.c_int32),
         ("bias_h", ctypes.c_int32),
+        ("p_drop", ctypes.c_float),
+        ("reserved2", ctypes.c_int32),
+        ("philox_seed", ctypes.c_uint64),
+        ("philox_offset", ctypes.c_uint64),
     ]
 
     def __init__(self, **kw):

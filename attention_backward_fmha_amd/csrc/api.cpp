@@ -104,6 +104,11 @@ fmha::KParams make_params(const fmha_bwd_args* a, const fmha::Plan& p, void* ws)
     k.bias_b = p.bias_b;
     k.bias_h = p.bias_h;
   }
+  k.drop_k = p.drop_k;
+  k.drop_scale = 256.0f / (float)p.drop_k;
+  k.seed_lo = (unsigned)(a->philox_seed & 0xFFFFFFFFu);
+  k.seed_hi = (unsigned)(a->philox_seed >> 32);
+  k.offset_lo = (unsigned)(a->philox_offset & 0xFFFFFFFFu);
   if (p.has_dbias) {
     if (ws != nullptr) k.dbias_acc = (float*)((char*)ws + p.dbias_acc_offset);
     k.dbias = (uint16_t*)a->dbias;

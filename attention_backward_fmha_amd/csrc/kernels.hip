@@ -210,6 +210,27 @@ __device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(unsigned, bf16x2{(__bf16)lo, (__bf16)hi});
 }
 
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3",
+// SC 2011) of counter c under key (k0, k1), in place.  The dropout keep mask of element
+// (b, h, i, j) is byte (j % 4) of output word (i % 4) for counter (j/4, i/4, b*Hq + h, offset).
+__device__ __forceinline__ void philox4x32_10(unsigned (&c)[4], unsigned k0, unsigned k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c[2];
+    const unsigned n0 = (unsigned)(p1 >> 32) ^ c[1] ^ k0;
+    const unsigned n2 = (unsigned)(p0 >> 32) ^ c[3] ^ k1;
+    c[0] = n0;
+    c[1] = (unsigned)p1;
+    c[2] = n2;
+    c[3] = (unsigned)p0;
+  }
+}
+
 // Value of lane (l ^ 1) and of lane (l ^ 2) (DPP quad permutations).
 __device__ __forceinline__ unsigned xor1(unsigned v) {
   return (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);
@@ -302,9 +323,10 @@ __device__ __forceinline__ void stage_block(uint16_t* rm, uint16_t* tr, int RS,
 }
 
 // DQM: 0 = fp32 atomic adds, 1 = deterministic fp32 splits, 2 = packed bf16 atomic adds.
-// BIAS: an additive bias joins the logits (and dS goes to the full-shape dbias scratch when
-// that is requested).
-template <int DQK, int DV, int TM_, int DQM, bool BIAS>
+// EXTRA: an additive bias and/or dropout.  The bias joins the logits (an absent bias reads
+// zeros from an empty resource), dS goes to the full-shape dbias scratch when that is
+// requested, and dropout's keep mask comes from Philox behind one uniform branch.
+template <int DQK, int DV, int TM_, int DQM, bool EXTRA>
 __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
   constexpr bool DET = DQM == 1;
   using T = MainTile<DQK, DV, TM_>;
@@ -487,8 +509,8 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
     // bias of the lane's (query, key) pairs, issued before the products that hide its latency;
     // register 16m + r pairs with the S/dP result register r of row tile m.  Rows past the
     // plane are outside the resource (zeros); keys past the tile end are masked below.
-    float bv[BIAS ? MT * 16 : 1];
-    if constexpr (BIAS) {
+    float bv[EXTRA ? MT * 16 : 1];
+    if constexpr (EXTRA) {
       const __amdgpu_buffer_rsrc_t rb =
           buffer_rsrc(p.bias + (int64_t)b * p.bias_s[0] + (int64_t)hq * p.bias_s[1], p.bias_plane_bytes);
       const int bs2 = (int)p.bias_s[2];
@@ -503,8 +525,8 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
         }
     }
     const __amdgpu_buffer_rsrc_t rdb = buffer_rsrc(
-        BIAS && p.dbias_acc != nullptr ? p.dbias_acc + ((int64_t)b * p.Hq + hq) * p.Sq * p.Sk : nullptr,
-        BIAS && p.dbias_acc != nullptr ? (uint32_t)p.Sq * (uint32_t)p.Sk * 4u : 0u);
+        EXTRA && p.dbias_acc != nullptr ? p.dbias_acc + ((int64_t)b * p.Hq + hq) * p.Sq * p.Sk : nullptr,
+        EXTRA && p.dbias_acc != nullptr ? (uint32_t)p.Sq * (uint32_t)p.Sk * 4u : 0u);
     f32x16 s_acc[MT];
     f32x16 dp_acc[MT];
 #pragma unroll
@@ -541,18 +563,31 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
         const int qr = 32 * m + 8 * c + 4 * hi;
         const f32x4 l4 = *(const f32x4*)&lse_lds[qr];
         const f32x4 d4 = *(const f32x4*)&dd_lds[qr];
+        // dropout: rows q0+qr .. +3 of this lane's key share one Philox output
+        float zf[4] = {1.f, 1.f, 1.f, 1.f};
+        if constexpr (EXTRA) {
+          if (p.drop_k < 256) {
+            const unsigned kpos = (unsigned)(key0 + key_l);
+            unsigned w[4] = {kpos >> 2, (unsigned)(q0 + qr) >> 2, (unsigned)(b * p.Hq + hq), p.offset_lo};
+            philox4x32_10(w, p.seed_lo, p.seed_hi);
+            const unsigned sh = 8u * (kpos & 3u);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              zf[e] = ((w[e] >> sh) & 0xFFu) < (unsigned)p.drop_k ? p.drop_scale : 0.f;
+          }
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * c + e;
           float xl = s_acc[m][r] * p.scale_log2 - l4[e];
-          if constexpr (BIAS) xl = __builtin_fmaf(bv[16 * m + r], kLog2e, xl);
+          if constexpr (EXTRA) xl = __builtin_fmaf(bv[16 * m + r], kLog2e, xl);
           float pv = __builtin_amdgcn_exp2f(xl);
           pv = (unsigned)(t0 - (32 * m + 8 * c + e)) <= span ? pv : 0.f;
-          const float dsv = pv * (dp_acc[m][r] - d4[e]);
-          pa[c >> 1][(c & 1) * 4 + e] = (__bf16)pv;
+          const float dsv = pv * (dp_acc[m][r] * zf[e] - d4[e]);
+          pa[c >> 1][(c & 1) * 4 + e] = (__bf16)(pv * zf[e]);
           sa[c >> 1][(c & 1) * 4 + e] = (__bf16)dsv;
           ds32[r] = dsv;
-          if constexpr (BIAS) {
+          if constexpr (EXTRA) {
             // full-shape dS for dbias: every (row, key) of the block, masked pairs as 0; rows
             // past the plane are dropped by the range check, keys past the tile end skipped
             if (p.dbias_acc != nullptr && key_ok)
@@ -958,7 +993,7 @@ struct FwdTile {
   static_assert(KBLK % 64 == 0, "staging blocks of K must fill whole waves");
 };
 
-template <int DQK, int DV, bool BIAS>
+template <int DQK, int DV, bool EXTRA>
 __global__ __launch_bounds__(256, DQK <= 128 ? 2 : 1) void k_fwd(const KParams p) {
   using T = FwdTile<DQK, DV>;
   constexpr int TQ = T::TQ, TK = T::TK, KS = T::KS, VS = T::VS;
@@ -1093,8 +1128,8 @@ __global__ __launch_bounds__(256, DQK <= 128 ? 2 : 1) void k_fwd(const KParams p
     // bias of this lane's query row for its keys of the tile, issued before the products
     // (2-byte loads: the row stride may be any value >= Sk); rows past the plane read zeros,
     // keys past the end are masked
-    float bz[BIAS ? 32 : 1];
-    if constexpr (BIAS) {
+    float bz[EXTRA ? 32 : 1];
+    if constexpr (EXTRA) {
       const __amdgpu_buffer_rsrc_t rb =
           buffer_rsrc(p.bias + (int64_t)b * p.bias_s[0] + (int64_t)h * p.bias_s[1], p.bias_plane_bytes);
       const int rowoff = row * (int)p.bias_s[2];
@@ -1129,7 +1164,7 @@ __global__ __launch_bounds__(256, DQK <= 128 ? 2 : 1) void k_fwd(const KParams p
       for (int r = 0; r < 16; ++r) {
         const int ko = 32 * kb + 8 * (r >> 2) + (r & 3);
         float x = s[kb][r] * p.scale_log2;
-        if constexpr (BIAS) x = __builtin_fmaf(bz[16 * kb + r], kLog2e, x);
+        if constexpr (EXTRA) x = __builtin_fmaf(bz[16 * kb + r], kLog2e, x);
         s[kb][r] = (unsigned)(t0 + ko) <= span ? x : -__builtin_inff();
         mt = fmaxf(mt, s[kb][r]);
       }
@@ -1144,13 +1179,28 @@ __global__ __launch_bounds__(256, DQK <= 128 ? 2 : 1) void k_fwd(const KParams p
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
+      for (int c = 0; c < 4; ++c) {
+        // dropout (P in P V only; the running sum is of the full softmax): keys
+        // kt0 + 32kb + 8c + 4hi .. +3 of this lane's row share one Philox output word
+        float zf[4] = {1.f, 1.f, 1.f, 1.f};
+        if constexpr (EXTRA) {
+          if (p.drop_k < 256) {
+            unsigned w[4] = {(unsigned)(kt0 + 32 * kb + 8 * c + 4 * hi) >> 2, (unsigned)row >> 2,
+                             (unsigned)(b * p.Hq + h), p.offset_lo};
+            philox4x32_10(w, p.seed_lo, p.seed_hi);
+            const unsigned word = (row & 2) ? ((row & 1) ? w[3] : w[2]) : ((row & 1) ? w[1] : w[0]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              zf[e] = ((word >> (8 * e)) & 0xFFu) < (unsigned)p.drop_k ? p.drop_scale : 0.f;
+          }
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float pv = __builtin_amdgcn_exp2f(s[kb][4 * c + e] - m_use);
           ls += pv;
-          pb[kb][c >> 1][(c & 1) * 4 + e] = (__bf16)pv;
+          pb[kb][c >> 1][(c & 1) * 4 + e] = (__bf16)(pv * zf[e]);
         }
+      }
     l_run = l_run * alpha + ls;
     // O^T = alpha * O^T + V^T P^T (reduction step ks = 2kb + t covers transposed positions
     // 16ks .. 16ks + 15)
@@ -1218,13 +1268,13 @@ hipError_t launch_fwd(const Plan& plan, const KParams& kp, hipStream_t stream) {
   const int64_t rows = (int64_t)plan.n_q_blocks * plan.tile_m;  // >= the longest segment
   const dim3 grid((unsigned)((rows + 127) / 128), (unsigned)plan.Hq, (unsigned)plan.B);
   if (plan.d_qk == 64) {
-    if (plan.has_bias) hipLaunchKernelGGL((k_fwd<64, 64, true>), grid, dim3(256), 0, stream, kp);
+    if (plan.has_bias || plan.drop_k < 256) hipLaunchKernelGGL((k_fwd<64, 64, true>), grid, dim3(256), 0, stream, kp);
     else hipLaunchKernelGGL((k_fwd<64, 64, false>), grid, dim3(256), 0, stream, kp);
   } else if (plan.d_qk == 128) {
-    if (plan.has_bias) hipLaunchKernelGGL((k_fwd<128, 128, true>), grid, dim3(256), 0, stream, kp);
+    if (plan.has_bias || plan.drop_k < 256) hipLaunchKernelGGL((k_fwd<128, 128, true>), grid, dim3(256), 0, stream, kp);
     else hipLaunchKernelGGL((k_fwd<128, 128, false>), grid, dim3(256), 0, stream, kp);
   } else {
-    if (plan.has_bias) hipLaunchKernelGGL((k_fwd<192, 128, true>), grid, dim3(256), 0, stream, kp);
+    if (plan.has_bias || plan.drop_k < 256) hipLaunchKernelGGL((k_fwd<192, 128, true>), grid, dim3(256), 0, stream, kp);
     else hipLaunchKernelGGL((k_fwd<192, 128, false>), grid, dim3(256), 0, stream, kp);
   }
   return hipGetLastError();
@@ -1238,7 +1288,7 @@ static void launch_main_t(const Plan& plan, const KParams& kp, dim3 grid, hipStr
     if (mode == 1) hipLaunchKernelGGL((k_bwd_main<DQK, DV, TM, 1, false>), grid, dim3(256), 0, stream, kp);
     else if (mode == 2) hipLaunchKernelGGL((k_bwd_main<DQK, DV, TM, 2, false>), grid, dim3(256), 0, stream, kp);
     else hipLaunchKernelGGL((k_bwd_main<DQK, DV, TM, 0, false>), grid, dim3(256), 0, stream, kp);
-  } else if (plan.has_bias) {
+  } else if (plan.has_bias || plan.drop_k < 256) {
     if (mode == 1) hipLaunchKernelGGL((k_bwd_main<DQK, DV, TM, 1, true>), grid, dim3(256), 0, stream, kp);
     else if (mode == 2) hipLaunchKernelGGL((k_bwd_main<DQK, DV, TM, 2, true>), grid, dim3(256), 0, stream, kp);
     else hipLaunchKernelGGL((k_bwd_main<DQK, DV, TM, 0, true>), grid, dim3(256), 0, stream, kp);

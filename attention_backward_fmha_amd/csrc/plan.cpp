@@ -89,6 +89,12 @@ int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t el, bool forwar
   if (a->reserved != 0) return fail(FMHA_ERR_INVALID_ARG, err, el, "reserved must be 0");
   if (a->dbias && !a->bias)
     return fail(FMHA_ERR_INVALID_ARG, err, el, "dbias needs a bias");
+  if (!(a->p_drop >= 0.f && a->p_drop < 1.f))
+    return fail(FMHA_ERR_INVALID_ARG, err, el, "p_drop must be in [0, 1)");
+  if (a->reserved2 != 0) return fail(FMHA_ERR_INVALID_ARG, err, el, "reserved2 must be 0");
+  p->drop_k = (int)floor((1.0 - (double)a->p_drop) * 256.0 + 0.5);
+  if (p->drop_k < 1)
+    return fail(FMHA_ERR_UNSUPPORTED, err, el, "p_drop too close to 1 (keep threshold rounds to 0)");
 
   p->B = a->B;
   p->Hq = a->Hq;
@@ -103,9 +109,9 @@ int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t el, bool forwar
   if (const char* e = getenv("FMHA_BWD_TILE_M")) {  // tuning knob: 32 or 64 for d_qk = 128
     if (a->d_qk == 128 && (atoi(e) == 32 || atoi(e) == 64)) p->tile_m = atoi(e);
   }
-  // with a bias, d_qk = 128 takes 32-row blocks too: the bias registers of 64-row blocks do
-  // not fit beside the rest of the main kernel's registers
-  if (a->bias != nullptr && a->d_qk == 128) p->tile_m = 32;
+  // with a bias or dropout, d_qk = 128 takes 32-row blocks too: the extra registers of
+  // 64-row blocks do not fit beside the rest of the main kernel's registers
+  if ((a->bias != nullptr || p->drop_k < 256) && a->d_qk == 128) p->tile_m = 32;
   p->tile_n = 128;
   p->deterministic = a->deterministic == 1;
   p->dq_bf16 = a->dq_acc_dtype == FMHA_DQ_ACC_BF16;

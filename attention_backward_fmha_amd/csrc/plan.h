@@ -41,6 +41,7 @@ struct Plan {
   int bias_b, bias_h;
   uint32_t bias_plane_bytes;  // bytes of one (batch, head) bias plane the kernels may read
   int64_t dbias_acc_offset, dbias_acc_bytes;  // fp32 [B][Hq][Sq][Sk] full-shape dS
+  int drop_k;            // dropout keep threshold on a random byte (256 = no dropout)
 };
 
 // Validates `a` and fills `p`.  Returns FMHA_OK or a negative status; on failure `err`

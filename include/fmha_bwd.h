@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define FMHA_BWD_ABI_VERSION 4u
+#define FMHA_BWD_ABI_VERSION 5u
 
 #if defined(__GNUC__)
 #define FMHA_BWD_API __attribute__((visibility("default")))
@@ -163,6 +163,19 @@ typedef struct fmha_bwd_args {
   int64_t dbias_stride[3];
   int32_t bias_b;          /* 1 or B (ignored without bias) */
   int32_t bias_h;          /* 1 or Hq */
+  /* Dropout on the attention probabilities, driven by a Philox seed and offset as in "Update
+     AITER subcommit and refactor internal AITER/CK FA API usage" (backward entry point).
+     The generator is Philox4x32-10 (Salmon et al., SC 2011).  Element (b, h, i, j) (segment
+     or batch b, query head h, positions i, j inside the segment) reads byte (j mod 4) of
+     output word (i mod 4) for key (seed low 32 bits, seed high 32 bits) and counter
+     (j / 4, i / 4, b * Hq + h, offset low 32 bits).  It is kept iff that byte is below
+     k = round((1 - p_drop) * 256), and a kept probability is scaled by 256 / k.  Dropout
+     applies to P in O = P V (fmha_fwd_run) and in the backward's dV and dP; lse is that of
+     the softmax without dropout.  p_drop = 0 (k = 256) is no dropout. */
+  float p_drop;            /* in [0, 1); k must come out >= 1 */
+  int32_t reserved2;       /* must be 0 */
+  uint64_t philox_seed;
+  uint64_t philox_offset;  /* only its low 32 bits are used */
 } fmha_bwd_args;
 
 /* Workspace bytes that prepare/run need for these arguments.  Host only: no GPU call, no

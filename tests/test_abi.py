@@ -58,7 +58,7 @@ int main(void) {
   printf("{\\n");
   F(B) F(scale) F(deterministic) F(seqstart_q_host) F(seqstart_k_dev) F(q) F(lse) F(dv)
   F(q_stride) F(dv_stride) F(lse_stride) F(seqstart_q_padded_host) F(seqstart_k_padded_dev)
-  F(dq_acc_dtype) F(bias) F(dbias_stride) F(bias_h)
+  F(dq_acc_dtype) F(bias) F(dbias_stride) F(bias_h) F(p_drop) F(philox_seed) F(philox_offset)
   G(nsplits) G(rows_q) G(workspace_bytes) G(flops) G(acc_rows) G(dq_acc_elem_bytes) G(dbias_acc_bytes)
   printf("\\"size_args\\": %zu, \\"size_info\\": %zu}\\n", sizeof(fmha_bwd_args), sizeof(fmha_bwd_plan_info));
   return 0;
@@ -250,6 +250,23 @@ def test_bias_row_stride_may_be_any_value_at_least_sk():
     a.bias_stride[2] = 333
     a.dbias_stride[2] = 335
     assert status_of(a) == _lib.OK
+
+
+@pytest.mark.parametrize("p,expected", [(0.0, 0), (0.1, 0), (0.5, 0), (0.998, 0), (0.999, -2),
+                                          (1.0, -1), (-0.1, -1), (float("nan"), -1)])
+def test_dropout_probability_range(p, expected):
+    """p_drop in [0, 1) with a keep threshold round((1-p)*256) of at least 1."""
+    a = batch_args()
+    a.p_drop = p
+    assert status_of(a) == expected
+
+
+def test_dropout_uses_32_row_blocks_at_d128():
+    a = batch_args()
+    a.p_drop = 0.1
+    assert _lib.plan_query(a).tile_m == 32
+    a.p_drop = 0.001  # rounds to k = 256: no dropout
+    assert _lib.plan_query(a).tile_m == 64
 
 
 def test_bias_needs_batch_mode():
