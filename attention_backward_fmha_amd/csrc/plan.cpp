@@ -224,12 +224,16 @@ int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t el, bool forwar
   // their dQ contributions into one split, so the reduction reads 1/tiles_per_item of the
   // per-tile partials.  The largest of 4 and 2 that still leaves two work items per compute
   // unit of an MI355X (256 CUs) is used, so that the heaviest causal items do not set the
-  // makespan.
+  // makespan; without a mask, or with a window bounded on both sides, every tile carries
+  // about the same work and one item per compute unit suffices.
   p->tiles_per_item = 1;
   if (p->deterministic) {
     const int64_t heads = (int64_t)p->Hkv * p->B;
+    const bool even_work = a->mask_type == FMHA_MASK_NONE ||
+                           (a->mask_type == FMHA_MASK_WINDOW && a->window_left >= 0 && a->window_right >= 0);
+    const int64_t min_items = even_work ? 256 : 2 * 256;
     for (int t : {4, 2}) {
-      if ((int64_t)((p->n_kv_tiles + t - 1) / t) * heads >= 2 * 256) {
+      if ((int64_t)((p->n_kv_tiles + t - 1) / t) * heads >= min_items) {
         p->tiles_per_item = t;
         break;
       }

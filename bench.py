@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--only-mode", action="store_true",
                     help="time only --mode (profiling runs); by default both modes are timed")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--bias", choices=["none", "11ss", "1hss", "b1ss", "bhss"], default="none",
+                    help="add a seeded bf16 bias of this shape (and compute dbias)")
+    ap.add_argument("--dropout", type=float, default=0.0, help="dropout probability (Philox)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (steps times), "
                          "the reference kernel for scaling HBM byte counters")
@@ -64,6 +67,27 @@ def copy_probe(mib, steps):
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_mib": mib, "bytes_read_per_copy": n * 4,
                       "bytes_written_per_copy": n * 4, "copies": steps}))
+
+
+def prepare_thd_inputs(w, device):
+    """Ragged (THD) workload: seeded segment lengths (seed 3, uniform in [56, 2048]), seeded
+    Q, K, V, dO [T, H, d] (bf16); O and LSE from the device forward.  Returns the tensors and
+    the sequence-offset arguments of make_call."""
+    import torch
+    import attention_backward_fmha_amd as F
+    from attention_backward_fmha_amd import inputs as I
+
+    lens = I.ragged_lengths(3, w["total"], 56, 2048)
+    T, Hq, Hkv, dqk, dv = w["total"], w["Hq"], w["Hkv"], w["d_qk"], w["d_v"]
+    x = I.draw(w["seed"], [(T, Hq, dqk), (T, Hkv, dqk), (T, Hkv, dv), (T, Hq, dv)], w["sigmas"])
+    dev = {n: torch.from_numpy(x[n]).to(torch.bfloat16).to(device) for n in x}
+    ss = I.seqstart(lens)
+    seq = dict(cu_seqlens_q=torch.from_numpy(ss).to(device), cu_seqlens_k=torch.from_numpy(ss).to(device),
+               cu_seqlens_q_host=ss, cu_seqlens_k_host=ss)
+    scale = 1.0 / math.sqrt(dqk)
+    o, lse = F.fwd(dev["q"], dev["k"], dev["v"], scale=scale, mask_type=w["mask"], **seq)
+    torch.cuda.synchronize()
+    return dev["q"], dev["k"], dev["v"], o, lse, dev["do"], scale, seq, lens
 
 
 def prepare_inputs(w, device):
@@ -177,7 +201,27 @@ def main():
     w = I.WORKLOADS[args.workload]
     device = torch.device("cuda:0")
     torch.cuda.set_device(device)
-    q, k, v, o, lse, do, scale = prepare_inputs(w, device)
+    thd = "total" in w
+    seq, lens = {}, None
+    if thd:
+        q, k, v, o, lse, do, scale, seq, lens = prepare_thd_inputs(w, device)
+        if args.bias != "none":
+            sys.exit("a bias needs a batch (BSHD) workload")
+    else:
+        q, k, v, o, lse, do, scale = prepare_inputs(w, device)
+    extra = dict(seq)
+    if args.bias != "none":
+        bb = w["B"] if args.bias[0] == "b" else 1
+        bh = w["Hq"] if args.bias[1] == "h" else 1
+        gen = torch.Generator(device=device).manual_seed(77)
+        bias = torch.randn((bb, bh, w["Sq"], w["Sk"]), generator=gen, device=device).to(torch.bfloat16)
+        extra.update(bias=bias, dbias=torch.empty_like(bias))
+    if args.dropout > 0:
+        extra.update(dropout_p=args.dropout, philox_seed=1234, philox_offset=0)
+    if args.bias != "none" or args.dropout > 0:  # O and LSE of the same forward (device, with bias/dropout)
+        fkw = {n: extra[n] for n in extra if n not in ("dbias",)}
+        o, lse = F.fwd(q, k, v, scale=scale, mask_type=w["mask"], window=w.get("window", (-1, -1)), **fkw)
+        torch.cuda.synchronize()
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
@@ -187,7 +231,7 @@ def main():
     def time_mode(mode):
         det, acc = MODE_ARGS[mode]
         call = F.make_call(q, k, v, o, lse, do, dq, dk, dv, scale=scale, mask_type=w["mask"],
-                           window=w.get("window", (-1, -1)), deterministic=det, dq_acc_dtype=acc)
+                           window=w.get("window", (-1, -1)), deterministic=det, dq_acc_dtype=acc, **extra)
         plan = call.plan()
         ws = torch.empty(call.workspace_size(), dtype=torch.uint8, device=device)
 
@@ -224,8 +268,9 @@ def main():
         """The device forward (fmha_fwd_run) on the same inputs, into scratch outputs."""
         o2 = torch.empty_like(o)
         lse2 = torch.empty_like(lse)
+        fkw = {n: extra[n] for n in extra if n not in ("dbias",)}
         call = F.make_call(q, k, v, o2, lse2, None, None, None, None, scale=scale,
-                           mask_type=w["mask"], window=w.get("window", (-1, -1)))
+                           mask_type=w["mask"], window=w.get("window", (-1, -1)), **fkw)
         for _ in range(args.warmup):
             F._lib.fwd_run(call.args, sh)
         t0 = torch.cuda.Event(enable_timing=True)
@@ -270,11 +315,14 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": args.workload,
-            "B": w["B"], "Hq": w["Hq"], "Hkv": w["Hkv"], "Sq": w["Sq"], "Sk": w["Sk"],
-            "d_qk": w["d_qk"], "d_v": w["d_v"], "mask": w["mask"], "layout": "bshd",
+            "B": len(lens) if thd else w["B"], "Hq": w["Hq"], "Hkv": w["Hkv"],
+            "Sq": max(lens) if thd else w["Sq"], "Sk": max(lens) if thd else w["Sk"],
+            "d_qk": w["d_qk"], "d_v": w["d_v"], "mask": w["mask"], "window": w.get("window"),
+            "layout": "thd" if thd else "bshd", "segments": lens,
             "dq_accumulation": args.mode, "nsplits": plan.nsplits,
             "flops_per_step": flops, "pct_of_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
             "modes": modes,
+            "bias": args.bias, "dbias": args.bias != "none", "dropout_p": args.dropout,
             "forward": time_forward(flops),
         },
         "roofline": {
@@ -284,11 +332,11 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(main_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": measured_traffic(args.workload, args.mode),
+            "traffic": None if (args.bias != "none" or args.dropout > 0) else measured_traffic(args.workload, args.mode),
             "avg_launch_ms": round(main_ms, 4),
         },
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not thd:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out))
 

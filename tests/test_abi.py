@@ -288,6 +288,11 @@ def test_tiles_per_item_keeps_two_items_per_cu():
         assert info.nsplits == -(-tiles // want)
     a = batch_args(B=2, Hq=32, Hkv=32, Sq=4096, Sk=4096, mask=1, deterministic=0)
     assert _lib.plan_query(a).tiles_per_item == 1
+    # a two-sided window (even work per tile) needs one item per compute unit only
+    w = batch_args(B=1, Hq=32, Hkv=8, Sq=16384, Sk=16384, mask=3, window=(4096, 0))
+    assert _lib.plan_query(w).tiles_per_item == 4
+    c = batch_args(B=1, Hq=32, Hkv=8, Sq=16384, Sk=16384, mask=2)
+    assert _lib.plan_query(c).tiles_per_item == 2
 
 
 def test_scale_must_be_positive():
