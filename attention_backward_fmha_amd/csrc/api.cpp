@@ -112,6 +112,8 @@ fmha::KParams make_params(const fmha_bwd_args* a, const fmha::Plan& p, void* ws)
   if (p.has_dbias) {
     if (ws != nullptr) k.dbias_acc = (float*)((char*)ws + p.dbias_acc_offset);
     k.dbias = (uint16_t*)a->dbias;
+    k.dbias_direct = p.dbias_direct ? 1 : 0;
+    k.dbias_plane_bytes = p.dbias_plane_bytes;
     for (int i = 0; i < 3; ++i) k.dbias_s[i] = a->dbias_stride[i];
   }
   return k;

@@ -52,6 +52,8 @@ struct KParams {
   float* dbias_acc;  // workspace: full-shape dS, fp32 [B][Hq][Sq][Sk]; null without dbias
   uint16_t* dbias;   // output, [bias_b][bias_h][Sq][Sk] with strides dbias_s
   int64_t dbias_s[3];
+  int dbias_direct;    // BHSS dbias: bf16 dS straight into dbias (plane bytes below)
+  uint32_t dbias_plane_bytes;
   int drop_k;          // dropout: keep iff the element's random byte < drop_k (256 = off)
   float drop_scale;    // 256 / drop_k
   unsigned seed_lo, seed_hi, offset_lo;  // Philox key and the counter's offset word

@@ -527,6 +527,9 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
     const __amdgpu_buffer_rsrc_t rdb = buffer_rsrc(
         EXTRA && p.dbias_acc != nullptr ? p.dbias_acc + ((int64_t)b * p.Hq + hq) * p.Sq * p.Sk : nullptr,
         EXTRA && p.dbias_acc != nullptr ? (uint32_t)p.Sq * (uint32_t)p.Sk * 4u : 0u);
+    const __amdgpu_buffer_rsrc_t rdbb = buffer_rsrc(
+        EXTRA && p.dbias_direct ? p.dbias + (int64_t)b * p.dbias_s[0] + (int64_t)hq * p.dbias_s[1] : nullptr,
+        EXTRA && p.dbias_direct ? p.dbias_plane_bytes : 0u);
     f32x16 s_acc[MT];
     f32x16 dp_acc[MT];
 #pragma unroll
@@ -590,11 +593,13 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
           if constexpr (EXTRA) {
             // full-shape dS for dbias: every (row, key) of the block, masked pairs as 0; rows
             // past the plane are dropped by the range check, keys past the tile end skipped
-            if (p.dbias_acc != nullptr && key_ok)
+            const unsigned drow = (unsigned)(q0 + 32 * m + 8 * c + 4 * hi + e);
+            if (p.dbias_direct && key_ok)
+              __builtin_amdgcn_raw_buffer_store_b16(
+                  to_bf16_bits(dsv), rdbb, (int)((drow * (unsigned)p.dbias_s[2] + (unsigned)(key0 + key_l)) * 2u), 0, 0);
+            else if (p.dbias_acc != nullptr && key_ok)
               __builtin_amdgcn_raw_buffer_store_b32(
-                  __float_as_uint(dsv), rdb,
-                  ((unsigned)(q0 + 32 * m + 8 * c + 4 * hi + e) * (unsigned)p.Sk + (unsigned)(key0 + key_l)) * 4u,
-                  0, 0);
+                  __float_as_uint(dsv), rdb, (drow * (unsigned)p.Sk + (unsigned)(key0 + key_l)) * 4u, 0, 0);
           }
         }
       }
@@ -951,6 +956,15 @@ __global__ __launch_bounds__(256) void k_dbias_reduce(const KParams p) {
   qblocks_for_tile(mg, p.Sq, p.Sk, j0 / 128, p.tile_m, 128, &lo, &hi);  // j0..j0+3: one tile
   const int qb = i / p.tile_m;
   const bool seen = qb >= lo && qb <= hi;
+  if (p.dbias_direct) {  // written by the main kernel where seen; zeros elsewhere
+    if (!seen) {
+      uint16_t* dst = p.dbias + (int64_t)ob * p.dbias_s[0] + (int64_t)oh * p.dbias_s[1] + (int64_t)i * p.dbias_s[2] + j0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (j0 + u < p.Sk) dst[u] = 0;
+    }
+    return;
+  }
   const int b0 = p.bias_b == 1 ? 0 : ob, b1 = p.bias_b == 1 ? p.B : ob + 1;
   const int h0 = p.bias_h == 1 ? 0 : oh, h1 = p.bias_h == 1 ? p.Hq : oh + 1;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};

@@ -213,8 +213,9 @@ int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t el, bool forwar
       if (((uintptr_t)a->dbias & 1u) != 0 || ds[0] < 0 || ds[1] < 0 || ds[2] < a->Sk)
         return fail(FMHA_ERR_UNSUPPORTED, err, el,
                     "dbias must be 2-byte aligned with non-negative strides and row stride >= Sk");
-      if (((int64_t)a->Sq + 256) * a->Sk >= (int64_t(1) << 30))
-        return fail(FMHA_ERR_UNSUPPORTED, err, el, "dbias plane too large ((Sq + 256) * Sk >= 2^30)");
+      if (((int64_t)a->Sq + 256) * a->Sk >= (int64_t(1) << 30) ||
+          ((int64_t)a->Sq + 256) * ds[2] + a->Sk >= (int64_t(1) << 30))
+        return fail(FMHA_ERR_UNSUPPORTED, err, el, "dbias plane too large ((Sq + 256) * row stride >= 2^30)");
     }
   }
 
@@ -259,8 +260,14 @@ int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t el, bool forwar
   p->dq_acc_offset = align_up(p->lse2_offset + p->d_bytes, 256);
   p->dq_acc_bytes = p->dq_bf16 ? (int64_t)p->B * p->split_stride * 2
                                : (int64_t)p->nsplits * p->split_stride * 4;
+  // A full-shape dbias (no broadcast dimension) is dS itself: the main kernel writes it as
+  // bf16, and the reduce stage only fills the pairs it skipped with zeros.  Broadcast shapes
+  // sum the full-shape dS, kept in fp32 in the workspace.
+  p->dbias_direct = p->has_dbias && p->bias_b == p->B && p->bias_h == p->Hq;
+  p->dbias_plane_bytes = (p->has_dbias && a->Sq > 0 && a->Sk > 0)
+                             ? (uint32_t)((((int64_t)a->Sq - 1) * a->dbias_stride[2] + a->Sk) * 2) : 0u;
   p->dbias_acc_offset = align_up(p->dq_acc_offset + p->dq_acc_bytes, 256);
-  p->dbias_acc_bytes = p->has_dbias ? (int64_t)p->B * p->Hq * p->Sq * p->Sk * 4 : 0;
+  p->dbias_acc_bytes = p->has_dbias && !p->dbias_direct ? (int64_t)p->B * p->Hq * p->Sq * p->Sk * 4 : 0;
   p->workspace_bytes = align_up(p->dbias_acc_offset + p->dbias_acc_bytes, 256);
   if (p->workspace_bytes == 0) p->workspace_bytes = 256;
   return FMHA_OK;
