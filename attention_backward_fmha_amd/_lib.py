@@ -6,7 +6,7 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libfmha_bwd.so")
 
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 MASK_NONE = 0
 MASK_CAUSAL_TOP_LEFT = 1
@@ -129,6 +129,7 @@ class PlanInfo(ctypes.Structure):
         ("reserved", ctypes.c_int32),
         ("dbias_acc_offset", ctypes.c_int64),
         ("dbias_acc_bytes", ctypes.c_int64),
+        ("reduce_read_bytes", ctypes.c_int64),
     ]
 
     def as_dict(self):

@@ -241,6 +241,7 @@ int fmha_bwd_plan_query(const fmha_bwd_args* args, fmha_bwd_plan_info* info) {
   info->workspace_bytes = p.workspace_bytes;
   info->pairs = fmha::count_pairs(args);
   info->flops = 2.0 * (3.0 * p.d_qk + 2.0 * p.d_v) * (double)info->pairs;
+  info->reduce_read_bytes = fmha::reduce_read_bytes(args, p);
   return FMHA_OK;
 }
 

@@ -287,4 +287,35 @@ int64_t count_pairs(const fmha_bwd_args* a) {
   return pairs * a->Hq;
 }
 
+int64_t reduce_read_bytes(const fmha_bwd_args* a, const Plan& p) {
+  const bool group = a->seqstart_q_host != nullptr;
+  int64_t total = 0;
+  for (int b = 0; b < a->B; ++b) {
+    const int64_t lq = group ? (int64_t)a->seqstart_q_host[b + 1] - a->seqstart_q_host[b] : a->Sq;
+    const int64_t lk = group ? (int64_t)a->seqstart_k_host[b + 1] - a->seqstart_k_host[b] : a->Sk;
+    if (!p.deterministic) {  // one row-major split: the segment's rows
+      total += lq * p.d_qk * (p.dq_bf16 ? 2 : 4);
+      continue;
+    }
+    // per query block: the splits whose key tiles touch it (as k_dq_reduce finds them)
+    const MaskGeom g = mask_geom(a->mask_type, a->window_left, a->window_right, lq, lk);
+    const int64_t nblk = (lq + p.tile_m - 1) / p.tile_m;
+    const int ntiles = (int)((lk + p.tile_n - 1) / p.tile_n);
+    for (int64_t qb = 0; qb < nblk; ++qb) {
+      int jlo = -1, jhi = -1;
+      for (int j = 0; j < ntiles; ++j) {
+        int64_t lo, hi;
+        qblocks_for_tile(g, lq, lk, j, p.tile_m, p.tile_n, &lo, &hi);
+        if (qb >= lo && qb <= hi) {
+          if (jlo < 0) jlo = j;
+          jhi = j;
+        }
+      }
+      if (jlo >= 0)
+        total += (int64_t)(jhi / p.tiles_per_item - jlo / p.tiles_per_item + 1) * p.tile_m * p.d_qk * 4;
+    }
+  }
+  return total * a->Hq;
+}
+
 }  // namespace fmha

@@ -55,4 +55,7 @@ int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t err_len, bool f
 // Allowed (query, key) pairs over all heads and segments (FLOP accounting).
 int64_t count_pairs(const fmha_bwd_args* a);
 
+// Bytes of the dQ accumulator that the reduce stage reads (bandwidth accounting).
+int64_t reduce_read_bytes(const fmha_bwd_args* a, const Plan& p);
+
 }  // namespace fmha

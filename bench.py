@@ -236,20 +236,22 @@ def main():
         ws = torch.empty(call.workspace_size(), dtype=torch.uint8, device=device)
 
         def step(evs=None):
+            # events: before prepare, after prepare, after dot, after main, after reduce
+            rec = (lambda i: evs[i].record(stream)) if evs is not None else (lambda i: None)
+            rec(0)
             call.prepare(ws, sh)
+            rec(1)
             call.run(ws, sh, F.STAGE_DOT)
-            if evs is not None:
-                evs[0].record(stream)
+            rec(2)
             call.run(ws, sh, F.STAGE_MAIN)
-            if evs is not None:
-                evs[1].record(stream)
+            rec(3)
             call.run(ws, sh, F.STAGE_REDUCE)
+            rec(4)
 
         for _ in range(args.warmup):
             step()
         torch.cuda.synchronize()
-        kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
+        kev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -259,10 +261,11 @@ def main():
         t1.record(stream)
         torch.cuda.synchronize()
         ms = t0.elapsed_time(t1) / args.steps
-        main_ms = sum(a_.elapsed_time(b_) for a_, b_ in kev) / args.steps
+        main_ms = sum(e[2].elapsed_time(e[3]) for e in kev) / args.steps
+        stage_ms = [sum(e[i].elapsed_time(e[i + 1]) for e in kev) / args.steps for i in range(4)]
         del ws
         torch.cuda.empty_cache()
-        return ms, main_ms, plan
+        return ms, main_ms, plan, stage_ms
 
     def time_forward(bwd_flops):
         """The device forward (fmha_fwd_run) on the same inputs, into scratch outputs."""
@@ -287,16 +290,32 @@ def main():
         return {"ms_per_call": round(f_ms, 4), "tflops": round(f_flops / (f_ms * 1e-3) / 1e12, 2),
                 "pct_of_bf16_peak": round(100.0 * f_flops / (f_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
 
-    ms, main_ms, plan = time_mode(args.mode)
-    runs = [(args.mode, ms, main_ms, plan)]
+    ms, main_ms, plan, stage_ms = time_mode(args.mode)
+    runs = [(args.mode, ms, main_ms, plan, stage_ms)]
     if not args.only_mode:
         runs += [(m,) + time_mode(m) for m in MODES if m != args.mode]
     flops = plan.flops
     tflops = flops / (ms * 1e-3) / 1e12
     main_tflops = flops / (main_ms * 1e-3) / 1e12
     modes = {}
-    for mode, m_ms, m_main, m_plan in runs:
-        modes[mode] = {
+    # algorithmic bytes of the HBM-bound stages (achieved GB/s = bytes / stage time)
+    rows = int(plan.rows_q)
+    dot_bytes = rows * w["Hq"] * (2 * w["d_v"] * 2 + 4) + rows * w["Hq"] * 8  # O, dO, LSE in; D, L out
+    dq_bytes = rows * w["Hq"] * w["d_qk"] * 2
+
+    def stage_entry(m_plan, st):
+        red = m_plan.reduce_read_bytes + dq_bytes
+        out_ = {"prepare_ms": round(st[0], 4), "dot_ms": round(st[1], 4), "main_ms": round(st[2], 4),
+                "reduce_ms": round(st[3], 4),
+                "dot_GBps": round(dot_bytes / (st[1] * 1e-3) / 1e9, 1),
+                "reduce_GBps": round(red / (st[3] * 1e-3) / 1e9, 1),
+                "reduce_bytes": int(red)}
+        if m_plan.needs_zero:
+            out_["prepare_GBps"] = round(m_plan.dq_acc_bytes / (st[0] * 1e-3) / 1e9, 1)
+        return out_
+
+    for mode, m_ms, m_main, m_plan, m_st in runs:
+        modes[mode] = {"stages": stage_entry(m_plan, m_st),
             "value": round(flops / (m_ms * 1e-3) / 1e12, 2), "ms_per_step": round(m_ms, 4),
             "main_kernel_ms": round(m_main, 4), "nsplits": m_plan.nsplits}
 

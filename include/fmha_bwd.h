@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define FMHA_BWD_ABI_VERSION 5u
+#define FMHA_BWD_ABI_VERSION 6u
 
 #if defined(__GNUC__)
 #define FMHA_BWD_API __attribute__((visibility("default")))
@@ -230,7 +230,10 @@ typedef struct fmha_bwd_plan_info {
   int32_t dq_acc_elem_bytes; /* 4 (fp32 accumulator) or 2 (bf16) */
   int32_t reserved;
   int64_t dbias_acc_offset;  /* byte offset of the fp32 full-shape dS [B][Hq][Sq][Sk] (dbias) */
-  int64_t dbias_acc_bytes;   /* 0 without dbias */
+  int64_t dbias_acc_bytes;   /* 0 without dbias, or when dbias is full-shape (written directly) */
+  int64_t reduce_read_bytes; /* bytes of the dQ accumulator the reduce stage reads (the
+                                splits that touch each query block, or the atomic modes'
+                                segment rows): for achieved-bandwidth figures */
 } fmha_bwd_plan_info;
 /* Accumulator layout.  Atomic mode: one split, rows_q rows, row-major ([row][d_qk]), row of
    a query = its D/LSE row.  Deterministic mode: split s holds the sum of the partials of key

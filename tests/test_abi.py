@@ -60,6 +60,7 @@ int main(void) {
   F(q_stride) F(dv_stride) F(lse_stride) F(seqstart_q_padded_host) F(seqstart_k_padded_dev)
   F(dq_acc_dtype) F(bias) F(dbias_stride) F(bias_h) F(p_drop) F(philox_seed) F(philox_offset)
   G(nsplits) G(rows_q) G(workspace_bytes) G(flops) G(acc_rows) G(dq_acc_elem_bytes) G(dbias_acc_bytes)
+  G(reduce_read_bytes)
   printf("\\"size_args\\": %zu, \\"size_info\\": %zu}\\n", sizeof(fmha_bwd_args), sizeof(fmha_bwd_plan_info));
   return 0;
 }
@@ -77,7 +78,7 @@ int main(void) {
         if k.startswith("size"):
             continue
         cls = _lib.PlanInfo if k in ("nsplits", "rows_q", "workspace_bytes", "flops", "acc_rows",
-                                     "dq_acc_elem_bytes", "dbias_acc_bytes") else Args
+                                     "dq_acc_elem_bytes", "dbias_acc_bytes", "reduce_read_bytes") else Args
         assert getattr(cls, k).offset == v, k
 
 
@@ -276,6 +277,21 @@ def test_bias_needs_batch_mode():
     g.bias_b, g.bias_h = 1, 1
     g.bias_stride[2] = 8
     assert status_of(g) == _lib.ERR_UNSUPPORTED
+
+
+def test_reduce_read_bytes_closed_forms():
+    """Causal 4096 with 64-row blocks and items of 4 key tiles: block qb is touched by key tiles
+    0 .. qb/2, i.e. splits 0 .. qb/8, so 288 split reads of 32 KiB per head; the atomic modes
+    read the segment rows once (fp32, or bf16)."""
+    a = batch_args(B=2, Hq=32, Hkv=32, Sq=4096, Sk=4096, mask=1)
+    assert _lib.plan_query(a).reduce_read_bytes == 64 * 288 * 64 * 128 * 4
+    a = batch_args(B=2, Hq=32, Hkv=32, Sq=4096, Sk=4096, mask=1, deterministic=0)
+    assert _lib.plan_query(a).reduce_read_bytes == 2 * 32 * 4096 * 128 * 4
+    a.dq_acc_dtype = _lib.DQ_ACC_BF16
+    assert _lib.plan_query(a).reduce_read_bytes == 2 * 32 * 4096 * 128 * 2
+    n = batch_args(B=1, Hq=2, Hkv=2, Sq=256, Sk=512, mask=0)  # no mask: every split, 4 blocks
+    info = _lib.plan_query(n)
+    assert info.reduce_read_bytes == 2 * 4 * info.nsplits * 64 * 128 * 4
 
 
 def test_tiles_per_item_keeps_two_items_per_cu():
