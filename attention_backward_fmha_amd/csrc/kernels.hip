@@ -231,12 +231,37 @@ __device__ __forceinline__ void philox4x32_10(unsigned (&c)[4], unsigned k0, uns
   }
 }
 
+// 4x4 byte transpose: t[k] holds byte k of w[0], w[1], w[2], w[3] in its bytes 0..3.
+__device__ __forceinline__ void byte_transpose4(const unsigned (&w)[4], unsigned (&t)[4]) {
+  const unsigned a0 = __builtin_amdgcn_perm(w[1], w[0], 0x05010400u);  // w0.0 w1.0 w0.1 w1.1
+  const unsigned a1 = __builtin_amdgcn_perm(w[1], w[0], 0x07030602u);  // w0.2 w1.2 w0.3 w1.3
+  const unsigned b0 = __builtin_amdgcn_perm(w[3], w[2], 0x05010400u);  // w2.0 w3.0 w2.1 w3.1
+  const unsigned b1 = __builtin_amdgcn_perm(w[3], w[2], 0x07030602u);  // w2.2 w3.2 w2.3 w3.3
+  t[0] = __builtin_amdgcn_perm(b0, a0, 0x05040100u);
+  t[1] = __builtin_amdgcn_perm(b0, a0, 0x07060302u);
+  t[2] = __builtin_amdgcn_perm(b1, a1, 0x05040100u);
+  t[3] = __builtin_amdgcn_perm(b1, a1, 0x07060302u);
+}
+
+__device__ __forceinline__ unsigned sel4(const unsigned (&v)[4], unsigned i) {
+  return (i & 2u) ? ((i & 1u) ? v[3] : v[2]) : ((i & 1u) ? v[1] : v[0]);
+}
+
 // Value of lane (l ^ 1) and of lane (l ^ 2) (DPP quad permutations).
 __device__ __forceinline__ unsigned xor1(unsigned v) {
   return (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);
 }
 __device__ __forceinline__ unsigned xor2(unsigned v) {
   return (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);
+}
+__device__ __forceinline__ unsigned xor3(unsigned v) {
+  return (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0x1B, 0xF, 0xF, true);
+}
+// Value of lane (l ^ 16): v_permlane16_swap of v with itself leaves lane l ^ 16's value in
+// the second result for lanes with bit 4 clear and in the first for the others.
+__device__ __forceinline__ unsigned xor16(unsigned v, int lane) {
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return (lane & 16) ? r[0] : r[1];
 }
 
 // dS of one 32-query tile to LDS, one row per query.  On entry d[4c + e] is dS(query
@@ -323,11 +348,14 @@ __device__ __forceinline__ void stage_block(uint16_t* rm, uint16_t* tr, int RS,
 }
 
 // DQM: 0 = fp32 atomic adds, 1 = deterministic fp32 splits, 2 = packed bf16 atomic adds.
-// EXTRA: an additive bias and/or dropout.  The bias joins the logits (an absent bias reads
-// zeros from an empty resource), dS goes to the full-shape dbias scratch when that is
-// requested, and dropout's keep mask comes from Philox behind one uniform branch.
-template <int DQK, int DV, int TM_, int DQM, bool EXTRA>
+// X: bit 0 = an additive bias, bit 1 = dropout.  The bias joins the logits (an absent bias
+// reads zeros from an empty resource) and dS goes to dbias or its full-shape scratch when
+// that is requested; dropout's keep mask comes from Philox behind one uniform branch (so the
+// bias instance serves bias with or without dropout).
+template <int DQK, int DV, int TM_, int DQM, int X>
 __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
+  constexpr bool XB = (X & 1) != 0;
+  constexpr bool XD = (X & 2) != 0;
   constexpr bool DET = DQM == 1;
   using T = MainTile<DQK, DV, TM_>;
   constexpr int TM = T::TM, MT = T::MT, TN = T::TN, QS = T::QS, OS = T::OS, KS = T::KS,
@@ -509,8 +537,8 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
     // bias of the lane's (query, key) pairs, issued before the products that hide its latency;
     // register 16m + r pairs with the S/dP result register r of row tile m.  Rows past the
     // plane are outside the resource (zeros); keys past the tile end are masked below.
-    float bv[EXTRA ? MT * 16 : 1];
-    if constexpr (EXTRA) {
+    float bv[XB ? MT * 16 : 1];
+    if constexpr (XB) {
       const __amdgpu_buffer_rsrc_t rb =
           buffer_rsrc(p.bias + (int64_t)b * p.bias_s[0] + (int64_t)hq * p.bias_s[1], p.bias_plane_bytes);
       const int bs2 = (int)p.bias_s[2];
@@ -525,11 +553,11 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
         }
     }
     const __amdgpu_buffer_rsrc_t rdb = buffer_rsrc(
-        EXTRA && p.dbias_acc != nullptr ? p.dbias_acc + ((int64_t)b * p.Hq + hq) * p.Sq * p.Sk : nullptr,
-        EXTRA && p.dbias_acc != nullptr ? (uint32_t)p.Sq * (uint32_t)p.Sk * 4u : 0u);
+        XB && p.dbias_acc != nullptr ? p.dbias_acc + ((int64_t)b * p.Hq + hq) * p.Sq * p.Sk : nullptr,
+        XB && p.dbias_acc != nullptr ? (uint32_t)p.Sq * (uint32_t)p.Sk * 4u : 0u);
     const __amdgpu_buffer_rsrc_t rdbb = buffer_rsrc(
-        EXTRA && p.dbias_direct ? p.dbias + (int64_t)b * p.dbias_s[0] + (int64_t)hq * p.dbias_s[1] : nullptr,
-        EXTRA && p.dbias_direct ? p.dbias_plane_bytes : 0u);
+        XB && p.dbias_direct ? p.dbias + (int64_t)b * p.dbias_s[0] + (int64_t)hq * p.dbias_s[1] : nullptr,
+        XB && p.dbias_direct ? p.dbias_plane_bytes : 0u);
     f32x16 s_acc[MT];
     f32x16 dp_acc[MT];
 #pragma unroll
@@ -561,36 +589,66 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
       // ---- P, dS of tile m: register r holds query 32m + 8(r/4) + 4*hi + r%4 ----
       bf16x8 pa[2], sa[2];
       float ds32[16];
+      // dropout: the tile's rows 32m + 8c + 4hi + (0..3) of this lane's key take bytes
+      // (key % 4) of the Philox output for (key / 4, row / 4).  The four lanes of one key
+      // quad (l, l^1, l^16, l^17: key bits 0-1 are lane bits 4 and 0) need the same four
+      // outputs (c = 0..3); each computes one (c = its position t in the group), transposes
+      // it to four per-key words of 4 row bytes, and the group trades them.
+      unsigned zw[4] = {~0u, ~0u, ~0u, ~0u};  // per c: keep bytes of rows e = 0..3
+      if constexpr (XD) {
+        if (p.drop_k < 256) {
+          const unsigned kpos = (unsigned)(key0 + key_l);
+          const unsigned t = (unsigned)(lane & 1) | ((unsigned)(lane >> 4) & 1u) << 1;
+          unsigned w[4] = {kpos >> 2, (unsigned)(q0 + 32 * m + 8 * (int)t + 4 * hi) >> 2,
+                           (unsigned)(b * p.Hq + hq), p.offset_lo};
+          philox4x32_10(w, p.seed_lo, p.seed_hi);
+          unsigned tw[4];
+          byte_transpose4(w, tw);  // tw[k]: the 4 row bytes of key k % 4
+          // round u: the lane at group position t ^ u sends what this lane needs
+          const unsigned kswap0 = ((t >> 1) & 1u) | ((t & 1u) << 1);  // key byte of position t
+          unsigned r[4];
+          r[0] = sel4(tw, kswap0);
+          {
+            const unsigned pu = t ^ 1u, ku = ((pu >> 1) & 1u) | ((pu & 1u) << 1);
+            r[1] = xor1(sel4(tw, ku));
+          }
+          {
+            const unsigned pu = t ^ 2u, ku = ((pu >> 1) & 1u) | ((pu & 1u) << 1);
+            r[2] = xor16(sel4(tw, ku), lane);
+          }
+          {
+            const unsigned pu = t ^ 3u, ku = ((pu >> 1) & 1u) | ((pu & 1u) << 1);
+            r[3] = xor16(xor1(sel4(tw, ku)), lane);
+          }
+#pragma unroll
+          for (int c = 0; c < 4; ++c) zw[c] = sel4(r, t ^ (unsigned)c);
+        }
+      }
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int qr = 32 * m + 8 * c + 4 * hi;
         const f32x4 l4 = *(const f32x4*)&lse_lds[qr];
         const f32x4 d4 = *(const f32x4*)&dd_lds[qr];
-        // dropout: rows q0+qr .. +3 of this lane's key share one Philox output
         float zf[4] = {1.f, 1.f, 1.f, 1.f};
-        if constexpr (EXTRA) {
+        if constexpr (XD) {
           if (p.drop_k < 256) {
-            const unsigned kpos = (unsigned)(key0 + key_l);
-            unsigned w[4] = {kpos >> 2, (unsigned)(q0 + qr) >> 2, (unsigned)(b * p.Hq + hq), p.offset_lo};
-            philox4x32_10(w, p.seed_lo, p.seed_hi);
-            const unsigned sh = 8u * (kpos & 3u);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              zf[e] = ((w[e] >> sh) & 0xFFu) < (unsigned)p.drop_k ? p.drop_scale : 0.f;
+              zf[e] = ((zw[c] >> (8 * e)) & 0xFFu) < (unsigned)p.drop_k ? p.drop_scale : 0.f;
           }
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * c + e;
           float xl = s_acc[m][r] * p.scale_log2 - l4[e];
-          if constexpr (EXTRA) xl = __builtin_fmaf(bv[16 * m + r], kLog2e, xl);
+          if constexpr (XB) xl = __builtin_fmaf(bv[16 * m + r], kLog2e, xl);
           float pv = __builtin_amdgcn_exp2f(xl);
           pv = (unsigned)(t0 - (32 * m + 8 * c + e)) <= span ? pv : 0.f;
           const float dsv = pv * (dp_acc[m][r] * zf[e] - d4[e]);
           pa[c >> 1][(c & 1) * 4 + e] = (__bf16)(pv * zf[e]);
           sa[c >> 1][(c & 1) * 4 + e] = (__bf16)dsv;
           ds32[r] = dsv;
-          if constexpr (EXTRA) {
+          if constexpr (XB) {
             // full-shape dS for dbias: every (row, key) of the block, masked pairs as 0; rows
             // past the plane are dropped by the range check, keys past the tile end skipped
             const unsigned drow = (unsigned)(q0 + 32 * m + 8 * c + 4 * hi + e);
@@ -1007,8 +1065,12 @@ struct FwdTile {
   static_assert(KBLK % 64 == 0, "staging blocks of K must fill whole waves");
 };
 
-template <int DQK, int DV, bool EXTRA>
-__global__ __launch_bounds__(256, DQK <= 128 ? 2 : 1) void k_fwd(const KParams p) {
+template <int DQK, int DV, int X>
+// X: bit 0 = bias, bit 1 = dropout (all four combinations are instances: the bias-and-dropout
+// one does not fit two work groups per CU)
+__global__ __launch_bounds__(256, DQK <= 128 && X != 3 ? 2 : 1) void k_fwd(const KParams p) {
+  constexpr bool XB = (X & 1) != 0;
+  constexpr bool XD = (X & 2) != 0;
   using T = FwdTile<DQK, DV>;
   constexpr int TQ = T::TQ, TK = T::TK, KS = T::KS, VS = T::VS;
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[TK * KS];  // K tile, row-major
@@ -1142,8 +1204,8 @@ __global__ __launch_bounds__(256, DQK <= 128 ? 2 : 1) void k_fwd(const KParams p
     // bias of this lane's query row for its keys of the tile, issued before the products
     // (2-byte loads: the row stride may be any value >= Sk); rows past the plane read zeros,
     // keys past the end are masked
-    float bz[EXTRA ? 32 : 1];
-    if constexpr (EXTRA) {
+    float bz[XB ? 32 : 1];
+    if constexpr (XB) {
       const __amdgpu_buffer_rsrc_t rb =
           buffer_rsrc(p.bias + (int64_t)b * p.bias_s[0] + (int64_t)h * p.bias_s[1], p.bias_plane_bytes);
       const int rowoff = row * (int)p.bias_s[2];
@@ -1178,7 +1240,7 @@ __global__ __launch_bounds__(256, DQK <= 128 ? 2 : 1) void k_fwd(const KParams p
       for (int r = 0; r < 16; ++r) {
         const int ko = 32 * kb + 8 * (r >> 2) + (r & 3);
         float x = s[kb][r] * p.scale_log2;
-        if constexpr (EXTRA) x = __builtin_fmaf(bz[16 * kb + r], kLog2e, x);
+        if constexpr (XB) x = __builtin_fmaf(bz[16 * kb + r], kLog2e, x);
         s[kb][r] = (unsigned)(t0 + ko) <= span ? x : -__builtin_inff();
         mt = fmaxf(mt, s[kb][r]);
       }
@@ -1191,21 +1253,33 @@ __global__ __launch_bounds__(256, DQK <= 128 ? 2 : 1) void k_fwd(const KParams p
     bf16x8 pb[2][2];
     float ls = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb) {
+      // dropout (P in P V only; the running sum is of the full softmax): keys
+      // kt0 + 32kb + 8c + 4hi .. +3 of this lane's row take word (row % 4) of the Philox
+      // output for (key / 4, row / 4).  The four lanes of one row quad need the same four
+      // outputs (c = 0..3): each computes one (c = row % 4) and the quad trades words.
+      unsigned zw[4] = {~0u, ~0u, ~0u, ~0u};
+      if constexpr (XD) {
+        if (p.drop_k < 256) {
+          const unsigned t = (unsigned)(lane & 3);  // == row % 4
+          unsigned w[4] = {(unsigned)(kt0 + 32 * kb + 8 * (int)t + 4 * hi) >> 2, (unsigned)row >> 2,
+                           (unsigned)(b * p.Hq + h), p.offset_lo};
+          philox4x32_10(w, p.seed_lo, p.seed_hi);
+          // round u: the lane at quad position t ^ u sends word t of its output
+          const unsigned r[4] = {sel4(w, t), xor1(sel4(w, t ^ 1u)), xor2(sel4(w, t ^ 2u)),
+                                 xor3(sel4(w, t ^ 3u))};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) zw[c] = sel4(r, t ^ (unsigned)c);
+        }
+      }
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        // dropout (P in P V only; the running sum is of the full softmax): keys
-        // kt0 + 32kb + 8c + 4hi .. +3 of this lane's row share one Philox output word
         float zf[4] = {1.f, 1.f, 1.f, 1.f};
-        if constexpr (EXTRA) {
+        if constexpr (XD) {
           if (p.drop_k < 256) {
-            unsigned w[4] = {(unsigned)(kt0 + 32 * kb + 8 * c + 4 * hi) >> 2, (unsigned)row >> 2,
-                             (unsigned)(b * p.Hq + h), p.offset_lo};
-            philox4x32_10(w, p.seed_lo, p.seed_hi);
-            const unsigned word = (row & 2) ? ((row & 1) ? w[3] : w[2]) : ((row & 1) ? w[1] : w[0]);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              zf[e] = ((word >> (8 * e)) & 0xFFu) < (unsigned)p.drop_k ? p.drop_scale : 0.f;
+              zf[e] = ((zw[c] >> (8 * e)) & 0xFFu) < (unsigned)p.drop_k ? p.drop_scale : 0.f;
           }
         }
 #pragma unroll
@@ -1215,6 +1289,7 @@ __global__ __launch_bounds__(256, DQK <= 128 ? 2 : 1) void k_fwd(const KParams p
           pb[kb][c >> 1][(c & 1) * 4 + e] = (__bf16)(pv * zf[e]);
         }
       }
+    }
     l_run = l_run * alpha + ls;
     // O^T = alpha * O^T + V^T P^T (reduction step ks = 2kb + t covers transposed positions
     // 16ks .. 16ks + 15)
@@ -1277,39 +1352,49 @@ hipError_t launch_dot(const Plan& plan, const KParams& kp, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int DQK, int DV>
+static void launch_fwd_t(const Plan& plan, const KParams& kp, dim3 grid, hipStream_t stream) {
+  const int x = (plan.has_bias ? 1 : 0) | (plan.drop_k < 256 ? 2 : 0);
+  if (x == 3) hipLaunchKernelGGL((k_fwd<DQK, DV, 3>), grid, dim3(256), 0, stream, kp);
+  else if (x == 2) hipLaunchKernelGGL((k_fwd<DQK, DV, 2>), grid, dim3(256), 0, stream, kp);
+  else if (x == 1) hipLaunchKernelGGL((k_fwd<DQK, DV, 1>), grid, dim3(256), 0, stream, kp);
+  else hipLaunchKernelGGL((k_fwd<DQK, DV, 0>), grid, dim3(256), 0, stream, kp);
+}
+
 hipError_t launch_fwd(const Plan& plan, const KParams& kp, hipStream_t stream) {
   if (plan.B == 0 || plan.n_q_blocks == 0) return hipSuccess;
   const int64_t rows = (int64_t)plan.n_q_blocks * plan.tile_m;  // >= the longest segment
   const dim3 grid((unsigned)((rows + 127) / 128), (unsigned)plan.Hq, (unsigned)plan.B);
   if (plan.d_qk == 64) {
-    if (plan.has_bias || plan.drop_k < 256) hipLaunchKernelGGL((k_fwd<64, 64, true>), grid, dim3(256), 0, stream, kp);
-    else hipLaunchKernelGGL((k_fwd<64, 64, false>), grid, dim3(256), 0, stream, kp);
+    launch_fwd_t<64, 64>(plan, kp, grid, stream);
   } else if (plan.d_qk == 128) {
-    if (plan.has_bias || plan.drop_k < 256) hipLaunchKernelGGL((k_fwd<128, 128, true>), grid, dim3(256), 0, stream, kp);
-    else hipLaunchKernelGGL((k_fwd<128, 128, false>), grid, dim3(256), 0, stream, kp);
+    launch_fwd_t<128, 128>(plan, kp, grid, stream);
   } else {
-    if (plan.has_bias || plan.drop_k < 256) hipLaunchKernelGGL((k_fwd<192, 128, true>), grid, dim3(256), 0, stream, kp);
-    else hipLaunchKernelGGL((k_fwd<192, 128, false>), grid, dim3(256), 0, stream, kp);
+    launch_fwd_t<192, 128>(plan, kp, grid, stream);
   }
   return hipGetLastError();
 }
 
-// WITH_BIAS = false for tile shapes the plan never uses with a bias (not compiled with one)
+// WITH_BIAS = false for tile shapes the plan never uses with a bias (not compiled with one).
+// Instances: X = 0 (plain), 2 (dropout), 3 (bias, with or without dropout).
 template <int DQK, int DV, int TM, bool WITH_BIAS = true>
 static void launch_main_t(const Plan& plan, const KParams& kp, dim3 grid, hipStream_t stream) {
   const int mode = plan.deterministic ? 1 : (plan.dq_bf16 ? 2 : 0);
-  if constexpr (!WITH_BIAS) {
-    if (mode == 1) hipLaunchKernelGGL((k_bwd_main<DQK, DV, TM, 1, false>), grid, dim3(256), 0, stream, kp);
-    else if (mode == 2) hipLaunchKernelGGL((k_bwd_main<DQK, DV, TM, 2, false>), grid, dim3(256), 0, stream, kp);
-    else hipLaunchKernelGGL((k_bwd_main<DQK, DV, TM, 0, false>), grid, dim3(256), 0, stream, kp);
-  } else if (plan.has_bias || plan.drop_k < 256) {
-    if (mode == 1) hipLaunchKernelGGL((k_bwd_main<DQK, DV, TM, 1, true>), grid, dim3(256), 0, stream, kp);
-    else if (mode == 2) hipLaunchKernelGGL((k_bwd_main<DQK, DV, TM, 2, true>), grid, dim3(256), 0, stream, kp);
-    else hipLaunchKernelGGL((k_bwd_main<DQK, DV, TM, 0, true>), grid, dim3(256), 0, stream, kp);
+  const bool drop = plan.drop_k < 256;
+  if (WITH_BIAS && plan.has_bias) {
+    if constexpr (WITH_BIAS) {
+      if (mode == 1) hipLaunchKernelGGL((k_bwd_main<DQK, DV, TM, 1, 3>), grid, dim3(256), 0, stream, kp);
+      else if (mode == 2) hipLaunchKernelGGL((k_bwd_main<DQK, DV, TM, 2, 3>), grid, dim3(256), 0, stream, kp);
+      else hipLaunchKernelGGL((k_bwd_main<DQK, DV, TM, 0, 3>), grid, dim3(256), 0, stream, kp);
+    }
+  } else if (drop) {
+    if (mode == 1) hipLaunchKernelGGL((k_bwd_main<DQK, DV, TM, 1, 2>), grid, dim3(256), 0, stream, kp);
+    else if (mode == 2) hipLaunchKernelGGL((k_bwd_main<DQK, DV, TM, 2, 2>), grid, dim3(256), 0, stream, kp);
+    else hipLaunchKernelGGL((k_bwd_main<DQK, DV, TM, 0, 2>), grid, dim3(256), 0, stream, kp);
   } else {
-    if (mode == 1) hipLaunchKernelGGL((k_bwd_main<DQK, DV, TM, 1, false>), grid, dim3(256), 0, stream, kp);
-    else if (mode == 2) hipLaunchKernelGGL((k_bwd_main<DQK, DV, TM, 2, false>), grid, dim3(256), 0, stream, kp);
-    else hipLaunchKernelGGL((k_bwd_main<DQK, DV, TM, 0, false>), grid, dim3(256), 0, stream, kp);
+    if (mode == 1) hipLaunchKernelGGL((k_bwd_main<DQK, DV, TM, 1, 0>), grid, dim3(256), 0, stream, kp);
+    else if (mode == 2) hipLaunchKernelGGL((k_bwd_main<DQK, DV, TM, 2, 0>), grid, dim3(256), 0, stream, kp);
+    else hipLaunchKernelGGL((k_bwd_main<DQK, DV, TM, 0, 0>), grid, dim3(256), 0, stream, kp);
   }
 }
 

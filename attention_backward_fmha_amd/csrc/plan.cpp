@@ -109,9 +109,9 @@ int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t el, bool forwar
   if (const char* e = getenv("FMHA_BWD_TILE_M")) {  // tuning knob: 32 or 64 for d_qk = 128
     if (a->d_qk == 128 && (atoi(e) == 32 || atoi(e) == 64)) p->tile_m = atoi(e);
   }
-  // with a bias or dropout, d_qk = 128 takes 32-row blocks too: the extra registers of
-  // 64-row blocks do not fit beside the rest of the main kernel's registers
-  if ((a->bias != nullptr || p->drop_k < 256) && a->d_qk == 128) p->tile_m = 32;
+  // with a bias, d_qk = 128 takes 32-row blocks too: the bias registers of 64-row blocks do
+  // not fit beside the rest of the main kernel's registers (dropout alone does fit)
+  if (a->bias != nullptr && a->d_qk == 128) p->tile_m = 32;
   p->tile_n = 128;
   p->deterministic = a->deterministic == 1;
   p->dq_bf16 = a->dq_acc_dtype == FMHA_DQ_ACC_BF16;

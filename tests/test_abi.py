@@ -263,12 +263,14 @@ def test_dropout_probability_range(p, expected):
     assert status_of(a) == expected
 
 
-def test_dropout_uses_32_row_blocks_at_d128():
+def test_block_rows_with_bias_and_dropout_at_d128():
+    """A bias at d_qk = 128 takes 32-row query blocks; dropout alone keeps 64."""
     a = batch_args()
     a.p_drop = 0.1
-    assert _lib.plan_query(a).tile_m == 32
-    a.p_drop = 0.001  # rounds to k = 256: no dropout
     assert _lib.plan_query(a).tile_m == 64
+    a = _with_bias(batch_args(), 1, 1, dbias=False)
+    a.p_drop = 0.1
+    assert _lib.plan_query(a).tile_m == 32
 
 
 def test_bias_needs_batch_mode():

@@ -168,3 +168,24 @@ def test_same_seed_same_bits_other_offset_other_result():
     for u, w in zip(a, b):
         assert np.array_equal(u, w)
     assert not np.array_equal(a[2], c[2])
+
+
+def test_forward_with_bias_and_dropout_matches_oracle():
+    import torch
+    import oracle
+    import attention_backward_fmha_amd as F
+    x = make_inputs(9106, B=2, Sq=200, Sk=333, Hq=4, Hkv=2, d_qk=128, d_v=128)
+    rng = np.random.default_rng(9107)
+    bias = I.round_bf16(rng.standard_normal((2, 1, 200, 333)).astype(np.float32))
+    drop = (0.25, 31337, 11)
+    o_ref, lse_ref = oracle.forward(x["q"], x["k"], x["v"], scale=0.088, mask_type=BR, bias=bias,
+                                    dropout=drop)
+    o, lse = F.fwd(to_dev_bf16(x["q"]), to_dev_bf16(x["k"]), to_dev_bf16(x["v"]), scale=0.088,
+                   mask_type=BR, bias=to_dev_bf16(bias), dropout_p=drop[0], philox_seed=drop[1],
+                   philox_offset=drop[2])
+    torch.cuda.synchronize()
+    assert_close("o", o.float().cpu().numpy().astype(np.float64), o_ref)
+    lse = lse.cpu().numpy().astype(np.float64)
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(np.isfinite(lse), fin)
+    assert np.abs(lse[fin] - lse_ref[fin]).max() <= 1e-3
