@@ -105,3 +105,32 @@ def assert_grads_close(got, ref, sq=None, sk=None, label=""):
                 a0, a1 = int(s[b]), int(s[b + 1])
                 if a1 > a0:
                     assert_close("%s%s[segment %d]" % (label, n, b), g[a0:a1], r[a0:a1])
+
+
+
+def single_key_floors(x, o, scale, allowed, group):
+    """Error floors of dQ and dK where every query row has at most one allowed key.
+
+    There dS = P (dP - D) vanishes exactly, so the exact dQ and dK are 0.  But the backward
+    gets O rounded to bf16 and computes D_i = dO_i . O~_i, so each such row leaves
+    delta_i = |dO_i . (O_i - O~_i)| in dS.  This gives |dQ_i| <= scale * delta_i * max|K| and
+    |dK_j| <= scale * (sum over the rows i that attend j and the query heads of j's group of
+    delta_i) * max|Q|.  x, o: one segment, arrays [rows, H, d]; allowed: [Lq, Lk] bool.
+    Returns the floors, twice the bound plus fp32 noise."""
+    ot = I.round_bf16(np.asarray(o, np.float32)).astype(np.float64)
+    delta = np.abs((np.asarray(x["do"], np.float64) * (np.asarray(o, np.float64) - ot)).sum(-1))  # [Lq, Hq]
+    kmax = float(np.abs(x["k"]).max()) if np.size(x["k"]) else 0.0
+    qmax = float(np.abs(x["q"]).max()) if np.size(x["q"]) else 0.0
+    fq = 2 * scale * (float(delta.max()) if delta.size else 0.0) * kmax + 1e-5
+    hq = delta.shape[1] if delta.ndim == 2 else 1
+    per_key = np.zeros(allowed.shape[1])
+    for h in range(hq):
+        per_key += allowed.T.astype(np.float64) @ delta[:, h]  # summed over the group's heads too
+    fk = 2 * scale * (float(per_key.max()) if per_key.size else 0.0) * qmax + 1e-5
+    return fq, fk
+
+
+def assert_vanishing(name, got, floor):
+    assert np.all(np.isfinite(got)), name
+    m = float(np.abs(got).max()) if np.size(got) else 0.0
+    assert m <= floor, "%s: exact value 0 (one key per row), max|got| = %.3g > floor %.3g" % (name, m, floor)
