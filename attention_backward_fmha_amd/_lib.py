@@ -20,6 +20,7 @@ OK = 0
 ERR_INVALID_ARG = -1
 ERR_UNSUPPORTED = -2
 ERR_WORKSPACE_TOO_SMALL = -3
+ERR_PLAN_MISMATCH = -4
 ERR_HIP = -5
 
 STAGE_DOT = 1

@@ -16,6 +16,11 @@ bool log_enabled() {
   return e && e[0] == '1';
 }
 
+bool debug_enabled() {
+  const char* e = getenv("FMHA_BWD_DEBUG");
+  return e && e[0] == '1';
+}
+
 int report(int status, const char* where, const char* msg) {
   if (status != FMHA_OK && log_enabled()) fprintf(stderr, "[fmha_bwd] %s: %s\n", where, msg);
   return status;
@@ -153,6 +158,9 @@ int fmha_bwd_prepare_workspace(const fmha_bwd_args* args, void* ws, size_t bytes
   st = check_ws(p, ws, bytes, "prepare_workspace");
   if (st != FMHA_OK) return st;
   log_plan(p, "prepare_workspace");
+  st = hip_status(fmha::launch_header((uint64_t*)ws, fmha::kWorkspaceMagic, p.fingerprint, (hipStream_t)stream),
+                  "prepare_workspace");
+  if (st != FMHA_OK) return st;
   if (p.needs_zero) {
     return hip_status(fmha::launch_zero((float*)((char*)ws + p.dq_acc_offset), p.dq_acc_bytes / 4,
                                         (hipStream_t)stream),
@@ -172,6 +180,16 @@ int fmha_bwd_run_stages(const fmha_bwd_args* args, void* ws, size_t bytes, int s
   log_plan(p, "run");
   const fmha::KParams kp = make_params(args, p, ws);
   hipStream_t s = (hipStream_t)stream;
+  if (debug_enabled()) {  // the workspace must have been prepared for these very arguments
+    uint64_t hdr[2] = {0, 0};
+    st = hip_status(hipStreamSynchronize(s), "run: debug header check");
+    if (st != FMHA_OK) return st;
+    st = hip_status(hipMemcpy(hdr, ws, sizeof hdr, hipMemcpyDeviceToHost), "run: debug header check");
+    if (st != FMHA_OK) return st;
+    if (hdr[0] != fmha::kWorkspaceMagic || hdr[1] != p.fingerprint)
+      return report(FMHA_ERR_PLAN_MISMATCH, "run",
+                    "the workspace was not prepared for these arguments (header fingerprint differs)");
+  }
   if (stages & FMHA_STAGE_DOT) {
     st = hip_status(fmha::launch_dot(p, kp, s), "run: dot stage");
     if (st != FMHA_OK) return st;
@@ -212,6 +230,7 @@ const char* fmha_bwd_status_string(int status) {
     case FMHA_ERR_UNSUPPORTED: return "FMHA_ERR_UNSUPPORTED";
     case FMHA_ERR_WORKSPACE_TOO_SMALL: return "FMHA_ERR_WORKSPACE_TOO_SMALL";
     case FMHA_ERR_HIP: return "FMHA_ERR_HIP";
+    case FMHA_ERR_PLAN_MISMATCH: return "FMHA_ERR_PLAN_MISMATCH";
     default: return "unknown fmha_bwd status";
   }
 }

@@ -65,5 +65,8 @@ hipError_t launch_main(const Plan& plan, const KParams& kp, hipStream_t stream);
 hipError_t launch_reduce(const Plan& plan, const KParams& kp, hipStream_t stream);
 hipError_t launch_dbias(const Plan& plan, const KParams& kp, hipStream_t stream);
 hipError_t launch_zero(float* ptr, int64_t count, hipStream_t stream);
+// Workspace header: magic value and plan fingerprint at ws[0], ws[1] (one vector store each).
+hipError_t launch_header(uint64_t* ws, uint64_t magic, uint64_t fingerprint, hipStream_t stream);
+constexpr uint64_t kWorkspaceMagic = 0x31445742414d4846ull;  // bytes "FHMABWD1"
 
 }  // namespace fmha

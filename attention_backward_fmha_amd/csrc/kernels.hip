@@ -1331,6 +1331,13 @@ __global__ __launch_bounds__(256, DQK <= 128 && X != 3 ? 2 : 1) void k_fwd(const
   }
 }
 
+__global__ __launch_bounds__(64) void k_header(uint64_t* ws, uint64_t magic, uint64_t fingerprint) {
+  if (threadIdx.x == 0) {
+    ws[0] = magic;
+    ws[1] = fingerprint;
+  }
+}
+
 __global__ __launch_bounds__(256) void k_zero(float* ptr, int64_t n4) {
   const int64_t stride = (int64_t)gridDim.x * 256;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride)
@@ -1445,6 +1452,11 @@ hipError_t launch_dbias(const Plan& plan, const KParams& kp, hipStream_t stream)
   const dim3 grid((unsigned)(((plan.Sk + 1023) / 1024) * (int64_t)plan.Sq), (unsigned)plan.bias_h,
                   (unsigned)plan.bias_b);
   hipLaunchKernelGGL(k_dbias_reduce, grid, dim3(256), 0, stream, kp);
+  return hipGetLastError();
+}
+
+hipError_t launch_header(uint64_t* ws, uint64_t magic, uint64_t fingerprint, hipStream_t stream) {
+  hipLaunchKernelGGL(k_header, dim3(1), dim3(64), 0, stream, ws, magic, fingerprint);
   return hipGetLastError();
 }
 

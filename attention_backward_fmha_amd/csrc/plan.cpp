@@ -1,6 +1,7 @@
 // plan.cpp -- argument validation and workspace layout (host only).
 //
 // Workspace layout (byte offsets 256-aligned):
+//   header  2 x uint64 (magic, plan fingerprint) written by prepare; 256 bytes
 //   D       fp32 [Hq][rows_q]                     rowsum(dO * O) from the first stage
 //   L       fp32 [Hq][rows_q]                     LSE * log2(e), also from the first stage
 //   dq_acc  fp32 [nsplits][Hq][acc_rows][d_qk]    dQ partials (deterministic: split s = key
@@ -38,6 +39,21 @@ int fail(int status, char* err, size_t len, const char* msg) {
 }
 
 int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+constexpr int64_t kHeaderBytes = 256;
+
+// FNV-1a, 64 bit, over the bytes of each value in turn.
+struct Fnv {
+  uint64_t h = 0xcbf29ce484222325ull;
+  void add(const void* p, size_t n) {
+    const unsigned char* c = (const unsigned char*)p;
+    for (size_t i = 0; i < n; ++i) {
+      h ^= c[i];
+      h *= 0x100000001b3ull;
+    }
+  }
+  template <class T> void v(T x) { add(&x, sizeof x); }
+};
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -254,9 +270,9 @@ int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t el, bool forwar
   if (p->dq_bf16) p->acc_rows = align_up(max_lq, 16);  // one slot per (segment, head)
   p->head_stride = p->acc_rows * p->d_qk;
   p->split_stride = (int64_t)p->Hq * p->head_stride;
-  p->d_offset = 0;
+  p->d_offset = kHeaderBytes;
   p->d_bytes = (int64_t)p->Hq * p->rows_q * 4;
-  p->lse2_offset = align_up(p->d_bytes, 256);
+  p->lse2_offset = align_up(p->d_offset + p->d_bytes, 256);
   p->dq_acc_offset = align_up(p->lse2_offset + p->d_bytes, 256);
   p->dq_acc_bytes = p->dq_bf16 ? (int64_t)p->B * p->split_stride * 2
                                : (int64_t)p->nsplits * p->split_stride * 4;
@@ -269,6 +285,23 @@ int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t el, bool forwar
   p->dbias_acc_offset = align_up(p->dq_acc_offset + p->dq_acc_bytes, 256);
   p->dbias_acc_bytes = p->has_dbias && !p->dbias_direct ? (int64_t)p->B * p->Hq * p->Sq * p->Sk * 4 : 0;
   p->workspace_bytes = align_up(p->dbias_acc_offset + p->dbias_acc_bytes, 256);
+  // what a run reads from the workspace depends on exactly these (and the segment offsets)
+  Fnv f;
+  for (int64_t x : {(int64_t)p->B, (int64_t)p->Hq, (int64_t)p->Hkv, (int64_t)p->Sq, (int64_t)p->Sk,
+                    (int64_t)p->d_qk, (int64_t)p->d_v, (int64_t)p->tile_m, (int64_t)p->tile_n,
+                    (int64_t)p->tiles_per_item, (int64_t)p->nsplits, (int64_t)p->deterministic,
+                    (int64_t)p->dq_bf16, (int64_t)p->group_mode, p->rows_q, p->acc_rows,
+                    (int64_t)p->acc_pad, p->d_offset, p->lse2_offset, p->dq_acc_offset,
+                    p->dq_acc_bytes, p->dbias_acc_offset, p->dbias_acc_bytes, p->workspace_bytes,
+                    (int64_t)a->mask_type, (int64_t)a->window_left, (int64_t)a->window_right})
+    f.v(x);
+  if (group && a->B > 0) {
+    f.add(a->seqstart_q_host, sizeof(int32_t) * (a->B + 1));
+    f.add(a->seqstart_k_host, sizeof(int32_t) * (a->B + 1));
+    if (a->seqstart_q_padded_host) f.add(a->seqstart_q_padded_host, sizeof(int32_t) * (a->B + 1));
+    if (a->seqstart_k_padded_host) f.add(a->seqstart_k_padded_host, sizeof(int32_t) * (a->B + 1));
+  }
+  p->fingerprint = f.h;
   if (p->workspace_bytes == 0) p->workspace_bytes = 256;
   return FMHA_OK;
 }

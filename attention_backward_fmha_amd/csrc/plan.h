@@ -42,6 +42,7 @@ struct Plan {
   uint32_t bias_plane_bytes;  // bytes of one (batch, head) bias plane the kernels may read
   int64_t dbias_acc_offset, dbias_acc_bytes;  // fp32 [B][Hq][Sq][Sk] full-shape dS
   int drop_k;            // dropout keep threshold on a random byte (256 = no dropout)
+  uint64_t fingerprint;  // FNV-1a of every layout quantity and the host seqstart arrays
   bool dbias_direct;     // full-shape (BHSS) dbias: the main kernel writes it directly
   uint32_t dbias_plane_bytes;
 };

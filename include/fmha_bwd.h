@@ -96,6 +96,8 @@ enum fmha_status {
   FMHA_ERR_INVALID_ARG = -1,          /* bad shape, pointer, stride, mask or seqstart */
   FMHA_ERR_UNSUPPORTED = -2,          /* valid but not built: head dims, alignment */
   FMHA_ERR_WORKSPACE_TOO_SMALL = -3,  /* workspace_bytes below fmha_bwd_workspace_size */
+  FMHA_ERR_PLAN_MISMATCH = -4,        /* FMHA_BWD_DEBUG=1 only: the workspace was prepared for
+                                         other arguments (plan fingerprint in its header) */
   FMHA_ERR_HIP = -5                   /* a HIP runtime call or kernel launch failed */
 };
 
@@ -182,13 +184,20 @@ typedef struct fmha_bwd_args {
    allocation, no synchronisation; device pointers are not dereferenced. */
 FMHA_BWD_API int fmha_bwd_workspace_size(const fmha_bwd_args* args, size_t* bytes);
 
-/* Initialise the workspace on `stream` (a hipStream_t; NULL = the default stream).  Atomic
-   modes (fp32 and bf16) zero the dQ accumulator; deterministic mode needs no initialisation
-   (every partial the reduction reads is written by the run).  Asynchronous. */
+/* Initialise the workspace on `stream` (a hipStream_t; NULL = the default stream): write its
+   header (a magic value and a fingerprint of the plan: every size, offset and split count and
+   the host seqstart arrays), and in the atomic modes (fp32 and bf16) zero the dQ
+   accumulator; deterministic mode needs no other initialisation (every partial the reduction
+   reads is written by the run).  Asynchronous; no memset nodes (graph capture safe).  Must
+   precede every fmha_bwd_run. */
 FMHA_BWD_API int fmha_bwd_prepare_workspace(const fmha_bwd_args* args, void* workspace,
                                size_t workspace_bytes, void* stream);
 
-/* Enqueue the three stages on `stream`.  Asynchronous; returns after the launches. */
+/* Enqueue the three stages on `stream`.  Asynchronous; returns after the launches.  With
+   FMHA_BWD_DEBUG=1 in the environment it first synchronizes `stream`, reads the workspace
+   header back and returns FMHA_ERR_PLAN_MISMATCH if prepare ran for other arguments (the
+   sizing/run disagreement of "[ROCm] Fix THD/ragged dQ backward on the bf16 dq_shuffle path
+   (gfx950)", Root cause); without it the header is not read. */
 FMHA_BWD_API int fmha_bwd_run(const fmha_bwd_args* args, void* workspace, size_t workspace_bytes,
                  void* stream);
 
@@ -219,7 +228,8 @@ typedef struct fmha_bwd_plan_info {
   int32_t tiles_per_item;  /* key tiles per main-kernel work item (deterministic split) */
   int64_t rows_q;          /* T_q: B*Sq (batch), seqstart_q[B] (group) or the padded q
                               offsets' last entry (padded group) */
-  int64_t d_offset;        /* byte offset of D = rowsum(dO*O), fp32 [Hq][rows_q] */
+  int64_t d_offset;        /* byte offset of D = rowsum(dO*O), fp32 [Hq][rows_q]; bytes 0..255
+                              of the workspace hold its header (magic, plan fingerprint) */
   int64_t dq_acc_offset;   /* byte offset of the fp32 accumulator [nsplits][Hq][acc_rows][d_qk] */
   int64_t dq_acc_bytes;
   int64_t workspace_bytes; /* == fmha_bwd_workspace_size */

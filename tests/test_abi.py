@@ -146,6 +146,14 @@ def test_workspace_size_and_plan_agree():
         assert info.nsplits <= -(-333 // 16)
 
 
+def test_workspace_starts_with_its_header():
+    """Bytes 0..255 hold the header prepare writes; D follows, then L, the accumulator."""
+    info = _lib.plan_query(batch_args())
+    assert info.d_offset == 256
+    assert info.dq_acc_offset >= 256 + 2 * 4 * 2 * 200 * 4  # D and L: [Hq][rows] fp32 each
+    assert _lib.status_string(_lib.ERR_PLAN_MISMATCH) == "FMHA_ERR_PLAN_MISMATCH"
+
+
 def test_group_mode_uses_physical_rows():
     lens = [100, 80, 76]
     a = group_args(lens, lens)
