@@ -263,9 +263,24 @@ def main():
         ms = t0.elapsed_time(t1) / args.steps
         main_ms = sum(e[2].elapsed_time(e[3]) for e in kev) / args.steps
         stage_ms = [sum(e[i].elapsed_time(e[i + 1]) for e in kev) / args.steps for i in range(4)]
+        cold = None
+        if mode == args.mode:
+            # cold L2/MALL: overwrite a 512 MiB scratch (twice the MALL) before each step
+            flush = torch.empty(512 << 20, dtype=torch.uint8, device=device)
+            times = []
+            for _ in range(min(args.steps, 10)):
+                flush.fill_(1)
+                a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a_.record(stream)
+                step()
+                b_.record(stream)
+                torch.cuda.synchronize()
+                times.append(a_.elapsed_time(b_))
+            cold = sorted(times)[len(times) // 2]
+            del flush
         del ws
         torch.cuda.empty_cache()
-        return ms, main_ms, plan, stage_ms
+        return ms, main_ms, plan, stage_ms, cold
 
     def time_forward(bwd_flops):
         """The device forward (fmha_fwd_run) on the same inputs, into scratch outputs."""
@@ -290,10 +305,18 @@ def main():
         return {"ms_per_call": round(f_ms, 4), "tflops": round(f_flops / (f_ms * 1e-3) / 1e12, 2),
                 "pct_of_bf16_peak": round(100.0 * f_flops / (f_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
 
-    ms, main_ms, plan, stage_ms = time_mode(args.mode)
+    ms, main_ms, plan, stage_ms, cold_ms = time_mode(args.mode)
     runs = [(args.mode, ms, main_ms, plan, stage_ms)]
     if not args.only_mode:
-        runs += [(m,) + time_mode(m) for m in MODES if m != args.mode]
+        runs += [(m,) + time_mode(m)[:4] for m in MODES if m != args.mode]
+    # host-side planning (validation, tiles, workspace map) per call
+    pcall = F.make_call(q, k, v, o, lse, do, dq, dk, dv, scale=scale, mask_type=w["mask"],
+                        window=w.get("window", (-1, -1)), deterministic=MODE_ARGS[args.mode][0],
+                        dq_acc_dtype=MODE_ARGS[args.mode][1], **extra)
+    t_p = time.perf_counter()
+    for _ in range(200):
+        pcall.workspace_size()
+    plan_us = (time.perf_counter() - t_p) / 200 * 1e6
     flops = plan.flops
     tflops = flops / (ms * 1e-3) / 1e12
     main_tflops = flops / (main_ms * 1e-3) / 1e12
@@ -340,6 +363,9 @@ def main():
             "layout": "thd" if thd else "bshd", "segments": lens,
             "dq_accumulation": args.mode, "nsplits": plan.nsplits,
             "flops_per_step": flops, "pct_of_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+            "cold_cache_ms_per_step": round(cold_ms, 4) if cold_ms else None,
+            "cold_cache_tflops": round(flops / (cold_ms * 1e-3) / 1e12, 2) if cold_ms else None,
+            "host_plan_us": round(plan_us, 2),
             "modes": modes,
             "bias": args.bias, "dbias": args.bias != "none", "dropout_p": args.dropout,
             "forward": time_forward(flops),
