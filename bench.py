@@ -154,11 +154,23 @@ def cpu_baseline(w, budget_s):
     (batch, query head) problems of the same shape and mask, as many as fit the time budget."""
     import oracle
     from attention_backward_fmha_amd import inputs as I
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+        info = threadpool_info()
+        threads = max([t.get("num_threads", 1) for t in info] or [1])
+        blas = ", ".join(sorted({"%s %s" % (t.get("internal_api", "?"), t.get("version", "")) for t in info
+                                 if t.get("user_api") == "blas"})) or blas
     except Exception:  # pragma: no cover
         threads = os.cpu_count()
+    cpu_model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:  # pragma: no cover
+        pass
     Sq, Sk, dqk, dv = w["Sq"], w["Sk"], w["d_qk"], w["d_v"]
     x = I.draw(w["seed"] + 100, [(1, Sq, 1, dqk), (1, Sk, 1, dqk), (1, Sk, 1, dv), (1, Sq, 1, dv)],
                w["sigmas"])
@@ -178,6 +190,8 @@ def cpu_baseline(w, budget_s):
         "value": flops_per * done / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
+        "cpu_model": cpu_model,
+        "blas": blas,
         "kind": "oracle",
         "sample": "%d repetitions of one (batch, head) problem of the workload (Sq=%d, Sk=%d, d=%d, "
                   "same mask; the workload has %d such problems), fp64 numpy, %.1f s"
