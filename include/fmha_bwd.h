@@ -1,14 +1,17 @@
 /*
  * fmha_bwd.h -- C ABI of the MI355X (gfx950) fused multi-head attention backward.
  *
- * Computes dQ, dK, dV of softmax attention O = softmax(scale * Q K^T + mask) V from Q, K, V,
- * the forward output O, its gradient dO and the forward log-sum-exp.  Three device stages run
- * on the caller's stream:
+ * Computes dQ, dK, dV (and optionally dbias) of softmax attention
+ * O = softmax(scale * Q K^T + bias + mask) V, with optional dropout on the probabilities, from
+ * Q, K, V, the forward output O, its gradient dO and the forward log-sum-exp.  Three device
+ * stages run on the caller's stream:
  *   1. D = rowsum(dO * O) into the workspace                                   (HBM bound)
- *   2. the main kernel: per (segment, K/V head, key tile) it recomputes P = exp(S - LSE),
- *      accumulates dV += P^T dO and dK += dS^T Q in registers and emits the tile's fp32
- *      contribution dS K to the dQ accumulator                                   (MFMA bound)
- *   3. dQ = bf16(scale * sum over splits of the accumulator)                   (HBM bound)
+ *   2. the main kernel: per (segment, K/V head, run of key tiles) it recomputes
+ *      P = exp(S - LSE), accumulates dV += P^T dO and dK += dS^T Q in registers and emits the
+ *      tiles' contribution dS K to the dQ accumulator (fp32 splits, fp32 atomics or bf16
+ *      atomics)                                                                  (MFMA bound)
+ *   3. dQ = bf16(scale * sum over splits of the accumulator), and dbias       (HBM bound)
+ * fmha_fwd_run computes O and LSE with the same arguments.
  *
  * The workspace protocol follows "[CK_TILE] FMHA BWD Use Persistent Kernels in Deterministic
  * Mode" (aiter PR 2216), commit messages: the launcher reports a workspace size, the caller
@@ -49,7 +52,11 @@
  * memory and keeps no state between calls.  Host seqstart arrays are read during the call
  * only.  Device pointers must stay valid until the stream work completes.  One workspace must
  * not serve two runs in flight at the same time, and fmha_bwd_prepare_workspace must precede
- * every fmha_bwd_run (in atomic mode it zeroes the accumulator each time).
+ * every fmha_bwd_run (it writes the workspace header, and in the atomic modes it zeroes the
+ * accumulator each time).
+ *
+ * ABI history (fields are only ever appended): 2 padded THD slots, 3 dq_acc_dtype, 4 bias and
+ * dbias, 5 dropout, 6 plan_info.reduce_read_bytes.
  *
  * Errors: every function returns FMHA_OK or a negative fmha_status and never aborts.  Set
  * FMHA_BWD_LOG=1 in the environment to have the reason printed to stderr.
@@ -112,8 +119,9 @@ typedef struct fmha_bwd_args {
   int32_t mask_type;     /* enum fmha_mask_type */
   int32_t window_left;   /* FMHA_MASK_WINDOW only; -1 = unbounded */
   int32_t window_right;  /* FMHA_MASK_WINDOW only; -1 = unbounded */
-  int32_t deterministic; /* 1: per-key-tile fp32 partials + ordered reduction, bit-reproducible;
-                            0: fp32 atomic accumulation of dQ */
+  int32_t deterministic; /* 1: fp32 partials per run of key tiles + ordered reduction,
+                            bit-reproducible; 0: atomic accumulation of dQ (fp32, or bf16
+                            with dq_acc_dtype) */
   /* Group (THD) mode iff seqstart_q_host != NULL.  Then all four arrays are required and hold
      the same B+1 non-decreasing physical token offsets (host copies for planning, device
      copies for the kernels); segment b covers tokens [seqstart[b], seqstart[b+1]). */
