@@ -6,7 +6,7 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libfmha_bwd.so")
 
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 MASK_NONE = 0
 MASK_CAUSAL_TOP_LEFT = 1
@@ -127,10 +127,12 @@ class PlanInfo(ctypes.Structure):
         ("flops", ctypes.c_double),
         ("acc_rows", ctypes.c_int64),
         ("dq_acc_elem_bytes", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("kv_parts", ctypes.c_int32),
         ("dbias_acc_offset", ctypes.c_int64),
         ("dbias_acc_bytes", ctypes.c_int64),
         ("reduce_read_bytes", ctypes.c_int64),
+        ("dkv_acc_offset", ctypes.c_int64),
+        ("dkv_acc_bytes", ctypes.c_int64),
     ]
 
     def as_dict(self):

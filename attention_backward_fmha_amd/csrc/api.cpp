@@ -109,6 +109,9 @@ fmha::KParams make_params(const fmha_bwd_args* a, const fmha::Plan& p, void* ws)
     k.bias_b = p.bias_b;
     k.bias_h = p.bias_h;
   }
+  k.kv_parts = p.kv_parts;
+  k.rows_k = p.rows_k;
+  if (ws != nullptr && p.dkv_acc_bytes > 0) k.dkv_acc = (float*)((char*)ws + p.dkv_acc_offset);
   k.drop_k = p.drop_k;
   k.drop_scale = 256.0f / (float)p.drop_k;
   k.seed_lo = (unsigned)(a->philox_seed & 0xFFFFFFFFu);
@@ -205,6 +208,10 @@ int fmha_bwd_run_stages(const fmha_bwd_args* args, void* ws, size_t bytes, int s
       st = hip_status(fmha::launch_dbias(p, kp, s), "run: dbias reduce");
       if (st != FMHA_OK) return st;
     }
+    if (p.kv_parts > 1) {
+      st = hip_status(fmha::launch_dkv_reduce(p, kp, s), "run: dK/dV reduce");
+      if (st != FMHA_OK) return st;
+    }
   }
   return FMHA_OK;
 }
@@ -252,6 +259,9 @@ int fmha_bwd_plan_query(const fmha_bwd_args* args, fmha_bwd_plan_info* info) {
   info->rows_q = p.rows_q;
   info->acc_rows = p.acc_rows;
   info->dq_acc_elem_bytes = p.dq_bf16 ? 2 : 4;
+  info->kv_parts = p.kv_parts;
+  info->dkv_acc_offset = p.dkv_acc_offset;
+  info->dkv_acc_bytes = p.dkv_acc_bytes;
   info->dbias_acc_offset = p.dbias_acc_offset;
   info->dbias_acc_bytes = p.dbias_acc_bytes;
   info->d_offset = p.d_offset;

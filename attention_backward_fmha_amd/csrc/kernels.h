@@ -54,6 +54,9 @@ struct KParams {
   int64_t dbias_s[3];
   int dbias_direct;    // BHSS dbias: bf16 dS straight into dbias (plane bytes below)
   uint32_t dbias_plane_bytes;
+  int kv_parts;        // work groups per key tile (>1: fp32 dK/dV partials in dkv_acc)
+  float* dkv_acc;      // workspace: fp32 [kv_parts][Hkv][rows_k][d_qk + d_v]
+  int64_t rows_k;
   int drop_k;          // dropout: keep iff the element's random byte < drop_k (256 = off)
   float drop_scale;    // 256 / drop_k
   unsigned seed_lo, seed_hi, offset_lo;  // Philox key and the counter's offset word
@@ -64,6 +67,7 @@ hipError_t launch_fwd(const Plan& plan, const KParams& kp, hipStream_t stream);
 hipError_t launch_main(const Plan& plan, const KParams& kp, hipStream_t stream);
 hipError_t launch_reduce(const Plan& plan, const KParams& kp, hipStream_t stream);
 hipError_t launch_dbias(const Plan& plan, const KParams& kp, hipStream_t stream);
+hipError_t launch_dkv_reduce(const Plan& plan, const KParams& kp, hipStream_t stream);
 hipError_t launch_zero(float* ptr, int64_t count, hipStream_t stream);
 // Workspace header: magic value and plan fingerprint at ws[0], ws[1] (one vector store each).
 hipError_t launch_header(uint64_t* ws, uint64_t magic, uint64_t fingerprint, hipStream_t stream);

@@ -44,6 +44,7 @@ struct Seg {
   int64_t lq, lk;   // segment lengths
   int64_t ws_row0;  // first workspace row of D and LSE2 (b*Sq in batch mode)
   int64_t acc_row0; // first accumulator row: ws_row0 + b*acc_pad
+  int64_t kws_row0; // first key row of the dK/dV partials (b*Sk in batch mode)
 };
 
 // Segment bounds; b is uniform across the work group and readfirstlane keeps the loaded
@@ -60,12 +61,14 @@ __device__ __forceinline__ Seg seg_of(const KParams& p, int b) {
     s.k_row0 = p.slot_k ? __builtin_amdgcn_readfirstlane(p.slot_k[b]) : k0;
     s.lk = (int64_t)k1 - k0;
     s.ws_row0 = s.q_row0;
+    s.kws_row0 = s.k_row0;
   } else {
     s.q_row0 = 0;
     s.k_row0 = 0;
     s.lq = p.Sq;
     s.lk = p.Sk;
     s.ws_row0 = (int64_t)b * p.Sq;
+    s.kws_row0 = (int64_t)b * p.Sk;
   }
   s.acc_row0 = s.ws_row0 + (int64_t)b * p.acc_pad;
   return s;
@@ -378,8 +381,12 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
   const int i16 = lane & 15;
 
   const int nbh = p.Hkv * p.B;
-  const int item = blockIdx.x / nbh;  // key tiles item*T .. item*T + T - 1; split `item`
-  const int rem = blockIdx.x - item * nbh;
+  // work group -> (item, part, head): item-major, so causal items with the most work start
+  // first; part `part` of kv_parts takes its share of the item's steps
+  const int ip = blockIdx.x / nbh;
+  const int item = ip / p.kv_parts;  // key tiles item*T .. item*T + T - 1; split `item`
+  const int part = ip - item * p.kv_parts;
+  const int rem = blockIdx.x - ip * nbh;
   const int g = rem % p.Hkv;
   const int b = rem / p.Hkv;
   const bool group = p.seqstart_q != nullptr;
@@ -684,15 +691,18 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
     }
   };
 
-  // step n covers query head h = g*group_size + n / nblk and query block qb_lo + n % nblk
-  int h = g * p.group_size;
-  int64_t q0 = qb_lo * TM;
-  if (nsteps > 0) {
+  // step n covers query head h = g*group_size + n / nblk and query block qb_lo + n % nblk;
+  // this work group's part takes steps n0 .. n1 - 1
+  const int n0 = (int)((int64_t)nsteps * part / p.kv_parts);
+  const int n1 = (int)((int64_t)nsteps * (part + 1) / p.kv_parts);
+  int h = g * p.group_size + (nblk > 0 ? n0 / nblk : 0);
+  int64_t q0 = (qb_lo + (nblk > 0 ? n0 % nblk : 0)) * TM;
+  if (n1 > n0) {
     load_step(true, h, q0);
     store_step();
   }
 
-  for (int n = 0; n < nsteps; ++n) {
+  for (int n = n0; n < n1; ++n) {
     const int nq = (int)min((int64_t)TM, sg.lq - q0);
     int h_next = h;
     int64_t q0_next = q0 + TM;
@@ -701,7 +711,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
       ++h_next;
     }
     __syncthreads();  // LDS holds step n; every wave is done with step n-1's dS
-    load_step(n + 1 < nsteps, h_next, q0_next);
+    load_step(n + 1 < n1, h_next, q0_next);
     const __amdgpu_buffer_rsrc_t rdq = DET
         ? buffer_rsrc(p.dq_acc + (int64_t)item * p.split_stride + (int64_t)h * p.head_stride +
                           (sg.acc_row0 + q0) * DQK, (uint32_t)TM * DQK * 4u)
@@ -801,19 +811,29 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
     q0 = q0_next;
   }
 
-  // ---- epilogue: dK = scale * dK_acc, dV = dV_acc as bf16 ----
+  // ---- epilogue: dK = scale * dK_acc, dV = dV_acc as bf16 (one part), or this part's fp32
+  // partials (row kws_row0 + key of [part][g][rows_k][d_qk + d_v], unscaled) ----
   // result row i of dK/dV is the key of lane i, 32*wave + kmap(i)
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int kl = wave * 32 + kmap(8 * (r >> 2) + 4 * hi + (r & 3));
     if (kl < nk) {
       const int64_t krow = sg.k_row0 + key0 + kl;
-      uint16_t* dkp = p.dk + elem_off(p.dk_s, group, b, krow, g) + l32;
-      uint16_t* dvp = p.dv + elem_off(p.dv_s, group, b, krow, g) + l32;
+      if (p.kv_parts == 1) {
+        uint16_t* dkp = p.dk + elem_off(p.dk_s, group, b, krow, g) + l32;
+        uint16_t* dvp = p.dv + elem_off(p.dv_s, group, b, krow, g) + l32;
 #pragma unroll
-      for (int n = 0; n < DQK / 32; ++n) dkp[32 * n] = to_bf16_bits(dk_acc[n][r] * p.scale);
+        for (int n = 0; n < DQK / 32; ++n) dkp[32 * n] = to_bf16_bits(dk_acc[n][r] * p.scale);
 #pragma unroll
-      for (int n = 0; n < DV / 32; ++n) dvp[32 * n] = to_bf16_bits(dv_acc[n][r]);
+        for (int n = 0; n < DV / 32; ++n) dvp[32 * n] = to_bf16_bits(dv_acc[n][r]);
+      } else {
+        const int64_t prow = sg.kws_row0 + key0 + kl;
+        float* pp = p.dkv_acc + (((int64_t)part * p.Hkv + g) * p.rows_k + prow) * (DQK + DV) + l32;
+#pragma unroll
+        for (int n = 0; n < DQK / 32; ++n) pp[32 * n] = dk_acc[n][r];
+#pragma unroll
+        for (int n = 0; n < DV / 32; ++n) pp[DQK + 32 * n] = dv_acc[n][r];
+      }
     }
   }
   if (nblk > 0) {
@@ -991,6 +1011,48 @@ __global__ __launch_bounds__(256) void k_dq_reduce(const KParams p) {
     convert_rows16<DQK, TM>(p, sg, group, b, h, qb, nq);
   } else {
     reduce_rows<DQK, TM>(p, sg, group, b, h, qb, nq);
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// dK = bf16(scale * sum of the parts' fp32 dK partials), dV = bf16(sum of the dV partials), in
+// ascending part order.  One work group per (64 key rows, K/V head, segment), four values per
+// thread and chunk.
+// ------------------------------------------------------------------------------------------
+template <int DQK, int DV>
+__global__ __launch_bounds__(256) void k_dkv_reduce(const KParams p) {
+  constexpr int W = DQK + DV;
+  constexpr int C4 = W / 4;                       // float4 chunks per row
+  constexpr int PER = (64 * C4 + 255) / 256;      // chunks per thread
+  const int g = blockIdx.y;
+  const int b = blockIdx.z;
+  const bool group = p.seqstart_q != nullptr;
+  const Seg sg = seg_of(p, b);
+  const int64_t k0 = (int64_t)blockIdx.x * 64;
+  if (k0 >= sg.lk) return;
+  const int nk = (int)min((int64_t)64, sg.lk - k0);
+  const int64_t part_stride = (int64_t)p.Hkv * p.rows_k * W;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int c = threadIdx.x + 256 * u;
+    const int r = c / C4;
+    if (r < nk) {
+      const int col = (c - r * C4) * 4;
+      const int64_t krow = sg.k_row0 + k0 + r;
+      const float* src = p.dkv_acc + ((int64_t)g * p.rows_k + sg.kws_row0 + k0 + r) * W + col;
+      f32x4 acc = *(const f32x4*)src;
+      for (int q = 1; q < p.kv_parts; ++q) acc += *(const f32x4*)(src + q * part_stride);
+      bf16x4 o;
+      if (col < DQK) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = (__bf16)(acc[e] * p.scale);
+        *(bf16x4*)(p.dk + elem_off(p.dk_s, group, b, krow, g) + col) = o;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = (__bf16)acc[e];
+        *(bf16x4*)(p.dv + elem_off(p.dv_s, group, b, krow, g) + (col - DQK)) = o;
+      }
+    }
   }
 }
 
@@ -1407,7 +1469,7 @@ static void launch_main_t(const Plan& plan, const KParams& kp, dim3 grid, hipStr
 
 hipError_t launch_main(const Plan& plan, const KParams& kp, hipStream_t stream) {
   const int64_t items = (int64_t)((plan.n_kv_tiles + plan.tiles_per_item - 1) / plan.tiles_per_item) *
-                        plan.Hkv * plan.B;
+                        plan.kv_parts * plan.Hkv * plan.B;
   if (items == 0) return hipSuccess;
   const dim3 grid((unsigned)items);
   if (plan.d_qk == 64) {
@@ -1443,6 +1505,19 @@ hipError_t launch_reduce(const Plan& plan, const KParams& kp, hipStream_t stream
     }
   } else {
     launch_reduce_t<192, 32>(plan, kp, stream);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_dkv_reduce(const Plan& plan, const KParams& kp, hipStream_t stream) {
+  if (plan.kv_parts <= 1 || plan.B == 0 || plan.n_kv_tiles == 0) return hipSuccess;
+  const dim3 grid((unsigned)(plan.n_kv_tiles * 2), (unsigned)plan.Hkv, (unsigned)plan.B);  // 64-row blocks
+  if (plan.d_qk == 64) {
+    hipLaunchKernelGGL((k_dkv_reduce<64, 64>), grid, dim3(256), 0, stream, kp);
+  } else if (plan.d_qk == 128) {
+    hipLaunchKernelGGL((k_dkv_reduce<128, 128>), grid, dim3(256), 0, stream, kp);
+  } else {
+    hipLaunchKernelGGL((k_dkv_reduce<192, 128>), grid, dim3(256), 0, stream, kp);
   }
   return hipGetLastError();
 }

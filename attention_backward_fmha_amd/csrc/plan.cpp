@@ -11,6 +11,7 @@
 //                                                 padding per segment; atomic: one split,
 //                                                 row-major, acc_rows = rows_q)
 //   dbias_acc fp32 [B][Hq][Sq][Sk]              full-shape dS when dbias is requested
+//   dkv_acc fp32 [kv_parts][Hkv][rows_k][d_qk + d_v]  dK, dV partials when kv_parts > 1
 //           or bf16 [B][Hq][acc_rows][d_qk]       bf16 atomic mode: one slot of
 //                                                 acc_rows = pad16(longest lq) rows per
 //                                                 (segment, head), indexed by the logical
@@ -164,6 +165,7 @@ int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t el, bool forwar
                     "a segment does not fit its padded slot (padded[b] + length > padded[b+1])");
     }
     p->rows_q = a->B > 0 ? (pq ? pq[a->B] : sq[a->B]) : 0;
+    p->rows_k = a->B > 0 ? (pk ? pk[a->B] : sk[a->B]) : 0;
   } else {
     if (a->seqstart_k_host || a->seqstart_q_dev || a->seqstart_k_dev)
       return fail(FMHA_ERR_INVALID_ARG, err, el,
@@ -172,6 +174,7 @@ int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t el, bool forwar
         a->seqstart_k_padded_dev)
       return fail(FMHA_ERR_INVALID_ARG, err, el, "padded seqstart arrays need group mode");
     p->rows_q = (int64_t)a->B * a->Sq;
+    p->rows_k = (int64_t)a->B * a->Sk;
   }
 
   // pointers and strides (only when there is data to touch)
@@ -256,9 +259,35 @@ int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t el, bool forwar
       }
     }
   }
-  if (const char* e = getenv("FMHA_BWD_TILES_PER_ITEM")) {  // tuning knob: 1, 2 or 4
-    if (p->deterministic && (atoi(e) == 1 || atoi(e) == 2 || atoi(e) == 4))
-      p->tiles_per_item = atoi(e);
+  // Too few (K/V head, key tile) items to give every CU one: split each item's steps (query
+  // heads x query blocks) over kv_parts work groups that add fp32 dK/dV partials, summed in
+  // ascending part order afterwards (one key tile per item then, so no part reads back
+  // another's dQ partial).
+  p->kv_parts = 1;
+  {
+    const int64_t heads = (int64_t)p->Hkv * p->B;
+    const int64_t items_now = (int64_t)((p->n_kv_tiles + p->tiles_per_item - 1) / p->tiles_per_item) * heads;
+    if (items_now > 0 && items_now < 256) {
+      p->tiles_per_item = 1;
+      const int64_t items1 = (int64_t)p->n_kv_tiles * heads;
+      int parts = (int)((512 + items1 - 1) / items1);
+      p->kv_parts = parts < 1 ? 1 : (parts > 8 ? 8 : parts);
+    }
+  }
+  // tuning knobs (tests use them); items of several tiles and parts exclude each other
+  if (const char* e = getenv("FMHA_BWD_TILES_PER_ITEM")) {  // 1, 2 or 4
+    const int v = atoi(e);
+    if (p->deterministic && (v == 1 || v == 2 || v == 4)) {
+      p->tiles_per_item = v;
+      if (v > 1) p->kv_parts = 1;
+    }
+  }
+  if (const char* e = getenv("FMHA_BWD_KV_PARTS")) {  // 1 .. 8
+    const int v = atoi(e);
+    if (v >= 1 && v <= 8) {
+      p->kv_parts = v;
+      if (v > 1) p->tiles_per_item = 1;
+    }
   }
   const int n_items = (p->n_kv_tiles + p->tiles_per_item - 1) / p->tiles_per_item;
   p->nsplits = p->deterministic ? (n_items > 0 ? n_items : 1) : 1;
@@ -284,7 +313,10 @@ int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t el, bool forwar
                              ? (uint32_t)((((int64_t)a->Sq - 1) * a->dbias_stride[2] + a->Sk) * 2) : 0u;
   p->dbias_acc_offset = align_up(p->dq_acc_offset + p->dq_acc_bytes, 256);
   p->dbias_acc_bytes = p->has_dbias && !p->dbias_direct ? (int64_t)p->B * p->Hq * p->Sq * p->Sk * 4 : 0;
-  p->workspace_bytes = align_up(p->dbias_acc_offset + p->dbias_acc_bytes, 256);
+  p->dkv_acc_offset = align_up(p->dbias_acc_offset + p->dbias_acc_bytes, 256);
+  p->dkv_acc_bytes = p->kv_parts > 1 && !forward
+                         ? (int64_t)p->kv_parts * p->Hkv * p->rows_k * (p->d_qk + p->d_v) * 4 : 0;
+  p->workspace_bytes = align_up(p->dkv_acc_offset + p->dkv_acc_bytes, 256);
   // what a run reads from the workspace depends on exactly these (and the segment offsets)
   Fnv f;
   for (int64_t x : {(int64_t)p->B, (int64_t)p->Hq, (int64_t)p->Hkv, (int64_t)p->Sq, (int64_t)p->Sk,
@@ -293,6 +325,7 @@ int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t el, bool forwar
                     (int64_t)p->dq_bf16, (int64_t)p->group_mode, p->rows_q, p->acc_rows,
                     (int64_t)p->acc_pad, p->d_offset, p->lse2_offset, p->dq_acc_offset,
                     p->dq_acc_bytes, p->dbias_acc_offset, p->dbias_acc_bytes, p->workspace_bytes,
+                    (int64_t)p->kv_parts, p->dkv_acc_offset, p->dkv_acc_bytes,
                     (int64_t)a->mask_type, (int64_t)a->window_left, (int64_t)a->window_right})
     f.v(x);
   if (group && a->B > 0) {

@@ -43,6 +43,9 @@ struct Plan {
   int64_t dbias_acc_offset, dbias_acc_bytes;  // fp32 [B][Hq][Sq][Sk] full-shape dS
   int drop_k;            // dropout keep threshold on a random byte (256 = no dropout)
   uint64_t fingerprint;  // FNV-1a of every layout quantity and the host seqstart arrays
+  int kv_parts;          // work groups per key tile sharing its steps (fp32 dK/dV partials)
+  int64_t rows_k;        // K rows: B*Sk, seqstart_k[B] or the padded k offsets' last entry
+  int64_t dkv_acc_offset, dkv_acc_bytes;  // fp32 [kv_parts][Hkv][rows_k][d_qk + d_v]
   bool dbias_direct;     // full-shape (BHSS) dbias: the main kernel writes it directly
   uint32_t dbias_plane_bytes;
 };

@@ -92,6 +92,9 @@ WORKLOADS = {
     "long_16384_window_4096": dict(B=1, Hq=32, Hkv=8, Sq=16384, Sk=16384, d_qk=128, d_v=128,
                                    mask=MASK_WINDOW, window=(4096, 0), seed=1004,
                                    sigmas=(1, 1, 1, 1)),
+    # one GPU's share of the 16384-token workload under 8-way K/V-head sharding
+    "long_16384_causal_shard_h4": dict(B=1, Hq=4, Hkv=1, Sq=16384, Sk=16384, d_qk=128, d_v=128,
+                                       mask=MASK_CAUSAL_BOTTOM_RIGHT, seed=1004, sigmas=(1, 1, 1, 1)),
     "cross_192_128": dict(B=4, Hq=16, Hkv=16, Sq=1024, Sk=4096, d_qk=192, d_v=128, mask=MASK_NONE,
                           seed=1005, sigmas=(1, 1, 0.5, 0.5)),
     "cross_64": dict(B=4, Hq=16, Hkv=16, Sq=1024, Sk=4096, d_qk=64, d_v=64, mask=MASK_NONE,

@@ -342,6 +342,8 @@ def main():
 
     def stage_entry(m_plan, st):
         red = m_plan.reduce_read_bytes + dq_bytes
+        if m_plan.kv_parts > 1:  # fp32 dK/dV partials of every part in, bf16 dK/dV out
+            red += m_plan.dkv_acc_bytes + m_plan.dkv_acc_bytes // (m_plan.kv_parts * 2)
         out_ = {"prepare_ms": round(st[0], 4), "dot_ms": round(st[1], 4), "main_ms": round(st[2], 4),
                 "reduce_ms": round(st[3], 4),
                 "dot_GBps": round(dot_bytes / (st[1] * 1e-3) / 1e9, 1),
@@ -354,7 +356,8 @@ def main():
     for mode, m_ms, m_main, m_plan, m_st in runs:
         modes[mode] = {"stages": stage_entry(m_plan, m_st),
             "value": round(flops / (m_ms * 1e-3) / 1e12, 2), "ms_per_step": round(m_ms, 4),
-            "main_kernel_ms": round(m_main, 4), "nsplits": m_plan.nsplits}
+            "main_kernel_ms": round(m_main, 4), "nsplits": m_plan.nsplits,
+            "tiles_per_item": m_plan.tiles_per_item, "kv_parts": m_plan.kv_parts}
 
     out = {
         "metric": "FMHA bwd TFLOP/s and % of bf16 MFMA peak, B*H*S*d=2*32*4096*128 causal",

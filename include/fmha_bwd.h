@@ -56,7 +56,8 @@
  * accumulator each time).
  *
  * ABI history (fields are only ever appended): 2 padded THD slots, 3 dq_acc_dtype, 4 bias and
- * dbias, 5 dropout, 6 plan_info.reduce_read_bytes.
+ * dbias, 5 dropout, 6 plan_info.reduce_read_bytes, 7 plan_info.kv_parts and the dK/dV
+ * partials region.
  *
  * Errors: every function returns FMHA_OK or a negative fmha_status and never aborts.  Set
  * FMHA_BWD_LOG=1 in the environment to have the reason printed to stderr.
@@ -71,7 +72,7 @@
 extern "C" {
 #endif
 
-#define FMHA_BWD_ABI_VERSION 6u
+#define FMHA_BWD_ABI_VERSION 7u
 
 #if defined(__GNUC__)
 #define FMHA_BWD_API __attribute__((visibility("default")))
@@ -246,12 +247,18 @@ typedef struct fmha_bwd_plan_info {
   int64_t acc_rows;        /* accumulator rows per head and split, or per segment and head in
                               bf16 mode (see below) */
   int32_t dq_acc_elem_bytes; /* 4 (fp32 accumulator) or 2 (bf16) */
-  int32_t reserved;
+  int32_t kv_parts;        /* work groups that share one key tile's steps (query heads x
+                              blocks); > 1 when there are too few K/V heads and tiles to fill
+                              the GPU: each part adds fp32 dK/dV partials that a final pass sums
+                              in ascending part order */
   int64_t dbias_acc_offset;  /* byte offset of the fp32 full-shape dS [B][Hq][Sq][Sk] (dbias) */
   int64_t dbias_acc_bytes;   /* 0 without dbias, or when dbias is full-shape (written directly) */
   int64_t reduce_read_bytes; /* bytes of the dQ accumulator the reduce stage reads (the
                                 splits that touch each query block, or the atomic modes'
                                 segment rows): for achieved-bandwidth figures */
+  int64_t dkv_acc_offset;    /* byte offset of the fp32 dK, dV partials [kv_parts][Hkv][rows_k]
+                                [d_qk + d_v] (only when kv_parts > 1) */
+  int64_t dkv_acc_bytes;
 } fmha_bwd_plan_info;
 /* Accumulator layout.  Atomic mode: one split, rows_q rows, row-major ([row][d_qk]), row of
    a query = its D/LSE row.  Deterministic mode: split s holds the sum of the partials of key

@@ -60,7 +60,7 @@ int main(void) {
   F(q_stride) F(dv_stride) F(lse_stride) F(seqstart_q_padded_host) F(seqstart_k_padded_dev)
   F(dq_acc_dtype) F(bias) F(dbias_stride) F(bias_h) F(p_drop) F(philox_seed) F(philox_offset)
   G(nsplits) G(rows_q) G(workspace_bytes) G(flops) G(acc_rows) G(dq_acc_elem_bytes) G(dbias_acc_bytes)
-  G(reduce_read_bytes)
+  G(reduce_read_bytes) G(kv_parts) G(dkv_acc_bytes)
   printf("\\"size_args\\": %zu, \\"size_info\\": %zu}\\n", sizeof(fmha_bwd_args), sizeof(fmha_bwd_plan_info));
   return 0;
 }
@@ -78,7 +78,8 @@ int main(void) {
         if k.startswith("size"):
             continue
         cls = _lib.PlanInfo if k in ("nsplits", "rows_q", "workspace_bytes", "flops", "acc_rows",
-                                     "dq_acc_elem_bytes", "dbias_acc_bytes", "reduce_read_bytes") else Args
+                                     "dq_acc_elem_bytes", "dbias_acc_bytes", "reduce_read_bytes",
+                                     "kv_parts", "dkv_acc_bytes") else Args
         assert getattr(cls, k).offset == v, k
 
 
@@ -302,6 +303,26 @@ def test_reduce_read_bytes_closed_forms():
     n = batch_args(B=1, Hq=2, Hkv=2, Sq=256, Sk=512, mask=0)  # no mask: every split, 4 blocks
     info = _lib.plan_query(n)
     assert info.reduce_read_bytes == 2 * 4 * info.nsplits * 64 * 128 * 4
+
+
+def test_kv_parts_fill_the_gpu_for_few_heads(monkeypatch):
+    """Fewer than 256 (K/V head, key tile) items: each item's steps are split over parts of
+    ceil(512 / items) work groups (at most 8), one key tile per item, with an fp32 dK/dV
+    partial region of parts x Hkv x rows_k x (d_qk + d_v)."""
+    monkeypatch.delenv("FMHA_BWD_KV_PARTS", raising=False)
+    monkeypatch.delenv("FMHA_BWD_TILES_PER_ITEM", raising=False)
+    shard = batch_args(B=1, Hq=4, Hkv=1, Sq=16384, Sk=16384, mask=2)  # 128 items
+    info = _lib.plan_query(shard)
+    assert (info.kv_parts, info.tiles_per_item) == (4, 1)
+    assert info.dkv_acc_bytes == 4 * 1 * 16384 * 256 * 4
+    assert info.dkv_acc_offset % 256 == 0 and info.dkv_acc_offset + info.dkv_acc_bytes <= info.workspace_bytes
+    head = _lib.plan_query(batch_args(B=2, Hq=32, Hkv=32, Sq=4096, Sk=4096, mask=1))
+    assert (head.kv_parts, head.dkv_acc_bytes) == (1, 0)
+    assert _lib.plan_query(batch_args()).kv_parts == 8  # 3 tiles x 4 heads: capped at 8
+    monkeypatch.setenv("FMHA_BWD_TILES_PER_ITEM", "2")  # several tiles per item: no parts
+    assert (_lib.plan_query(batch_args()).kv_parts, _lib.plan_query(batch_args()).tiles_per_item) == (1, 2)
+    monkeypatch.setenv("FMHA_BWD_KV_PARTS", "3")  # parts win, one tile per item
+    assert (_lib.plan_query(batch_args()).kv_parts, _lib.plan_query(batch_args()).tiles_per_item) == (3, 1)
 
 
 def test_tiles_per_item_keeps_two_items_per_cu():
