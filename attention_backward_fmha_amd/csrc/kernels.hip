@@ -395,6 +395,27 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
   // query blocks whose partial this item has already written into its split (a contiguous
   // range: consecutive tiles touch overlapping or adjacent ranges)
   int64_t w_lo = 1, w_hi = 0;
+  // Parts own steps (query head h, query block qb) of the union of the item's tiles' query
+  // block ranges [u_lo, u_hi], numbered h-major: union step u = (h - g*group_size) * nbu +
+  // qb - u_lo, part `part` owning u in [nu*part/kv_parts, nu*(part+1)/kv_parts).  Ownership
+  // does not depend on the tile, so the split blocks a part reads back on a later tile are
+  // exactly the ones it wrote itself.
+  int64_t u_lo = 1, u_hi = 0;
+  for (int tsub = 0; tsub < p.tiles_per_item; ++tsub) {
+    const int j = item * p.tiles_per_item + tsub;
+    if ((int64_t)j * TN >= sg.lk) break;
+    int64_t lo, hi;
+    qblocks_for_tile(mg, sg.lq, sg.lk, j, TM, TN, &lo, &hi);
+    if (hi >= lo) {
+      const bool had = u_hi >= u_lo;
+      u_lo = had ? min(u_lo, lo) : lo;
+      u_hi = had ? max(u_hi, hi) : hi;
+    }
+  }
+  const int64_t nbu = u_hi >= u_lo ? u_hi - u_lo + 1 : 0;
+  const int64_t nu = nbu * p.group_size;
+  const int64_t u_a = nu * part / p.kv_parts;
+  const int64_t u_e = nu * (part + 1) / p.kv_parts;
   for (int tsub = 0; tsub < p.tiles_per_item; ++tsub) {
   const int j = item * p.tiles_per_item + tsub;
   const int64_t key0 = (int64_t)j * TN;
@@ -692,9 +713,15 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
   };
 
   // step n covers query head h = g*group_size + n / nblk and query block qb_lo + n % nblk;
-  // this work group's part takes steps n0 .. n1 - 1
-  const int n0 = (int)((int64_t)nsteps * part / p.kv_parts);
-  const int n1 = (int)((int64_t)nsteps * (part + 1) / p.kv_parts);
+  // this work group's part takes steps n0 .. n1 - 1: the tile's steps that come before union
+  // step u number (u / nbu) * nblk + clamp(u_lo + u % nbu - qb_lo, 0, nblk)
+  const auto steps_before = [&](int64_t u) -> int {
+    if (nbu == 0) return 0;
+    const int64_t c = min(max(u_lo + u % nbu - qb_lo, (int64_t)0), (int64_t)nblk);
+    return (int)((u / nbu) * nblk + c);
+  };
+  const int n0 = steps_before(u_a);
+  const int n1 = steps_before(u_e);
   int h = g * p.group_size + (nblk > 0 ? n0 / nblk : 0);
   int64_t q0 = (qb_lo + (nblk > 0 ? n0 % nblk : 0)) * TM;
   if (n1 > n0) {

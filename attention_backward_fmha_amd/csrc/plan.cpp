@@ -261,33 +261,36 @@ int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t el, bool forwar
   }
   // Too few (K/V head, key tile) items to give every CU one: split each item's steps (query
   // heads x query blocks) over kv_parts work groups that add fp32 dK/dV partials, summed in
-  // ascending part order afterwards (one key tile per item then, so no part reads back
-  // another's dQ partial).
+  // ascending part order afterwards, aiming at 512 work groups.  A part owns the same (query
+  // head, query block) pairs on every tile of its item, so deterministic items keep the
+  // largest of 4 and 2 tiles for which 8 parts still reach that count.
   p->kv_parts = 1;
   {
     const int64_t heads = (int64_t)p->Hkv * p->B;
     const int64_t items_now = (int64_t)((p->n_kv_tiles + p->tiles_per_item - 1) / p->tiles_per_item) * heads;
     if (items_now > 0 && items_now < 256) {
       p->tiles_per_item = 1;
-      const int64_t items1 = (int64_t)p->n_kv_tiles * heads;
-      int parts = (int)((512 + items1 - 1) / items1);
-      p->kv_parts = parts < 1 ? 1 : (parts > 8 ? 8 : parts);
+      if (p->deterministic) {
+        for (int t : {4, 2}) {
+          if ((int64_t)((p->n_kv_tiles + t - 1) / t) * heads * 8 >= 512) {
+            p->tiles_per_item = t;
+            break;
+          }
+        }
+      }
+      const int64_t items = (int64_t)((p->n_kv_tiles + p->tiles_per_item - 1) / p->tiles_per_item) * heads;
+      const int64_t parts = (512 + items - 1) / items;
+      p->kv_parts = (int)(parts < 1 ? 1 : (parts > 8 ? 8 : parts));
     }
   }
-  // tuning knobs (tests use them); items of several tiles and parts exclude each other
+  // tuning knobs (tests use them), each overriding its own choice
   if (const char* e = getenv("FMHA_BWD_TILES_PER_ITEM")) {  // 1, 2 or 4
     const int v = atoi(e);
-    if (p->deterministic && (v == 1 || v == 2 || v == 4)) {
-      p->tiles_per_item = v;
-      if (v > 1) p->kv_parts = 1;
-    }
+    if (p->deterministic && (v == 1 || v == 2 || v == 4)) p->tiles_per_item = v;
   }
   if (const char* e = getenv("FMHA_BWD_KV_PARTS")) {  // 1 .. 8
     const int v = atoi(e);
-    if (v >= 1 && v <= 8) {
-      p->kv_parts = v;
-      if (v > 1) p->tiles_per_item = 1;
-    }
+    if (v >= 1 && v <= 8) p->kv_parts = v;
   }
   const int n_items = (p->n_kv_tiles + p->tiles_per_item - 1) / p->tiles_per_item;
   p->nsplits = p->deterministic ? (n_items > 0 ? n_items : 1) : 1;

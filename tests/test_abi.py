@@ -307,22 +307,27 @@ def test_reduce_read_bytes_closed_forms():
 
 def test_kv_parts_fill_the_gpu_for_few_heads(monkeypatch):
     """Fewer than 256 (K/V head, key tile) items: each item's steps are split over parts of
-    ceil(512 / items) work groups (at most 8), one key tile per item, with an fp32 dK/dV
-    partial region of parts x Hkv x rows_k x (d_qk + d_v)."""
+    ceil(512 / items) work groups (at most 8), with an fp32 dK/dV partial region of parts x
+    Hkv x rows_k x (d_qk + d_v).  Deterministic items keep the largest of 4 and 2 tiles for
+    which 8 parts still make 512 work groups; the other modes use one tile per item."""
     monkeypatch.delenv("FMHA_BWD_KV_PARTS", raising=False)
     monkeypatch.delenv("FMHA_BWD_TILES_PER_ITEM", raising=False)
-    shard = batch_args(B=1, Hq=4, Hkv=1, Sq=16384, Sk=16384, mask=2)  # 128 items
+    shard = batch_args(B=1, Hq=4, Hkv=1, Sq=16384, Sk=16384, mask=2)  # 128 key tiles, one K/V head
+    info = _lib.plan_query(shard)
+    assert (info.kv_parts, info.tiles_per_item, info.nsplits) == (8, 2, 64)
+    assert info.dkv_acc_bytes == 8 * 1 * 16384 * 256 * 4
+    assert info.dkv_acc_offset % 256 == 0 and info.dkv_acc_offset + info.dkv_acc_bytes <= info.workspace_bytes
+    shard.deterministic = 0
     info = _lib.plan_query(shard)
     assert (info.kv_parts, info.tiles_per_item) == (4, 1)
-    assert info.dkv_acc_bytes == 4 * 1 * 16384 * 256 * 4
-    assert info.dkv_acc_offset % 256 == 0 and info.dkv_acc_offset + info.dkv_acc_bytes <= info.workspace_bytes
     head = _lib.plan_query(batch_args(B=2, Hq=32, Hkv=32, Sq=4096, Sk=4096, mask=1))
     assert (head.kv_parts, head.dkv_acc_bytes) == (1, 0)
-    assert _lib.plan_query(batch_args()).kv_parts == 8  # 3 tiles x 4 heads: capped at 8
-    monkeypatch.setenv("FMHA_BWD_TILES_PER_ITEM", "2")  # several tiles per item: no parts
-    assert (_lib.plan_query(batch_args()).kv_parts, _lib.plan_query(batch_args()).tiles_per_item) == (1, 2)
-    monkeypatch.setenv("FMHA_BWD_KV_PARTS", "3")  # parts win, one tile per item
-    assert (_lib.plan_query(batch_args()).kv_parts, _lib.plan_query(batch_args()).tiles_per_item) == (3, 1)
+    small = batch_args()  # 3 key tiles x 4 heads: one tile per item, parts capped at 8
+    assert (_lib.plan_query(small).kv_parts, _lib.plan_query(small).tiles_per_item) == (8, 1)
+    monkeypatch.setenv("FMHA_BWD_TILES_PER_ITEM", "2")  # the knobs override independently
+    assert (_lib.plan_query(small).kv_parts, _lib.plan_query(small).tiles_per_item) == (8, 2)
+    monkeypatch.setenv("FMHA_BWD_KV_PARTS", "3")
+    assert (_lib.plan_query(small).kv_parts, _lib.plan_query(small).tiles_per_item) == (3, 2)
 
 
 def test_tiles_per_item_keeps_two_items_per_cu():

@@ -46,8 +46,25 @@ def test_split_key_tiles_match_oracle(case, parts, mode, monkeypatch):
     assert_grads_close(got, ref, sq, sk)
 
 
-def test_split_key_tiles_are_bit_identical(monkeypatch):
+@pytest.mark.parametrize("tiles", [2, 4])
+@pytest.mark.parametrize("parts", [3, 8])
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_parts_of_multi_tile_items_match_oracle(case, parts, tiles, monkeypatch):
+    """Deterministic items of several key tiles, split into parts: a part adds its dQ partial
+    of a later tile onto the split blocks it wrote for an earlier one."""
+    monkeypatch.setenv("FMHA_BWD_KV_PARTS", str(parts))
+    monkeypatch.setenv("FMHA_BWD_TILES_PER_ITEM", str(tiles))
+    x, sq, sk, scale, mask, window = _inputs(case, 9403)
+    o, lse = oracle_forward(x, scale=scale, mask=mask, window=window, sq=sq, sk=sk)
+    ref = oracle_backward(x, scale=scale, mask=mask, window=window, sq=sq, sk=sk)
+    got = run_gpu(x, o, lse, scale=scale, mask=mask, window=window, sq=sq, sk=sk)
+    assert_grads_close(got, ref, sq, sk)
+
+
+@pytest.mark.parametrize("tiles", ["1", "2"])
+def test_split_key_tiles_are_bit_identical(tiles, monkeypatch):
     monkeypatch.setenv("FMHA_BWD_KV_PARTS", "5")
+    monkeypatch.setenv("FMHA_BWD_TILES_PER_ITEM", tiles)
     x, sq, sk, scale, mask, window = _inputs(CASES[0], 9402)
     o, lse = oracle_forward(x, scale=scale, mask=mask, sq=sq, sk=sk)
     first = run_gpu(x, o, lse, scale=scale, mask=mask, sq=sq, sk=sk)
