@@ -1042,22 +1042,24 @@ __global__ __launch_bounds__(256) void k_dq_reduce(const KParams p) {
 }
 
 // ------------------------------------------------------------------------------------------
-// dK = bf16(scale * sum of the parts' fp32 dK partials), dV = bf16(sum of the dV partials), in
-// ascending part order.  One work group per (64 key rows, K/V head, segment), four values per
-// thread and chunk.
+// dK = bf16(scale * sum of the parts' dK partials), dV = bf16(sum of the dV partials), in
+// ascending part order.  One work group per (8 key rows, K/V head, segment), four values per
+// thread and chunk; the loads of all parts of a chunk are issued before the sum.
 // ------------------------------------------------------------------------------------------
+constexpr int kDkvRows = 8;  // key rows per work group of k_dkv_reduce
+
 template <int DQK, int DV>
 __global__ __launch_bounds__(256) void k_dkv_reduce(const KParams p) {
   constexpr int W = DQK + DV;
-  constexpr int C4 = W / 4;                       // float4 chunks per row
-  constexpr int PER = (64 * C4 + 255) / 256;      // chunks per thread
+  constexpr int C4 = W / 4;                              // float4 chunks per row
+  constexpr int PER = (kDkvRows * C4 + 255) / 256;       // chunks per thread
   const int g = blockIdx.y;
   const int b = blockIdx.z;
   const bool group = p.seqstart_q != nullptr;
   const Seg sg = seg_of(p, b);
-  const int64_t k0 = (int64_t)blockIdx.x * 64;
+  const int64_t k0 = (int64_t)blockIdx.x * kDkvRows;
   if (k0 >= sg.lk) return;
-  const int nk = (int)min((int64_t)64, sg.lk - k0);
+  const int nk = (int)min((int64_t)kDkvRows, sg.lk - k0);
   const int64_t part_stride = (int64_t)p.Hkv * p.rows_k * W;
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
@@ -1067,8 +1069,14 @@ __global__ __launch_bounds__(256) void k_dkv_reduce(const KParams p) {
       const int col = (c - r * C4) * 4;
       const int64_t krow = sg.k_row0 + k0 + r;
       const float* src = p.dkv_acc + ((int64_t)g * p.rows_k + sg.kws_row0 + k0 + r) * W + col;
-      f32x4 acc = *(const f32x4*)src;
-      for (int q = 1; q < p.kv_parts; ++q) acc += *(const f32x4*)(src + q * part_stride);
+      f32x4 part[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        part[q] = q < p.kv_parts ? *(const f32x4*)(src + q * part_stride) : f32x4{};
+      f32x4 acc = part[0];
+#pragma unroll
+      for (int q = 1; q < 8; ++q)
+        if (q < p.kv_parts) acc += part[q];
       bf16x4 o;
       if (col < DQK) {
 #pragma unroll
@@ -1538,7 +1546,8 @@ hipError_t launch_reduce(const Plan& plan, const KParams& kp, hipStream_t stream
 
 hipError_t launch_dkv_reduce(const Plan& plan, const KParams& kp, hipStream_t stream) {
   if (plan.kv_parts <= 1 || plan.B == 0 || plan.n_kv_tiles == 0) return hipSuccess;
-  const dim3 grid((unsigned)(plan.n_kv_tiles * 2), (unsigned)plan.Hkv, (unsigned)plan.B);  // 64-row blocks
+  if (plan.kv_parts > 8) return hipErrorInvalidValue;  // the reduce sums at most 8 parts
+  const dim3 grid((unsigned)(plan.n_kv_tiles * (128 / kDkvRows)), (unsigned)plan.Hkv, (unsigned)plan.B);
   if (plan.d_qk == 64) {
     hipLaunchKernelGGL((k_dkv_reduce<64, 64>), grid, dim3(256), 0, stream, kp);
   } else if (plan.d_qk == 128) {
