@@ -259,12 +259,27 @@ int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t el, bool forwar
       }
     }
   }
+  // Long causal segments (8192 keys or more) whose 4-tile items number between one and two
+  // per CU: 4 tiles per item, split into parts that make about 1024 work groups.  The parts
+  // balance the heavy causal items, and the dK/dV partials they add are small next to the
+  // work of such long rows, while the dQ reduction reads half of what 2-tile items leave.
+  p->kv_parts = 1;
+  if (p->deterministic && max_lk >= 8192) {
+    const int64_t heads = (int64_t)p->Hkv * p->B;
+    const bool even_work = a->mask_type == FMHA_MASK_NONE ||
+                           (a->mask_type == FMHA_MASK_WINDOW && a->window_left >= 0 && a->window_right >= 0);
+    const int64_t items4 = (int64_t)((p->n_kv_tiles + 3) / 4) * heads;
+    if (!even_work && items4 >= 256 && items4 < 512) {
+      p->tiles_per_item = 4;
+      const int64_t parts = (1024 + items4 - 1) / items4;
+      p->kv_parts = (int)(parts > 4 ? 4 : parts);
+    }
+  }
   // Too few (K/V head, key tile) items to give every CU one: split each item's steps (query
   // heads x query blocks) over kv_parts work groups that add fp32 dK/dV partials, summed in
   // ascending part order afterwards, aiming at 512 work groups.  A part owns the same (query
   // head, query block) pairs on every tile of its item, so deterministic items keep the
   // largest of 4 and 2 tiles for which 8 parts still reach that count.
-  p->kv_parts = 1;
   {
     const int64_t heads = (int64_t)p->Hkv * p->B;
     const int64_t items_now = (int64_t)((p->n_kv_tiles + p->tiles_per_item - 1) / p->tiles_per_item) * heads;

@@ -332,20 +332,25 @@ def test_kv_parts_fill_the_gpu_for_few_heads(monkeypatch):
 
 def test_tiles_per_item_keeps_two_items_per_cu():
     """Deterministic work items take 4 key tiles when that leaves >= 512 items, else 2, else 1;
-    the split count follows."""
-    for B, H, S, want in ((2, 32, 4096, 4), (1, 8, 16384, 2), (2, 16, 2048, 1)):
+    the split count follows.  Causal segments of 8192 keys or more whose 4-tile items number
+    256 to 511 take 4 tiles split into parts (at most 4) that make about 1024 work groups."""
+    for B, H, S, want, parts in ((2, 32, 4096, 4, 1), (1, 8, 16384, 4, 4), (1, 12, 16384, 4, 3),
+                                 (1, 8, 8192, 1, 1), (2, 16, 2048, 1, 1)):
         a = batch_args(B=B, Hq=H, Hkv=H, Sq=S, Sk=S, mask=1)
         info = _lib.plan_query(a)
         tiles = -(-S // 128)
-        assert info.tiles_per_item == want, (B, H, S)
+        assert (info.tiles_per_item, info.kv_parts) == (want, parts), (B, H, S)
         assert info.nsplits == -(-tiles // want)
     a = batch_args(B=2, Hq=32, Hkv=32, Sq=4096, Sk=4096, mask=1, deterministic=0)
     assert _lib.plan_query(a).tiles_per_item == 1
     # a two-sided window (even work per tile) needs one item per compute unit only
     w = batch_args(B=1, Hq=32, Hkv=8, Sq=16384, Sk=16384, mask=3, window=(4096, 0))
     assert _lib.plan_query(w).tiles_per_item == 4
+    assert _lib.plan_query(w).kv_parts == 1
     c = batch_args(B=1, Hq=32, Hkv=8, Sq=16384, Sk=16384, mask=2)
-    assert _lib.plan_query(c).tiles_per_item == 2
+    assert (_lib.plan_query(c).tiles_per_item, _lib.plan_query(c).kv_parts) == (4, 4)
+    c.deterministic = 0
+    assert (_lib.plan_query(c).tiles_per_item, _lib.plan_query(c).kv_parts) == (1, 1)
 
 
 def test_scale_must_be_positive():
