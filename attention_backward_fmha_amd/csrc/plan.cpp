@@ -299,9 +299,9 @@ int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t el, bool forwar
     }
   }
   // tuning knobs (tests use them), each overriding its own choice
-  if (const char* e = getenv("FMHA_BWD_TILES_PER_ITEM")) {  // 1, 2 or 4
+  if (const char* e = getenv("FMHA_BWD_TILES_PER_ITEM")) {  // 1, 2, 4 or 8
     const int v = atoi(e);
-    if (p->deterministic && (v == 1 || v == 2 || v == 4)) p->tiles_per_item = v;
+    if (p->deterministic && (v == 1 || v == 2 || v == 4 || v == 8)) p->tiles_per_item = v;
   }
   if (const char* e = getenv("FMHA_BWD_KV_PARTS")) {  // 1 .. 8
     const int v = atoi(e);

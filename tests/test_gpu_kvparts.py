@@ -46,7 +46,7 @@ def test_split_key_tiles_match_oracle(case, parts, mode, monkeypatch):
     assert_grads_close(got, ref, sq, sk)
 
 
-@pytest.mark.parametrize("tiles", [2, 4])
+@pytest.mark.parametrize("tiles", [2, 4, 8])
 @pytest.mark.parametrize("parts", [3, 8])
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_parts_of_multi_tile_items_match_oracle(case, parts, tiles, monkeypatch):
