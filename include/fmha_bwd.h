@@ -247,10 +247,11 @@ typedef struct fmha_bwd_plan_info {
   int64_t acc_rows;        /* accumulator rows per head and split, or per segment and head in
                               bf16 mode (see below) */
   int32_t dq_acc_elem_bytes; /* 4 (fp32 accumulator) or 2 (bf16) */
-  int32_t kv_parts;        /* work groups that share one key tile's steps (query heads x
+  int32_t kv_parts;        /* work groups that share one work item's steps (query heads x
                               blocks); > 1 when there are too few K/V heads and tiles to fill
-                              the GPU: each part adds fp32 dK/dV partials that a final pass sums
-                              in ascending part order */
+                              the GPU, or for long causal segments in deterministic mode: each
+                              part stores fp32 dK/dV partials that the reduce stage sums in
+                              ascending part order (see below) */
   int64_t dbias_acc_offset;  /* byte offset of the fp32 full-shape dS [B][Hq][Sq][Sk] (dbias) */
   int64_t dbias_acc_bytes;   /* 0 without dbias, or when dbias is full-shape (written directly) */
   int64_t reduce_read_bytes; /* bytes of the dQ accumulator the reduce stage reads (the
@@ -273,7 +274,13 @@ typedef struct fmha_bwd_plan_info {
    count rounded up to a multiple of 16, and query i of segment b at row i of slot (b, h):
    the slot is indexed by the logical position, so neither the physical (padded) layout of
    the tensors nor other segments' rows can move it.  The unscaled sum dS K is accumulated
-   there; the reduction multiplies by scale and rounds to bf16 into dq. */
+   there; the reduction multiplies by scale and rounds to bf16 into dq.
+   dK/dV partials (kv_parts > 1): fp32 [kv_parts][Hkv][rows_k][d_qk + d_v], rows_k = B*Sk in
+   batch mode (key j of batch entry b at row b*Sk + j), else the last entry of the padded or
+   plain key offsets (key j of segment b at row start_b + j); each row holds the unscaled dK
+   sum, then the dV sum, of the part's steps.  The reduce stage writes dK = bf16(scale * sum)
+   and dV = bf16(sum) over the parts; with kv_parts > 1 dK and dV are therefore written by the
+   reduce stage, not the main one. */
 
 FMHA_BWD_API int fmha_bwd_plan_query(const fmha_bwd_args* args, fmha_bwd_plan_info* info);
 
