@@ -202,7 +202,7 @@ def cpu_baseline(w, budget_s):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (each GPU would run "
+        print("bench.py measures one GPU: the library has no multi-GPU path (each GPU would run "
               "its own share of heads/segments independently); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     if args.copy_probe_mib:
