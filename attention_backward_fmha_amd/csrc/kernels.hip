@@ -875,8 +875,8 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
 // Stage 3: dQ = bf16(scale * sum of the partials), one block of TM rows per work group.
 // Deterministic mode sums, in ascending split order, exactly the key tiles whose rows meet the
 // block (qblocks_for_tile, as the main kernel) -- a contiguous range of tiles, since both ends
-// of a tile's query range move monotonically with its keys; the next split's loads are in
-// flight while the current one is added.
+// of a tile's query range move monotonically with its keys; the next pair of splits is in
+// flight while the current pair is added.
 // ------------------------------------------------------------------------------------------
 template <int DQK, int TM>
 __device__ __forceinline__ void reduce_tiles(const KParams& p, const Seg& sg, bool group, int b,
@@ -907,49 +907,51 @@ __device__ __forceinline__ void reduce_tiles(const KParams& p, const Seg& sg, bo
   }
   const float* base = p.dq_acc + (int64_t)h * p.head_stride + (sg.acc_row0 + (int64_t)qb * TM) * DQK;
   f32x4 acc[PPT][4];
-  f32x4 cur[PPT][4];
 #pragma unroll
   for (int pr = 0; pr < PPT; ++pr)
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc[pr][u] = cur[pr][u] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto load = [&](int jt, f32x4 (&x)[PPT][4]) {
-    const float* src = base + (int64_t)jt * p.split_stride;
+    for (int u = 0; u < 4; ++u) acc[pr][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // splits j, j+1 into x[0], x[1].  The loads are issued unconditionally, so the waits before
+  // the adds count exactly the loads issued after them; a split past jhi has an empty
+  // resource (loads return 0 and touch no memory) and is not added.
+  auto load2 = [&](int j, f32x4 (&x)[2][PPT][4]) {
 #pragma unroll
-    for (int pr = 0; pr < PPT; ++pr) {
-      const int pair = tid + 256 * pr;
-      if ((NT * 64) % 256 == 0 || pair < NT * 64) {
+    for (int t = 0; t < 2; ++t) {
+      const bool in = j + t <= jhi;
+      const __amdgpu_buffer_rsrc_t r = buffer_rsrc(base + (in ? (int64_t)(j + t) * p.split_stride : 0),
+                                                   in ? (uint32_t)(NT * 1024 * 4) : 0u);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) x[pr][u] = *(const f32x4*)(src + pair * 16 + 4 * u);
+      for (int pr = 0; pr < PPT; ++pr) {
+        const int pair = tid + 256 * pr;
+        if ((NT * 64) % 256 == 0 || pair < NT * 64) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            x[t][pr][u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (pair * 16 + 4 * u) * 4, 0, 0));
+        }
       }
     }
   };
-  // two splits per iteration, the next two in flight
-  auto add = [&](const f32x4 (&x)[PPT][4]) {
+  auto add2 = [&](int j, const f32x4 (&x)[2][PPT][4]) {
 #pragma unroll
-    for (int pr = 0; pr < PPT; ++pr)
+    for (int t = 0; t < 2; ++t) {
+      if (j + t > jhi) continue;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) acc[pr][u] += x[pr][u];
+      for (int pr = 0; pr < PPT; ++pr)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc[pr][u] += x[t][pr][u];
+    }
   };
-  f32x4 nxt[PPT][4];
-#pragma unroll
-  for (int pr = 0; pr < PPT; ++pr)
-#pragma unroll
-    for (int u = 0; u < 4; ++u) nxt[pr][u] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (jhi >= jlo) load(jlo, cur);
-  if (jhi >= jlo + 1) load(jlo + 1, nxt);
-  for (int jt = jlo; jt <= jhi; jt += 2) {  // ascending split order
-    f32x4 c2[PPT][4] = {}, n2[PPT][4] = {};
-    if (jt + 2 <= jhi) load(jt + 2, c2);
-    if (jt + 3 <= jhi) load(jt + 3, n2);
-    add(cur);
-    if (jt + 1 <= jhi) add(nxt);
-#pragma unroll
-    for (int pr = 0; pr < PPT; ++pr)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        cur[pr][u] = c2[pr][u];
-        nxt[pr][u] = n2[pr][u];
-      }
+  // Two register buffers of two splits each take turns, so that the next pair of splits is
+  // in flight while the current pair is added and no registers are copied between
+  // iterations (a copy would make each iteration wait for the loads it has just issued).
+  // The adds run in ascending split order.
+  f32x4 xa[2][PPT][4], xb[2][PPT][4];
+  if (jhi >= jlo) load2(jlo, xa);
+  for (int jt = jlo; jt <= jhi; jt += 4) {
+    load2(jt + 2, xb);
+    add2(jt, xa);
+    load2(jt + 4, xa);
+    add2(jt + 2, xb);
   }
   const int64_t q0 = (int64_t)qb * TM;
 #pragma unroll
