@@ -759,7 +759,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
         if (NT % 4 == 0 || ti < NT) {
 #pragma unroll
           for (int u = 0; u < 4; ++u)
-            prev[tt][u] = __builtin_amdgcn_raw_buffer_load_b128(rprev, (ti * 1024 + lane * 16) * 4 + 16 * u, 0, 0);
+            prev[tt][u] = __builtin_amdgcn_raw_buffer_load_b128(rprev, (ti * 1024 + u * 256 + lane * 4) * 4, 0, 0);
         }
       }
     }
@@ -768,7 +768,9 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
 
     // ---- dQ_i partial = dS K_j  (reduction over the tile's 128 keys) ----
     // Deterministic: the item's split block of this step (its own rows, padding included),
-    // the earlier tiles' sum plus this tile's, stored lane by lane per 32x32 tile.  Atomic:
+    // the earlier tiles' sum plus this tile's, per 32x32 tile as four 1 KB chunks (chunk u =
+    // result registers 4u .. 4u+3 of every lane, lane order), so each 16-byte-per-lane store
+    // or read-back covers one contiguous kilobyte.  Atomic:
     // fp32 adds into the row-major accumulator; the resource covers the block's valid rows,
     // so rows past the segment end are dropped (offsets go entirely in the per-lane operand:
     // the scalar offset is outside the range check).
@@ -795,7 +797,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
           acc = mfma(da[kk], bk, acc);
         }
         if (DET) {
-          const int voff = (ti * 1024 + lane * 16) * 4;
+          const int voff = (ti * 1024 + lane * 4) * 4;
 #pragma unroll
           for (int u = 0; u < 4; ++u)
             __builtin_amdgcn_raw_buffer_store_b128(
@@ -803,7 +805,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
                       __float_as_uint(__uint_as_float(prev[tt][u][1]) + acc[4 * u + 1]),
                       __float_as_uint(__uint_as_float(prev[tt][u][2]) + acc[4 * u + 2]),
                       __float_as_uint(__uint_as_float(prev[tt][u][3]) + acc[4 * u + 3])},
-                rdq, voff + 16 * u, 0, 0);
+                rdq, voff + 1024 * u, 0, 0);
         } else if (DQM == 2) {
           // packed bf16 adds.  Each lane packs rows (k, 8+k) of its column; lanes 2c and 2c+1
           // swap the packed words, and the even lane keeps row k of columns 2c, 2c+1, the odd
@@ -926,7 +928,7 @@ __device__ __forceinline__ void reduce_tiles(const KParams& p, const Seg& sg, bo
         if ((NT * 64) % 256 == 0 || pair < NT * 64) {
 #pragma unroll
           for (int u = 0; u < 4; ++u)
-            x[t][pr][u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (pair * 16 + 4 * u) * 4, 0, 0));
+            x[t][pr][u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, ((pair >> 6) * 1024 + u * 256 + (pair & 63) * 4) * 4, 0, 0));
         }
       }
     }

@@ -268,8 +268,10 @@ typedef struct fmha_bwd_plan_info {
    the tile_m*d_qk values starting at row a_b + i*tile_m, a_b = (first D row of segment b) +
    b*tile_m, so blocks of different segments never share rows.  Inside a block the values
    are grouped in 32x32 tiles, tile t = (r/32)*(d_qk/32) + c/32 at offset 1024*t, and tile
-   element (r, c) (r, c < 32) at 16*(c + 32*((r/4)%2)) + 4*(r/8) + r%4: the result layout of
-   a 32x32 matrix-core product, stored lane by lane.  bf16 mode (dq_acc_dtype =
+   element (r, c) (r, c < 32) at 256*(r/8) + 4*(c + 32*((r/4)%2)) + r%4: the result layout of
+   a 32x32 matrix-core product (lane c + 32*((r/4)%2), register 4*(r/8) + r%4) stored as four
+   1 KB chunks, chunk u holding registers 4u .. 4u+3 of every lane in lane order, so that
+   one 16-byte-per-lane access covers a contiguous kilobyte.  bf16 mode (dq_acc_dtype =
    FMHA_DQ_ACC_BF16): bf16 [B][Hq][acc_rows][d_qk], acc_rows = the longest segment's query
    count rounded up to a multiple of 16, and query i of segment b at row i of slot (b, h):
    the slot is indexed by the logical position, so neither the physical (padded) layout of

@@ -60,12 +60,12 @@ def _touch(mask, window, lq, lk, tm, tn):
 def _block_offsets(tm, d):
     """Offset of element (r, c) inside a deterministic accumulator block, as documented with
     fmha_bwd_plan_info: 32x32 tiles t = (r/32)*(d/32) + c/32 at 1024*t, element (r, c) of a
-    tile at 16*(c + 32*((r/4)%2)) + 4*(r/8) + r%4."""
+    tile at 256*(r/8) + 4*(c + 32*((r/4)%2)) + r%4."""
     r = np.arange(tm)[:, None]
     c = np.arange(d)[None, :]
     t = (r // 32) * (d // 32) + c // 32
     rr, cc = r % 32, c % 32
-    return 1024 * t + 16 * (cc + 32 * ((rr // 4) % 2)) + 4 * (rr // 8) + rr % 4
+    return 1024 * t + 256 * (rr // 8) + 4 * (cc + 32 * ((rr // 4) % 2)) + rr % 4
 
 
 @pytest.mark.parametrize("mask,window", [(NONE, (-1, -1)), (TL, (-1, -1)), (WIN, (100, 0))])
