@@ -744,10 +744,11 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
                           (sg.acc_row0 + q0) * DQK, (uint32_t)TM * DQK * 4u)
         : buffer_rsrc(p.dq_acc + (int64_t)h * p.head_stride + (sg.acc_row0 + q0) * DQK,
                       (uint32_t)nq * DQK * 4u);
-    // bf16 mode: slot (b, h) of the bf16 accumulator, rows = logical query positions
+    // bf16 mode: the step's block of slot (b, h) of the bf16 accumulator (rows = logical query
+    // positions; the slot is padded to whole blocks, so the block is inside it)
     const __amdgpu_buffer_rsrc_t r16 =
         buffer_rsrc((const uint16_t*)p.dq_acc + (int64_t)b * p.split_stride + (int64_t)h * p.head_stride +
-                        q0 * DQK, (uint32_t)nq * DQK * 2u);
+                        q0 * DQK, (uint32_t)TM * DQK * 2u);
     compute_step((int)q0, h);
     if (DET) {  // issued late: the S/dP accumulators are dead by now
       const int64_t qbn = q0 / TM;
@@ -809,19 +810,19 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
         } else if (DQM == 2) {
           // packed bf16 adds.  Each lane packs rows (k, 8+k) of its column; lanes 2c and 2c+1
           // swap the packed words, and the even lane keeps row k of columns 2c, 2c+1, the odd
-          // lane row 8+k.  The resource covers the block's valid rows, so the hardware range
-          // check drops rows past the segment end.  (No builtin exposes the buffer form of
-          // this atomic; it is written out, without return value, so no wait depends on it.)
+          // lane row 8+k.  The block is stored in this order: tile ti at 2048*ti bytes, the
+          // words of register pair k2 at 256*k2, lane l's word at 4*l, so each atomic covers
+          // 256 contiguous bytes.  Rows past the segment end add zeros (their P is 0) into the
+          // slot's padding.  (No builtin exposes the buffer form of this atomic; it is written
+          // out, without return value, so no wait depends on it.)
           const bool odd = (lane & 1) != 0;
           const unsigned sel = odd ? 0x03020706u : 0x05040100u;
-          const int col_off = (32 * nd + (l32 & ~1)) * 2;
 #pragma unroll
           for (int k2 = 0; k2 < 8; ++k2) {
             const unsigned mine = pack_bf16(acc[k2], acc[8 + k2]);
             const unsigned other = xor1(mine);
             const unsigned v = __builtin_amdgcn_perm(other, mine, sel);
-            const int r = odd ? 8 + k2 : k2;
-            const int voff = (32 * mq + 8 * (r >> 2) + 4 * hi + (r & 3)) * DQK * 2 + col_off;
+            const int voff = ti * 2048 + k2 * 256 + lane * 4;
             asm volatile("buffer_atomic_pk_add_bf16 %0, %1, %2, 0 offen" ::"v"(v), "v"(voff), "s"(r16));
           }
         } else {
@@ -996,26 +997,35 @@ __device__ __forceinline__ void reduce_rows(const KParams& p, const Seg& sg, boo
   }
 }
 
-// bf16 accumulator: slot (b, h), row = logical query position.
+// bf16 accumulator: slot (b, h), row = logical query position, each block of TM rows in the
+// order the main kernel's packed atomics use: tile ti = (row/32)*(DQK/32) + col/32 at 1024*ti
+// elements, and in it word w (elements 2w, 2w+1) = 64*k2 + l holds row 8*(r/4) + 4*(l/32) +
+// r%4, r = k2 + 8*(l%2), of the tile, columns 2*((l%32)/2) and the next.  Read word by word
+// (coalesced), written two dQ columns at a time.
 template <int DQK, int TM>
 __device__ __forceinline__ void convert_rows16(const KParams& p, const Seg& sg, bool group, int b,
                                                int h, int qb, int nq) {
-  constexpr int C4 = DQK / 4;                   // 4-element chunks per row
-  constexpr int PER = (TM * C4 + 255) / 256;    // chunks per thread
+  constexpr int WORDS = TM * DQK / 2;
+  static_assert(WORDS % 256 == 0, "a block is a whole number of words per thread");
+  constexpr int PER = WORDS / 256;
   const int tid = threadIdx.x;
   const int64_t q0 = (int64_t)qb * TM;
-  const uint16_t* base = (const uint16_t*)p.dq_acc + (int64_t)b * p.split_stride +
-                         (int64_t)h * p.head_stride + q0 * DQK;
+  const unsigned* base = (const unsigned*)((const uint16_t*)p.dq_acc + (int64_t)b * p.split_stride +
+                                           (int64_t)h * p.head_stride + q0 * DQK);
+  unsigned w[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) w[u] = base[tid + 256 * u];
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
-    const int c = tid + 256 * u;
-    const int r = c / C4;
-    if (r < nq) {
-      const bf16x4 x = *(const bf16x4*)(base + (int64_t)r * DQK + (c - r * C4) * 4);
-      bf16x4 o;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = (__bf16)((float)x[e] * p.scale);
-      *(bf16x4*)(p.dq + elem_off(p.dq_s, group, b, sg.q_row0 + q0 + r, h) + (c - r * C4) * 4) = o;
+    const int idx = tid + 256 * u;
+    const int ti = idx >> 9, k2 = (idx >> 6) & 7, l = idx & 63;
+    const int r = k2 + 8 * (l & 1);
+    const int row = 32 * (ti / (DQK / 32)) + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+    const int col = 32 * (ti % (DQK / 32)) + 2 * ((l & 31) >> 1);
+    if (row < nq) {
+      const bf16x2 x = __builtin_bit_cast(bf16x2, w[u]);
+      *(unsigned*)(p.dq + elem_off(p.dq_s, group, b, sg.q_row0 + q0 + row, h) + col) =
+          pack_bf16((float)x[0] * p.scale, (float)x[1] * p.scale);
     }
   }
 }

@@ -13,9 +13,10 @@
 //   dbias_acc fp32 [B][Hq][Sq][Sk]              full-shape dS when dbias is requested
 //   dkv_acc fp32 [kv_parts][Hkv][rows_k][d_qk + d_v]  dK, dV partials when kv_parts > 1
 //           or bf16 [B][Hq][acc_rows][d_qk]       bf16 atomic mode: one slot of
-//                                                 acc_rows = pad16(longest lq) rows per
-//                                                 (segment, head), indexed by the logical
-//                                                 query position
+//                                                 acc_rows = the longest lq rounded up to
+//                                                 tile_m rows per (segment, head), indexed
+//                                                 by the logical query position, each block
+//                                                 of tile_m rows in matrix-core tile order
 // One layout serves batch and group mode: row = b*Sq + i in batch mode and seqstart_q[b] + i
 // in group mode (the physical token), so a ragged segment never aliases another one's rows --
 // unlike the layout mix-up in "[ROCm] Fix THD/ragged dQ backward on the bf16 dq_shuffle path
@@ -314,7 +315,7 @@ int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t el, bool forwar
 
   p->acc_pad = p->deterministic ? p->tile_m : 0;
   p->acc_rows = p->rows_q + (int64_t)p->B * p->acc_pad;
-  if (p->dq_bf16) p->acc_rows = align_up(max_lq, 16);  // one slot per (segment, head)
+  if (p->dq_bf16) p->acc_rows = align_up(max_lq, p->tile_m);  // one slot per (segment, head)
   p->head_stride = p->acc_rows * p->d_qk;
   p->split_stride = (int64_t)p->Hq * p->head_stride;
   p->d_offset = kHeaderBytes;

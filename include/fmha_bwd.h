@@ -273,9 +273,13 @@ typedef struct fmha_bwd_plan_info {
    1 KB chunks, chunk u holding registers 4u .. 4u+3 of every lane in lane order, so that
    one 16-byte-per-lane access covers a contiguous kilobyte.  bf16 mode (dq_acc_dtype =
    FMHA_DQ_ACC_BF16): bf16 [B][Hq][acc_rows][d_qk], acc_rows = the longest segment's query
-   count rounded up to a multiple of 16, and query i of segment b at row i of slot (b, h):
-   the slot is indexed by the logical position, so neither the physical (padded) layout of
-   the tensors nor other segments' rows can move it.  The unscaled sum dS K is accumulated
+   count rounded up to a multiple of tile_m, and query i of segment b in block i/tile_m of
+   slot (b, h): the slot is indexed by the logical position, so neither the physical
+   (padded) layout of the tensors nor other segments' rows can move it.  Each block of
+   tile_m*d_qk values is in matrix-core tile order: tile t = (r/32)*(d_qk/32) + c/32 at
+   1024*t, and in it element pair w (elements 2w, 2w+1; w = 64*k + l, k < 8, l < 64) holds
+   row 8*(q/4) + 4*(l/32) + q%4 (q = k + 8*(l%2)) of the tile, columns 2*((l%32)/2) and the
+   next, so that each packed atomic of the main kernel covers 256 contiguous bytes.  The unscaled sum dS K is accumulated
    there; the reduction multiplies by scale and rounds to bf16 into dq.
    dK/dV partials (kv_parts > 1): fp32 [kv_parts][Hkv][rows_k][d_qk + d_v], rows_k = B*Sk in
    batch mode (key j of batch entry b at row b*Sk + j), else the last entry of the padded or

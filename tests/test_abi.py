@@ -187,15 +187,16 @@ def test_forward_argument_errors():
 
 
 def test_bf16_accumulator_plan():
-    """bf16 accumulation: one zeroed bf16 slot of pad16(longest segment) rows per (segment,
-    head), indexed by logical position, whatever the physical layout."""
+    """bf16 accumulation: one zeroed bf16 slot per (segment, head) of the longest segment's
+    rows rounded up to the query block, indexed by logical position, whatever the physical
+    layout."""
     a = batch_args(deterministic=0)
     a.dq_acc_dtype = _lib.DQ_ACC_BF16
     info = _lib.plan_query(a)
     assert _lib.workspace_size(a) == info.workspace_bytes
     assert (info.nsplits, info.needs_zero, info.dq_acc_elem_bytes) == (1, 1, 2)
-    assert info.acc_rows == 208  # Sq = 200 rounded up to 16
-    assert info.dq_acc_bytes == 2 * 4 * 208 * 128 * 2
+    assert info.tile_m == 64 and info.acc_rows == 256  # Sq = 200 rounded up to 64
+    assert info.dq_acc_bytes == 2 * 4 * 256 * 128 * 2
     lens = [103, 77, 61]
     g = group_args(lens, lens, deterministic=0)
     g.dq_acc_dtype = _lib.DQ_ACC_BF16
@@ -204,8 +205,8 @@ def test_bf16_accumulator_plan():
     g.seqstart_q_padded_dev = FAKE
     g._keep2 = pq
     info = _lib.plan_query(g)
-    assert info.rows_q == 256 and info.acc_rows == 112  # 103 -> 112
-    assert info.dq_acc_bytes == 3 * 4 * 112 * 128 * 2
+    assert info.rows_q == 256 and info.acc_rows == 128  # 103 -> 128
+    assert info.dq_acc_bytes == 3 * 4 * 128 * 128 * 2
     assert info.dq_acc_offset + info.dq_acc_bytes <= info.workspace_bytes
     assert _lib.plan_query(batch_args(deterministic=0)).dq_acc_elem_bytes == 4
 
