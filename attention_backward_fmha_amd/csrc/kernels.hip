@@ -175,9 +175,9 @@ struct MainTile {
   static constexpr int NV = (QBLK + OBLK + 255) / 256;  // blocks per thread
   static constexpr int NT = MT * (DQK / 32);            // 32x32 tiles of a dQ block
   static constexpr int NTW = (NT + 3) / 4;              // dQ tiles per wave
-  // every dQ tile of a wave uses the same 32 head-dim columns: their K operand is kept in
-  // registers for the whole work item
-  static constexpr bool KT_REGS = (DQK / 32) % 4 == 0 || NT <= 4;
+  // every dQ tile of a wave (tiles wave + 4*tt) uses the same 32 head-dim columns when the
+  // DQK/32 column tiles divide 4: their K operand is kept in registers for the whole work item
+  static constexpr bool KT_REGS = 4 % (DQK / 32) == 0 || NT <= 4;
   // a wave's staging blocks are all Q or all dO, so the choice of buffer is wave-uniform
   static_assert(QBLK % 64 == 0, "staging blocks of Q must fill whole waves");
 };
@@ -1522,7 +1522,11 @@ hipError_t launch_main(const Plan& plan, const KParams& kp, hipStream_t stream) 
   if (items == 0) return hipSuccess;
   const dim3 grid((unsigned)items);
   if (plan.d_qk == 64) {
-    launch_main_t<64, 64, 64>(plan, kp, grid, stream);
+    if (plan.tile_m == 128) {
+      launch_main_t<64, 64, 128, false>(plan, kp, grid, stream);  // bias: tile_m is 64
+    } else {
+      launch_main_t<64, 64, 64>(plan, kp, grid, stream);
+    }
   } else if (plan.d_qk == 128) {
     if (plan.tile_m == 32) {
       launch_main_t<128, 128, 32>(plan, kp, grid, stream);
@@ -1545,7 +1549,11 @@ static void launch_reduce_t(const Plan& plan, const KParams& kp, hipStream_t str
 hipError_t launch_reduce(const Plan& plan, const KParams& kp, hipStream_t stream) {
   if (plan.n_q_blocks == 0 || plan.B == 0) return hipSuccess;
   if (plan.d_qk == 64) {
-    launch_reduce_t<64, 64>(plan, kp, stream);
+    if (plan.tile_m == 128) {
+      launch_reduce_t<64, 128>(plan, kp, stream);
+    } else {
+      launch_reduce_t<64, 64>(plan, kp, stream);
+    }
   } else if (plan.d_qk == 128) {
     if (plan.tile_m == 32) {
       launch_reduce_t<128, 32>(plan, kp, stream);

@@ -122,14 +122,22 @@ int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t el, bool forwar
   p->Sk = a->Sk;
   p->d_qk = a->d_qk;
   p->d_v = a->d_v;
-  // query rows per main-kernel block: 64, or 32 for d_qk = 192 (register and LDS budget)
-  p->tile_m = a->d_qk == 192 ? 32 : 64;
-  if (const char* e = getenv("FMHA_BWD_TILE_M")) {  // tuning knob: 32 or 64 for d_qk = 128
-    if (a->d_qk == 128 && (atoi(e) == 32 || atoi(e) == 64)) p->tile_m = atoi(e);
+  // query rows per main-kernel block (register and LDS budget): 64 for d_qk = 128, 32 for
+  // d_qk = 192, and for d_qk = 64 128 rows (its smaller accumulators leave room for four
+  // 32-row tiles, which halves the per-step overheads per FLOP) except with fp32 dQ atomics,
+  // which were faster with 64-row blocks
+  const bool fp32_atomics = a->deterministic == 0 && a->dq_acc_dtype == FMHA_DQ_ACC_FP32;
+  p->tile_m = a->d_qk == 192 ? 32 : (a->d_qk == 64 && !fp32_atomics ? 128 : 64);
+  if (const char* e = getenv("FMHA_BWD_TILE_M")) {  // tuning knob: 32/64 (d_qk 128), 64/128 (d_qk 64)
+    const int v = atoi(e);
+    if ((a->d_qk == 128 && (v == 32 || v == 64)) || (a->d_qk == 64 && (v == 64 || v == 128)))
+      p->tile_m = v;
   }
-  // with a bias, d_qk = 128 takes 32-row blocks too: the bias registers of 64-row blocks do
-  // not fit beside the rest of the main kernel's registers (dropout alone does fit)
+  // with a bias, blocks are half as tall (32 rows at d_qk = 128, 64 at d_qk = 64): the bias
+  // registers of the taller blocks do not fit beside the rest of the main kernel's registers
+  // (dropout alone does fit)
   if (a->bias != nullptr && a->d_qk == 128) p->tile_m = 32;
+  if (a->bias != nullptr && a->d_qk == 64) p->tile_m = 64;
   p->tile_n = 128;
   p->deterministic = a->deterministic == 1;
   p->dq_bf16 = a->dq_acc_dtype == FMHA_DQ_ACC_BF16;

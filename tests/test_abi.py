@@ -283,6 +283,24 @@ def test_block_rows_with_bias_and_dropout_at_d128():
     assert _lib.plan_query(a).tile_m == 32
 
 
+def test_block_rows_by_head_dim():
+    """128-row query blocks at d_qk = 64 (64 with a bias or fp32 dQ atomics), 64 at 128, 32
+    at 192; the deterministic accumulator pads each segment by one block."""
+    def plan(dqk, dv, bias=False, det=1, bf16=False):
+        a = batch_args(d_qk=dqk, d_v=dv, deterministic=det)
+        if bf16:
+            a.dq_acc_dtype = _lib.DQ_ACC_BF16
+        return _lib.plan_query(_with_bias(a, 1, 1, dbias=False) if bias else a)
+    assert plan(64, 64).tile_m == 128
+    assert plan(64, 64, det=0, bf16=True).tile_m == 128
+    assert plan(64, 64, det=0).tile_m == 64  # fp32 atomics
+    assert plan(64, 64, bias=True).tile_m == 64
+    assert plan(128, 128).tile_m == 64
+    assert plan(192, 128).tile_m == 32
+    info = plan(64, 64)
+    assert info.acc_rows == info.rows_q + 2 * 128  # two batch entries, one block of padding each
+
+
 def test_bias_needs_batch_mode():
     g = group_args([5, 7], [5, 7])
     g.bias = FAKE
