@@ -80,3 +80,24 @@ def test_group_empty_and_uneven_segments():
 def test_bottom_right_rows_without_keys():
     # Lq > Lk with bottom-right causal: the first Lq - Lk rows see no key (dQ = 0)
     _run_batch(2003, 1, 300, 100, 2, 2, 64, 64, BR)
+
+
+@pytest.mark.parametrize("mode", ["det", "atomic", "atomic16"])
+@pytest.mark.parametrize("mask,window", [(TL, (-1, -1)), (BR, (-1, -1)), (WIN, (90, 7)), (NONE, (-1, -1))],
+                         ids=["tl", "br", "win90_7", "none"])
+def test_group_d64_block_heights(mask, window, mode):
+    """d = 64 takes 128-row query blocks in the deterministic and bf16-accumulator modes and 64-row
+    blocks with fp32 atomics: ragged segments around 64/128-row boundaries (2, 63..65, 127..129,
+    255, 300 queries), GQA 6/2, every mode.  Every segment has rows with two or more allowed keys
+    under each mask (where no row does, the exact dQ is 0 and a relative bar cannot hold)."""
+    lens_q = [2, 63, 64, 65, 127, 128, 129, 255, 300]
+    lens_k = [7, 65, 64, 200, 128, 3, 129, 255, 290]
+    sq, sk = seq_offsets(lens_q), seq_offsets(lens_k)
+    x = make_inputs(3101, lens_q=lens_q, lens_k=lens_k, Hq=6, Hkv=2, d_qk=64, d_v=64)
+    scale = 1.0 / np.sqrt(64)
+    o, lse = oracle_forward(x, scale=scale, mask=mask, window=window, sq=sq, sk=sk)
+    ref = oracle_backward(x, scale=scale, mask=mask, window=window, sq=sq, sk=sk)
+    det, acc = {"det": (True, "fp32"), "atomic": (False, "fp32"), "atomic16": (False, "bf16")}[mode]
+    got = run_gpu(x, o, lse, scale=scale, mask=mask, window=window, sq=sq, sk=sk,
+                  deterministic=det, dq_acc_dtype=acc)
+    assert_grads_close(got, ref, sq=sq, sk=sk)
