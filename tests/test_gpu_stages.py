@@ -144,12 +144,13 @@ def test_prepare_zeroes_the_atomic_accumulator():
     assert int(acc.count_nonzero()) == 0
 
 
-def test_deterministic_mode_is_bit_identical_over_10_runs():
+@pytest.mark.parametrize("d", [128, 64, 192], ids=["d128", "d64_128rows", "d192"])
+def test_deterministic_mode_is_bit_identical_over_10_runs(d):
     import torch
     import attention_backward_fmha_amd as F
     lens = [700, 130, 1000]
     sq = seq_offsets(lens)
-    x = make_inputs(4005, lens_q=lens, lens_k=lens, Hq=8, Hkv=2, d_qk=128, d_v=128)
+    x = make_inputs(4005, lens_q=lens, lens_k=lens, Hq=8, Hkv=2, d_qk=d, d_v=min(d, 128))
     o, lse = oracle_forward(x, scale=0.088, mask=TL, sq=sq, sk=sq)
     call, ws, t = _setup(x, o, lse, scale=0.088, mask=TL, sq=sq, sk=sq)
     stream = torch.cuda.current_stream().cuda_stream
