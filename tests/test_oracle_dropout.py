@@ -4,6 +4,9 @@
   reproduce numpy's own Philox4x64-10 bit generator exactly, which pins the round function,
   the key schedule and the round count.  The 32-bit variant that the dropout uses differs
   only in its published constants (Salmon et al., SC 2011).
+* The 32-bit variant is pinned to the published known-answer vectors of Philox4x32-10 that
+  ship with the authors' Random123 library (Salmon et al., SC 2011), so a wrong multiplier,
+  Weyl constant, word order or round count fails; planted swaps of the constants are caught.
 * Its 32-bit output is checked statistically: byte histogram, keep rate, and independence of
   heads, batches and offsets.
 * The backward with dropout is the gradient of the forward with dropout (central finite
@@ -37,6 +40,41 @@ def test_philox_structure_matches_numpy_philox4x64(key, counter):
         ctr = [(c >> (64 * w)) & (2**64 - 1) for w in range(4)]
         got = [int(x) for x in A.philox(ctr, key, **A.PHILOX_4X64)]
         assert got == raw
+
+
+# Philox4x32-10 known answers (Random123 known-answer vectors; Salmon, Moraes, Dror, Shaw,
+# "Parallel Random Numbers: As Easy as 1, 2, 3", SC 2011): counter words c0..c3, key words
+# k0, k1 -> output words.
+PHILOX4X32_KAT = [
+    ((0x00000000, 0x00000000, 0x00000000, 0x00000000), (0x00000000, 0x00000000),
+     (0x6627E8D5, 0xE169C58D, 0xBC57AC4C, 0x9B00DBD8)),
+    ((0xFFFFFFFF, 0xFFFFFFFF, 0xFFFFFFFF, 0xFFFFFFFF), (0xFFFFFFFF, 0xFFFFFFFF),
+     (0x408F276D, 0x41C83B0E, 0xA20BC7C6, 0x6D5451FD)),
+    ((0x243F6A88, 0x85A308D3, 0x13198A2E, 0x03707344), (0xA4093822, 0x299F31D0),
+     (0xD16CFE09, 0x94FDCCEB, 0x5001E420, 0x24126EA1)),
+]
+
+
+@pytest.mark.parametrize("counter,key,expect", PHILOX4X32_KAT)
+def test_philox4x32_matches_published_known_answers(counter, key, expect):
+    got = tuple(int(x) for x in A.philox(counter, key, **A.PHILOX_4X32))
+    assert got == expect
+
+
+def _kat_ok(consts):
+    return all(tuple(int(x) for x in A.philox(c, k, **consts)) == e for c, k, e in PHILOX4X32_KAT)
+
+
+@pytest.mark.parametrize("label,consts", [
+    ("multipliers swapped", dict(A.PHILOX_4X32, M=A.PHILOX_4X32["M"][::-1])),
+    ("Weyl constants swapped", dict(A.PHILOX_4X32, W=A.PHILOX_4X32["W"][::-1])),
+    ("first multiplier off by one", dict(A.PHILOX_4X32, M=(A.PHILOX_4X32["M"][0] ^ 1, A.PHILOX_4X32["M"][1]))),
+    ("second Weyl constant off by one", dict(A.PHILOX_4X32, W=(A.PHILOX_4X32["W"][0], A.PHILOX_4X32["W"][1] ^ 1))),
+    ("nine rounds", dict(A.PHILOX_4X32, rounds=9)),
+])
+def test_philox_known_answers_catch_planted_constant_mistakes(label, consts):
+    assert _kat_ok(A.PHILOX_4X32)
+    assert not _kat_ok(consts), label
 
 
 def test_philox4x32_bytes_are_uniform_and_keep_rate_matches():
