@@ -16,6 +16,8 @@ adds instead of fp32 ones: about half the atomic traffic, less accurate dQ.
 ``dropout_p``, ``philox_seed``, ``philox_offset``: dropout on the probabilities of O = P V
 (forward) and in dV, dP (backward), with the Philox keep mask of ``include/fmha_bwd.h``; the
 backward must get the forward's values.
+``tune`` (tests and tuning): a dict of layout overrides ``kernel`` (KERNEL_FOUR_WAVE or
+KERNEL_WIDE), ``tile_m``, ``tiles_per_item``, ``kv_parts``; absent keys leave the plan's choice.
 """
 
 import numpy as np
@@ -23,6 +25,7 @@ import numpy as np
 from . import _lib
 from ._lib import (  # noqa: F401
     MASK_NONE, MASK_CAUSAL_TOP_LEFT, MASK_CAUSAL_BOTTOM_RIGHT, MASK_WINDOW, DQ_ACC_FP32, DQ_ACC_BF16,
+    KERNEL_AUTO, KERNEL_FOUR_WAVE, KERNEL_WIDE,
     STAGE_DOT, STAGE_MAIN, STAGE_REDUCE, STAGE_ALL,
     Args, PlanInfo, FmhaError, status_string, workspace_size, plan_query,
 )
@@ -68,12 +71,22 @@ def _ptr(t):
     return 0 if t is None else t.data_ptr()
 
 
+def _check_lse(lse, shape):
+    """The ABI reads LSE with a unit sequence stride from device memory."""
+    if tuple(lse.shape) != tuple(shape):
+        raise ValueError("lse must have shape %s, got %s" % (tuple(shape), tuple(lse.shape)))
+    if not lse.is_cuda:
+        raise ValueError("lse must be a device tensor")
+    if lse.numel() > 0 and lse.shape[-1] > 1 and lse.stride(-1) != 1:
+        raise ValueError("lse must have a unit stride along the sequence")
+
+
 def make_call(q, k, v, o, lse, do, dq, dk, dv, *, scale=None, mask_type=MASK_NONE,
               window=(-1, -1), deterministic=True, cu_seqlens_q=None, cu_seqlens_k=None,
               cu_seqlens_q_host=None, cu_seqlens_k_host=None, max_seqlen_q=None,
               max_seqlen_k=None, cu_seqlens_q_padded=None, cu_seqlens_k_padded=None,
               cu_seqlens_q_padded_host=None, cu_seqlens_k_padded_host=None, dq_acc_dtype="fp32",
-              bias=None, dbias=None, dropout_p=0.0, philox_seed=0, philox_offset=0):
+              bias=None, dbias=None, dropout_p=0.0, philox_seed=0, philox_offset=0, tune=None):
     """Fill the C argument struct from tensors (no device work)."""
     group = cu_seqlens_q is not None
     d_qk = q.shape[-1]
@@ -99,6 +112,7 @@ def make_call(q, k, v, o, lse, do, dq, dk, dv, *, scale=None, mask_type=MASK_NON
         a.seqstart_q_dev = cu_seqlens_q.data_ptr()
         a.seqstart_k_dev = cu_seqlens_k.data_ptr()
         a.Hq, a.Hkv = q.shape[1], k.shape[1]
+        _check_lse(lse, (a.Hq, q.shape[0]))
         a.lse_stride[0] = 0
         a.lse_stride[1] = lse.stride(0)
         for side, dev_t, host in (("q", cu_seqlens_q_padded, cu_seqlens_q_padded_host),
@@ -114,6 +128,7 @@ def make_call(q, k, v, o, lse, do, dq, dk, dv, *, scale=None, mask_type=MASK_NON
     else:
         a.B, a.Sq, a.Hq = q.shape[0], q.shape[1], q.shape[2]
         a.Sk, a.Hkv = k.shape[1], k.shape[2]
+        _check_lse(lse, (a.B, a.Hq, a.Sq))
         a.lse_stride[0] = lse.stride(0)
         a.lse_stride[1] = lse.stride(1)
     a.d_qk, a.d_v = d_qk, d_v
@@ -124,6 +139,10 @@ def make_call(q, k, v, o, lse, do, dq, dk, dv, *, scale=None, mask_type=MASK_NON
     if dq_acc_dtype not in ("fp32", "bf16"):
         raise ValueError("dq_acc_dtype must be 'fp32' or 'bf16'")
     a.dq_acc_dtype = DQ_ACC_BF16 if dq_acc_dtype == "bf16" else DQ_ACC_FP32
+    for key, val in (tune or {}).items():
+        if key not in ("kernel", "tile_m", "tiles_per_item", "kv_parts"):
+            raise ValueError("unknown tune key %r" % key)
+        setattr(a, "tune_" + key, int(val))
     a.p_drop = float(dropout_p)
     a.philox_seed = int(philox_seed) & (2**64 - 1)
     a.philox_offset = int(philox_offset) & (2**64 - 1)
@@ -158,7 +177,7 @@ def bwd(q, k, v, o, lse, do, *, scale=None, mask_type=MASK_NONE, window=(-1, -1)
         cu_seqlens_k_host=None, max_seqlen_q=None, max_seqlen_k=None, cu_seqlens_q_padded=None,
         cu_seqlens_k_padded=None, cu_seqlens_q_padded_host=None, cu_seqlens_k_padded_host=None,
         workspace=None, out=None, dq_acc_dtype="fp32", bias=None, bias_grad=False, dropout_p=0.0,
-        philox_seed=0, philox_offset=0):
+        philox_seed=0, philox_offset=0, tune=None):
     """Gradients (dq, dk, dv) of softmax attention, and dbias when ``bias_grad``; see the
     module docstring for layouts."""
     import torch
@@ -188,7 +207,7 @@ def bwd(q, k, v, o, lse, do, *, scale=None, mask_type=MASK_NONE, window=(-1, -1)
                      cu_seqlens_q_padded_host=cu_seqlens_q_padded_host,
                      cu_seqlens_k_padded_host=cu_seqlens_k_padded_host, dq_acc_dtype=dq_acc_dtype,
                      bias=bias, dbias=dbias, dropout_p=dropout_p, philox_seed=philox_seed,
-                     philox_offset=philox_offset)
+                     philox_offset=philox_offset, tune=tune)
     nbytes = call.workspace_size()
     if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)

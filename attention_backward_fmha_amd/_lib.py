@@ -6,7 +6,7 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libfmha_bwd.so")
 
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 MASK_NONE = 0
 MASK_CAUSAL_TOP_LEFT = 1
@@ -15,6 +15,10 @@ MASK_WINDOW = 3
 
 DQ_ACC_FP32 = 0
 DQ_ACC_BF16 = 1
+
+KERNEL_AUTO = 0
+KERNEL_FOUR_WAVE = 1
+KERNEL_WIDE = 2
 
 OK = 0
 ERR_INVALID_ARG = -1
@@ -95,6 +99,10 @@ class Args(ctypes.Structure):
         ("reserved2", ctypes.c_int32),
         ("philox_seed", ctypes.c_uint64),
         ("philox_offset", ctypes.c_uint64),
+        ("tune_kernel", ctypes.c_int32),
+        ("tune_tile_m", ctypes.c_int32),
+        ("tune_tiles_per_item", ctypes.c_int32),
+        ("tune_kv_parts", ctypes.c_int32),
     ]
 
     def __init__(self, **kw):
@@ -133,6 +141,8 @@ class PlanInfo(ctypes.Structure):
         ("reduce_read_bytes", ctypes.c_int64),
         ("dkv_acc_offset", ctypes.c_int64),
         ("dkv_acc_bytes", ctypes.c_int64),
+        ("kernel", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
     def as_dict(self):

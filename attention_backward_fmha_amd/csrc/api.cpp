@@ -36,10 +36,11 @@ void log_plan(const fmha::Plan& p, const char* where) {
   if (!log_enabled()) return;
   fprintf(stderr,
           "[fmha_bwd] %s: mode=%s dq_acc=%s B=%d Hq=%d Hkv=%d Sq=%d Sk=%d d=(%d,%d) tile=(%d,%d) "
-          "kv_tiles=%d q_blocks=%d nsplits=%d zero=%d ws=%lld (D@%lld acc@%lld+%lld)\n",
+          "kv_tiles=%d q_blocks=%d nsplits=%d T=%d parts=%d kernel=%d zero=%d ws=%lld (D@%lld acc@%lld+%lld)\n",
           where, p.group_mode ? "group" : "batch",
           p.deterministic ? "split-fp32" : (p.dq_bf16 ? "atomic-bf16" : "atomic-fp32"), p.B, p.Hq, p.Hkv, p.Sq, p.Sk, p.d_qk, p.d_v,
-          p.tile_m, p.tile_n, p.n_kv_tiles, p.n_q_blocks, p.nsplits, (int)p.needs_zero,
+          p.tile_m, p.tile_n, p.n_kv_tiles, p.n_q_blocks, p.nsplits, p.tiles_per_item, p.kv_parts,
+          p.kernel, (int)p.needs_zero,
           (long long)p.workspace_bytes, (long long)p.d_offset, (long long)p.dq_acc_offset,
           (long long)p.dq_acc_bytes);
 }
@@ -100,6 +101,7 @@ fmha::KParams make_params(const fmha_bwd_args* a, const fmha::Plan& p, void* ws)
   k.scale = a->scale;
   k.scale_log2 = a->scale * 1.4426950408889634f;
   k.tile_m = p.tile_m;
+  k.tile_n = p.tile_n;
   if (p.has_bias) {
     k.bias = (const uint16_t*)a->bias;
     k.bias_s[0] = p.bias_b == 1 ? 0 : a->bias_stride[0];
@@ -271,6 +273,7 @@ int fmha_bwd_plan_query(const fmha_bwd_args* args, fmha_bwd_plan_info* info) {
   info->pairs = fmha::count_pairs(args);
   info->flops = 2.0 * (3.0 * p.d_qk + 2.0 * p.d_v) * (double)info->pairs;
   info->reduce_read_bytes = fmha::reduce_read_bytes(args, p);
+  info->kernel = p.kernel;
   return FMHA_OK;
 }
 

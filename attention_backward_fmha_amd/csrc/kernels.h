@@ -43,6 +43,7 @@ struct KParams {
   float scale;
   float scale_log2;  // scale * log2(e)
   int tile_m;        // query rows per main-kernel block
+  int tile_n;        // keys per main-kernel tile
   // additive bias (batch mode): plane (b, h) at bias + b*bias_s[0] + h*bias_s[1] (strides of
   // broadcast dimensions are 0), row stride bias_s[2]
   const uint16_t* bias;
@@ -65,6 +66,7 @@ struct KParams {
 hipError_t launch_dot(const Plan& plan, const KParams& kp, hipStream_t stream);
 hipError_t launch_fwd(const Plan& plan, const KParams& kp, hipStream_t stream);
 hipError_t launch_main(const Plan& plan, const KParams& kp, hipStream_t stream);
+hipError_t launch_main_wide(const Plan& plan, const KParams& kp, dim3 grid, hipStream_t stream);
 hipError_t launch_reduce(const Plan& plan, const KParams& kp, hipStream_t stream);
 hipError_t launch_dbias(const Plan& plan, const KParams& kp, hipStream_t stream);
 hipError_t launch_dkv_reduce(const Plan& plan, const KParams& kp, hipStream_t stream);

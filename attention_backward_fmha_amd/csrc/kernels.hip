@@ -23,84 +23,12 @@
 // per work item with ds_read_b64_tr_b16: in each 16-lane group, lane s points at 4 consecutive
 // elements of row (s/4), columns 4*(s%4)..4*(s%4)+3 of a 4x16 block, and lane i receives
 // column i of the block (4 values, one per row).
+#include "device.h"
 #include "kernels.h"
 #include "tiling.h"
 
 namespace fmha {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
-
-constexpr float kLog2e = 1.4426950408889634f;
-
-struct Seg {
-  int64_t q_row0;   // first tensor row of the segment (0 in batch mode)
-  int64_t k_row0;
-  int64_t lq, lk;   // segment lengths
-  int64_t ws_row0;  // first workspace row of D and LSE2 (b*Sq in batch mode)
-  int64_t acc_row0; // first accumulator row: ws_row0 + b*acc_pad
-  int64_t kws_row0; // first key row of the dK/dV partials (b*Sk in batch mode)
-};
-
-// Segment bounds; b is uniform across the work group and readfirstlane keeps the loaded
-// offsets in scalar registers, so everything derived from them stays wave-uniform.
-__device__ __forceinline__ Seg seg_of(const KParams& p, int b) {
-  Seg s;
-  if (p.seqstart_q != nullptr) {
-    const int q0 = __builtin_amdgcn_readfirstlane(p.seqstart_q[b]);
-    const int q1 = __builtin_amdgcn_readfirstlane(p.seqstart_q[b + 1]);
-    const int k0 = __builtin_amdgcn_readfirstlane(p.seqstart_k[b]);
-    const int k1 = __builtin_amdgcn_readfirstlane(p.seqstart_k[b + 1]);
-    s.q_row0 = p.slot_q ? __builtin_amdgcn_readfirstlane(p.slot_q[b]) : q0;
-    s.lq = (int64_t)q1 - q0;
-    s.k_row0 = p.slot_k ? __builtin_amdgcn_readfirstlane(p.slot_k[b]) : k0;
-    s.lk = (int64_t)k1 - k0;
-    s.ws_row0 = s.q_row0;
-    s.kws_row0 = s.k_row0;
-  } else {
-    s.q_row0 = 0;
-    s.k_row0 = 0;
-    s.lq = p.Sq;
-    s.lk = p.Sk;
-    s.ws_row0 = (int64_t)b * p.Sq;
-    s.kws_row0 = (int64_t)b * p.Sk;
-  }
-  s.acc_row0 = s.ws_row0 + (int64_t)b * p.acc_pad;
-  return s;
-}
-
-// Element offset of (segment b, tensor row `row`, head h, column 0).
-__device__ __forceinline__ int64_t elem_off(const int64_t s[3], bool group, int b, int64_t row,
-                                            int h) {
-  return (group ? 0 : (int64_t)b * s[0]) + row * s[1] + (int64_t)h * s[2];
-}
-
-__device__ __forceinline__ bf16x8 tr_read(const uint16_t* p0, const uint16_t* p1) {
-  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0));
-  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p1));
-  const s16x8 c = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, c);
-}
-
-// Raw buffer resource over [base, base + bytes): loads past the end return 0 and stores or
-// atomics past the end are dropped by the hardware range check.  Callers pass every offset in
-// the per-lane offset operand and 0 as the scalar offset.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ uint16_t to_bf16_bits(float x) {
-  return __builtin_bit_cast(uint16_t, (__bf16)x);
-}
 
 // ------------------------------------------------------------------------------------------
 // Stage 1: D = rowsum(dO * O).  DV/8 lanes per row, 16 bytes per lane per tensor.
@@ -198,21 +126,6 @@ __device__ __forceinline__ int tpos(int q) {
 __device__ __forceinline__ int qrow(int r) { return r ^ ((r >> 4) & 3); }
 __device__ __forceinline__ int dsrow(int r) { return r ^ ((r & 8) >> 1); }
 
-// Key (inside the wave's 32) held by lane l32: bit 4 of the lane is bit 0 of the key and lane
-// bits 0..3 are key bits 1..4.  With it the dS exchange below ends with lane bits 2, 3 naming
-// an aligned group of 8 keys and the exchanged register bits naming the key inside the group.
-__device__ __forceinline__ int kmap(int l) {
-  return ((l >> 4) & 1) | ((l & 15) << 1);
-}
-
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
-  return __builtin_bit_cast(unsigned, bf16x2{(__bf16)lo, (__bf16)hi});
-}
-
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3",
 // SC 2011) of counter c under key (k0, k1), in place.  The dropout keep mask of element
 // (b, h, i, j) is byte (j % 4) of output word (i % 4) for counter (j/4, i/4, b*Hq + h, offset).
@@ -248,23 +161,6 @@ __device__ __forceinline__ void byte_transpose4(const unsigned (&w)[4], unsigned
 
 __device__ __forceinline__ unsigned sel4(const unsigned (&v)[4], unsigned i) {
   return (i & 2u) ? ((i & 1u) ? v[3] : v[2]) : ((i & 1u) ? v[1] : v[0]);
-}
-
-// Value of lane (l ^ 1) and of lane (l ^ 2) (DPP quad permutations).
-__device__ __forceinline__ unsigned xor1(unsigned v) {
-  return (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);
-}
-__device__ __forceinline__ unsigned xor2(unsigned v) {
-  return (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);
-}
-__device__ __forceinline__ unsigned xor3(unsigned v) {
-  return (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0x1B, 0xF, 0xF, true);
-}
-// Value of lane (l ^ 16): v_permlane16_swap of v with itself leaves lane l ^ 16's value in
-// the second result for lanes with bit 4 clear and in the first for the others.
-__device__ __forceinline__ unsigned xor16(unsigned v, int lane) {
-  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-  return (lane & 16) ? r[0] : r[1];
 }
 
 // dS of one 32-query tile to LDS, one row per query.  On entry d[4c + e] is dS(query
@@ -884,7 +780,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
 template <int DQK, int TM>
 __device__ __forceinline__ void reduce_tiles(const KParams& p, const Seg& sg, bool group, int b,
                                              int h, int qb, int nq, int part) {
-  constexpr int TN = 128;
+  const int TN = p.tile_n;
   constexpr int NT = (TM / 32) * (DQK / 32);   // 32x32 tiles per block
   constexpr int PPT = 1;                        // (tile, lane) pairs per thread
   const int tid = threadIdx.x + 256 * part;     // the block's pairs are split over work groups
@@ -1521,6 +1417,7 @@ hipError_t launch_main(const Plan& plan, const KParams& kp, hipStream_t stream) 
                         plan.kv_parts * plan.Hkv * plan.B;
   if (items == 0) return hipSuccess;
   const dim3 grid((unsigned)items);
+  if (plan.kernel == FMHA_KERNEL_WIDE) return launch_main_wide(plan, kp, grid, stream);
   if (plan.d_qk == 64) {
     if (plan.tile_m == 128) {
       launch_main_t<64, 64, 128, false>(plan, kp, grid, stream);  // bias: tile_m is 64
@@ -1569,7 +1466,7 @@ hipError_t launch_reduce(const Plan& plan, const KParams& kp, hipStream_t stream
 hipError_t launch_dkv_reduce(const Plan& plan, const KParams& kp, hipStream_t stream) {
   if (plan.kv_parts <= 1 || plan.B == 0 || plan.n_kv_tiles == 0) return hipSuccess;
   if (plan.kv_parts > 8) return hipErrorInvalidValue;  // the reduce sums at most 8 parts
-  const dim3 grid((unsigned)(plan.n_kv_tiles * (128 / kDkvRows)), (unsigned)plan.Hkv, (unsigned)plan.B);
+  const dim3 grid((unsigned)(plan.n_kv_tiles * (plan.tile_n / kDkvRows)), (unsigned)plan.Hkv, (unsigned)plan.B);
   if (plan.d_qk == 64) {
     hipLaunchKernelGGL((k_dkv_reduce<64, 64>), grid, dim3(256), 0, stream, kp);
   } else if (plan.d_qk == 128) {

@@ -1,0 +1,520 @@
+// kernels_wide.hip -- the main backward kernel in its wide layout (gfx950): eight waves per
+// work group, two per SIMD, 256-key tiles, 32-row query blocks.  Serves d_qk = d_v = 128
+// without bias or dropout; kernels.hip holds the four-wave layout for the other cases and the
+// other stages.
+#include "device.h"
+#include "kernels.h"
+#include "tiling.h"
+
+namespace fmha {
+namespace {
+
+// ------------------------------------------------------------------------------------------
+// Stage 2, wide layout (d_qk = d_v = 128, no bias, no dropout).  512 threads = 8 waves, two
+// per SIMD, so that one wave's matrix products overlap the other's LDS reads and exponentials
+// (one wave per SIMD cannot keep more than about a quarter of the CU's LDS bandwidth busy).
+// A key tile has 256 keys; wave w owns keys 32w .. 32w+31 (lane l32 holds key 32w +
+// kmap(l32)), keeps its dK and dV accumulators and its V rows in registers, and reads K from
+// LDS.  A step is one query block of 32 rows of one query head:
+//   S = Q K_w^T, dP = dO V_w^T              A operands: Q, dO rows from LDS (16-byte reads)
+//   P = exp2(S*scale*log2e - L), dS = P (dP - D)            the lane's key, 16 queries
+//   dV_w += P^T dO, dK_w += dS^T Q          A from registers, B by transposing LDS reads
+//   dS -> LDS (query-major)
+//   dQ = dS K over the tile's 256 keys      one 32x32 output tile per wave, done by the four
+//                                           waves of one half, the halves taking turns
+// Q, dO, L, D and dS are double-buffered, so a step has one barrier: the half that computes
+// the step's dQ does it at the start of the next step, while the other half already works on
+// that step.
+//
+// LDS tiles are row-major with rows padded by 16 bytes, so that consecutive rows start 4
+// banks apart and every LDS offset of the unrolled loops is a per-lane base plus a constant:
+//   - 16-byte row reads (16 lanes read 16 consecutive rows at one column) touch 64 distinct
+//     banks;
+//   - a transposing 8-byte read takes 4 rows of 32 bytes per 16-lane group, and is free of
+//     conflicts when its 4 rows are spaced by 2 (2 row offsets = 8 banks): the dV/dK products
+//     read query rows {0, 2, 8, 10} (+1) of a 16-row group, i.e. their reduction slots take
+//     the S/dP result registers in that order, and the K tile is stored with its keys
+//     permuted inside each 32-key block (krow below) so that 4 consecutive keys land on 4
+//     rows spaced by 2, while the 16 keys one row read of S takes (every other key, see
+//     kmap) land on 16 distinct rows.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+
+constexpr int kRowQ = 136;   // Q, dO and K rows: 128 bf16 + 8 of padding (see below)
+constexpr int kRowS = 264;   // dS rows: 256 bf16 + 8
+
+// LDS row of key k of the tile.  32-key blocks stay in place; inside a block the key's bits
+// k0..k4 go to row bits r0 = k3, r1 = k0 ^ k2, r2 = k1, r3 = k4, r4 = k2 (one-to-one, and
+// linear over GF(2)).
+__device__ __forceinline__ int krow(int k) {
+  return (k & ~31) | ((k >> 3) & 1) | (((k ^ (k >> 2)) & 1) << 1) | (((k >> 1) & 1) << 2) |
+         (((k >> 4) & 1) << 3) | (((k >> 2) & 1) << 4);
+}
+
+// Physical row of dS row r: bits 0..3 of r go to bits (0, 2, 1, 3).  The dS exchange writes
+// rows {0, 2, 8, 10} (+ a constant) from one 16-lane group, which then start 16 banks apart;
+// the 16 consecutive rows the dQ operand reads stay on distinct banks.
+__device__ __forceinline__ int ds_row(int r) {
+  return (r & 16) | (r & 1) | ((r >> 1) & 1) << 2 | ((r >> 2) & 1) << 1 | (r & 8);
+}
+
+// x as three bf16 parts (x = p1 + p2 + p3 to within fp32 rounding) followed by five zeros.
+__device__ __forceinline__ u32x4 split3(float x) {
+  const __bf16 p1 = (__bf16)x;
+  const float r1 = x - (float)p1;
+  const __bf16 p2 = (__bf16)r1;
+  const __bf16 p3 = (__bf16)(r1 - (float)p2);
+  return u32x4{__builtin_bit_cast(unsigned, bf16x2{p1, p2}), (unsigned)__builtin_bit_cast(uint16_t, p3), 0u, 0u};
+}
+
+// dS of the wave's 32 keys (columns 32*wave ..) for the step's 32 queries into the swizzled
+// query-major tile; the exchange is write_ds_tile's.
+__device__ __forceinline__ void write_ds_wide(uint16_t* ds, const float (&d)[16], int wave, int lane) {
+  unsigned w[4][2];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+#pragma unroll
+    for (int e1 = 0; e1 < 2; ++e1) {
+      const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(d[4 * c + 2 * e1]),
+                                                      __float_as_uint(d[4 * c + 2 * e1 + 1]),
+                                                      false, false);
+      w[c][e1] = pack_bf16(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    }
+  }
+  const bool x0 = (lane & 1) != 0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const unsigned t0 = xor1(w[c][0]);
+    const unsigned t1 = xor1(w[c][1]);
+    const unsigned n0 = x0 ? t1 : w[c][0];
+    const unsigned n1 = x0 ? w[c][1] : t0;
+    w[c][0] = n0;
+    w[c][1] = n1;
+  }
+  const bool x1 = (lane & 2) != 0;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const unsigned a = w[2 * u][s];
+      const unsigned b = w[2 * u + 1][s];
+      const unsigned ta = xor2(a);
+      const unsigned tb = xor2(b);
+      w[2 * u][s] = x1 ? tb : a;
+      w[2 * u + 1][s] = x1 ? b : ta;
+    }
+  }
+  const int row = 8 * ((lane >> 1) & 1) + 4 * (lane >> 5) + 2 * (lane & 1) + ((lane >> 4) & 1);
+  const int col = 32 * wave + 8 * ((lane >> 2) & 3);
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+    *(u32x4*)&ds[ds_row(row + 16 * u) * kRowS + col] =
+        u32x4{w[2 * u][0], w[2 * u][1], w[2 * u + 1][0], w[2 * u + 1][1]};
+}
+
+template <int DQM>
+__global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
+  constexpr int D = 128, TN = 256, TM = 32;
+  constexpr bool DET = DQM == 1;
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[TN * kRowQ];          // K tile
+  __shared__ __attribute__((aligned(16))) uint16_t qo_lds[2][2][TM * kRowQ];   // [buffer][Q, dO]
+  __shared__ __attribute__((aligned(16))) uint16_t ds_lds[2][TM * kRowS];      // [buffer] dS
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  const int g16 = lane >> 4;
+  const int i16 = lane & 15;
+
+  const int nbh = p.Hkv * p.B;
+  const int ip = blockIdx.x / nbh;
+  const int item = ip / p.kv_parts;
+  const int part = ip - item * p.kv_parts;
+  const int rem = blockIdx.x - ip * nbh;
+  const int g = rem % p.Hkv;
+  const int b = rem / p.Hkv;
+  const bool group = p.seqstart_q != nullptr;
+  const Seg sg = seg_of(p, b);
+  const MaskGeom mg = mask_geom(p.mask_type, p.window_left, p.window_right, sg.lq, sg.lk);
+  int64_t w_lo = 1, w_hi = 0;  // query blocks already in this item's split (deterministic)
+  int64_t u_lo = 1, u_hi = 0;  // union of the item's tiles' query block ranges (parts)
+  for (int tsub = 0; tsub < p.tiles_per_item; ++tsub) {
+    const int j = item * p.tiles_per_item + tsub;
+    if ((int64_t)j * TN >= sg.lk) break;
+    int64_t lo, hi2;
+    qblocks_for_tile(mg, sg.lq, sg.lk, j, TM, TN, &lo, &hi2);
+    if (hi2 >= lo) {
+      const bool had = u_hi >= u_lo;
+      u_lo = had ? min(u_lo, lo) : lo;
+      u_hi = had ? max(u_hi, hi2) : hi2;
+    }
+  }
+  const int64_t nbu = u_hi >= u_lo ? u_hi - u_lo + 1 : 0;
+  const int64_t nu = nbu * p.group_size;
+  const int64_t u_a = nu * part / p.kv_parts;
+  const int64_t u_e = nu * (part + 1) / p.kv_parts;
+
+  const int tr_row = i16 >> 2;                        // row inside a 4-row transposing read
+  const int tr_col = 16 * (g16 & 1) + 4 * (i16 & 3);  // its columns inside a 32-column tile
+  const int key_w = 32 * wave + kmap(l32);            // the lane's key inside the tile
+  // query rows of the lane's transposing reads of Q and dO (reduction step 0; +16 for step 1,
+  // +1 for the second read): 4hi + {0, 2, 8, 10}
+  const int tq_row = 4 * hi + 2 * (tr_row & 1) + 8 * (tr_row >> 1);
+  // K rows of the lane's transposing reads for dQ (key group 0; + 32*(kk/2) + 8*(kk%2) for
+  // reduction step kk): keys 8hi + tr_row and 8hi + 4 + tr_row
+  const int tk_row0 = krow(8 * hi + tr_row), tk_row1 = krow(8 * hi + 4 + tr_row);
+  const float inv_c = 1.f / p.scale_log2;
+  // B operand of ones in reduction slots 0..2 of lane half 0 (bf16 1.0 = 0x3F80), zeros in
+  // half 1: the product with a padding chunk adds its three parts
+  const bf16x8 ones3 = __builtin_bit_cast(bf16x8, u32x4{hi ? 0u : 0x3F803F80u, hi ? 0u : 0x3F80u, 0u, 0u});
+  const int qs1 = (int)p.q_s[1];
+  const int os1 = (int)p.do_s[1];
+
+  for (int tsub = 0; tsub < p.tiles_per_item; ++tsub) {
+    const int j = item * p.tiles_per_item + tsub;
+    const int64_t key0 = (int64_t)j * TN;
+    if (key0 >= sg.lk) break;
+    if (tsub > 0) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();  // every wave is done with the previous tile's LDS
+    }
+    const int nk = (int)min((int64_t)TN, sg.lk - key0);
+    int64_t qb_lo, qb_hi;
+    qblocks_for_tile(mg, sg.lq, sg.lk, j, TM, TN, &qb_lo, &qb_hi);
+    const int nblk = qb_hi >= qb_lo ? (int)(qb_hi - qb_lo + 1) : 0;
+    const int64_t lo64 = mg.left >= 0 ? mg.delta - mg.left : -sg.lq;
+    const int64_t hi64 = mg.right >= 0 ? mg.delta + mg.right : sg.lk;
+    const int lo_d = (int)max(lo64, -sg.lq);
+    const int hi_d = (int)min(hi64, sg.lk);
+    const unsigned span = (unsigned)(hi_d - lo_d);
+
+    // K tile -> LDS (8 chunks per thread), the wave's V rows -> registers (B operand of dP)
+    {
+      const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(
+          p.k + elem_off(p.k_s, group, b, sg.k_row0 + key0, g), (uint32_t)((nk - 1) * (int)p.k_s[1] + D) * 2u);
+      const int ks1 = (int)p.k_s[1];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int id = tid + 512 * i;
+        const int kr = id >> 4, c = id & 15;
+        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rk, (kr * ks1 + c * 8) * 2, 0, 0);
+        *(u32x4*)&k_lds[krow(kr) * kRowQ + c * 8] = x;
+      }
+    }
+    bf16x8 vw[D / 16];
+    {
+      const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(
+          p.v + elem_off(p.v_s, group, b, sg.k_row0 + key0, g), (uint32_t)((nk - 1) * (int)p.v_s[1] + D) * 2u);
+      const int vs1 = (int)p.v_s[1];
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk)
+        vw[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, (key_w * vs1 + 16 * kk + 8 * hi) * 2, 0, 0));
+    }
+    f32x16 dk_acc[D / 32], dv_acc[D / 32];
+#pragma unroll
+    for (int n = 0; n < D / 32; ++n) {
+      dk_acc[n] = f32x16{};
+      dv_acc[n] = f32x16{};
+    }
+
+    // steps of this part: as in k_bwd_main
+    const auto steps_before = [&](int64_t u) -> int {
+      if (nbu == 0) return 0;
+      const int64_t c = min(max(u_lo + u % nbu - qb_lo, (int64_t)0), (int64_t)nblk);
+      return (int)((u / nbu) * nblk + c);
+    };
+    const int n0 = steps_before(u_a);
+    const int n1 = steps_before(u_e);
+
+    // ---- step cursors.  Steps run over (query head, query block) head-major; a cursor holds
+    // a step's number, query head and first row.  Buffer resources span one query head's
+    // rows of the segment and a step's rows go into the per-lane offset, so rows past the
+    // segment end read as zeros and stores or atomics to them are dropped; a resource is
+    // rebuilt only when the head changes ----
+    struct Cur {
+      int n, h, r;
+    };
+    const int row_lo = (int)qb_lo * TM, row_hi = (int)qb_hi * TM;
+    const int lq = (int)sg.lq;
+    auto advance = [&](Cur& c) {
+      ++c.n;
+      c.r += TM;
+      if (c.r > row_hi) {
+        c.r = row_lo;
+        ++c.h;
+      }
+    };
+    const uint32_t q_bytes = lq > 0 ? (uint32_t)((lq - 1) * qs1 + D) * 2u : 0u;
+    const uint32_t o_bytes = lq > 0 ? (uint32_t)((lq - 1) * os1 + D) * 2u : 0u;
+    Cur pc;  // the step being prefetched
+    pc.n = n0;
+    pc.h = g * p.group_size + (nblk > 0 ? n0 / nblk : 0);
+    pc.r = row_lo + (nblk > 0 ? n0 % nblk : 0) * TM;
+    __amdgpu_buffer_rsrc_t rq, ro, rl, rd;
+    auto head_rsrc = [&](int hh) {
+      rq = buffer_rsrc(p.q + elem_off(p.q_s, group, b, sg.q_row0, hh), q_bytes);
+      ro = buffer_rsrc(p.dout + elem_off(p.do_s, group, b, sg.q_row0, hh), o_bytes);
+      const int64_t w0 = (int64_t)hh * p.rows_q + sg.ws_row0;
+      rl = buffer_rsrc(p.lse2 + w0, (uint32_t)lq * 4u);
+      rd = buffer_rsrc(p.dsum + w0, (uint32_t)lq * 4u);
+    };
+    head_rsrc(pc.h);
+
+    // ---- staging: thread t loads 16 bytes of Q and of dO (row t/16, chunk t%16); wave 0
+    // loads L (lanes 0..31) and D (lanes 32..63) ----
+    u32x4 q_pre, o_pre;
+    float ld_pre = 0.f;
+    int nq_pre = 0;
+    const int st_row = tid >> 4, st_c = tid & 15;
+    const int q_lane = (st_row * qs1 + st_c * 8) * 2, o_lane = (st_row * os1 + st_c * 8) * 2;
+    auto load_step = [&]() {  // the prefetch cursor's step, then advance it
+      const bool valid = pc.n < n1;
+      const __amdgpu_buffer_rsrc_t none = buffer_rsrc(p.q, 0u);
+      nq_pre = valid ? min(TM, lq - pc.r) : 0;
+      q_pre = __builtin_amdgcn_raw_buffer_load_b128(valid ? rq : none, q_lane + pc.r * qs1 * 2, 0, 0);
+      o_pre = __builtin_amdgcn_raw_buffer_load_b128(valid ? ro : none, o_lane + pc.r * os1 * 2, 0, 0);
+      if (wave == 0) {  // two loads with wave-uniform resources
+        const float lv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(valid ? rl : none, (pc.r + l32) * 4, 0, 0));
+        const float dv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(valid ? rd : none, (pc.r + l32) * 4, 0, 0));
+        ld_pre = lane < 32 ? lv : dv;
+      }
+      const int h_old = pc.h;
+      advance(pc);
+      if (pc.h != h_old && pc.n < n1) head_rsrc(pc.h);
+    };
+    auto store_step = [&](int buf) {
+      *(u32x4*)&qo_lds[buf][0][st_row * kRowQ + st_c * 8] = q_pre;
+      *(u32x4*)&qo_lds[buf][1][st_row * kRowQ + st_c * 8] = o_pre;
+      // the padding columns of Q row r carry -L2[r]/c, those of dO row r carry -D[r] (three
+      // bf16 parts each); a row past the segment end gets -1e30, so its P is exactly 0
+      if (wave == 0) {
+        const float x = lane < 32 ? (l32 < nq_pre ? -ld_pre * inv_c : -1e30f) : -ld_pre;
+        *(u32x4*)&qo_lds[buf][hi][l32 * kRowQ + D] = split3(x);
+      }
+    };
+
+    // ---- dQ of a finished step from ds_lds[buf]: this wave's 32 columns ----
+    // accumulator resources of one query head (rebuilt when the head changes)
+    auto dq_rsrc = [&](int hh) -> __amdgpu_buffer_rsrc_t {
+      if (DET)
+        return buffer_rsrc(p.dq_acc + (int64_t)item * p.split_stride + (int64_t)hh * p.head_stride +
+                               sg.acc_row0 * D, (uint32_t)(row_hi + TM) * D * 4u);
+      if (DQM == 2)
+        return buffer_rsrc((const uint16_t*)p.dq_acc + (int64_t)b * p.split_stride + (int64_t)hh * p.head_stride,
+                           (uint32_t)(row_hi + TM) * D * 2u);
+      return buffer_rsrc(p.dq_acc + (int64_t)hh * p.head_stride + sg.acc_row0 * D, (uint32_t)lq * D * 4u);
+    };
+    const int nd = wave & 3;
+    auto dq_step = [&](int buf, const __amdgpu_buffer_rsrc_t& rdq, int r) {
+      // deterministic mode: the partial an earlier tile of the item left for this block is
+      // read back first, so the products below hide the load latency
+      u32x4 prev[4];
+      if (DET) {
+        const int qbn = r / TM;
+        const __amdgpu_buffer_rsrc_t rprev = qbn >= w_lo && qbn <= w_hi ? rdq : buffer_rsrc(p.dq_acc, 0u);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          prev[u] = __builtin_amdgcn_raw_buffer_load_b128(rprev, (r * D + nd * 1024 + u * 256 + lane * 4) * 4, 0, 0);
+      }
+      f32x16 acc = f32x16{};
+      const uint16_t* dsb = &ds_lds[buf][ds_row(l32) * kRowS + 8 * hi];
+      const uint16_t* kt0 = &k_lds[tk_row0 * kRowQ + 32 * nd + tr_col];
+      const uint16_t* kt1 = &k_lds[tk_row1 * kRowQ + 32 * nd + tr_col];
+      // operands of reduction step kk: dS row chunk and the transposed K block; loaded two
+      // steps ahead of their product (the fences keep that order)
+      bf16x8 da[2], bk[2];
+      auto ld = [&](int kk) {
+        const int kb = (32 * (kk >> 1) + 8 * (kk & 1)) * kRowQ;
+        da[kk & 1] = *(const bf16x8*)&dsb[16 * kk];
+        bk[kk & 1] = tr_read(&kt0[kb], &kt1[kb]);
+      };
+      ld(0);
+      ld(1);
+#pragma unroll
+      for (int kk = 0; kk < TN / 16; ++kk) {
+        acc = mfma(da[kk & 1], bk[kk & 1], acc);
+        __builtin_amdgcn_sched_barrier(0);
+        if (kk + 2 < TN / 16) ld(kk + 2);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (DET) {
+        const int voff = (r * D + nd * 1024 + lane * 4) * 4;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          __builtin_amdgcn_raw_buffer_store_b128(
+              u32x4{__float_as_uint(__uint_as_float(prev[u][0]) + acc[4 * u]),
+                    __float_as_uint(__uint_as_float(prev[u][1]) + acc[4 * u + 1]),
+                    __float_as_uint(__uint_as_float(prev[u][2]) + acc[4 * u + 2]),
+                    __float_as_uint(__uint_as_float(prev[u][3]) + acc[4 * u + 3])},
+              rdq, voff + 1024 * u, 0, 0);
+      } else if (DQM == 2) {
+        // packed bf16 adds: lanes 2c and 2c+1 trade their (row k, row 8+k) words so that each
+        // holds one row of columns 2c, 2c+1; the block is stored tile by tile (tile nd at
+        // 2048 bytes * nd), register pair k2 at 256 * k2, lane l's word at 4 * l
+        const bool odd = (lane & 1) != 0;
+        const unsigned sel = odd ? 0x03020706u : 0x05040100u;
+#pragma unroll
+        for (int k2 = 0; k2 < 8; ++k2) {
+          const unsigned mine = pack_bf16(acc[k2], acc[8 + k2]);
+          const unsigned other = xor1(mine);
+          const unsigned v = __builtin_amdgcn_perm(other, mine, sel);
+          const int voff = r * D * 2 + nd * 2048 + k2 * 256 + lane * 4;
+          asm volatile("buffer_atomic_pk_add_bf16 %0, %1, %2, 0 offen" ::"v"(v), "v"(voff), "s"(rdq));
+        }
+      } else {
+        // register rr holds row 8(rr/4) + 4hi + rr%4, column 32nd + l32
+        const int voff = ((r + 4 * hi) * D + 32 * nd + l32) * 4;
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr)
+          __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[rr], rdq, voff + (8 * (rr >> 2) + (rr & 3)) * D * 4, 0, 0);
+      }
+    };
+
+    Cur cc = pc;  // the step being computed
+    if (n1 > n0) {
+      load_step();
+      store_step(0);
+      load_step();
+    }
+    __syncthreads();
+    Cur dc = cc;  // the step whose dQ is pending (the previous one)
+    __amdgpu_buffer_rsrc_t rdq = dq_rsrc(dc.h);
+    const bool key_ok = key_w < nk;
+    for (int n = n0; n < n1; ++n) {
+      const int buf = (n - n0) & 1;
+      // the pending dQ of step n-1, by the half whose turn it is
+      if (n > n0 && (wave >> 2) == ((n - 1 - n0) & 1)) dq_step(buf ^ 1, rdq, dc.r);
+      const int q0 = cc.r;
+      // ---- S, dP, P, dS, dV, dK of step n (branch-free: masked pairs get P = 0) ----
+      {
+        float ds32[16];
+        const uint16_t* qb = qo_lds[buf][0];
+        const uint16_t* ob = qo_lds[buf][1];
+        // S and dP, interleaved; the scheduling groups keep the LDS reads two reduction steps
+        // ahead of the products that use them
+        f32x16 s_acc = f32x16{}, dp_acc = f32x16{};
+        const uint16_t* qrow = &qb[l32 * kRowQ + 8 * hi];
+        const uint16_t* orow = &ob[l32 * kRowQ + 8 * hi];
+        const uint16_t* krw = &k_lds[krow(key_w) * kRowQ + 8 * hi];
+        // S and dP interleaved; operands loaded two reduction steps ahead of their products.
+        // A ninth step multiplies the padding chunk of the Q and dO rows by ones3, which adds
+        // -L2/c to S and -D to dP: then P = exp2(c S) and dS = P dP directly.
+        bf16x8 qa[2], kb2[2], oa[2];
+        auto ld = [&](int kk) {
+          if (kk < D / 16) {
+            qa[kk & 1] = *(const bf16x8*)&qrow[16 * kk];
+            kb2[kk & 1] = *(const bf16x8*)&krw[16 * kk];
+            oa[kk & 1] = *(const bf16x8*)&orow[16 * kk];
+          } else {
+            qa[kk & 1] = *(const bf16x8*)&qb[l32 * kRowQ + D];
+            oa[kk & 1] = *(const bf16x8*)&ob[l32 * kRowQ + D];
+          }
+        };
+        ld(0);
+        ld(1);
+#pragma unroll
+        for (int kk = 0; kk <= D / 16; ++kk) {
+          s_acc = mfma(qa[kk & 1], kk < D / 16 ? kb2[kk & 1] : ones3, s_acc);
+          dp_acc = mfma(oa[kk & 1], kk < D / 16 ? vw[kk] : ones3, dp_acc);
+          __builtin_amdgcn_sched_barrier(0);
+          if (kk + 2 <= D / 16) ld(kk + 2);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // P = exp2(c S), 0 for masked pairs; dS = P dP
+        bf16x8 pa[2], sa[2];
+        {
+          const int t0 = key_ok ? (int)key0 - q0 + key_w - lo_d - 4 * hi : (int)span + TM + 1;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * c + e;
+              float pv = __builtin_amdgcn_exp2f(s_acc[r] * p.scale_log2);
+              pv = (unsigned)(t0 - (8 * c + e)) <= span ? pv : 0.f;
+              const float dsv = pv * dp_acc[r];
+              // reduction slot of (c, e) in step c/2: the Q/dO rows the transposing reads give
+              const int slot = 2 * (c & 1) + (e >> 1) + 4 * (e & 1);
+              pa[c >> 1][slot] = (__bf16)pv;
+              sa[c >> 1][slot] = (__bf16)dsv;
+              ds32[r] = dsv;
+            }
+          }
+        }
+        // dV += P^T dO, dK += dS^T Q: reduction step t covers queries 16t .. 16t + 15; lane
+        // half hi takes rows 16t + 4hi + {0, 2, 8, 10} and then + 1.  Operand pairs are loaded
+        // two products ahead; the dS exchange runs under the first products.
+        bf16x8 bo[2], bq[2];
+        auto ldv = [&](int i) {
+          const int t = i >> 2, n2 = i & 3;
+          const int r1 = 16 * t + tq_row;
+          const int col = 32 * n2 + tr_col;
+          bo[i & 1] = tr_read(&ob[r1 * kRowQ + col], &ob[(r1 + 1) * kRowQ + col]);
+          bq[i & 1] = tr_read(&qb[r1 * kRowQ + col], &qb[(r1 + 1) * kRowQ + col]);
+        };
+        ldv(0);
+        ldv(1);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          dv_acc[i & 3] = mfma(pa[i >> 2], bo[i & 1], dv_acc[i & 3]);
+          dk_acc[i & 3] = mfma(sa[i >> 2], bq[i & 1], dk_acc[i & 3]);
+          __builtin_amdgcn_sched_barrier(0);
+          if (i + 2 < 8) ldv(i + 2);
+          if (i == 0) write_ds_wide(ds_lds[buf], ds32, wave, lane);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+
+      store_step(buf ^ 1);  // step n+1's tiles (zeros after the last step)
+      if (dc.h != cc.h) rdq = dq_rsrc(cc.h);
+      dc = cc;
+      advance(cc);
+      __syncthreads();  // step n's dS and step n+1's tiles are complete
+      load_step();
+    }
+    // the last step's dQ
+    if (n1 > n0 && (wave >> 2) == ((n1 - 1 - n0) & 1)) dq_step((n1 - 1 - n0) & 1, rdq, dc.r);
+
+    // ---- epilogue: dK = scale * dK_acc, dV = dV_acc as bf16, or this part's fp32 partials ----
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kl = wave * 32 + kmap(8 * (r >> 2) + 4 * hi + (r & 3));
+      if (kl < nk) {
+        const int64_t krow = sg.k_row0 + key0 + kl;
+        if (p.kv_parts == 1) {
+          uint16_t* dkp = p.dk + elem_off(p.dk_s, group, b, krow, g) + l32;
+          uint16_t* dvp = p.dv + elem_off(p.dv_s, group, b, krow, g) + l32;
+#pragma unroll
+          for (int n = 0; n < D / 32; ++n) dkp[32 * n] = to_bf16_bits(dk_acc[n][r] * p.scale);
+#pragma unroll
+          for (int n = 0; n < D / 32; ++n) dvp[32 * n] = to_bf16_bits(dv_acc[n][r]);
+        } else {
+          const int64_t prow = sg.kws_row0 + key0 + kl;
+          float* pp = p.dkv_acc + (((int64_t)part * p.Hkv + g) * p.rows_k + prow) * (2 * D) + l32;
+#pragma unroll
+          for (int n = 0; n < D / 32; ++n) pp[32 * n] = dk_acc[n][r];
+#pragma unroll
+          for (int n = 0; n < D / 32; ++n) pp[D + 32 * n] = dv_acc[n][r];
+        }
+      }
+    }
+    if (nblk > 0) {
+      const bool had = w_hi >= w_lo;
+      w_lo = had ? min(w_lo, qb_lo) : qb_lo;
+      w_hi = had ? max(w_hi, qb_hi) : qb_hi;
+    }
+  }  // tiles of the item
+}
+
+}  // namespace
+
+hipError_t launch_main_wide(const Plan& plan, const KParams& kp, dim3 grid, hipStream_t stream) {
+  const int mode = plan.deterministic ? 1 : (plan.dq_bf16 ? 2 : 0);
+  if (mode == 1) hipLaunchKernelGGL((k_bwd_wide<1>), grid, dim3(512), 0, stream, kp);
+  else if (mode == 2) hipLaunchKernelGGL((k_bwd_wide<2>), grid, dim3(512), 0, stream, kp);
+  else hipLaunchKernelGGL((k_bwd_wide<0>), grid, dim3(512), 0, stream, kp);
+  return hipGetLastError();
+}
+
+}  // namespace fmha

@@ -122,23 +122,55 @@ int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t el, bool forwar
   p->Sk = a->Sk;
   p->d_qk = a->d_qk;
   p->d_v = a->d_v;
-  // query rows per main-kernel block (register and LDS budget): 64 for d_qk = 128, 32 for
-  // d_qk = 192, and for d_qk = 64 128 rows (its smaller accumulators leave room for four
-  // 32-row tiles, which halves the per-step overheads per FLOP) except with fp32 dQ atomics,
-  // which were faster with 64-row blocks
-  const bool fp32_atomics = a->deterministic == 0 && a->dq_acc_dtype == FMHA_DQ_ACC_FP32;
-  p->tile_m = a->d_qk == 192 ? 32 : (a->d_qk == 64 && !fp32_atomics ? 128 : 64);
-  if (const char* e = getenv("FMHA_BWD_TILE_M")) {  // tuning knob: 32/64 (d_qk 128), 64/128 (d_qk 64)
-    const int v = atoi(e);
-    if ((a->d_qk == 128 && (v == 32 || v == 64)) || (a->d_qk == 64 && (v == 64 || v == 128)))
+  // Layout overrides (arguments like the others: nothing here reads the environment, so one
+  // argument struct always yields one plan)
+  if (a->tune_kernel < FMHA_KERNEL_AUTO || a->tune_kernel > FMHA_KERNEL_WIDE)
+    return fail(FMHA_ERR_INVALID_ARG, err, el, "unknown tune_kernel");
+  if (a->tune_tiles_per_item != 0 && a->tune_tiles_per_item != 1 && a->tune_tiles_per_item != 2 &&
+      a->tune_tiles_per_item != 4 && a->tune_tiles_per_item != 8)
+    return fail(FMHA_ERR_INVALID_ARG, err, el, "tune_tiles_per_item must be 0, 1, 2, 4 or 8");
+  if (a->tune_kv_parts < 0 || a->tune_kv_parts > 8)
+    return fail(FMHA_ERR_INVALID_ARG, err, el, "tune_kv_parts must be in 0 .. 8");
+  const bool with_bias = a->bias != nullptr;
+  const bool with_dropout = p->drop_k < 256;
+  // The wide kernel (eight waves, 256-key tiles) serves d_qk = d_v = 128 without bias or
+  // dropout; its 32-bit tile offsets need sequence strides below 2^22 elements.
+  const bool wide_ok = a->d_qk == 128 && a->d_v == 128 && !with_bias && !with_dropout &&
+                       a->q_stride[1] < (int64_t(1) << 22) && a->k_stride[1] < (int64_t(1) << 22) &&
+                       a->v_stride[1] < (int64_t(1) << 22) && a->do_stride[1] < (int64_t(1) << 22);
+  if (a->tune_kernel == FMHA_KERNEL_WIDE && !wide_ok)
+    return fail(FMHA_ERR_INVALID_ARG, err, el,
+                "tune_kernel = FMHA_KERNEL_WIDE needs d_qk = d_v = 128, no bias, no dropout and "
+                "sequence strides below 2^22");
+  p->kernel = (a->tune_kernel == FMHA_KERNEL_FOUR_WAVE || !wide_ok) ? FMHA_KERNEL_FOUR_WAVE
+                                                                    : FMHA_KERNEL_WIDE;
+  if (p->kernel == FMHA_KERNEL_WIDE) {
+    p->tile_m = 32;
+    p->tile_n = 256;
+    if (a->tune_tile_m != 0 && a->tune_tile_m != 32)
+      return fail(FMHA_ERR_INVALID_ARG, err, el, "the wide kernel's query blocks have 32 rows");
+  } else {
+    // query rows per block (register and LDS budget): 64 for d_qk = 128, 32 for d_qk = 192,
+    // and for d_qk = 64 128 rows (its smaller accumulators leave room for four 32-row
+    // tiles, which halves the per-step overheads per FLOP) except with fp32 dQ atomics,
+    // which were faster with 64-row blocks
+    const bool fp32_atomics = a->deterministic == 0 && a->dq_acc_dtype == FMHA_DQ_ACC_FP32;
+    p->tile_m = a->d_qk == 192 ? 32 : (a->d_qk == 64 && !fp32_atomics ? 128 : 64);
+    // with a bias, blocks are half as tall (32 rows at d_qk = 128, 64 at d_qk = 64): the bias
+    // registers of the taller blocks do not fit beside the rest of the main kernel's
+    // registers (dropout alone does fit)
+    if (with_bias && a->d_qk == 128) p->tile_m = 32;
+    if (with_bias && a->d_qk == 64) p->tile_m = 64;
+    if (a->tune_tile_m != 0) {
+      const int v = a->tune_tile_m;
+      const bool ok = (a->d_qk == 128 && (v == 32 || (v == 64 && !with_bias))) ||
+                      (a->d_qk == 64 && ((v == 64) || (v == 128 && !with_bias))) ||
+                      (a->d_qk == 192 && v == 32);
+      if (!ok) return fail(FMHA_ERR_INVALID_ARG, err, el, "tune_tile_m is not a block height of this kernel");
       p->tile_m = v;
+    }
+    p->tile_n = 128;
   }
-  // with a bias, blocks are half as tall (32 rows at d_qk = 128, 64 at d_qk = 64): the bias
-  // registers of the taller blocks do not fit beside the rest of the main kernel's registers
-  // (dropout alone does fit)
-  if (a->bias != nullptr && a->d_qk == 128) p->tile_m = 32;
-  if (a->bias != nullptr && a->d_qk == 64) p->tile_m = 64;
-  p->tile_n = 128;
   p->deterministic = a->deterministic == 1;
   p->dq_bf16 = a->dq_acc_dtype == FMHA_DQ_ACC_BF16;
 
@@ -307,15 +339,14 @@ int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t el, bool forwar
       p->kv_parts = (int)(parts < 1 ? 1 : (parts > 8 ? 8 : parts));
     }
   }
-  // tuning knobs (tests use them), each overriding its own choice
-  if (const char* e = getenv("FMHA_BWD_TILES_PER_ITEM")) {  // 1, 2, 4 or 8
-    const int v = atoi(e);
-    if (p->deterministic && (v == 1 || v == 2 || v == 4 || v == 8)) p->tiles_per_item = v;
-  }
-  if (const char* e = getenv("FMHA_BWD_KV_PARTS")) {  // 1 .. 8
-    const int v = atoi(e);
-    if (v >= 1 && v <= 8) p->kv_parts = v;
-  }
+  // the overrides, each replacing its own choice
+  if (a->tune_tiles_per_item != 0 && p->deterministic) p->tiles_per_item = a->tune_tiles_per_item;
+  if (a->tune_kv_parts != 0) p->kv_parts = a->tune_kv_parts;
+  // bf16 accumulation rounds the running sum once per key tile: past 64 additions per dQ
+  // element its error estimate (relative rms u*sqrt(n/6), u = 2^-8) leaves the cosine bar
+  if (p->dq_bf16 && p->n_kv_tiles > 64)
+    return fail(FMHA_ERR_UNSUPPORTED, err, el,
+                "the bf16 dQ accumulator is limited to 64 key tiles per segment (accuracy); use fp32");
   const int n_items = (p->n_kv_tiles + p->tiles_per_item - 1) / p->tiles_per_item;
   p->nsplits = p->deterministic ? (n_items > 0 ? n_items : 1) : 1;
   p->needs_zero = !p->deterministic;
@@ -353,7 +384,8 @@ int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t el, bool forwar
                     (int64_t)p->acc_pad, p->d_offset, p->lse2_offset, p->dq_acc_offset,
                     p->dq_acc_bytes, p->dbias_acc_offset, p->dbias_acc_bytes, p->workspace_bytes,
                     (int64_t)p->kv_parts, p->dkv_acc_offset, p->dkv_acc_bytes,
-                    (int64_t)a->mask_type, (int64_t)a->window_left, (int64_t)a->window_right})
+                    (int64_t)a->mask_type, (int64_t)a->window_left, (int64_t)a->window_right,
+                    (int64_t)p->kernel})
     f.v(x);
   if (group && a->B > 0) {
     f.add(a->seqstart_q_host, sizeof(int32_t) * (a->B + 1));

@@ -17,6 +17,7 @@ struct Plan {
   int B, Hq, Hkv, group_size;
   int Sq, Sk;            // batch: lengths; group: maximum segment lengths
   int d_qk, d_v;
+  int kernel;            // enum fmha_kernel: FMHA_KERNEL_FOUR_WAVE or FMHA_KERNEL_WIDE
   int tile_m, tile_n;    // query rows per block, keys per tile
   int n_kv_tiles;        // key tiles of the longest segment
   int tiles_per_item;    // key tiles per main-kernel work item; deterministic split = item

@@ -57,7 +57,7 @@
  *
  * ABI history (fields are only ever appended): 2 padded THD slots, 3 dq_acc_dtype, 4 bias and
  * dbias, 5 dropout, 6 plan_info.reduce_read_bytes, 7 plan_info.kv_parts and the dK/dV
- * partials region.
+ * partials region, 8 the layout overrides (tune_*) and plan_info.kernel.
  *
  * Errors: every function returns FMHA_OK or a negative fmha_status and never aborts.  Set
  * FMHA_BWD_LOG=1 in the environment to have the reason printed to stderr.
@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define FMHA_BWD_ABI_VERSION 7u
+#define FMHA_BWD_ABI_VERSION 8u
 
 #if defined(__GNUC__)
 #define FMHA_BWD_API __attribute__((visibility("default")))
@@ -187,7 +187,26 @@ typedef struct fmha_bwd_args {
   int32_t reserved2;       /* must be 0 */
   uint64_t philox_seed;
   uint64_t philox_offset;  /* only its low 32 bits are used */
+  /* Layout overrides for tests and tuning; 0 = the plan's own choice.  They are arguments
+     like the others: the plan reads nothing but this struct and the host seqstart arrays, so
+     the sizing, prepare and run calls of one argument struct always agree, and the plan's
+     fingerprint covers the layout they select.  A value the chosen kernel cannot use is
+     FMHA_ERR_INVALID_ARG. */
+  int32_t tune_kernel;          /* FMHA_KERNEL_* below */
+  int32_t tune_tile_m;          /* query rows per block of the four-wave kernel: 32 or 64 at
+                                   d_qk = 128, 64 or 128 at d_qk = 64 */
+  int32_t tune_tiles_per_item;  /* deterministic mode: key tiles per work item, 1, 2, 4 or 8 */
+  int32_t tune_kv_parts;        /* work groups sharing one work item's steps, 1 .. 8 */
 } fmha_bwd_args;
+
+/* Main-kernel layouts (fmha_bwd_args.tune_kernel, fmha_bwd_plan_info.kernel). */
+enum fmha_kernel {
+  FMHA_KERNEL_AUTO = 0,  /* the plan's choice: FMHA_KERNEL_WIDE where it applies */
+  FMHA_KERNEL_FOUR_WAVE = 1, /* 256 threads, 128-key tiles, 32-128-row query blocks; every
+                                head dim, bias and dropout */
+  FMHA_KERNEL_WIDE = 2   /* 512 threads (two waves per SIMD), 256-key tiles, 32-row query
+                            blocks; d_qk = d_v = 128 without bias or dropout */
+};
 
 /* Workspace bytes that prepare/run need for these arguments.  Host only: no GPU call, no
    allocation, no synchronisation; device pointers are not dereferenced. */
@@ -260,6 +279,8 @@ typedef struct fmha_bwd_plan_info {
   int64_t dkv_acc_offset;    /* byte offset of the fp32 dK, dV partials [kv_parts][Hkv][rows_k]
                                 [d_qk + d_v] (only when kv_parts > 1) */
   int64_t dkv_acc_bytes;
+  int32_t kernel;            /* enum fmha_kernel: the main-kernel layout the run launches */
+  int32_t reserved;
 } fmha_bwd_plan_info;
 /* Accumulator layout.  Atomic mode: one split, rows_q rows, row-major ([row][d_qk]), row of
    a query = its D/LSE row.  Deterministic mode: split s holds the sum of the partials of key

@@ -51,7 +51,7 @@ def to_dev_f32(a):
 
 
 def run_gpu(x, o, lse, *, scale, mask, window=(-1, -1), sq=None, sk=None, deterministic=True,
-            dq_acc_dtype="fp32"):
+            dq_acc_dtype="fp32", tune=None):
     """Round O to bf16 and LSE to fp32 as the forward would store them, run the library."""
     import torch
     import attention_backward_fmha_amd as F
@@ -65,7 +65,7 @@ def run_gpu(x, o, lse, *, scale, mask, window=(-1, -1), sq=None, sk=None, determ
                   cu_seqlens_q_host=np.asarray(sq, np.int32),
                   cu_seqlens_k_host=np.asarray(sk, np.int32))
     dq, dk, dv = F.bwd(q, k, v, od, ld, do, scale=scale, mask_type=mask, window=window,
-                       deterministic=deterministic, dq_acc_dtype=dq_acc_dtype, **kw)
+                       deterministic=deterministic, dq_acc_dtype=dq_acc_dtype, tune=tune, **kw)
     torch.cuda.synchronize()
     return tuple(t.float().cpu().numpy().astype(np.float64) for t in (dq, dk, dv))
 

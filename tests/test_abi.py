@@ -93,10 +93,12 @@ def test_mask_numbering_matches_pages():
 
 
 def batch_args(B=2, Hq=4, Hkv=2, Sq=200, Sk=333, d_qk=128, d_v=128, mask=0, window=(-1, -1),
-               deterministic=1):
+               deterministic=1, kernel=_lib.KERNEL_FOUR_WAVE):
+    """Arguments with fake device pointers.  The layout rules most tests here check are the
+    four-wave kernel's, so that kernel is requested unless `kernel` says otherwise."""
     a = Args(B=B, Hq=Hq, Hkv=Hkv, Sq=Sq, Sk=Sk, d_qk=d_qk, d_v=d_v, scale=1.0 / np.sqrt(d_qk),
              mask_type=mask, window_left=window[0], window_right=window[1],
-             deterministic=deterministic)
+             deterministic=deterministic, tune_kernel=kernel)
     for n in ("q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv"):
         setattr(a, n, FAKE)
     for n, H, d, S in (("q_stride", Hq, d_qk, Sq), ("k_stride", Hkv, d_qk, Sk), ("v_stride", Hkv, d_v, Sk),
@@ -109,11 +111,12 @@ def batch_args(B=2, Hq=4, Hkv=2, Sq=200, Sk=333, d_qk=128, d_v=128, mask=0, wind
     return a
 
 
-def group_args(lens_q, lens_k, Hq=4, Hkv=2, d=128, mask=1, deterministic=1):
+def group_args(lens_q, lens_k, Hq=4, Hkv=2, d=128, mask=1, deterministic=1,
+               kernel=_lib.KERNEL_FOUR_WAVE):
     sq = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32)
     sk = np.concatenate([[0], np.cumsum(lens_k)]).astype(np.int32)
     a = batch_args(B=len(lens_q), Hq=Hq, Hkv=Hkv, Sq=max(lens_q), Sk=max(lens_k), d_qk=d, d_v=d,
-                   mask=mask, deterministic=deterministic)
+                   mask=mask, deterministic=deterministic, kernel=kernel)
     a.seqstart_q_host = sq.ctypes.data
     a.seqstart_k_host = sk.ctypes.data
     a.seqstart_q_dev = FAKE
@@ -324,13 +327,11 @@ def test_reduce_read_bytes_closed_forms():
     assert info.reduce_read_bytes == 2 * 4 * info.nsplits * 64 * 128 * 4
 
 
-def test_kv_parts_fill_the_gpu_for_few_heads(monkeypatch):
+def test_kv_parts_fill_the_gpu_for_few_heads():
     """Fewer than 256 (K/V head, key tile) items: each item's steps are split over parts of
     ceil(512 / items) work groups (at most 8), with an fp32 dK/dV partial region of parts x
     Hkv x rows_k x (d_qk + d_v).  Deterministic items keep the largest of 4 and 2 tiles for
     which 8 parts still make 512 work groups; the other modes use one tile per item."""
-    monkeypatch.delenv("FMHA_BWD_KV_PARTS", raising=False)
-    monkeypatch.delenv("FMHA_BWD_TILES_PER_ITEM", raising=False)
     shard = batch_args(B=1, Hq=4, Hkv=1, Sq=16384, Sk=16384, mask=2)  # 128 key tiles, one K/V head
     info = _lib.plan_query(shard)
     assert (info.kv_parts, info.tiles_per_item, info.nsplits) == (8, 2, 64)
@@ -343,10 +344,75 @@ def test_kv_parts_fill_the_gpu_for_few_heads(monkeypatch):
     assert (head.kv_parts, head.dkv_acc_bytes) == (1, 0)
     small = batch_args()  # 3 key tiles x 4 heads: one tile per item, parts capped at 8
     assert (_lib.plan_query(small).kv_parts, _lib.plan_query(small).tiles_per_item) == (8, 1)
-    monkeypatch.setenv("FMHA_BWD_TILES_PER_ITEM", "2")  # the knobs override independently
+    small.tune_tiles_per_item = 2  # the overrides apply independently
     assert (_lib.plan_query(small).kv_parts, _lib.plan_query(small).tiles_per_item) == (8, 2)
-    monkeypatch.setenv("FMHA_BWD_KV_PARTS", "3")
+    small.tune_kv_parts = 3
     assert (_lib.plan_query(small).kv_parts, _lib.plan_query(small).tiles_per_item) == (3, 2)
+
+
+def test_plan_reads_only_its_arguments(monkeypatch):
+    """The plan is a pure function of the argument struct (and the host seqstart arrays): the
+    environment variables that once tuned it change nothing between the sizing, prepare and
+    run calls ("[ROCm] Fix THD/ragged dQ backward on the bf16 dq_shuffle path (gfx950)", Root
+    cause: a sizing pass that disagreed with the run)."""
+    for kernel in (_lib.KERNEL_AUTO, _lib.KERNEL_FOUR_WAVE):
+        a = batch_args(B=2, Hq=16, Hkv=16, Sq=2048, Sk=2048, mask=1, kernel=kernel)
+        size = _lib.workspace_size(a)
+        before = _lib.plan_query(a).as_dict()
+        for name, val in (("FMHA_BWD_TILE_M", "32"), ("FMHA_BWD_TILES_PER_ITEM", "4"),
+                          ("FMHA_BWD_KV_PARTS", "3")):
+            monkeypatch.setenv(name, val)
+        assert _lib.plan_query(a).as_dict() == before
+        assert _lib.workspace_size(a) == size
+
+
+def test_wide_kernel_plan():
+    """d_qk = d_v = 128 without bias or dropout runs the eight-wave kernel: 256-key tiles and
+    32-row query blocks; the deterministic and bf16 accumulators follow that block height."""
+    for det, acc in ((1, _lib.DQ_ACC_FP32), (0, _lib.DQ_ACC_FP32), (0, _lib.DQ_ACC_BF16)):
+        a = batch_args(B=2, Hq=4, Hkv=2, Sq=200, Sk=333, deterministic=det, kernel=_lib.KERNEL_AUTO)
+        a.dq_acc_dtype = acc
+        info = _lib.plan_query(a)
+        assert (info.kernel, info.tile_m, info.tile_n) == (_lib.KERNEL_WIDE, 32, 256)
+        assert info.n_kv_tiles == 2 and info.n_q_blocks == 7
+        assert _lib.workspace_size(a) == info.workspace_bytes
+        if det:
+            assert info.acc_rows == 2 * 200 + 2 * 32 and info.nsplits == 2
+        elif acc == _lib.DQ_ACC_BF16:
+            assert info.acc_rows == 224  # 200 rounded up to 32
+    # other head dims, a bias, dropout, or an explicit request keep the four-wave kernel
+    for d_qk, d_v in ((64, 64), (192, 128)):
+        assert _lib.plan_query(batch_args(d_qk=d_qk, d_v=d_v, kernel=_lib.KERNEL_AUTO)).kernel == _lib.KERNEL_FOUR_WAVE
+    drop = batch_args(kernel=_lib.KERNEL_AUTO)
+    drop.p_drop = 0.1
+    assert _lib.plan_query(drop).kernel == _lib.KERNEL_FOUR_WAVE
+    assert _lib.plan_query(batch_args()).kernel == _lib.KERNEL_FOUR_WAVE
+    # the wide kernel cannot be forced where it does not apply; its block height is fixed
+    bad = batch_args(d_qk=64, d_v=64, kernel=_lib.KERNEL_WIDE)
+    assert status_of(bad) == _lib.ERR_INVALID_ARG
+    bad = batch_args(kernel=_lib.KERNEL_WIDE)
+    bad.tune_tile_m = 64
+    assert status_of(bad) == _lib.ERR_INVALID_ARG
+    for field, val in (("tune_kernel", 3), ("tune_tiles_per_item", 3), ("tune_kv_parts", 9),
+                       ("tune_kv_parts", -1)):
+        a = batch_args()
+        setattr(a, field, val)
+        assert status_of(a) == _lib.ERR_INVALID_ARG, field
+
+
+def test_bf16_accumulator_tile_limit():
+    """bf16 accumulation adds one rounded contribution per key tile; the plan refuses more than
+    64 tiles per segment, where the error estimate u*sqrt(n/6) (u = 2^-8) leaves the cosine
+    bar, instead of returning a dQ outside it."""
+    for kernel, tile_n in ((_lib.KERNEL_AUTO, 256), (_lib.KERNEL_FOUR_WAVE, 128)):
+        ok = batch_args(B=1, Hq=4, Hkv=4, Sq=256, Sk=64 * tile_n, deterministic=0, kernel=kernel)
+        ok.dq_acc_dtype = _lib.DQ_ACC_BF16
+        assert _lib.plan_query(ok).n_kv_tiles == 64
+        over = batch_args(B=1, Hq=4, Hkv=4, Sq=256, Sk=64 * tile_n + 1, deterministic=0, kernel=kernel)
+        over.dq_acc_dtype = _lib.DQ_ACC_BF16
+        assert status_of(over) == _lib.ERR_UNSUPPORTED
+        over.dq_acc_dtype = _lib.DQ_ACC_FP32
+        assert status_of(over) == _lib.OK
 
 
 def test_tiles_per_item_keeps_two_items_per_cu():

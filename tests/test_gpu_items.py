@@ -1,10 +1,13 @@
 """Deterministic work items of several key tiles (tiles_per_item forced to 2 and 4 through the
-FMHA_BWD_TILES_PER_ITEM knob): each item adds its tiles' dQ contributions into one split, the
-later tiles reading back what the earlier ones wrote.  Windows make consecutive tiles touch
-different query blocks, so blocks written by only some of an item's tiles are covered."""
+tune_tiles_per_item argument), in both main-kernel layouts: each item adds its tiles' dQ
+contributions into one split, the later tiles reading back what the earlier ones wrote.
+Windows make consecutive tiles touch different query blocks, so blocks written by only some of
+an item's tiles are covered."""
 
 import numpy as np
 import pytest
+
+import attention_backward_fmha_amd as F
 
 from gpu_common import assert_grads_close, make_inputs, oracle_backward, oracle_forward, run_gpu, seq_offsets
 
@@ -19,10 +22,14 @@ CASES = [
 ]
 
 
+KERNELS = [F.KERNEL_WIDE, F.KERNEL_FOUR_WAVE]
+
+
+@pytest.mark.parametrize("kernel", KERNELS, ids=["wide", "four_wave"])
 @pytest.mark.parametrize("tpi", [2, 4])
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
-def test_items_of_several_tiles(case, tpi, monkeypatch):
-    monkeypatch.setenv("FMHA_BWD_TILES_PER_ITEM", str(tpi))
+def test_items_of_several_tiles(case, tpi, kernel):
+    tune = dict(tiles_per_item=tpi, kernel=kernel)
     _, shape, (hq, hkv), mask, window = case
     if "lens" in shape:
         lens = shape["lens"]
@@ -33,18 +40,20 @@ def test_items_of_several_tiles(case, tpi, monkeypatch):
         x = make_inputs(7002, B=shape["B"], Sq=shape["Sq"], Sk=shape["Sk"], Hq=hq, Hkv=hkv, d_qk=128, d_v=128)
     o, lse = oracle_forward(x, scale=0.088, mask=mask, window=window, sq=sq, sk=sk)
     ref = oracle_backward(x, scale=0.088, mask=mask, window=window, sq=sq, sk=sk)
-    got = run_gpu(x, o, lse, scale=0.088, mask=mask, window=window, sq=sq, sk=sk, deterministic=True)
+    got = run_gpu(x, o, lse, scale=0.088, mask=mask, window=window, sq=sq, sk=sk, deterministic=True,
+                  tune=tune)
     assert_grads_close(got, ref, sq, sk)
 
 
-def test_items_of_four_tiles_are_bit_identical(monkeypatch):
-    monkeypatch.setenv("FMHA_BWD_TILES_PER_ITEM", "4")
+@pytest.mark.parametrize("kernel", KERNELS, ids=["wide", "four_wave"])
+def test_items_of_four_tiles_are_bit_identical(kernel):
+    tune = dict(tiles_per_item=4, kernel=kernel)
     lens = [700, 130, 1000]
     sq = seq_offsets(lens)
     x = make_inputs(7003, lens_q=lens, lens_k=lens, Hq=8, Hkv=2, d_qk=128, d_v=128)
     o, lse = oracle_forward(x, scale=0.088, mask=TL, sq=sq, sk=sq)
-    first = run_gpu(x, o, lse, scale=0.088, mask=TL, sq=sq, sk=sq, deterministic=True)
+    first = run_gpu(x, o, lse, scale=0.088, mask=TL, sq=sq, sk=sq, deterministic=True, tune=tune)
     for _ in range(4):
-        again = run_gpu(x, o, lse, scale=0.088, mask=TL, sq=sq, sk=sq, deterministic=True)
+        again = run_gpu(x, o, lse, scale=0.088, mask=TL, sq=sq, sk=sq, deterministic=True, tune=tune)
         for a, b in zip(first, again):
             assert np.array_equal(a, b)

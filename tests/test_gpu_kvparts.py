@@ -1,10 +1,12 @@
 """Key tiles whose steps (query heads x query blocks) are split over several work groups
-(FMHA_BWD_KV_PARTS forces the count; the plan uses parts when there are too few K/V heads and
-tiles to fill the GPU).  Each part adds fp32 dK/dV partials and a final pass sums them in
+(tune_kv_parts forces the count; the plan uses parts when there are too few K/V heads and
+tiles to fill the GPU), in both main-kernel layouts at d = 128.  Each part adds fp32 dK/dV partials and a final pass sums them in
 ascending part order, so deterministic mode stays bit-reproducible."""
 
 import numpy as np
 import pytest
+
+import attention_backward_fmha_amd as F
 
 from gpu_common import assert_grads_close, make_inputs, oracle_backward, oracle_forward, run_gpu, seq_offsets
 
@@ -32,43 +34,48 @@ def _inputs(case, seed):
     return x, sq, sk, 1.0 / np.sqrt(dqk), mask, window
 
 
+# (case, kernel): both layouts where d = 128 selects the wide one by default
+CASE_KERNELS = [(c, k) for c in CASES for k in ([F.KERNEL_AUTO, F.KERNEL_FOUR_WAVE] if c[3] == (128, 128)
+                                                 else [F.KERNEL_AUTO])]
+CK_IDS = ["%s-%s" % (c[0], {F.KERNEL_AUTO: "auto", F.KERNEL_FOUR_WAVE: "four_wave"}[k]) for c, k in CASE_KERNELS]
+
+
 @pytest.mark.parametrize("mode", ["det", "atomic", "atomic16"])
 @pytest.mark.parametrize("parts", [1, 3, 8])
-@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
-def test_split_key_tiles_match_oracle(case, parts, mode, monkeypatch):
-    monkeypatch.setenv("FMHA_BWD_KV_PARTS", str(parts))
+@pytest.mark.parametrize("case,kernel", CASE_KERNELS, ids=CK_IDS)
+def test_split_key_tiles_match_oracle(case, kernel, parts, mode):
+    tune = dict(kv_parts=parts, kernel=kernel)
     x, sq, sk, scale, mask, window = _inputs(case, 9401)
     o, lse = oracle_forward(x, scale=scale, mask=mask, window=window, sq=sq, sk=sk)
     ref = oracle_backward(x, scale=scale, mask=mask, window=window, sq=sq, sk=sk)
     det, acc = {"det": (True, "fp32"), "atomic": (False, "fp32"), "atomic16": (False, "bf16")}[mode]
     got = run_gpu(x, o, lse, scale=scale, mask=mask, window=window, sq=sq, sk=sk, deterministic=det,
-                  dq_acc_dtype=acc)
+                  dq_acc_dtype=acc, tune=tune)
     assert_grads_close(got, ref, sq, sk)
 
 
 @pytest.mark.parametrize("tiles", [2, 4, 8])
 @pytest.mark.parametrize("parts", [3, 8])
-@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
-def test_parts_of_multi_tile_items_match_oracle(case, parts, tiles, monkeypatch):
+@pytest.mark.parametrize("case,kernel", CASE_KERNELS, ids=CK_IDS)
+def test_parts_of_multi_tile_items_match_oracle(case, kernel, parts, tiles):
     """Deterministic items of several key tiles, split into parts: a part adds its dQ partial
     of a later tile onto the split blocks it wrote for an earlier one."""
-    monkeypatch.setenv("FMHA_BWD_KV_PARTS", str(parts))
-    monkeypatch.setenv("FMHA_BWD_TILES_PER_ITEM", str(tiles))
+    tune = dict(kv_parts=parts, tiles_per_item=tiles, kernel=kernel)
     x, sq, sk, scale, mask, window = _inputs(case, 9403)
     o, lse = oracle_forward(x, scale=scale, mask=mask, window=window, sq=sq, sk=sk)
     ref = oracle_backward(x, scale=scale, mask=mask, window=window, sq=sq, sk=sk)
-    got = run_gpu(x, o, lse, scale=scale, mask=mask, window=window, sq=sq, sk=sk)
+    got = run_gpu(x, o, lse, scale=scale, mask=mask, window=window, sq=sq, sk=sk, tune=tune)
     assert_grads_close(got, ref, sq, sk)
 
 
-@pytest.mark.parametrize("tiles", ["1", "2"])
-def test_split_key_tiles_are_bit_identical(tiles, monkeypatch):
-    monkeypatch.setenv("FMHA_BWD_KV_PARTS", "5")
-    monkeypatch.setenv("FMHA_BWD_TILES_PER_ITEM", tiles)
+@pytest.mark.parametrize("kernel", [F.KERNEL_WIDE, F.KERNEL_FOUR_WAVE], ids=["wide", "four_wave"])
+@pytest.mark.parametrize("tiles", [1, 2])
+def test_split_key_tiles_are_bit_identical(tiles, kernel):
+    tune = dict(kv_parts=5, tiles_per_item=tiles, kernel=kernel)
     x, sq, sk, scale, mask, window = _inputs(CASES[0], 9402)
     o, lse = oracle_forward(x, scale=scale, mask=mask, sq=sq, sk=sk)
-    first = run_gpu(x, o, lse, scale=scale, mask=mask, sq=sq, sk=sk)
+    first = run_gpu(x, o, lse, scale=scale, mask=mask, sq=sq, sk=sk, tune=tune)
     for _ in range(4):
-        again = run_gpu(x, o, lse, scale=scale, mask=mask, sq=sq, sk=sk)
+        again = run_gpu(x, o, lse, scale=scale, mask=mask, sq=sq, sk=sk, tune=tune)
         for a, b in zip(first, again):
             assert np.array_equal(a, b)

@@ -7,6 +7,7 @@ import os
 import numpy as np
 import pytest
 
+import attention_backward_fmha_amd as F
 from gpu_common import (assert_grads_close, make_inputs, oracle_backward, oracle_forward,
                         run_gpu, seq_offsets)
 
@@ -21,24 +22,31 @@ def _segments():
         return json.load(f)
 
 
+# main-kernel layouts at d = 128: the default (eight waves, 256-key tiles) and the four-wave one
+KERNELS = [F.KERNEL_AUTO, F.KERNEL_FOUR_WAVE]
+KERNEL_IDS = ["wide", "four_wave"]
+
+
 def _run_batch(seed, B, Sq, Sk, Hq, Hkv, d_qk, d_v, mask, window=(-1, -1), deterministic=True,
-               sigmas=(1, 1, 1, 1)):
+               sigmas=(1, 1, 1, 1), kernel=F.KERNEL_AUTO):
     x = make_inputs(seed, B=B, Sq=Sq, Sk=Sk, Hq=Hq, Hkv=Hkv, d_qk=d_qk, d_v=d_v, sigmas=sigmas)
     scale = 1.0 / np.sqrt(d_qk)
     o, lse = oracle_forward(x, scale=scale, mask=mask, window=window)
     ref = oracle_backward(x, scale=scale, mask=mask, window=window)
-    got = run_gpu(x, o, lse, scale=scale, mask=mask, window=window, deterministic=deterministic)
+    got = run_gpu(x, o, lse, scale=scale, mask=mask, window=window, deterministic=deterministic,
+                  tune=dict(kernel=kernel))
     assert_grads_close(got, ref)
 
 
-def _run_group(seed, lens_q, lens_k, Hq, Hkv, d_qk, d_v, mask, window=(-1, -1), deterministic=True):
+def _run_group(seed, lens_q, lens_k, Hq, Hkv, d_qk, d_v, mask, window=(-1, -1), deterministic=True,
+               kernel=F.KERNEL_AUTO):
     sq, sk = seq_offsets(lens_q), seq_offsets(lens_k)
     x = make_inputs(seed, lens_q=lens_q, lens_k=lens_k, Hq=Hq, Hkv=Hkv, d_qk=d_qk, d_v=d_v)
     scale = 1.0 / np.sqrt(d_qk)
     o, lse = oracle_forward(x, scale=scale, mask=mask, window=window, sq=sq, sk=sk)
     ref = oracle_backward(x, scale=scale, mask=mask, window=window, sq=sq, sk=sk)
     got = run_gpu(x, o, lse, scale=scale, mask=mask, window=window, sq=sq, sk=sk,
-                  deterministic=deterministic)
+                  deterministic=deterministic, tune=dict(kernel=kernel))
     assert_grads_close(got, ref, sq=sq, sk=sk)
 
 
@@ -47,13 +55,14 @@ def test_tiny_no_mask_d64():
     _run_batch(1001, 1, 64, 64, 1, 1, 64, 64, NONE)
 
 
+@pytest.mark.parametrize("kernel", KERNELS, ids=KERNEL_IDS)
 @pytest.mark.parametrize("deterministic", [True, False], ids=["det", "atomic"])
 @pytest.mark.parametrize("mask,window", [(NONE, (-1, -1)), (TL, (-1, -1)), (BR, (-1, -1)),
                                          (WIN, (37, 5)), (WIN, (-1, 20)), (WIN, (70, -1))],
                          ids=["none", "tl", "br", "win37_5", "win_l_inf", "win_r_inf"])
-def test_batch_masks_d128(mask, window, deterministic):
+def test_batch_masks_d128(mask, window, deterministic, kernel):
     # Sq != Sk and neither a multiple of the tiles: several tiles plus ragged tails
-    _run_batch(2001, 2, 200, 333, 4, 2, 128, 128, mask, window, deterministic)
+    _run_batch(2001, 2, 200, 333, 4, 2, 128, 128, mask, window, deterministic, kernel=kernel)
 
 
 @pytest.mark.parametrize("d_qk,d_v", [(64, 64), (192, 128)])
@@ -64,10 +73,11 @@ def test_batch_head_dims(d_qk, d_v, mask):
 
 @pytest.mark.parametrize("name", ["split_100_80_76", "split_200_56", "split_103_77_61",
                                   "split_64x4", "split_128_128", "single_256"])
+@pytest.mark.parametrize("kernel", KERNELS, ids=KERNEL_IDS)
 @pytest.mark.parametrize("deterministic", [True, False], ids=["det", "atomic"])
-def test_group_fixed_packings_causal(name, deterministic):
+def test_group_fixed_packings_causal(name, deterministic, kernel):
     lens = _segments()["fixed_from_pages"][name]
-    _run_group(3001, lens, lens, 8, 2, 128, 128, TL, deterministic=deterministic)
+    _run_group(3001, lens, lens, 8, 2, 128, 128, TL, deterministic=deterministic, kernel=kernel)
 
 
 def test_group_empty_and_uneven_segments():
