@@ -87,6 +87,10 @@ WORKLOADS = {
                                   mask=MASK_CAUSAL_TOP_LEFT, seed=1002, sigmas=(1, 1, 1, 1)),
     "thd_gqa_llama3_8192": dict(Hq=32, Hkv=8, d_qk=128, d_v=128, total=8192, mask=MASK_CAUSAL_TOP_LEFT,
                                 seed=1003, sigmas=(1, 1, 1, 1)),
+    # the same tokens with the pages' fixed splits [100, 80, 76] and [200, 56] packed first
+    "thd_gqa_llama3_8192_mixed": dict(Hq=32, Hkv=8, d_qk=128, d_v=128, total=8192,
+                                      prefix=(100, 80, 76, 200, 56), mask=MASK_CAUSAL_TOP_LEFT,
+                                      seed=1003, sigmas=(1, 1, 1, 1)),
     "long_16384_causal_br": dict(B=1, Hq=32, Hkv=8, Sq=16384, Sk=16384, d_qk=128, d_v=128,
                                  mask=MASK_CAUSAL_BOTTOM_RIGHT, seed=1004, sigmas=(1, 1, 1, 1)),
     "long_16384_window_4096": dict(B=1, Hq=32, Hkv=8, Sq=16384, Sk=16384, d_qk=128, d_v=128,

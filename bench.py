@@ -48,6 +48,10 @@ def parse():
     ap.add_argument("--only-mode", action="store_true",
                     help="time only --mode (profiling runs); by default both modes are timed")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the graded configurations reported beside the headline")
+    ap.add_argument("--workload-steps", type=int, default=10,
+                    help="timed steps per mode of each graded configuration")
     ap.add_argument("--bias", choices=["none", "11ss", "1hss", "b1ss", "bhss"], default="none",
                     help="add a seeded bf16 bias of this shape (and compute dbias)")
     ap.add_argument("--dropout", type=float, default=0.0, help="dropout probability (Philox)")
@@ -70,14 +74,15 @@ def copy_probe(mib, steps):
 
 
 def prepare_thd_inputs(w, device):
-    """Ragged (THD) workload: seeded segment lengths (seed 3, uniform in [56, 2048]), seeded
+    """Ragged (THD) workload: seeded segment lengths (the workload's fixed prefix, then seed 3,
+    uniform in [56, 2048]), seeded
     Q, K, V, dO [T, H, d] (bf16); O and LSE from the device forward.  Returns the tensors and
     the sequence-offset arguments of make_call."""
     import torch
     import attention_backward_fmha_amd as F
     from attention_backward_fmha_amd import inputs as I
 
-    lens = I.ragged_lengths(3, w["total"], 56, 2048)
+    lens = I.ragged_lengths(3, w["total"], 56, 2048, prefix=w.get("prefix", ()))
     T, Hq, Hkv, dqk, dv = w["total"], w["Hq"], w["Hkv"], w["d_qk"], w["d_v"]
     x = I.draw(w["seed"], [(T, Hq, dqk), (T, Hkv, dqk), (T, Hkv, dv), (T, Hq, dv)], w["sigmas"])
     dev = {n: torch.from_numpy(x[n]).to(torch.bfloat16).to(device) for n in x}
@@ -130,13 +135,22 @@ def prepare_inputs(w, device):
     return dev["q"], dev["k"], dev["v"], o, lse, dev["do"], scale
 
 
-def measured_traffic(workload, mode):
+# main-kernel name -> the source file that holds it
+KERNEL_SOURCES = {"k_bwd_main": "kernels.hip", "k_bwd_wide": "kernels_wide.hip"}
+
+
+def main_kernel_name(plan):
+    """The main kernel a plan launches (plan.kernel: 1 four-wave layout, 2 wide layout)."""
+    return "k_bwd_wide" if plan.kernel == 2 else "k_bwd_main"
+
+
+def measured_traffic(kernel, workload, mode):
     """HBM bytes per launch of the main kernel from the committed rocprofv3 counter summary,
     or None when there is none or the kernel source changed since it was taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "k_bwd_main_%s_%s_traffic.txt" % (workload, mode))
-    src = os.path.join(ROOT, "attention_backward_fmha_amd", "csrc", "kernels.hip")
-    if not os.path.exists(path):
+    path = os.path.join(ROOT, "profiles", "%s_%s_%s_traffic.txt" % (kernel, workload, mode))
+    src = os.path.join(ROOT, "attention_backward_fmha_amd", "csrc", KERNEL_SOURCES[kernel])
+    if not os.path.exists(path) or not os.path.exists(src):
         return None
     fields = {}
     for line in open(path):
@@ -186,17 +200,161 @@ def cpu_baseline(w, budget_s):
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        avail = os.cpu_count()
     return {
         "value": flops_per * done / dt / 1e12,
         "unit": "TFLOP/s",
-        "cores": int(threads),
+        # threads the oracle's BLAS ran with (its matrix products are the only parallel part),
+        # never more than the cores this process may run on
+        "cores": int(min(threads, avail)),
+        "host_cores_available": int(avail),
         "cpu_model": cpu_model,
         "blas": blas,
         "kind": "oracle",
         "sample": "%d repetitions of one (batch, head) problem of the workload (Sq=%d, Sk=%d, d=%d, "
-                  "same mask; the workload has %d such problems), fp64 numpy, %.1f s"
+                  "same mask; the workload has %d such problems), fp64 numpy; each repetition "
+                  "recomputes the forward (P, O, LSE) before the gradients, %.1f s"
                   % (done, Sq, Sk, dqk, w["B"] * w["Hq"], dt),
     }
+
+
+# The graded configurations reported beside the headline: (workload, modes, timed steps).
+# Each is timed in every dQ-accumulation mode it is run in; the 16384-token ones use fewer
+# steps (about 8 ms each).
+GRADED = [
+    ("bshd_causal_2x16x2048", MODES, None),
+    ("thd_gqa_llama3_8192", MODES, None),
+    ("thd_gqa_llama3_8192_mixed", MODES, None),
+    ("long_16384_causal_br", ("deterministic", "atomic"), 3),
+    ("long_16384_window_4096", ("deterministic", "atomic"), 3),
+    ("cross_192_128", MODES, None),
+    ("cross_64", MODES, None),
+]
+
+
+def time_steps(step, stream, steps, warmup):
+    """Mean ms per step over ``steps`` back-to-back steps after ``warmup`` untimed ones, with
+    events on the launch stream only around the whole loop."""
+    import torch
+    for _ in range(warmup):
+        step(None)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        step(None)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
+def time_stages(step, stream, steps):
+    """Mean ms of each stage (prepare, dot, main, reduce) from events recorded between the
+    stages' launches on the launch stream."""
+    import torch
+    kev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for s_ in range(steps):
+        step(kev[s_])
+    torch.cuda.synchronize()
+    return [sum(e[i].elapsed_time(e[i + 1]) for e in kev) / steps for i in range(4)]
+
+
+def make_step(call, ws, sh, stream):
+    import attention_backward_fmha_amd as F
+
+    def step(evs):
+        rec = (lambda i: evs[i].record(stream)) if evs is not None else (lambda i: None)
+        rec(0)
+        call.prepare(ws, sh)
+        rec(1)
+        call.run(ws, sh, F.STAGE_DOT)
+        rec(2)
+        call.run(ws, sh, F.STAGE_MAIN)
+        rec(3)
+        call.run(ws, sh, F.STAGE_REDUCE)
+        rec(4)
+    return step
+
+
+def stage_entry(w, m_plan, st):
+    """Stage times with the achieved GB/s of the HBM-bound stages (algorithmic bytes)."""
+    rows = int(m_plan.rows_q)
+    dot_bytes = rows * w["Hq"] * (2 * w["d_v"] * 2 + 4) + rows * w["Hq"] * 8  # O, dO, LSE in; D, L out
+    dq_bytes = rows * w["Hq"] * w["d_qk"] * 2
+    red = m_plan.reduce_read_bytes + dq_bytes
+    if m_plan.kv_parts > 1:  # fp32 dK/dV partials of every part in, bf16 dK/dV out
+        red += m_plan.dkv_acc_bytes + m_plan.dkv_acc_bytes // (m_plan.kv_parts * 2)
+    out_ = {"prepare_ms": round(st[0], 4), "dot_ms": round(st[1], 4), "main_ms": round(st[2], 4),
+            "reduce_ms": round(st[3], 4),
+            "dot_GBps": round(dot_bytes / (st[1] * 1e-3) / 1e9, 1),
+            "reduce_GBps": round(red / (st[3] * 1e-3) / 1e9, 1),
+            "reduce_bytes": int(red)}
+    if m_plan.needs_zero:
+        out_["prepare_GBps"] = round(m_plan.dq_acc_bytes / (st[0] * 1e-3) / 1e9, 1)
+    return out_
+
+
+def device_inputs(w, device):
+    """Inputs of a graded workload: seeded Q, K, V, dO and the device forward's O and LSE."""
+    import torch
+    import attention_backward_fmha_amd as F
+    from attention_backward_fmha_amd import inputs as I
+    if "total" in w:
+        return prepare_thd_inputs(w, device)
+    B, Hq, Hkv, Sq, Sk, dqk, dv = (w[k] for k in ("B", "Hq", "Hkv", "Sq", "Sk", "d_qk", "d_v"))
+    x = I.draw(w["seed"], [(B, Sq, Hq, dqk), (B, Sk, Hkv, dqk), (B, Sk, Hkv, dv), (B, Sq, Hq, dv)],
+               w["sigmas"])
+    dev = {n: torch.from_numpy(x[n]).to(torch.bfloat16).to(device) for n in x}
+    del x
+    scale = 1.0 / math.sqrt(dqk)
+    o, lse = F.fwd(dev["q"], dev["k"], dev["v"], scale=scale, mask_type=w["mask"],
+                   window=w.get("window", (-1, -1)))
+    torch.cuda.synchronize()
+    return dev["q"], dev["k"], dev["v"], o, lse, dev["do"], scale, {}, None
+
+
+def graded_workload(name, modes, steps, warmup, device):
+    """TFLOP/s, share of the bf16 peak, per-stage ms and the plan's split of one graded
+    workload in each of ``modes``."""
+    import torch
+    import attention_backward_fmha_amd as F
+    from attention_backward_fmha_amd import inputs as I
+    w = I.WORKLOADS[name]
+    q, k, v, o, lse, do, scale, seq, lens = device_inputs(w, device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    stream = torch.cuda.current_stream(device)
+    out = {"segments": lens} if lens is not None else {}
+    res = {}
+    for mode in modes:
+        det, acc = MODE_ARGS[mode]
+        call = F.make_call(q, k, v, o, lse, do, dq, dk, dv, scale=scale, mask_type=w["mask"],
+                           window=w.get("window", (-1, -1)), deterministic=det, dq_acc_dtype=acc, **seq)
+        try:
+            plan = call.plan()
+        except F.FmhaError as e:  # e.g. the bf16 accumulator past its key-length bound
+            res[mode] = {"unsupported": str(e)}
+            continue
+        ws = torch.empty(call.workspace_size(), dtype=torch.uint8, device=device)
+        step = make_step(call, ws, stream.cuda_stream, stream)
+        ms = time_steps(step, stream, steps, warmup)
+        st = time_stages(step, stream, steps)
+        out["flops_per_step"] = plan.flops
+        tf = plan.flops / (ms * 1e-3) / 1e12
+        res[mode] = {"tflops": round(tf, 2), "pct_of_bf16_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 2),
+                     "ms_per_step": round(ms, 4), "stages": stage_entry(w, plan, st),
+                     "main_kernel": main_kernel_name(plan), "nsplits": plan.nsplits,
+                     "tiles_per_item": plan.tiles_per_item, "kv_parts": plan.kv_parts,
+                     "tile_m": plan.tile_m, "tile_n": plan.tile_n, "steps": steps}
+        del ws
+    out["modes"] = res
+    del q, k, v, o, lse, do, dq, dk, dv
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -242,43 +400,19 @@ def main():
     stream = torch.cuda.current_stream(device)
     sh = stream.cuda_stream
 
-    def time_mode(mode):
+    def time_mode(mode, headline):
         det, acc = MODE_ARGS[mode]
         call = F.make_call(q, k, v, o, lse, do, dq, dk, dv, scale=scale, mask_type=w["mask"],
                            window=w.get("window", (-1, -1)), deterministic=det, dq_acc_dtype=acc, **extra)
         plan = call.plan()
         ws = torch.empty(call.workspace_size(), dtype=torch.uint8, device=device)
-
-        def step(evs=None):
-            # events: before prepare, after prepare, after dot, after main, after reduce
-            rec = (lambda i: evs[i].record(stream)) if evs is not None else (lambda i: None)
-            rec(0)
-            call.prepare(ws, sh)
-            rec(1)
-            call.run(ws, sh, F.STAGE_DOT)
-            rec(2)
-            call.run(ws, sh, F.STAGE_MAIN)
-            rec(3)
-            call.run(ws, sh, F.STAGE_REDUCE)
-            rec(4)
-
-        for _ in range(args.warmup):
-            step()
-        torch.cuda.synchronize()
-        kev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t0.record(stream)
-        for s_ in range(args.steps):
-            step(kev[s_])
-        t1.record(stream)
-        torch.cuda.synchronize()
-        ms = t0.elapsed_time(t1) / args.steps
-        main_ms = sum(e[2].elapsed_time(e[3]) for e in kev) / args.steps
-        stage_ms = [sum(e[i].elapsed_time(e[i + 1]) for e in kev) / args.steps for i in range(4)]
+        step = make_step(call, ws, sh, stream)
+        # the timed region: exactly args.steps whole steps, events only around the loop
+        ms = time_steps(step, stream, args.steps, args.warmup)
+        # stage breakdown in a separate pass (events between the stage launches)
+        stage_ms = time_stages(step, stream, args.steps)
         cold = None
-        if mode == args.mode:
+        if headline:
             # cold L2/MALL: overwrite a 512 MiB scratch (twice the MALL) before each step
             flush = torch.empty(512 << 20, dtype=torch.uint8, device=device)
             times = []
@@ -286,7 +420,7 @@ def main():
                 flush.fill_(1)
                 a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 a_.record(stream)
-                step()
+                step(None)
                 b_.record(stream)
                 torch.cuda.synchronize()
                 times.append(a_.elapsed_time(b_))
@@ -294,7 +428,7 @@ def main():
             del flush
         del ws
         torch.cuda.empty_cache()
-        return ms, main_ms, plan, stage_ms, cold
+        return ms, stage_ms[2], plan, stage_ms, cold
 
     def time_forward(bwd_flops):
         """The device forward (fmha_fwd_run) on the same inputs, into scratch outputs."""
@@ -319,10 +453,10 @@ def main():
         return {"ms_per_call": round(f_ms, 4), "tflops": round(f_flops / (f_ms * 1e-3) / 1e12, 2),
                 "pct_of_bf16_peak": round(100.0 * f_flops / (f_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
 
-    ms, main_ms, plan, stage_ms, cold_ms = time_mode(args.mode)
+    ms, main_ms, plan, stage_ms, cold_ms = time_mode(args.mode, True)
     runs = [(args.mode, ms, main_ms, plan, stage_ms)]
     if not args.only_mode:
-        runs += [(m,) + time_mode(m)[:4] for m in MODES if m != args.mode]
+        runs += [(m,) + time_mode(m, False)[:4] for m in MODES if m != args.mode]
     # host-side planning (validation, tiles, workspace map) per call
     pcall = F.make_call(q, k, v, o, lse, do, dq, dk, dv, scale=scale, mask_type=w["mask"],
                         window=w.get("window", (-1, -1)), deterministic=MODE_ARGS[args.mode][0],
@@ -335,29 +469,14 @@ def main():
     tflops = flops / (ms * 1e-3) / 1e12
     main_tflops = flops / (main_ms * 1e-3) / 1e12
     modes = {}
-    # algorithmic bytes of the HBM-bound stages (achieved GB/s = bytes / stage time)
-    rows = int(plan.rows_q)
-    dot_bytes = rows * w["Hq"] * (2 * w["d_v"] * 2 + 4) + rows * w["Hq"] * 8  # O, dO, LSE in; D, L out
-    dq_bytes = rows * w["Hq"] * w["d_qk"] * 2
-
-    def stage_entry(m_plan, st):
-        red = m_plan.reduce_read_bytes + dq_bytes
-        if m_plan.kv_parts > 1:  # fp32 dK/dV partials of every part in, bf16 dK/dV out
-            red += m_plan.dkv_acc_bytes + m_plan.dkv_acc_bytes // (m_plan.kv_parts * 2)
-        out_ = {"prepare_ms": round(st[0], 4), "dot_ms": round(st[1], 4), "main_ms": round(st[2], 4),
-                "reduce_ms": round(st[3], 4),
-                "dot_GBps": round(dot_bytes / (st[1] * 1e-3) / 1e9, 1),
-                "reduce_GBps": round(red / (st[3] * 1e-3) / 1e9, 1),
-                "reduce_bytes": int(red)}
-        if m_plan.needs_zero:
-            out_["prepare_GBps"] = round(m_plan.dq_acc_bytes / (st[0] * 1e-3) / 1e9, 1)
-        return out_
-
     for mode, m_ms, m_main, m_plan, m_st in runs:
-        modes[mode] = {"stages": stage_entry(m_plan, m_st),
+        modes[mode] = {"stages": stage_entry(w, m_plan, m_st),
             "value": round(flops / (m_ms * 1e-3) / 1e12, 2), "ms_per_step": round(m_ms, 4),
-            "main_kernel_ms": round(m_main, 4), "nsplits": m_plan.nsplits,
-            "tiles_per_item": m_plan.tiles_per_item, "kv_parts": m_plan.kv_parts}
+            "main_kernel": main_kernel_name(m_plan), "main_kernel_ms": round(m_main, 4),
+            "nsplits": m_plan.nsplits, "tiles_per_item": m_plan.tiles_per_item,
+            "kv_parts": m_plan.kv_parts}
+    forward = time_forward(flops)
+    kname = main_kernel_name(plan)
 
     out = {
         "metric": "FMHA bwd TFLOP/s and % of bf16 MFMA peak, B*H*S*d=2*32*4096*128 causal",
@@ -385,19 +504,31 @@ def main():
             "host_plan_us": round(plan_us, 2),
             "modes": modes,
             "bias": args.bias, "dbias": args.bias != "none", "dropout_p": args.dropout,
-            "forward": time_forward(flops),
+            "forward": forward,
         },
         "roofline": {
-            "kernel": "k_bwd_main",
+            "kernel": kname,
             "bound": "mfma",
             "achieved": round(main_tflops, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(main_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": None if (args.bias != "none" or args.dropout > 0) else measured_traffic(args.workload, args.mode),
+            "traffic": None if (args.bias != "none" or args.dropout > 0)
+            else measured_traffic(kname, args.workload, args.mode),
             "avg_launch_ms": round(main_ms, 4),
         },
     }
+    del q, k, v, o, lse, do, dq, dk, dv, pcall
+    extra.clear()
+    torch.cuda.empty_cache()
+    if not args.no_workloads:
+        out["workloads"] = {}
+        for name, wmodes, wsteps in GRADED:
+            if name == args.workload:
+                continue
+            out["workloads"][name] = graded_workload(
+                name, wmodes, wsteps or args.workload_steps, min(args.warmup, 2), device)
+            print("workload %s done" % name, file=sys.stderr, flush=True)
     if not args.no_cpu_baseline and not thd:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out))

@@ -29,10 +29,10 @@ def test_more_than_one_gpu_is_refused_with_a_message():
 def _fake_tree(tmp_path, source, recorded_sha):
     csrc = tmp_path / "attention_backward_fmha_amd" / "csrc"
     csrc.mkdir(parents=True)
-    (csrc / "kernels.hip").write_bytes(source)
+    (csrc / "kernels_wide.hip").write_bytes(source)
     prof = tmp_path / "profiles"
     prof.mkdir()
-    (prof / "k_bwd_main_w_deterministic_traffic.txt").write_text(
+    (prof / "k_bwd_wide_w_deterministic_traffic.txt").write_text(
         "# comment: not a field\nkernel_source_sha256: %s\nmode: deterministic\n"
         "read_bytes_per_launch: 1000\nwrite_bytes_per_launch: 234\n" % recorded_sha)
 
@@ -42,10 +42,11 @@ def test_traffic_is_read_only_for_the_source_it_was_measured_on(tmp_path, monkey
     source = b"// kernel source\n"
     _fake_tree(tmp_path, source, hashlib.sha256(source).hexdigest())
     monkeypatch.setattr(b, "ROOT", str(tmp_path))
-    assert b.measured_traffic("w", "deterministic") == 1234
-    assert b.measured_traffic("w", "atomic") is None  # no summary for that mode
-    (tmp_path / "attention_backward_fmha_amd" / "csrc" / "kernels.hip").write_bytes(source + b"// edited\n")
-    assert b.measured_traffic("w", "deterministic") is None  # the kernel changed since
+    assert b.measured_traffic("k_bwd_wide", "w", "deterministic") == 1234
+    assert b.measured_traffic("k_bwd_wide", "w", "atomic") is None  # no summary for that mode
+    assert b.measured_traffic("k_bwd_main", "w", "deterministic") is None  # another kernel
+    (tmp_path / "attention_backward_fmha_amd" / "csrc" / "kernels_wide.hip").write_bytes(source + b"// edited\n")
+    assert b.measured_traffic("k_bwd_wide", "w", "deterministic") is None  # the kernel changed since
 
 
 def test_committed_traffic_summaries_are_well_formed():

@@ -1,5 +1,7 @@
-"""Parity at the workloads' full sizes, in the launch configuration the benchmark times, on
-sampled output rows that the oracle computes one by one (dQ rows per query, dK/dV rows per key).
+"""Parity at the largest workloads' full sizes (the 2x32x4096 causal headline and the
+16384-token ones), in the launch configuration the benchmark times, on sampled output rows that
+the oracle computes one by one (dQ rows per query, dK/dV rows per key).  The other graded
+workloads are compared as whole tensors in test_gpu_fullsize_whole.py.
 
 O and LSE (the backward's inputs) are computed by the oracle forward for the K/V groups whose
 rows are checked; the other heads get O = 0 and LSE = +inf (their P is exactly 0), which the
@@ -108,29 +110,7 @@ def test_headline_2x32x4096_causal(deterministic):
     _run(w, deterministic=deterministic, checks=[(0, 0), (1, 31)])
 
 
-@pytest.mark.parametrize("deterministic", [True, False], ids=["det", "atomic"])
-def test_bshd_causal_2x16x2048(deterministic):
-    w = I.WORKLOADS["bshd_causal_2x16x2048"]
-    _run(w, deterministic=deterministic, checks=[(0, 3), (1, 15)])
-
-
-@pytest.mark.parametrize("packing", ["random_8192", "mixed_8192"])
-@pytest.mark.parametrize("deterministic", [True, False], ids=["det", "atomic"])
-def test_thd_gqa_llama3_8192(packing, deterministic):
-    lens = json.load(open(os.path.join(GOLDEN, "segments.json")))[packing]
-    w = I.WORKLOADS["thd_gqa_llama3_8192"]
-    last = len(lens) - 1
-    _run(w, lens=lens, deterministic=deterministic, checks=[(0, 0), (1, 7), (last, 3)])
-
-
 @pytest.mark.parametrize("name", ["long_16384_causal_br", "long_16384_window_4096"])
 def test_long_16384(name):
     w = I.WORKLOADS[name]
     _run(w, deterministic=True, checks=[(0, 5)])
-
-
-@pytest.mark.parametrize("name", ["cross_192_128", "cross_64"])
-@pytest.mark.parametrize("deterministic", [True, False], ids=["det", "atomic"])
-def test_cross_attention(name, deterministic):
-    w = I.WORKLOADS[name]
-    _run(w, deterministic=deterministic, checks=[(0, 0), (3, 15)])
