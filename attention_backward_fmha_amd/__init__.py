@@ -50,6 +50,11 @@ class BwdCall:
     def run(self, ws, stream, stages=STAGE_ALL):
         _lib.run(self.args, ws.data_ptr(), ws.numel() * ws.element_size(), stream, stages)
 
+    def run_noalloc(self, stream):
+        """prepare + run in the library's static scratch (fmha_bwd_run_noalloc): no workspace
+        argument and no device allocation."""
+        _lib.run_noalloc(self.args, stream)
+
 
 def _strides(t, group):
     if t is None:

@@ -40,7 +40,10 @@ EXPORTS = (
     "fmha_bwd_plan_query",
     "fmha_bwd_run_stages",
     "fmha_fwd_run",
+    "fmha_bwd_run_noalloc",
 )
+
+NOALLOC_MAX_BYTES = 256 << 20  # FMHA_BWD_NOALLOC_MAX_BYTES
 
 _i64x3 = ctypes.c_int64 * 3
 
@@ -175,6 +178,7 @@ def lib():
                                           ctypes.c_void_p]
         L.fmha_bwd_plan_query.argtypes = [ap, ctypes.POINTER(PlanInfo)]
         L.fmha_fwd_run.argtypes = [ap, ctypes.c_void_p]
+        L.fmha_bwd_run_noalloc.argtypes = [ap, ctypes.c_void_p]
         L.fmha_bwd_status_string.argtypes = [ctypes.c_int]
         L.fmha_bwd_status_string.restype = ctypes.c_char_p
         for name in EXPORTS:
@@ -220,6 +224,12 @@ def run(args, ws_ptr, ws_bytes, stream, stages=STAGE_ALL):
                                        int(stages), ctypes.c_void_p(stream))
     if st != OK:
         raise FmhaError(st, "fmha_bwd_run")
+
+
+def run_noalloc(args, stream):
+    st = lib().fmha_bwd_run_noalloc(ctypes.byref(args), ctypes.c_void_p(stream))
+    if st != OK:
+        raise FmhaError(st, "fmha_bwd_run_noalloc")
 
 
 def fwd_run(args, stream):

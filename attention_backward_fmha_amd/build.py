@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfmha_bwd.so")
-SOURCES = ["kernels.hip", "kernels_wide.hip", "api.cpp", "plan.cpp"]
+SOURCES = ["kernels.hip", "kernels_wide.hip", "api.cpp", "plan.cpp", "noalloc.hip"]
 ARCH = "gfx950"
 
 

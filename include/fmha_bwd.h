@@ -49,7 +49,7 @@
  *   - Rows with no allowed key get dQ = 0 and contribute nothing to dK and dV.
  *
  * Ownership: the caller owns every tensor and the workspace; the library allocates no device
- * memory and keeps no state between calls.  Host seqstart arrays are read during the call
+ * memory and keeps no state between calls (fmha_bwd_run_noalloc's static scratch aside).  Host seqstart arrays are read during the call
  * only.  Device pointers must stay valid until the stream work completes.  One workspace must
  * not serve two runs in flight at the same time, and fmha_bwd_prepare_workspace must precede
  * every fmha_bwd_run (it writes the workspace header, and in the atomic modes it zeroes the
@@ -240,6 +240,19 @@ FMHA_BWD_API int fmha_fwd_run(const fmha_bwd_args* args, void* stream);
 
 /* Static string naming a status code. */
 FMHA_BWD_API const char* fmha_bwd_status_string(int status);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+   loops, harnesses that forbid hipMalloc): fmha_bwd_prepare_workspace followed by fmha_bwd_run
+   on `stream`, with a workspace the library owns instead of a caller's -- a static device
+   array of FMHA_BWD_NOALLOC_MAX_BYTES bytes, one per GPU, held until the process ends (its
+   address is looked up on the first call on each device).  Calls no allocating routine.
+   Arguments whose fmha_bwd_workspace_size exceeds the maximum return
+   FMHA_ERR_WORKSPACE_TOO_SMALL before any device work.  Every call on one GPU shares that
+   GPU's array, which keeps the last call's contents (prepare re-initialises what must start
+   at zero): calls that overlap on one GPU (other streams, other threads) race and must be
+   serialised by the caller.  Results equal those of prepare + run with a caller workspace. */
+#define FMHA_BWD_NOALLOC_MAX_BYTES (256u << 20)
+FMHA_BWD_API int fmha_bwd_run_noalloc(const fmha_bwd_args* args, void* stream);
 
 /* ---- test and measurement hooks -------------------------------------------------------- */
 

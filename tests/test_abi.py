@@ -545,6 +545,17 @@ def test_workspace_too_small_is_reported_before_any_device_work():
     assert _lib.status_string(_lib.ERR_WORKSPACE_TOO_SMALL) == "FMHA_ERR_WORKSPACE_TOO_SMALL"
 
 
+def test_noalloc_rejects_arguments_beyond_its_scratch_before_any_device_work():
+    a = batch_args(B=2, Hq=32, Hkv=32, Sq=4096, Sk=4096, mask=1, deterministic=1,
+                   kernel=_lib.KERNEL_AUTO)
+    assert _lib.workspace_size(a) > _lib.NOALLOC_MAX_BYTES
+    assert _lib.lib().fmha_bwd_run_noalloc(ctypes.byref(a), None) == _lib.ERR_WORKSPACE_TOO_SMALL
+    a.Hq = 3  # invalid arguments are reported as such
+    assert _lib.lib().fmha_bwd_run_noalloc(ctypes.byref(a), None) == _lib.ERR_INVALID_ARG
+    m = re.search(r"#define FMHA_BWD_NOALLOC_MAX_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == _lib.NOALLOC_MAX_BYTES
+
+
 def test_sizing_is_a_pure_function_of_the_arguments():
     """The same arguments always give the same plan, and only the fields that define the
     problem change it (pointer values do not)."""
