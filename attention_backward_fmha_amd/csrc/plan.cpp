@@ -300,21 +300,56 @@ int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t el, bool forwar
       }
     }
   }
-  // Long causal segments (8192 keys or more) whose 4-tile items number between one and two
-  // per CU: 4 tiles per item, split into parts that make about 1024 work groups.  The parts
-  // balance the heavy causal items, and the dK/dV partials they add are small next to the
-  // work of such long rows, while the dQ reduction reads half of what 2-tile items leave.
+  // Long causal segments (8192 keys or more) whose 4-tile items (counted in 128-key tiles)
+  // number between one and two per CU: 4 tiles per item, split into parts that make about
+  // 1024 work groups of the four-wave layout or 512 of the wide one (one per CU at a time,
+  // two rounds).  The parts balance the heavy causal items, and the dK/dV partials they add
+  // are small next to the work of such long rows, while the dQ reduction reads 1/4 of what
+  // one-tile items leave.
   p->kv_parts = 1;
+  bool long_rule = false;
   if (p->deterministic && max_lk >= 8192) {
     const int64_t heads = (int64_t)p->Hkv * p->B;
     const bool even_work = a->mask_type == FMHA_MASK_NONE ||
                            (a->mask_type == FMHA_MASK_WINDOW && a->window_left >= 0 && a->window_right >= 0);
-    const int64_t items4 = (int64_t)((p->n_kv_tiles + 3) / 4) * heads;
-    if (!even_work && items4 >= 256 && items4 < 512) {
+    const int64_t tiles128 = (max_lk + 127) / 128;
+    const int64_t items4_128 = (tiles128 + 3) / 4 * heads;
+    if (!even_work && items4_128 >= 256 && items4_128 < 512) {
       p->tiles_per_item = 4;
-      const int64_t parts = (1024 + items4 - 1) / items4;
+      const int64_t items4 = (int64_t)((p->n_kv_tiles + 3) / 4) * heads;
+      const int64_t target = p->kernel == FMHA_KERNEL_WIDE ? 512 : 1024;
+      const int64_t parts = (target + items4 - 1) / items4;
       p->kv_parts = (int)(parts > 4 ? 4 : parts);
+      long_rule = true;
     }
+  }
+  // Wide layout, uneven items: the (segment, K/V head, key tile) items' steps (query heads x
+  // query blocks) are counted from the mask and the segment lengths.  When the heaviest item
+  // has more than 1.6 times the steps each CU would get with a perfect split, and the items
+  // are long enough (64 steps or more on average) for the fp32 dK/dV partials to be cheap
+  // next to their work, two parts halve the heaviest item.  Measured on MI355X: 8192 ragged
+  // tokens of the Llama-3-8B head shape gain 12-15%, while 2x16x2048 causal (36 steps per
+  // item) loses 10%, its partials costing more than the balance gains.
+  // (Batches of more than 4096 segment tiles fill the GPU anyway and skip the count.)
+  const int nseg = group ? a->B : (a->B > 0 ? 1 : 0);
+  if (p->kernel == FMHA_KERNEL_WIDE && !long_rule && !forward && (int64_t)nseg * p->n_kv_tiles <= 4096) {
+    int64_t total = 0, heaviest = 0, nonempty = 0;
+    for (int b = 0; b < nseg; ++b) {
+      const int64_t lq = group ? (int64_t)a->seqstart_q_host[b + 1] - a->seqstart_q_host[b] : a->Sq;
+      const int64_t lk = group ? (int64_t)a->seqstart_k_host[b + 1] - a->seqstart_k_host[b] : a->Sk;
+      const int64_t reps = group ? p->Hkv : (int64_t)p->Hkv * a->B;
+      const MaskGeom g = mask_geom(a->mask_type, a->window_left, a->window_right, lq, lk);
+      for (int j = 0; (int64_t)j * p->tile_n < lk; ++j) {
+        int64_t lo, hi;
+        qblocks_for_tile(g, lq, lk, j, p->tile_m, p->tile_n, &lo, &hi);
+        if (hi < lo) continue;
+        const int64_t steps = (hi - lo + 1) * p->group_size;
+        total += steps * reps;
+        nonempty += reps;
+        if (steps > heaviest) heaviest = steps;
+      }
+    }
+    if (nonempty > 0 && heaviest * 256 * 5 > total * 8 && total >= 64 * nonempty) p->kv_parts = 2;
   }
   // Too few (K/V head, key tile) items to give every CU one: split each item's steps (query
   // heads x query blocks) over kv_parts work groups that add fp32 dK/dV partials, summed in

@@ -400,6 +400,37 @@ def test_wide_kernel_plan():
         assert status_of(a) == _lib.ERR_INVALID_ARG, field
 
 
+def test_wide_plan_splits_uneven_items():
+    """Wide layout: two parts when the heaviest (segment, K/V head, key tile) item has more
+    than 1.6x the steps a CU would get from a perfect split and the items average 64 steps or
+    more; long causal rows take 4-tile items in parts that make about 512 work groups."""
+    auto = _lib.KERNEL_AUTO
+    random_8192 = [1673, 226, 413, 527, 417, 1652, 1788, 1496]
+    mixed_8192 = [100, 80, 76, 200, 56, 1673, 226, 413, 527, 417, 1652, 1788, 984]
+    for lens in (random_8192, mixed_8192):
+        for det, acc in ((1, _lib.DQ_ACC_FP32), (0, _lib.DQ_ACC_FP32), (0, _lib.DQ_ACC_BF16)):
+            a = group_args(lens, lens, Hq=32, Hkv=8, mask=1, deterministic=det, kernel=auto)
+            a.dq_acc_dtype = acc
+            info = _lib.plan_query(a)
+            assert info.kernel == _lib.KERNEL_WIDE
+            assert (info.kv_parts, info.tiles_per_item) == (2, 1), (lens[0], det, acc)
+            assert info.dkv_acc_bytes == 2 * 8 * 8192 * 256 * 4
+    # 2x16x2048 causal: items of 36 steps on average keep one part
+    for det in (1, 0):
+        info = _lib.plan_query(batch_args(B=2, Hq=16, Hkv=16, Sq=2048, Sk=2048, mask=1,
+                                          deterministic=det, kernel=auto))
+        assert (info.kv_parts, info.tiles_per_item) == (1, 1)
+    info = _lib.plan_query(batch_args(B=2, Hq=32, Hkv=32, Sq=4096, Sk=4096, mask=1, kernel=auto))
+    assert (info.kv_parts, info.tiles_per_item, info.nsplits) == (1, 2, 8)
+    c4 = batch_args(B=1, Hq=32, Hkv=8, Sq=16384, Sk=16384, mask=2, kernel=auto)
+    info = _lib.plan_query(c4)
+    assert (info.kv_parts, info.tiles_per_item, info.nsplits) == (4, 4, 16)
+    c4.deterministic = 0
+    assert _lib.plan_query(c4).kv_parts == 1
+    w = batch_args(B=1, Hq=32, Hkv=8, Sq=16384, Sk=16384, mask=3, window=(4096, 0), kernel=auto)
+    assert (_lib.plan_query(w).kv_parts, _lib.plan_query(w).tiles_per_item) == (1, 2)
+
+
 def test_bf16_accumulator_tile_limit():
     """bf16 accumulation adds one rounded contribution per key tile; the plan refuses more than
     64 tiles per segment, where the error estimate u*sqrt(n/6) (u = 2^-8) leaves the cosine
