@@ -1,7 +1,8 @@
 """Summaries of rocprofv3 CSV output (``-f csv``) for the files kept under ``profiles/``.
 
     python -m attention_backward_fmha_amd.rocprof_summary stats DIR [--match TEXT] [--top N]
-        per-kernel calls / total / average duration from DIR/*kernel_stats.csv
+        per-kernel calls / total / average duration from DIR/*kernel_stats.csv, and the
+        median duration of each kernel's dispatches from DIR/*kernel_trace.csv
     python -m attention_backward_fmha_amd.rocprof_summary traffic --kernel NAME \\
         --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR --copy-mib N
         HBM bytes per launch of NAME: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) scaled by
@@ -29,6 +30,24 @@ def kernel_stats(dir_):
                          float(r["AverageNs"]), float(r.get("Percentage", 0.0))))
     rows.sort(key=lambda x: -x[2])
     return rows
+
+
+def median_durations(dir_):
+    """Kernel name -> median dispatch duration (ns) from the kernel trace, if there is one."""
+    try:
+        path = _one(dir_, "*kernel_trace.csv")
+    except FileNotFoundError:
+        return {}
+    durs = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            durs.setdefault(r["Kernel_Name"], []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    out = {}
+    for name, d in durs.items():
+        d.sort()
+        n = len(d)
+        out[name] = d[n // 2] if n % 2 else 0.5 * (d[n // 2 - 1] + d[n // 2])
+    return out
 
 
 def counter_avg(dir_, counter, kernel):
@@ -59,11 +78,13 @@ def main(argv=None):
     t.add_argument("--copy-kernel", default="copyBuffer")
     a = ap.parse_args(argv)
     if a.cmd == "stats":
-        print("| kernel | calls | total ms | average us | % |")
-        print("|---|---:|---:|---:|---:|")
+        print("| kernel | calls | total ms | average us | median us | % |")
+        print("|---|---:|---:|---:|---:|---:|")
         rows = [r for r in kernel_stats(a.dir) if a.match in r[0]]
+        med = median_durations(a.dir)
         for name, calls, tot, avg, pct in rows[: a.top]:
-            print("| %s | %d | %.3f | %.1f | %.1f |" % (name[:90], calls, tot / 1e6, avg / 1e3, pct))
+            m = "%.1f" % (med[name] / 1e3) if name in med else "-"
+            print("| %s | %d | %.3f | %.1f | %s | %.1f |" % (name[:90], calls, tot / 1e6, avg / 1e3, m, pct))
     else:
         nbytes = a.copy_mib * (1 << 20)
         cf, _ = counter_avg(a.copy_fetch, "FETCH_SIZE", a.copy_kernel)
