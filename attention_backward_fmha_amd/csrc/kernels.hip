@@ -852,19 +852,32 @@ __device__ __forceinline__ void reduce_tiles(const KParams& p, const Seg& sg, bo
     load2(jt + 4, xa);
     add2(jt + 2, xb);
   }
+  // The work group's (up to) four 32x32 tiles go through LDS as bf16, so that each store
+  // writes 16 bytes of a row and 16 consecutive threads cover 256 contiguous bytes of it.
+  static_assert(PPT == 1, "one (tile, lane) pair per thread");
+  __shared__ __attribute__((aligned(16))) uint16_t stage[4][32][40];  // [tile slot][row][col]
   const int64_t q0 = (int64_t)qb * TM;
+  const int slot = threadIdx.x >> 6;
+  if ((NT * 64) % 256 == 0 || tid < NT * 64) {
+    const int ln = tid & 63;
 #pragma unroll
-  for (int pr = 0; pr < PPT; ++pr) {
-    const int pair = tid + 256 * pr;
-    if ((NT * 64) % 256 == 0 || pair < NT * 64) {
-      const int ti = pair >> 6, ln = pair & 63;
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        stage[slot][8 * u + 4 * (ln >> 5) + e][ln & 31] = to_bf16_bits(acc[0][u][e] * p.scale);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int c = threadIdx.x + 256 * k;  // 4 slots x 32 rows x 4 chunks of 8 columns
+    const int row = c >> 4, sl = (c >> 2) & 3, ch = c & 3;
+    const int ti = 4 * part + sl;
+    if (ti < NT) {
       const int mq = ti / (DQK / 32), nd = ti % (DQK / 32);
-      uint16_t* dst = p.dq + elem_off(p.dq_s, group, b, sg.q_row0 + q0, h) + 32 * nd + (ln & 31);
-#pragma unroll
-      for (int sl = 0; sl < 16; ++sl) {
-        const int row = 32 * mq + 8 * (sl >> 2) + 4 * (ln >> 5) + (sl & 3);
-        if (row < nq) dst[(int64_t)row * p.dq_s[1]] = to_bf16_bits(acc[pr][sl >> 2][sl & 3] * p.scale);
-      }
+      const int r = 32 * mq + row;
+      if (r < nq)
+        *(u32x4*)(p.dq + elem_off(p.dq_s, group, b, sg.q_row0 + q0 + r, h) + 32 * nd + 8 * ch) =
+            *(const u32x4*)&stage[sl][row][8 * ch];
     }
   }
 }
