@@ -19,12 +19,16 @@ namespace {
 //   S = Q K_w^T, dP = dO V_w^T              A operands: Q, dO rows from LDS (16-byte reads)
 //   P = exp2(S*scale*log2e - L), dS = P (dP - D)            the lane's key, 16 queries
 //   dV_w += P^T dO, dK_w += dS^T Q          A from registers, B by transposing LDS reads
-//   dS -> LDS (query-major)
+//   dS -> LDS (key-major: each lane writes its key's 16 queries as four 8-byte runs)
 //   dQ = dS K over the tile's 256 keys      one 32x32 output tile per wave, done by the four
-//                                           waves of one half, the halves taking turns
+//                                           waves of one half, the halves taking turns; its
+//                                           A operand comes from the key-major dS and its B
+//                                           operand from K, both by transposing reads
 // Q, dO, L, D and dS are double-buffered, so a step has one barrier: the half that computes
 // the step's dQ does it at the start of the next step, while the other half already works on
-// that step.
+// that step.  The masks are applied only to the 32 x 32 blocks that straddle a mask edge or
+// the tile's last key (a wave-uniform test), and the L/D loads of the next step are selected
+// where they are stored, so no wave waits on a global load inside a step.
 //
 // LDS tiles are row-major with rows padded by 16 bytes, so that consecutive rows start 4
 // banks apart and every LDS offset of the unrolled loops is a per-lane base plus a constant:
@@ -37,11 +41,8 @@ namespace {
 //     permuted inside each 32-key block (krow below) so that 4 consecutive keys land on 4
 //     rows spaced by 2, while the 16 keys one row read of S takes (every other key, see
 //     kmap) land on 16 distinct rows.
-constexpr int kSchedMfma = 0x008;
-constexpr int kSchedDsRead = 0x100;
-
 constexpr int kRowQ = 136;   // Q, dO and K rows: 128 bf16 + 8 of padding (see below)
-constexpr int kRowS = 264;   // dS rows: 256 bf16 + 8
+constexpr int kRowT = 36;    // dS^T rows (one per key): 32 bf16 + 4
 
 // LDS row of key k of the tile.  32-key blocks stay in place; inside a block the key's bits
 // k0..k4 go to row bits r0 = k3, r1 = k0 ^ k2, r2 = k1, r3 = k4, r4 = k2 (one-to-one, and
@@ -49,13 +50,6 @@ constexpr int kRowS = 264;   // dS rows: 256 bf16 + 8
 __device__ __forceinline__ int krow(int k) {
   return (k & ~31) | ((k >> 3) & 1) | (((k ^ (k >> 2)) & 1) << 1) | (((k >> 1) & 1) << 2) |
          (((k >> 4) & 1) << 3) | (((k >> 2) & 1) << 4);
-}
-
-// Physical row of dS row r: bits 0..3 of r go to bits (0, 2, 1, 3).  The dS exchange writes
-// rows {0, 2, 8, 10} (+ a constant) from one 16-lane group, which then start 16 banks apart;
-// the 16 consecutive rows the dQ operand reads stay on distinct banks.
-__device__ __forceinline__ int ds_row(int r) {
-  return (r & 16) | (r & 1) | ((r >> 1) & 1) << 2 | ((r >> 2) & 1) << 1 | (r & 8);
 }
 
 // x as three bf16 parts (x = p1 + p2 + p3 to within fp32 rounding) followed by five zeros.
@@ -67,49 +61,13 @@ __device__ __forceinline__ u32x4 split3(float x) {
   return u32x4{__builtin_bit_cast(unsigned, bf16x2{p1, p2}), (unsigned)__builtin_bit_cast(uint16_t, p3), 0u, 0u};
 }
 
-// dS of the wave's 32 keys (columns 32*wave ..) for the step's 32 queries into the swizzled
-// query-major tile; the exchange is write_ds_tile's.
-__device__ __forceinline__ void write_ds_wide(uint16_t* ds, const float (&d)[16], int wave, int lane) {
-  unsigned w[4][2];
+// dS of the lane's key for the step's 32 queries into the key-major tile: register 4u + e
+// holds query 8u + 4hi + e, so each u is one 8-byte write of four consecutive queries.  With
+// 72-byte rows the 16 even (or odd) keys one 16-lane pass writes land on distinct bank pairs.
+__device__ __forceinline__ void write_dst(uint16_t* dst, const float (&d)[16], int key, int hi) {
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-#pragma unroll
-    for (int e1 = 0; e1 < 2; ++e1) {
-      const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(d[4 * c + 2 * e1]),
-                                                      __float_as_uint(d[4 * c + 2 * e1 + 1]),
-                                                      false, false);
-      w[c][e1] = pack_bf16(__uint_as_float(r[0]), __uint_as_float(r[1]));
-    }
-  }
-  const bool x0 = (lane & 1) != 0;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const unsigned t0 = xor1(w[c][0]);
-    const unsigned t1 = xor1(w[c][1]);
-    const unsigned n0 = x0 ? t1 : w[c][0];
-    const unsigned n1 = x0 ? w[c][1] : t0;
-    w[c][0] = n0;
-    w[c][1] = n1;
-  }
-  const bool x1 = (lane & 2) != 0;
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const unsigned a = w[2 * u][s];
-      const unsigned b = w[2 * u + 1][s];
-      const unsigned ta = xor2(a);
-      const unsigned tb = xor2(b);
-      w[2 * u][s] = x1 ? tb : a;
-      w[2 * u + 1][s] = x1 ? b : ta;
-    }
-  }
-  const int row = 8 * ((lane >> 1) & 1) + 4 * (lane >> 5) + 2 * (lane & 1) + ((lane >> 4) & 1);
-  const int col = 32 * wave + 8 * ((lane >> 2) & 3);
-#pragma unroll
-  for (int u = 0; u < 2; ++u)
-    *(u32x4*)&ds[ds_row(row + 16 * u) * kRowS + col] =
-        u32x4{w[2 * u][0], w[2 * u][1], w[2 * u + 1][0], w[2 * u + 1][1]};
+  for (int u = 0; u < 4; ++u)
+    *(u32x2*)&dst[key * kRowT + 8 * u + 4 * hi] = u32x2{pack_bf16(d[4 * u], d[4 * u + 1]), pack_bf16(d[4 * u + 2], d[4 * u + 3])};
 }
 
 template <int DQM>
@@ -118,10 +76,11 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
   constexpr bool DET = DQM == 1;
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[TN * kRowQ];          // K tile
   __shared__ __attribute__((aligned(16))) uint16_t qo_lds[2][2][TM * kRowQ];   // [buffer][Q, dO]
-  __shared__ __attribute__((aligned(16))) uint16_t ds_lds[2][TM * kRowS];      // [buffer] dS
+  __shared__ __attribute__((aligned(16))) uint16_t ds_lds[2][TN * kRowT];      // [buffer] dS^T
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // the same value, in a scalar register
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
@@ -265,7 +224,7 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
     // ---- staging: thread t loads 16 bytes of Q and of dO (row t/16, chunk t%16); wave 0
     // loads L (lanes 0..31) and D (lanes 32..63) ----
     u32x4 q_pre, o_pre;
-    float ld_pre = 0.f;
+    float l_pre = 0.f, d_pre = 0.f;  // wave 0: L (lanes 0..31) and D (lanes 32..63) loads in flight
     int nq_pre = 0;
     const int st_row = tid >> 4, st_c = tid & 15;
     const int q_lane = (st_row * qs1 + st_c * 8) * 2, o_lane = (st_row * os1 + st_c * 8) * 2;
@@ -278,7 +237,8 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
       if (wave == 0) {  // two loads with wave-uniform resources
         const float lv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(valid ? rl : none, (pc.r + l32) * 4, 0, 0));
         const float dv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(valid ? rd : none, (pc.r + l32) * 4, 0, 0));
-        ld_pre = lane < 32 ? lv : dv;
+        l_pre = lv;  // selected where they are stored, so nothing waits for the loads here
+        d_pre = dv;
       }
       const int h_old = pc.h;
       advance(pc);
@@ -290,7 +250,7 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
       // the padding columns of Q row r carry -L2[r]/c, those of dO row r carry -D[r] (three
       // bf16 parts each); a row past the segment end gets -1e30, so its P is exactly 0
       if (wave == 0) {
-        const float x = lane < 32 ? (l32 < nq_pre ? -ld_pre * inv_c : -1e30f) : -ld_pre;
+        const float x = lane < 32 ? (l32 < nq_pre ? -l_pre * inv_c : -1e30f) : -d_pre;
         *(u32x4*)&qo_lds[buf][hi][l32 * kRowQ + D] = split3(x);
       }
     };
@@ -319,7 +279,8 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
           prev[u] = __builtin_amdgcn_raw_buffer_load_b128(rprev, (r * D + nd * 1024 + u * 256 + lane * 4) * 4, 0, 0);
       }
       f32x16 acc = f32x16{};
-      const uint16_t* dsb = &ds_lds[buf][ds_row(l32) * kRowS + 8 * hi];
+      // A operand: keys 16kk + 8hi .. +7 of query l32, two transposing reads of the key-major dS
+      const uint16_t* dsb = &ds_lds[buf][(8 * hi + tr_row) * kRowT + tr_col];
       const uint16_t* kt0 = &k_lds[tk_row0 * kRowQ + 32 * nd + tr_col];
       const uint16_t* kt1 = &k_lds[tk_row1 * kRowQ + 32 * nd + tr_col];
       // operands of reduction step kk: dS row chunk and the transposed K block; loaded two
@@ -327,7 +288,7 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
       bf16x8 da[2], bk[2];
       auto ld = [&](int kk) {
         const int kb = (32 * (kk >> 1) + 8 * (kk & 1)) * kRowQ;
-        da[kk & 1] = *(const bf16x8*)&dsb[16 * kk];
+        da[kk & 1] = tr_read(&dsb[16 * kk * kRowT], &dsb[(16 * kk + 4) * kRowT]);
         bk[kk & 1] = tr_read(&kt0[kb], &kt1[kb]);
       };
       ld(0);
@@ -355,13 +316,14 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
         // 2048 bytes * nd), register pair k2 at 256 * k2, lane l's word at 4 * l
         const bool odd = (lane & 1) != 0;
         const unsigned sel = odd ? 0x03020706u : 0x05040100u;
+        const int vbase = r * D * 2 + nd * 2048 + lane * 4;
 #pragma unroll
         for (int k2 = 0; k2 < 8; ++k2) {
           const unsigned mine = pack_bf16(acc[k2], acc[8 + k2]);
           const unsigned other = xor1(mine);
           const unsigned v = __builtin_amdgcn_perm(other, mine, sel);
-          const int voff = r * D * 2 + nd * 2048 + k2 * 256 + lane * 4;
-          asm volatile("buffer_atomic_pk_add_bf16 %0, %1, %2, 0 offen" ::"v"(v), "v"(voff), "s"(rdq));
+          asm volatile("buffer_atomic_pk_add_bf16 %0, %1, %2, 0 offen offset:%3" ::"v"(v), "v"(vbase), "s"(rdq),
+                       "n"(k2 * 256));
         }
       } else {
         // register rr holds row 8(rr/4) + 4hi + rr%4, column 32nd + l32
@@ -422,17 +384,29 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
           if (kk + 2 <= D / 16) ld(kk + 2);
           __builtin_amdgcn_sched_barrier(0);
         }
-        // P = exp2(c S), 0 for masked pairs; dS = P dP
+        // P = exp2(c S), 0 for masked pairs; dS = P dP.  The mask is applied only when some
+        // (key, query) pair of the wave's 32 x 32 block is outside it (the block straddles
+        // the mask's edge or the tile's last key): a wave-uniform test per step
         bf16x8 pa[2], sa[2];
         {
-          const int t0 = key_ok ? (int)key0 - q0 + key_w - lo_d - 4 * hi : (int)span + TM + 1;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) ds32[r] = __builtin_amdgcn_exp2f(s_acc[r] * p.scale_log2);
+          const int dmin = (int)key0 + 32 * wave_s - q0 - (TM - 1) - lo_d;  // min over the block of key - query - lo_d
+          const bool full = 32 * wave_s + 32 <= nk && dmin >= 0 && dmin + 62 <= (int)span;
+          if (!full) {
+            const int t0 = key_ok ? (int)key0 - q0 + key_w - lo_d - 4 * hi : (int)span + TM + 1;
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                ds32[4 * c + e] = (unsigned)(t0 - (8 * c + e)) <= span ? ds32[4 * c + e] : 0.f;
+          }
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int r = 4 * c + e;
-              float pv = __builtin_amdgcn_exp2f(s_acc[r] * p.scale_log2);
-              pv = (unsigned)(t0 - (8 * c + e)) <= span ? pv : 0.f;
+              const float pv = ds32[r];
               const float dsv = pv * dp_acc[r];
               // reduction slot of (c, e) in step c/2: the Q/dO rows the transposing reads give
               const int slot = 2 * (c & 1) + (e >> 1) + 4 * (e & 1);
@@ -446,12 +420,14 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
         // half hi takes rows 16t + 4hi + {0, 2, 8, 10} and then + 1.  Operand pairs are loaded
         // two products ahead; the dS exchange runs under the first products.
         bf16x8 bo[2], bq[2];
+        // per-lane bases; each read adds a constant, which becomes the instruction's offset
+        const uint16_t* obl = &ob[tq_row * kRowQ + tr_col];
+        const uint16_t* qbl = &qb[tq_row * kRowQ + tr_col];
         auto ldv = [&](int i) {
           const int t = i >> 2, n2 = i & 3;
-          const int r1 = 16 * t + tq_row;
-          const int col = 32 * n2 + tr_col;
-          bo[i & 1] = tr_read(&ob[r1 * kRowQ + col], &ob[(r1 + 1) * kRowQ + col]);
-          bq[i & 1] = tr_read(&qb[r1 * kRowQ + col], &qb[(r1 + 1) * kRowQ + col]);
+          const int off = 16 * t * kRowQ + 32 * n2;
+          bo[i & 1] = tr_read(obl + off, obl + off + kRowQ);
+          bq[i & 1] = tr_read(qbl + off, qbl + off + kRowQ);
         };
         ldv(0);
         ldv(1);
@@ -461,7 +437,7 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
           dk_acc[i & 3] = mfma(sa[i >> 2], bq[i & 1], dk_acc[i & 3]);
           __builtin_amdgcn_sched_barrier(0);
           if (i + 2 < 8) ldv(i + 2);
-          if (i == 0) write_ds_wide(ds_lds[buf], ds32, wave, lane);
+          if (i == 0) write_dst(ds_lds[buf], ds32, key_w, hi);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
