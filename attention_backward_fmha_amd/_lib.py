@@ -145,7 +145,7 @@ class PlanInfo(ctypes.Structure):
         ("dkv_acc_offset", ctypes.c_int64),
         ("dkv_acc_bytes", ctypes.c_int64),
         ("kernel", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("ordered_groups", ctypes.c_int32),
     ]
 
     def as_dict(self):

@@ -126,6 +126,8 @@ fmha::KParams make_params(const fmha_bwd_args* a, const fmha::Plan& p, void* ws)
     k.dbias_plane_bytes = p.dbias_plane_bytes;
     for (int i = 0; i < 3; ++i) k.dbias_s[i] = a->dbias_stride[i];
   }
+  k.order_n = p.order_n;
+  k.order = (ws != nullptr && p.order_n > 0) ? (int32_t*)((char*)ws + p.order_offset) : nullptr;
   return k;
 }
 
@@ -167,9 +169,10 @@ int fmha_bwd_prepare_workspace(const fmha_bwd_args* args, void* ws, size_t bytes
                   "prepare_workspace");
   if (st != FMHA_OK) return st;
   if (p.needs_zero) {
-    return hip_status(fmha::launch_zero((float*)((char*)ws + p.dq_acc_offset), p.dq_acc_bytes / 4,
-                                        (hipStream_t)stream),
-                      "prepare_workspace");
+    st = hip_status(fmha::launch_zero((float*)((char*)ws + p.dq_acc_offset), p.dq_acc_bytes / 4,
+                                      (hipStream_t)stream),
+                    "prepare_workspace");
+    if (st != FMHA_OK) return st;
   }
   return FMHA_OK;
 }
@@ -274,6 +277,7 @@ int fmha_bwd_plan_query(const fmha_bwd_args* args, fmha_bwd_plan_info* info) {
   info->flops = 2.0 * (3.0 * p.d_qk + 2.0 * p.d_v) * (double)info->pairs;
   info->reduce_read_bytes = fmha::reduce_read_bytes(args, p);
   info->kernel = p.kernel;
+  info->ordered_groups = p.order_n;
   return FMHA_OK;
 }
 

@@ -61,6 +61,8 @@ struct KParams {
   int drop_k;          // dropout: keep iff the element's random byte < drop_k (256 = off)
   float drop_scale;    // 256 / drop_k
   unsigned seed_lo, seed_hi, offset_lo;  // Philox key and the counter's offset word
+  int32_t* order;      // workspace: the wide kernel's work groups in cost order, or null
+  int order_n;
 };
 
 hipError_t launch_dot(const Plan& plan, const KParams& kp, hipStream_t stream);

@@ -33,12 +33,76 @@ namespace {
 // ------------------------------------------------------------------------------------------
 // Stage 1: D = rowsum(dO * O).  DV/8 lanes per row, 16 bytes per lane per tensor.
 // ------------------------------------------------------------------------------------------
+// Steps of work group w of the wide kernel (grid order; group mode, 32-row blocks, 256-key
+// tiles): the (query head, query block) pairs of its item's tiles, shared evenly by the
+// item's parts, plus a constant for the tile loads and the epilogue; 0 for a work group
+// whose segment has no such tile.  lens holds the segments' (lq, lk) pairs.
+__device__ int wide_steps(const KParams& p, const int* lens, int w) {
+  const int nbh = p.Hkv * p.B;
+  const int ip = w / nbh;
+  const int item = ip / p.kv_parts;
+  const int part = ip - item * p.kv_parts;
+  const int b = (w - ip * nbh) / p.Hkv;
+  const int lq = lens[2 * b], lk = lens[2 * b + 1];
+  const MaskGeom mg = mask_geom(p.mask_type, p.window_left, p.window_right, lq, lk);
+  int steps = 0;
+  for (int tsub = 0; tsub < p.tiles_per_item; ++tsub) {
+    const int j = item * p.tiles_per_item + tsub;
+    if (j * 256 >= lk) break;
+    int64_t lo, hi;
+    rows_for_keys(mg, lq, (int64_t)j * 256, min(j * 256 + 255, lk - 1), &lo, &hi);
+    if (hi >= lo) steps += ((int)hi / 32 - (int)lo / 32 + 1) * p.group_size;
+  }
+  if (steps == 0) return 0;
+  return steps * (part + 1) / p.kv_parts - steps * part / p.kv_parts + 6;
+}
+
+// The wide kernel's work groups (at most 2048, over at most 2048 segments) sorted by the key
+// (65535 - steps) * 2048 + w, i.e. most steps first and ties in grid order, with a bitonic
+// network in LDS; order[i] is the work group of rank i.  Run by the first work group of the D
+// stage, so it costs no launch of its own and overlaps that stage's memory traffic.
+__device__ void order_work_groups(const KParams& p, int* key, int* lens) {
+  const int n = p.order_n;
+  for (int b = threadIdx.x; b < p.B; b += blockDim.x) {
+    lens[2 * b] = p.seqstart_q[b + 1] - p.seqstart_q[b];
+    lens[2 * b + 1] = p.seqstart_k[b + 1] - p.seqstart_k[b];
+  }
+  __syncthreads();
+  int N = 2;
+  while (N < n) N <<= 1;
+  for (int w = threadIdx.x; w < N; w += blockDim.x)
+    key[w] = w < n ? ((65535 - min(wide_steps(p, lens, w), 65535)) << 11) | w : 0x7fffffff;
+  __syncthreads();
+  for (int k = 2; k <= N; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int t = threadIdx.x; t < N / 2; t += blockDim.x) {
+        const int i = 2 * t - (t & (j - 1));  // 2j * (t / j) + t % j, j a power of two
+        const int a = key[i], c = key[i + j];
+        if ((a > c) == ((i & k) == 0)) {
+          key[i] = c;
+          key[i + j] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int r = threadIdx.x; r < n; r += blockDim.x) p.order[r] = key[r] & 2047;
+}
+
 template <int DV>
 __global__ __launch_bounds__(256) void k_dot(const KParams p) {
+  // with a cost order, work group 0 builds it (dispatched first, it overlaps the others)
+  const int blk = (int)blockIdx.x - (p.order_n > 0 ? 1 : 0);
+  if (blk < 0) {
+    __shared__ int key[2048];
+    __shared__ int lens[2 * 2048];
+    order_work_groups(p, key, lens);
+    return;
+  }
   constexpr int LPR = DV / 8;
   constexpr int RPB = 256 / LPR;
   const int tid = threadIdx.x;
-  const int64_t r = (int64_t)blockIdx.x * RPB + tid / LPR;  // r = row*Hq + h
+  const int64_t r = (int64_t)blk * RPB + tid / LPR;  // r = row*Hq + h
   const int c8 = tid % LPR;
   const bool group = p.seqstart_q != nullptr;
   const bool valid = r < p.rows_q * p.Hq;
@@ -1370,7 +1434,9 @@ hipError_t launch_dot(const Plan& plan, const KParams& kp, hipStream_t stream) {
   const int64_t rows = plan.rows_q * plan.Hq;
   if (rows == 0) return hipSuccess;
   const int rpb = 256 / (plan.d_v / 8);
-  const int64_t blocks = (rows + rpb - 1) / rpb;
+  // one more work group ranks the wide kernel's work groups when the plan orders them
+  if (plan.order_n > 2048 || (plan.order_n > 0 && kp.order == nullptr)) return hipErrorInvalidValue;
+  const int64_t blocks = (rows + rpb - 1) / rpb + (plan.order_n > 0 ? 1 : 0);
   if (plan.d_v == 64) {
     hipLaunchKernelGGL(k_dot<64>, dim3((unsigned)blocks), dim3(256), 0, stream, kp);
   } else {

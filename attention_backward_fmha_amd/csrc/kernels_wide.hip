@@ -88,10 +88,13 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
   const int i16 = lane & 15;
 
   const int nbh = p.Hkv * p.B;
-  const int ip = blockIdx.x / nbh;
+  // the work group's work item: grid order, or the cost order prepare wrote
+  int wid = p.order != nullptr ? p.order[blockIdx.x] : (int)blockIdx.x;
+  if ((unsigned)wid >= gridDim.x) wid = (int)blockIdx.x;  // a list from another prepare: stay in range
+  const int ip = wid / nbh;
   const int item = ip / p.kv_parts;
   const int part = ip - item * p.kv_parts;
-  const int rem = blockIdx.x - ip * nbh;
+  const int rem = wid - ip * nbh;
   const int g = rem % p.Hkv;
   const int b = rem / p.Hkv;
   const bool group = p.seqstart_q != nullptr;
@@ -349,7 +352,7 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
       // the pending dQ of step n-1, by the half whose turn it is
       if (n > n0 && (wave >> 2) == ((n - 1 - n0) & 1)) dq_step(buf ^ 1, rdq, dc.r);
       const int q0 = cc.r;
-      // ---- S, dP, P, dS, dV, dK of step n (branch-free: masked pairs get P = 0) ----
+      // ---- S, dP, P, dS, dV, dK of step n ----
       {
         float ds32[16];
         const uint16_t* qb = qo_lds[buf][0];

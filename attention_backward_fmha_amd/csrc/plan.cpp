@@ -409,7 +409,20 @@ int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t el, bool forwar
   p->dkv_acc_offset = align_up(p->dbias_acc_offset + p->dbias_acc_bytes, 256);
   p->dkv_acc_bytes = p->kv_parts > 1 && !forward
                          ? (int64_t)p->kv_parts * p->Hkv * p->rows_k * (p->d_qk + p->d_v) * 4 : 0;
-  p->workspace_bytes = align_up(p->dkv_acc_offset + p->dkv_acc_bytes, 256);
+  // Ragged batches in the wide layout: the main kernel's work groups take their items longest
+  // first (a list one extra work group of the D stage builds), instead of in grid order, where the short
+  // segments' items and the empty ones of the grid's rectangle interleave with the long ones.
+  // A greedy longest-first list schedule of the 8192-token packings' work groups on 256 CUs
+  // ends about 12% earlier than the grid order.  Up to 2048 work groups (the list is ranked by
+  // one work group); larger grids fill the GPU in any order.
+  p->order_n = 0;
+  p->order_offset = align_up(p->dkv_acc_offset + p->dkv_acc_bytes, 256);
+  if (group && !forward && p->kernel == FMHA_KERNEL_WIDE) {
+    const int64_t wgs = (int64_t)((p->n_kv_tiles + p->tiles_per_item - 1) / p->tiles_per_item) *
+                        p->kv_parts * p->Hkv * p->B;
+    if (wgs > 1 && wgs <= 2048) p->order_n = (int)wgs;
+  }
+  p->workspace_bytes = align_up(p->order_offset + (int64_t)p->order_n * 4, 256);
   // what a run reads from the workspace depends on exactly these (and the segment offsets)
   Fnv f;
   for (int64_t x : {(int64_t)p->B, (int64_t)p->Hq, (int64_t)p->Hkv, (int64_t)p->Sq, (int64_t)p->Sk,
@@ -420,7 +433,7 @@ int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t el, bool forwar
                     p->dq_acc_bytes, p->dbias_acc_offset, p->dbias_acc_bytes, p->workspace_bytes,
                     (int64_t)p->kv_parts, p->dkv_acc_offset, p->dkv_acc_bytes,
                     (int64_t)a->mask_type, (int64_t)a->window_left, (int64_t)a->window_right,
-                    (int64_t)p->kernel})
+                    (int64_t)p->kernel, (int64_t)p->order_n, p->order_offset})
     f.v(x);
   if (group && a->B > 0) {
     f.add(a->seqstart_q_host, sizeof(int32_t) * (a->B + 1));

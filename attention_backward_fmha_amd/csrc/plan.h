@@ -49,6 +49,8 @@ struct Plan {
   int64_t dkv_acc_offset, dkv_acc_bytes;  // fp32 [kv_parts][Hkv][rows_k][d_qk + d_v]
   bool dbias_direct;     // full-shape (BHSS) dbias: the main kernel writes it directly
   uint32_t dbias_plane_bytes;
+  int order_n;           // > 0: main-kernel work groups in a cost order of this many entries
+  int64_t order_offset;  // int32 [order_n] written by the D stage's last work group
 };
 
 // Validates `a` and fills `p`.  Returns FMHA_OK or a negative status; on failure `err`

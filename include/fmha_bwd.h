@@ -293,7 +293,10 @@ typedef struct fmha_bwd_plan_info {
                                 [d_qk + d_v] (only when kv_parts > 1) */
   int64_t dkv_acc_bytes;
   int32_t kernel;            /* enum fmha_kernel: the main-kernel layout the run launches */
-  int32_t reserved;
+  int32_t ordered_groups;    /* > 0: the main kernel's work groups take their work items in
+                                descending order of their steps (a list of this many entries
+                                that the run's D stage writes at the end of the workspace);
+                                0: grid order */
 } fmha_bwd_plan_info;
 /* Accumulator layout.  Atomic mode: one split, rows_q rows, row-major ([row][d_qk]), row of
    a query = its D/LSE row.  Deterministic mode: split s holds the sum of the partials of key

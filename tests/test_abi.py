@@ -431,6 +431,26 @@ def test_wide_plan_splits_uneven_items():
     assert (_lib.plan_query(w).kv_parts, _lib.plan_query(w).tiles_per_item) == (1, 2)
 
 
+def test_ragged_wide_plans_order_their_work_groups():
+    """Ragged batches in the wide layout take a longest-first list of the main kernel's work
+    groups (written by prepare at the end of the workspace); batch mode, the four-wave layout
+    and grids of more than 2048 work groups keep the grid order."""
+    auto = _lib.KERNEL_AUTO
+    lens = [1673, 226, 413, 527, 417, 1652, 1788, 1496]
+    for det in (1, 0):
+        a = group_args(lens, lens, Hq=32, Hkv=8, mask=1, deterministic=det, kernel=auto)
+        info = _lib.plan_query(a)
+        wgs = -(-info.n_kv_tiles // info.tiles_per_item) * info.kv_parts * 8 * len(lens)
+        assert info.ordered_groups == wgs == 7 * 2 * 8 * 8
+        assert info.workspace_bytes >= info.dkv_acc_offset + info.dkv_acc_bytes + 4 * wgs
+        assert _lib.workspace_size(a) == info.workspace_bytes
+    assert _lib.plan_query(group_args(lens, lens, Hq=32, Hkv=8, mask=1)).ordered_groups == 0  # four-wave
+    assert _lib.plan_query(batch_args(B=2, Hq=32, Hkv=32, Sq=4096, Sk=4096, mask=1, kernel=auto)).ordered_groups == 0
+    many = group_args([2048] * 200, [2048] * 200, Hq=32, Hkv=8, mask=1, kernel=auto)
+    info = _lib.plan_query(many)  # 2 items of 4 tiles x 8 K/V heads x 200 segments > 2048
+    assert info.tiles_per_item == 4 and info.ordered_groups == 0
+
+
 def test_bf16_accumulator_tile_limit():
     """bf16 accumulation adds one rounded contribution per key tile; the plan refuses more than
     64 tiles per segment, where the error estimate u*sqrt(n/6) (u = 2^-8) leaves the cosine
