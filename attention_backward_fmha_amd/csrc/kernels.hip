@@ -36,14 +36,15 @@ namespace {
 // Steps of work group w of the wide kernel (grid order; group mode, 32-row blocks, 256-key
 // tiles): the (query head, query block) pairs of its item's tiles, shared evenly by the
 // item's parts, plus a constant for the tile loads and the epilogue; 0 for a work group
-// whose segment has no such tile.  lens holds the segments' (lq, lk) pairs.
-__device__ int wide_steps(const KParams& p, const int* lens, int w) {
+// whose segment has no such tile.
+__device__ int wide_steps(const KParams& p, int w) {
   const int nbh = p.Hkv * p.B;
   const int ip = w / nbh;
   const int item = ip / p.kv_parts;
   const int part = ip - item * p.kv_parts;
   const int b = (w - ip * nbh) / p.Hkv;
-  const int lq = lens[2 * b], lk = lens[2 * b + 1];
+  const int lq = p.seqstart_q[b + 1] - p.seqstart_q[b];
+  const int lk = p.seqstart_k[b + 1] - p.seqstart_k[b];
   const MaskGeom mg = mask_geom(p.mask_type, p.window_left, p.window_right, lq, lk);
   int steps = 0;
   for (int tsub = 0; tsub < p.tiles_per_item; ++tsub) {
@@ -57,21 +58,16 @@ __device__ int wide_steps(const KParams& p, const int* lens, int w) {
   return steps * (part + 1) / p.kv_parts - steps * part / p.kv_parts + 6;
 }
 
-// The wide kernel's work groups (at most 2048, over at most 2048 segments) sorted by the key
+// The wide kernel's work groups (at most 2048) sorted by the key
 // (65535 - steps) * 2048 + w, i.e. most steps first and ties in grid order, with a bitonic
 // network in LDS; order[i] is the work group of rank i.  Run by the first work group of the D
 // stage, so it costs no launch of its own and overlaps that stage's memory traffic.
-__device__ void order_work_groups(const KParams& p, int* key, int* lens) {
+__device__ void order_work_groups(const KParams& p, int* key) {
   const int n = p.order_n;
-  for (int b = threadIdx.x; b < p.B; b += blockDim.x) {
-    lens[2 * b] = p.seqstart_q[b + 1] - p.seqstart_q[b];
-    lens[2 * b + 1] = p.seqstart_k[b + 1] - p.seqstart_k[b];
-  }
-  __syncthreads();
   int N = 2;
   while (N < n) N <<= 1;
   for (int w = threadIdx.x; w < N; w += blockDim.x)
-    key[w] = w < n ? ((65535 - min(wide_steps(p, lens, w), 65535)) << 11) | w : 0x7fffffff;
+    key[w] = w < n ? ((65535 - min(wide_steps(p, w), 65535)) << 11) | w : 0x7fffffff;
   __syncthreads();
   for (int k = 2; k <= N; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
@@ -95,8 +91,7 @@ __global__ __launch_bounds__(256) void k_dot(const KParams p) {
   const int blk = (int)blockIdx.x - (p.order_n > 0 ? 1 : 0);
   if (blk < 0) {
     __shared__ int key[2048];
-    __shared__ int lens[2 * 2048];
-    order_work_groups(p, key, lens);
+    order_work_groups(p, key);
     return;
   }
   constexpr int LPR = DV / 8;
