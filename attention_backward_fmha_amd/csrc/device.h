@@ -75,6 +75,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// Cache-policy operand of the buffer loads and stores of the deterministic dQ partials: the
+// non-temporal bit, so that the partials (written once, read back once) stream through the
+// caches instead of displacing the Q, K, V and dO tiles that other work groups re-read.  The
+// dK/dV partials of split key tiles use the same policy through the non-temporal builtins.
+// Measured on one MI355X: the causal 2 x 32 x 4096 deterministic step 1.05 -> 0.99 ms, the
+// 8192-token ragged GQA one 0.556 -> 0.506 ms.
+constexpr int kPartialPolicy = 2;
+
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }

@@ -715,7 +715,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
         if (NT % 4 == 0 || ti < NT) {
 #pragma unroll
           for (int u = 0; u < 4; ++u)
-            prev[tt][u] = __builtin_amdgcn_raw_buffer_load_b128(rprev, (ti * 1024 + u * 256 + lane * 4) * 4, 0, 0);
+            prev[tt][u] = __builtin_amdgcn_raw_buffer_load_b128(rprev, (ti * 1024 + u * 256 + lane * 4) * 4, 0, kPartialPolicy);
         }
       }
     }
@@ -761,7 +761,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
                       __float_as_uint(__uint_as_float(prev[tt][u][1]) + acc[4 * u + 1]),
                       __float_as_uint(__uint_as_float(prev[tt][u][2]) + acc[4 * u + 2]),
                       __float_as_uint(__uint_as_float(prev[tt][u][3]) + acc[4 * u + 3])},
-                rdq, voff + 1024 * u, 0, 0);
+                rdq, voff + 1024 * u, 0, kPartialPolicy);
         } else if (DQM == 2) {
           // packed bf16 adds.  Each lane packs rows (k, 8+k) of its column; lanes 2c and 2c+1
           // swap the packed words, and the even lane keeps row k of columns 2c, 2c+1, the odd
@@ -815,9 +815,9 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
         const int64_t prow = sg.kws_row0 + key0 + kl;
         float* pp = p.dkv_acc + (((int64_t)part * p.Hkv + g) * p.rows_k + prow) * (DQK + DV) + l32;
 #pragma unroll
-        for (int n = 0; n < DQK / 32; ++n) pp[32 * n] = dk_acc[n][r];
+        for (int n = 0; n < DQK / 32; ++n) __builtin_nontemporal_store(dk_acc[n][r], &pp[32 * n]);
 #pragma unroll
-        for (int n = 0; n < DV / 32; ++n) pp[DQK + 32 * n] = dv_acc[n][r];
+        for (int n = 0; n < DV / 32; ++n) __builtin_nontemporal_store(dv_acc[n][r], &pp[DQK + 32 * n]);
       }
     }
   }
@@ -884,7 +884,7 @@ __device__ __forceinline__ void reduce_tiles(const KParams& p, const Seg& sg, bo
         if ((NT * 64) % 256 == 0 || pair < NT * 64) {
 #pragma unroll
           for (int u = 0; u < 4; ++u)
-            x[t][pr][u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, ((pair >> 6) * 1024 + u * 256 + (pair & 63) * 4) * 4, 0, 0));
+            x[t][pr][u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, ((pair >> 6) * 1024 + u * 256 + (pair & 63) * 4) * 4, 0, kPartialPolicy));
         }
       }
     }
@@ -1054,7 +1054,7 @@ __global__ __launch_bounds__(256) void k_dkv_reduce(const KParams p) {
       f32x4 part[8];
 #pragma unroll
       for (int q = 0; q < 8; ++q)
-        part[q] = q < p.kv_parts ? *(const f32x4*)(src + q * part_stride) : f32x4{};
+        part[q] = q < p.kv_parts ? __builtin_nontemporal_load((const f32x4*)(src + q * part_stride)) : f32x4{};
       f32x4 acc = part[0];
 #pragma unroll
       for (int q = 1; q < 8; ++q)

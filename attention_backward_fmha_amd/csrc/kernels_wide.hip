@@ -279,7 +279,7 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
         const __amdgpu_buffer_rsrc_t rprev = qbn >= w_lo && qbn <= w_hi ? rdq : buffer_rsrc(p.dq_acc, 0u);
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-          prev[u] = __builtin_amdgcn_raw_buffer_load_b128(rprev, (r * D + nd * 1024 + u * 256 + lane * 4) * 4, 0, 0);
+          prev[u] = __builtin_amdgcn_raw_buffer_load_b128(rprev, (r * D + nd * 1024 + u * 256 + lane * 4) * 4, 0, kPartialPolicy);
       }
       f32x16 acc = f32x16{};
       // A operand: keys 16kk + 8hi .. +7 of query l32, two transposing reads of the key-major dS
@@ -312,7 +312,7 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
                     __float_as_uint(__uint_as_float(prev[u][1]) + acc[4 * u + 1]),
                     __float_as_uint(__uint_as_float(prev[u][2]) + acc[4 * u + 2]),
                     __float_as_uint(__uint_as_float(prev[u][3]) + acc[4 * u + 3])},
-              rdq, voff + 1024 * u, 0, 0);
+              rdq, voff + 1024 * u, 0, kPartialPolicy);
       } else if (DQM == 2) {
         // packed bf16 adds: lanes 2c and 2c+1 trade their (row k, row 8+k) words so that each
         // holds one row of columns 2c, 2c+1; the block is stored tile by tile (tile nd at
@@ -472,9 +472,9 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
           const int64_t prow = sg.kws_row0 + key0 + kl;
           float* pp = p.dkv_acc + (((int64_t)part * p.Hkv + g) * p.rows_k + prow) * (2 * D) + l32;
 #pragma unroll
-          for (int n = 0; n < D / 32; ++n) pp[32 * n] = dk_acc[n][r];
+          for (int n = 0; n < D / 32; ++n) __builtin_nontemporal_store(dk_acc[n][r], &pp[32 * n]);
 #pragma unroll
-          for (int n = 0; n < D / 32; ++n) pp[D + 32 * n] = dv_acc[n][r];
+          for (int n = 0; n < D / 32; ++n) __builtin_nontemporal_store(dv_acc[n][r], &pp[D + 32 * n]);
         }
       }
     }
