@@ -50,7 +50,7 @@ struct Plan {
   bool dbias_direct;     // full-shape (BHSS) dbias: the main kernel writes it directly
   uint32_t dbias_plane_bytes;
   int order_n;           // > 0: main-kernel work groups in a cost order of this many entries
-  int64_t order_offset;  // int32 [order_n] written by the D stage's last work group
+  int64_t order_offset;  // int32 [order_n] written by the D stage's first work group
 };
 
 // Validates `a` and fills `p`.  Returns FMHA_OK or a negative status; on failure `err`
