@@ -1075,49 +1075,86 @@ __global__ __launch_bounds__(256) void k_dkv_reduce(const KParams p) {
 
 // ------------------------------------------------------------------------------------------
 // dbias = the full-shape dS summed over the bias's broadcast dimensions (ascending batch, then
-// head, fp32), rounded to bf16.  One work group per (query row, output plane, 1024 columns),
-// four columns per thread.  A (row, key) pair lies in a (query block, key tile) pair the main
-// kernel skipped (no allowed pair there) exactly when qblocks_for_tile excludes the row's
-// block; such entries were never written and count as 0, so the scratch needs no zeroing.
+// head, fp32), rounded to bf16.  One work group per (kDbiasRows query rows, output plane, 1024
+// columns), four consecutive columns per thread (one 16-byte load per plane and row, one
+// 8-byte store per row where dbias is aligned for it).  A (row, key) pair lies in a (query
+// block, key tile) pair the main kernel skipped (no allowed pair there) exactly when
+// qblocks_for_tile excludes the row's block; such entries were never written and count as 0,
+// so the scratch needs no zeroing.
 // ------------------------------------------------------------------------------------------
+constexpr int kDbiasRows = 32;
+
+__device__ __forceinline__ void store_bf16x4(uint16_t* dst, const float (&v)[4], int n, bool vec) {
+  if (vec && n == 4) {
+    *(u32x2*)dst = u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+  } else {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (u < n) dst[u] = to_bf16_bits(v[u]);
+  }
+}
+
 __global__ __launch_bounds__(256) void k_dbias_reduce(const KParams p) {
   const int nchunk = (p.Sk + 1023) / 1024;
-  const int i = (int)blockIdx.x / nchunk;     // query row
-  const int chunk = (int)blockIdx.x - i * nchunk;
+  const int i0 = ((int)blockIdx.x / nchunk) * kDbiasRows;  // first query row
+  const int chunk = (int)blockIdx.x % nchunk;
   const int oh = blockIdx.y;                  // output head index (0 when broadcast)
   const int ob = blockIdx.z;                  // output batch index
   const int j0 = (chunk * 256 + (int)threadIdx.x) * 4;
   if (j0 >= p.Sk) return;
+  const int n = min(4, p.Sk - j0);
+  const int i1 = min(i0 + kDbiasRows, p.Sq);
   const MaskGeom mg = mask_geom(p.mask_type, p.window_left, p.window_right, p.Sq, p.Sk);
   int64_t lo, hi;
   qblocks_for_tile(mg, p.Sq, p.Sk, j0 / 128, p.tile_m, 128, &lo, &hi);  // j0..j0+3: one tile
-  const int qb = i / p.tile_m;
-  const bool seen = qb >= lo && qb <= hi;
+  uint16_t* dst0 = p.dbias + (int64_t)ob * p.dbias_s[0] + (int64_t)oh * p.dbias_s[1] + j0;
+  const int64_t ds2 = p.dbias_s[2];
+  const bool vec = (((uintptr_t)dst0 | (uintptr_t)(ds2 * 2)) & 7u) == 0;
+  const float zero[4] = {0.f, 0.f, 0.f, 0.f};
   if (p.dbias_direct) {  // written by the main kernel where seen; zeros elsewhere
-    if (!seen) {
-      uint16_t* dst = p.dbias + (int64_t)ob * p.dbias_s[0] + (int64_t)oh * p.dbias_s[1] + (int64_t)i * p.dbias_s[2] + j0;
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (j0 + u < p.Sk) dst[u] = 0;
+    for (int i = i0; i < i1; ++i) {
+      const int64_t qb = i / p.tile_m;
+      if (qb < lo || qb > hi) store_bf16x4(dst0 + (int64_t)i * ds2, zero, n, vec);
     }
     return;
   }
   const int b0 = p.bias_b == 1 ? 0 : ob, b1 = p.bias_b == 1 ? p.B : ob + 1;
   const int h0 = p.bias_h == 1 ? 0 : oh, h1 = p.bias_h == 1 ? p.Hq : oh + 1;
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  if (seen) {
-    for (int bb = b0; bb < b1; ++bb)
-      for (int hh = h0; hh < h1; ++hh) {
-        const float* src = p.dbias_acc + (((int64_t)bb * p.Hq + hh) * p.Sq + i) * p.Sk + j0;
+  const int nh = h1 - h0, planes = (b1 - b0) * nh;
+  const int64_t plane = (int64_t)p.Sq * p.Sk;
+  const bool vload = (p.Sk & 3) == 0;  // rows of the fp32 scratch start 16-byte aligned
+  for (int i = i0; i < i1; ++i) {
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    const int64_t qb = i / p.tile_m;
+    if (qb >= lo && qb <= hi) {
+      const float* src0 = p.dbias_acc + (int64_t)i * p.Sk + j0;
+      // the planes in ascending (batch, head) order; eight loads in flight
+      for (int q = 0; q < planes; q += 8) {
+        f32x4 x[8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (j0 + u < p.Sk) acc[u] += src[u];
+        for (int t = 0; t < 8; ++t) {
+          x[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (q + t < planes) {
+            const int bb = b0 + (q + t) / nh, hh = h0 + (q + t) % nh;
+            const float* src = src0 + ((int64_t)bb * p.Hq + hh) * plane;
+            if (vload && n == 4) {
+              x[t] = *(const f32x4*)src;
+            } else {
+#pragma unroll
+              for (int u = 0; u < 4; ++u)
+                if (u < n) x[t][u] = src[u];
+            }
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          if (q + t < planes)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) acc[u] += x[t][u];
       }
+    }
+    store_bf16x4(dst0 + (int64_t)i * ds2, acc, n, vec);
   }
-  uint16_t* dst = p.dbias + (int64_t)ob * p.dbias_s[0] + (int64_t)oh * p.dbias_s[1] + (int64_t)i * p.dbias_s[2] + j0;
-#pragma unroll
-  for (int u = 0; u < 4; ++u)
-    if (j0 + u < p.Sk) dst[u] = to_bf16_bits(acc[u]);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1553,8 +1590,8 @@ hipError_t launch_dkv_reduce(const Plan& plan, const KParams& kp, hipStream_t st
 
 hipError_t launch_dbias(const Plan& plan, const KParams& kp, hipStream_t stream) {
   if (!plan.has_dbias || plan.B == 0 || plan.Sq == 0 || plan.Sk == 0) return hipSuccess;
-  const dim3 grid((unsigned)(((plan.Sk + 1023) / 1024) * (int64_t)plan.Sq), (unsigned)plan.bias_h,
-                  (unsigned)plan.bias_b);
+  const dim3 grid((unsigned)(((plan.Sk + 1023) / 1024) * (((int64_t)plan.Sq + kDbiasRows - 1) / kDbiasRows)),
+                  (unsigned)plan.bias_h, (unsigned)plan.bias_b);
   hipLaunchKernelGGL(k_dbias_reduce, grid, dim3(256), 0, stream, kp);
   return hipGetLastError();
 }
