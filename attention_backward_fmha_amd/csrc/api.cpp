@@ -120,7 +120,9 @@ fmha::KParams make_params(const fmha_bwd_args* a, const fmha::Plan& p, void* ws)
   k.seed_hi = (unsigned)(a->philox_seed >> 32);
   k.offset_lo = (unsigned)(a->philox_offset & 0xFFFFFFFFu);
   if (p.has_dbias) {
-    if (ws != nullptr) k.dbias_acc = (float*)((char*)ws + p.dbias_acc_offset);
+    // the fp32 full-shape dS region exists only for a broadcast dbias; with a direct (BHSS)
+    // dbias the pointer stays null, so nothing can address a region the workspace lacks
+    if (ws != nullptr && p.dbias_acc_bytes > 0) k.dbias_acc = (float*)((char*)ws + p.dbias_acc_offset);
     k.dbias = (uint16_t*)a->dbias;
     k.dbias_direct = p.dbias_direct ? 1 : 0;
     k.dbias_plane_bytes = p.dbias_plane_bytes;
