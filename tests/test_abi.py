@@ -387,6 +387,14 @@ def test_wide_kernel_plan():
     drop.p_drop = 0.1
     assert _lib.plan_query(drop).kernel == _lib.KERNEL_FOUR_WAVE
     assert _lib.plan_query(batch_args()).kernel == _lib.KERNEL_FOUR_WAVE
+    # a query head's rows of a whole segment must stay inside 32-bit offsets for the wide
+    # kernel: (Sq + 32) * 4096 elements of sequence stride reaches 2^30 at Sq = 262112
+    ok = batch_args(B=1, Hq=32, Hkv=8, Sq=262112 - 1, Sk=256, kernel=_lib.KERNEL_AUTO)
+    assert _lib.plan_query(ok).kernel == _lib.KERNEL_WIDE
+    long_q = batch_args(B=1, Hq=32, Hkv=8, Sq=262112, Sk=256, kernel=_lib.KERNEL_AUTO)
+    assert _lib.plan_query(long_q).kernel == _lib.KERNEL_FOUR_WAVE
+    long_q.tune_kernel = _lib.KERNEL_WIDE
+    assert status_of(long_q) == _lib.ERR_INVALID_ARG
     # the wide kernel cannot be forced where it does not apply; its block height is fixed
     bad = batch_args(d_qk=64, d_v=64, kernel=_lib.KERNEL_WIDE)
     assert status_of(bad) == _lib.ERR_INVALID_ARG
