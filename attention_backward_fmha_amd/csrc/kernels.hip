@@ -538,9 +538,6 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
     const __amdgpu_buffer_rsrc_t rdb = buffer_rsrc(
         XB && p.dbias_acc != nullptr ? p.dbias_acc + ((int64_t)b * p.Hq + hq) * p.Sq * p.Sk : nullptr,
         XB && p.dbias_acc != nullptr ? (uint32_t)p.Sq * (uint32_t)p.Sk * 4u : 0u);
-    const __amdgpu_buffer_rsrc_t rdbb = buffer_rsrc(
-        XB && p.dbias_direct ? p.dbias + (int64_t)b * p.dbias_s[0] + (int64_t)hq * p.dbias_s[1] : nullptr,
-        XB && p.dbias_direct ? p.dbias_plane_bytes : 0u);
     f32x16 s_acc[MT];
     f32x16 dp_acc[MT];
 #pragma unroll
@@ -632,13 +629,11 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
           sa[c >> 1][(c & 1) * 4 + e] = (__bf16)dsv;
           ds32[r] = dsv;
           if constexpr (XB) {
-            // full-shape dS for dbias: every (row, key) of the block, masked pairs as 0; rows
-            // past the plane are dropped by the range check, keys past the tile end skipped
+            // broadcast dbias: the full-shape fp32 dS, every (row, key) of the block, masked
+            // pairs as 0; rows past the plane are dropped by the range check, keys past the
+            // tile end skipped (a full-shape dbias is copied from the dS tile below)
             const unsigned drow = (unsigned)(q0 + 32 * m + 8 * c + 4 * hi + e);
-            if (p.dbias_direct && key_ok)
-              __builtin_amdgcn_raw_buffer_store_b16(
-                  to_bf16_bits(dsv), rdbb, (int)((drow * (unsigned)p.dbias_s[2] + (unsigned)(key0 + key_l)) * 2u), 0, 0);
-            else if (p.dbias_acc != nullptr && key_ok)
+            if (p.dbias_acc != nullptr && key_ok)
               __builtin_amdgcn_raw_buffer_store_b32(
                   __float_as_uint(dsv), rdb, (drow * (unsigned)p.Sk + (unsigned)(key0 + key_l)) * 4u, 0, 0);
           }
@@ -721,6 +716,30 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
     }
 
     __syncthreads();  // dS complete; every wave is done reading this step's Q, dO tiles
+
+    // full-shape dbias: the step's dS tile in LDS (bf16, masked pairs 0) is dbias for its
+    // (row, key) pairs; 16-byte copies of 8 keys where dbias is aligned for them
+    if constexpr (XB) {
+      if (p.dbias_direct) {
+        uint16_t* dplane = p.dbias + (int64_t)b * p.dbias_s[0] + (int64_t)h * p.dbias_s[1];
+        const int64_t ds2 = p.dbias_s[2];
+        const bool vec = (((uintptr_t)dplane | (uintptr_t)(ds2 * 2)) & 15u) == 0;
+#pragma unroll
+        for (int c = tid; c < TM * (TN / 8); c += 256) {
+          const int row = c / (TN / 8), j = (int)key0 + 8 * (c % (TN / 8));
+          const int64_t i = q0 + row;
+          if (i < p.Sq && j < p.Sk) {
+            const uint16_t* src = &ds_lds[dsrow(row) * SR + (j - (int)key0)];
+            uint16_t* dst = dplane + i * ds2 + j;
+            if (vec && j + 8 <= p.Sk) {
+              *(u32x4*)dst = *(const u32x4*)src;
+            } else {
+              for (int e = 0; e < 8 && j + e < p.Sk; ++e) dst[e] = src[e];
+            }
+          }
+        }
+      }
+    }
 
     // ---- dQ_i partial = dS K_j  (reduction over the tile's 128 keys) ----
     // Deterministic: the item's split block of this step (its own rows, padding included),
