@@ -326,6 +326,8 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t ds_lds[TM * SR];   // dS (query-major)
   __shared__ __attribute__((aligned(16))) float lse_lds[256];        // LSE_i * log2(e)
   __shared__ __attribute__((aligned(16))) float dd_lds[256];         // D_i
+  // bias instances: each wave's 32 keys of the step's bias rows, keys in lane order
+  __shared__ __attribute__((aligned(16))) uint16_t bias_lds[XB && DQK <= 128 ? 4 * TM * 32 : 8];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -399,6 +401,9 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
   // K tile -> LDS (row-major); the wave's V rows -> registers (B operand of dP).
   const int key_l = wave * 32 + kmap(l32);
   const bool key_ok = key_l < nk;
+  // bias rows start 16-byte aligned and no 8-key chunk straddles Sk (the bias staging below)
+  const bool bias_rows16 = XB && ((uintptr_t)p.bias & 15u) == 0 &&
+                           ((p.bias_s[0] | p.bias_s[1] | p.bias_s[2]) & 7) == 0 && (p.Sk & 7) == 0;
   bf16x8 vw[DV / 16];
   {
     const int64_t krow = sg.k_row0 + key0 + (key_ok ? key_l : 0);
@@ -520,20 +525,37 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
     // bias of the lane's (query, key) pairs, issued before the products that hide its latency;
     // register 16m + r pairs with the S/dP result register r of row tile m.  Rows past the
     // plane are outside the resource (zeros); keys past the tile end are masked below.
+    // With 16-byte aligned bias rows and Sk a multiple of 8 the wave loads its 32 keys of
+    // the step's rows as 16-byte chunks (no chunk straddles Sk or the plane end), stages
+    // them in its own LDS region with the keys in lane order, and reads them back with
+    // transposing reads that give each lane its key for 4 rows at once; otherwise (and at
+    // d_qk = 192, whose registers have no room for the chunks) one 2-byte load per value.
+    constexpr bool kStage = XB && DQK <= 128;
     float bv[XB ? MT * 16 : 1];
+    u32x4 braw[kStage ? TM / 16 : 1];
+    const bool bias_vec = kStage && bias_rows16;
     if constexpr (XB) {
       const __amdgpu_buffer_rsrc_t rb =
           buffer_rsrc(p.bias + (int64_t)b * p.bias_s[0] + (int64_t)hq * p.bias_s[1], p.bias_plane_bytes);
       const int bs2 = (int)p.bias_s[2];
-      const int col = (int)key0 + key_l;
+      if (kStage && bias_vec) {
 #pragma unroll
-      for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = q0 + 32 * m + 8 * (r >> 2) + 4 * hi + (r & 3);
-          const unsigned short x = __builtin_amdgcn_raw_buffer_load_b16(rb, (row * bs2 + col) * 2, 0, 0);
-          bv[16 * m + r] = __uint_as_float((unsigned)x << 16);
+        for (int c = 0; c < TM / 16; ++c) {
+          const int qc = lane + 64 * c;  // chunk qc: row qc / 4, keys 8 * (qc % 4) .. + 7
+          braw[c] = __builtin_amdgcn_raw_buffer_load_b128(
+              rb, ((q0 + (qc >> 2)) * bs2 + (int)key0 + 32 * wave + 8 * (qc & 3)) * 2, 0, 0);
         }
+      } else {
+        const int col = (int)key0 + key_l;
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = q0 + 32 * m + 8 * (r >> 2) + 4 * hi + (r & 3);
+            const unsigned short x = __builtin_amdgcn_raw_buffer_load_b16(rb, (row * bs2 + col) * 2, 0, 0);
+            bv[16 * m + r] = __uint_as_float((unsigned)x << 16);
+          }
+      }
     }
     const __amdgpu_buffer_rsrc_t rdb = buffer_rsrc(
         XB && p.dbias_acc != nullptr ? p.dbias_acc + ((int64_t)b * p.Hq + hq) * p.Sq * p.Sk : nullptr,
@@ -560,6 +582,34 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
       for (int kk = 0; kk < DQK / 16; ++kk) s_acc[m] = mfma(qa[kk], kf[kk], s_acc[m]);
 #pragma unroll
       for (int kk = 0; kk < DV / 16; ++kk) dp_acc[m] = mfma(oa[kk], vw[kk], dp_acc[m]);
+    }
+    if constexpr (kStage) {
+      if (bias_vec) {
+        // key k of the wave's 32 goes to position 16 * (k % 2) + k / 2 of its row, the inverse
+        // of kmap, so lane l finds its key at position l % 32
+        uint16_t* bw = &bias_lds[wave * TM * 32];
+#pragma unroll
+        for (int c = 0; c < TM / 16; ++c) {
+          const int qc = lane + 64 * c, row = qc >> 2, j = qc & 3;
+          const u32x4 x = braw[c];
+          *(u32x2*)&bw[row * 32 + 4 * j] =
+              u32x2{(x[0] & 0xFFFFu) | (x[1] << 16), (x[2] & 0xFFFFu) | (x[3] << 16)};
+          *(u32x2*)&bw[row * 32 + 16 + 4 * j] =
+              u32x2{(x[0] >> 16) | (x[1] & 0xFFFF0000u), (x[2] >> 16) | (x[3] & 0xFFFF0000u)};
+        }
+        // rows 32m + 8u + 4hi + e of the lane's key: lane s of a 16-lane group points at row
+        // s / 4 of the 4-row block and its positions 4 (s % 4) .. + 3 of the group's 16
+        const int i16 = lane & 15;
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const s16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)&bw[
+                (32 * m + 8 * u + 4 * hi + (i16 >> 2)) * 32 + 16 * (g16 & 1) + 4 * (i16 & 3)]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) bv[16 * m + 4 * u + e] = __uint_as_float((unsigned)(unsigned short)t[e] << 16);
+          }
+      }
     }
     // mask: pair (row, key) allowed iff (unsigned)(key - row - lo_d) <= span; keys past the
     // tile end get an offset that fails for every row of the block

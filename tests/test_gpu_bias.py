@@ -45,6 +45,11 @@ CASES = [
     ("1hss_none_cross_d64", (2, 130, 333), (4, 2), (64, 64), (1, 4), NONE, (-1, -1)),
     ("b1ss_window_d192", (3, 200, 200), (2, 1), (192, 128), (3, 1), WIN, (40, 3)),
     ("bhss_br_lq_gt_lk", (1, 150, 70), (2, 2), (128, 128), (1, 2), BR, (-1, -1)),
+    # Sk a multiple of 8 with aligned rows: the main kernel stages the bias in 16-byte chunks
+    ("bhss_causal_d128_sk8", (2, 200, 264), (4, 4), (128, 128), (2, 4), TL, (-1, -1)),
+    ("11ss_br_gqa_sk8", (2, 256, 256), (8, 2), (128, 128), (1, 1), BR, (-1, -1)),
+    ("1hss_none_d64_sk8", (2, 130, 320), (4, 2), (64, 64), (1, 4), NONE, (-1, -1)),
+    ("b1ss_window_d128_sk8", (3, 150, 200), (2, 1), (128, 128), (3, 1), WIN, (40, 3)),
 ]
 
 
