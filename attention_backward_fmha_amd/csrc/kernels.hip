@@ -531,9 +531,10 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
     // transposing reads that give each lane its key for 4 rows at once; otherwise (and at
     // d_qk = 192, whose registers have no room for the chunks) one 2-byte load per value.
     constexpr bool kStage = XB && DQK <= 128;
-    float bv[XB ? MT * 16 : 1];
+    constexpr bool kVecOnly = XB && DQK == 128 && TM == 64;  // the plan takes it only when aligned
+    float bv[XB && !kVecOnly ? MT * 16 : 1];
     u32x4 braw[kStage ? TM / 16 : 1];
-    const bool bias_vec = kStage && bias_rows16;
+    const bool bias_vec = kStage && (kVecOnly || bias_rows16);
     if constexpr (XB) {
       const __amdgpu_buffer_rsrc_t rb =
           buffer_rsrc(p.bias + (int64_t)b * p.bias_s[0] + (int64_t)hq * p.bias_s[1], p.bias_plane_bytes);
@@ -545,7 +546,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
           braw[c] = __builtin_amdgcn_raw_buffer_load_b128(
               rb, ((q0 + (qc >> 2)) * bs2 + (int)key0 + 32 * wave + 8 * (qc & 3)) * 2, 0, 0);
         }
-      } else {
+      } else if constexpr (!kVecOnly) {
         const int col = (int)key0 + key_l;
 #pragma unroll
         for (int m = 0; m < MT; ++m)
@@ -597,18 +598,6 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
           *(u32x2*)&bw[row * 32 + 16 + 4 * j] =
               u32x2{(x[0] >> 16) | (x[1] & 0xFFFF0000u), (x[2] >> 16) | (x[3] & 0xFFFF0000u)};
         }
-        // rows 32m + 8u + 4hi + e of the lane's key: lane s of a 16-lane group points at row
-        // s / 4 of the 4-row block and its positions 4 (s % 4) .. + 3 of the group's 16
-        const int i16 = lane & 15;
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const s16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)&bw[
-                (32 * m + 8 * u + 4 * hi + (i16 >> 2)) * 32 + 16 * (g16 & 1) + 4 * (i16 & 3)]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) bv[16 * m + 4 * u + e] = __uint_as_float((unsigned)(unsigned short)t[e] << 16);
-          }
       }
     }
     // mask: pair (row, key) allowed iff (unsigned)(key - row - lo_d) <= span; keys past the
@@ -619,6 +608,26 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
       // ---- P, dS of tile m: register r holds query 32m + 8(r/4) + 4*hi + r%4 ----
       bf16x8 pa[2], sa[2];
       float ds32[16];
+      // the bias of tile m: rows 32m + 8u + 4hi + e of the lane's key (staged: lane s of a
+      // 16-lane group points at row s / 4 of the 4-row block and its positions 4 (s % 4) .. + 3
+      // of the group's 16)
+      float bm[XB ? 16 : 1];
+      if constexpr (XB) {
+        if (kStage && bias_vec) {
+          const uint16_t* bw = &bias_lds[wave * TM * 32];
+          const int i16 = lane & 15;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const s16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)&bw[
+                (32 * m + 8 * u + 4 * hi + (i16 >> 2)) * 32 + 16 * (g16 & 1) + 4 * (i16 & 3)]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) bm[4 * u + e] = __uint_as_float((unsigned)(unsigned short)t[e] << 16);
+          }
+        } else if constexpr (!kVecOnly) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) bm[r] = bv[16 * m + r];
+        }
+      }
       // dropout: the tile's rows 32m + 8c + 4hi + (0..3) of this lane's key take bytes
       // (key % 4) of the Philox output for (key / 4, row / 4).  The four lanes of one key
       // quad (l, l^1, l^16, l^17: key bits 0-1 are lane bits 4 and 0) need the same four
@@ -671,7 +680,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * c + e;
           float xl = s_acc[m][r] * p.scale_log2 - l4[e];
-          if constexpr (XB) xl = __builtin_fmaf(bv[16 * m + r], kLog2e, xl);
+          if constexpr (XB) xl = __builtin_fmaf(bm[r], kLog2e, xl);
           float pv = __builtin_amdgcn_exp2f(xl);
           pv = (unsigned)(t0 - (32 * m + 8 * c + e)) <= span ? pv : 0.f;
           const float dsv = pv * (dp_acc[m][r] * zf[e] - d4[e]);
@@ -1608,7 +1617,7 @@ hipError_t launch_main(const Plan& plan, const KParams& kp, hipStream_t stream) 
     if (plan.tile_m == 32) {
       launch_main_t<128, 128, 32>(plan, kp, grid, stream);
     } else {
-      launch_main_t<128, 128, 64, false>(plan, kp, grid, stream);  // bias: tile_m is 32
+      launch_main_t<128, 128, 64>(plan, kp, grid, stream);
     }
   } else {
     launch_main_t<192, 128, 32>(plan, kp, grid, stream);

@@ -164,12 +164,17 @@ int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t el, bool forwar
     p->tile_m = a->d_qk == 192 ? 32 : (a->d_qk == 64 && !fp32_atomics ? 128 : 64);
     // with a bias, blocks are half as tall (32 rows at d_qk = 128, 64 at d_qk = 64): the bias
     // registers of the taller blocks do not fit beside the rest of the main kernel's
-    // registers (dropout alone does fit)
-    if (with_bias && a->d_qk == 128) p->tile_m = 32;
+    // registers (dropout alone does fit).  At d_qk = 128, 64-row blocks stay when the kernel
+    // can stage the bias in 16-byte chunks (rows 16-byte aligned, Sk a multiple of 8; the
+    // same test as the kernel's), which needs no bias registers across the step.
+    const int64_t bstr = (a->bias_b == 1 ? 0 : a->bias_stride[0]) | (a->bias_h == 1 ? 0 : a->bias_stride[1]) |
+                         a->bias_stride[2];
+    const bool staged = ((uintptr_t)a->bias & 15u) == 0 && (bstr & 7) == 0 && (a->Sk & 7) == 0;
+    if (with_bias && a->d_qk == 128) p->tile_m = staged ? 64 : 32;
     if (with_bias && a->d_qk == 64) p->tile_m = 64;
     if (a->tune_tile_m != 0) {
       const int v = a->tune_tile_m;
-      const bool ok = (a->d_qk == 128 && (v == 32 || (v == 64 && !with_bias))) ||
+      const bool ok = (a->d_qk == 128 && (v == 32 || (v == 64 && (!with_bias || staged)))) ||
                       (a->d_qk == 64 && ((v == 64) || (v == 128 && !with_bias))) ||
                       (a->d_qk == 192 && v == 32);
       if (!ok) return fail(FMHA_ERR_INVALID_ARG, err, el, "tune_tile_m is not a block height of this kernel");

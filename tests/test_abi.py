@@ -277,13 +277,32 @@ def test_dropout_probability_range(p, expected):
 
 
 def test_block_rows_with_bias_and_dropout_at_d128():
-    """A bias at d_qk = 128 takes 32-row query blocks; dropout alone keeps 64."""
+    """A bias at d_qk = 128 takes 32-row query blocks unless the main kernel can stage it in
+    16-byte chunks; dropout alone keeps 64."""
     a = batch_args()
     a.p_drop = 0.1
     assert _lib.plan_query(a).tile_m == 64
     a = _with_bias(batch_args(), 1, 1, dbias=False)
     a.p_drop = 0.1
     assert _lib.plan_query(a).tile_m == 32
+    # 64-row blocks where the kernel stages the bias in 16-byte chunks: rows 16-byte aligned
+    # (pointer and every stride of a non-broadcast dimension a multiple of 8) and Sk % 8 == 0
+    for bb, bh in ((1, 1), (2, 4)):
+        st = _with_bias(batch_args(Sk=336), bb, bh, dbias=False)
+        assert _lib.plan_query(st).tile_m == 64
+        st.tune_tile_m = 32
+        assert _lib.plan_query(st).tile_m == 32
+    odd = _with_bias(batch_args(Sk=336), 2, 4, dbias=False)
+    odd.bias_stride[0] += 4  # a batch stride that breaks 16-byte rows
+    assert _lib.plan_query(odd).tile_m == 32
+    odd.tune_tile_m = 64
+    assert status_of(odd) == _lib.ERR_INVALID_ARG
+    bcast = _with_bias(batch_args(Sk=336), 1, 1, dbias=False)
+    bcast.bias_stride[0] += 4  # broadcast dimensions' strides do not matter
+    assert _lib.plan_query(bcast).tile_m == 64
+    moved = _with_bias(batch_args(Sk=336), 1, 1, dbias=False)
+    moved.bias = FAKE + 8
+    assert _lib.plan_query(moved).tile_m == 32
 
 
 def test_block_rows_by_head_dim():

@@ -25,7 +25,7 @@ def _oracle(x, bias, **kw):
     return o, lse, grads
 
 
-def _run(x, o, lse, bias, *, scale, mask, window, deterministic=True, dq_acc_dtype="fp32"):
+def _run(x, o, lse, bias, *, scale, mask, window, deterministic=True, dq_acc_dtype="fp32", tune=None):
     import torch
     import attention_backward_fmha_amd as F
     q, k, v, do = (to_dev_bf16(x[n]) for n in ("q", "k", "v", "do"))
@@ -33,7 +33,8 @@ def _run(x, o, lse, bias, *, scale, mask, window, deterministic=True, dq_acc_dty
     ld = to_dev_f32(lse.astype(np.float32))
     bd = to_dev_bf16(bias)
     out = F.bwd(q, k, v, od, ld, do, scale=scale, mask_type=mask, window=window,
-                deterministic=deterministic, dq_acc_dtype=dq_acc_dtype, bias=bd, bias_grad=True)
+                deterministic=deterministic, dq_acc_dtype=dq_acc_dtype, bias=bd, bias_grad=True,
+                tune=tune)
     torch.cuda.synchronize()
     return tuple(t.float().cpu().numpy().astype(np.float64) for t in out)
 
@@ -75,6 +76,19 @@ def test_backward_with_bias_matches_oracle(case, mode):
         for hh in range(bias.shape[1]):
             if np.abs(ref[3][bb, hh]).max() > 0:
                 assert_close("dbias[%d,%d]" % (bb, hh), got[3][bb, hh], ref[3][bb, hh])
+
+
+@pytest.mark.parametrize("tile_m", [32, 64])
+def test_staged_bias_at_both_block_heights(tile_m):
+    """d_qk = 128 with 16-byte aligned bias rows and Sk % 8 == 0: the main kernel stages the
+    bias through LDS at 32-row blocks and at the 64-row blocks the plan takes for it."""
+    x, bias, scale, mask, window = _case_inputs(("bhss_sk8", (2, 200, 264), (4, 2), (128, 128), (2, 4), TL,
+                                                 (-1, -1)), 9005)
+    kw = dict(scale=scale, mask_type=mask, window_left=window[0], window_right=window[1])
+    o, lse, ref = _oracle(x, bias, **kw)
+    got = _run(x, o, lse, bias, scale=scale, mask=mask, window=window, tune={"tile_m": tile_m})
+    assert_grads_close(got[:3], ref[:3])
+    assert_close("dbias", got[3], ref[3])
 
 
 def test_dbias_is_bit_identical_across_runs_and_modes():
