@@ -1390,27 +1390,46 @@ __global__ __launch_bounds__(256, DQK <= 128 && X != 3 ? 2 : 1) void k_fwd(const
     load_tile(true, (int64_t)t_lo * TK);
     store_tile();
   }
+  // bias rows 8-byte aligned and Sk a multiple of 4 (the bias loads below)
+  const bool bias_runs8 = XB && ((uintptr_t)p.bias & 7u) == 0 &&
+                          ((p.bias_s[0] | p.bias_s[1] | p.bias_s[2]) & 3) == 0 && (p.Sk & 3) == 0;
   for (int it = 0; it < ntiles; ++it) {
     const int64_t kt0 = (int64_t)(t_lo + it) * TK;
     __syncthreads();  // LDS holds tile it
     load_tile(it + 1 < ntiles, kt0 + TK);
 
-    // bias of this lane's query row for its keys of the tile, issued before the products
-    // (2-byte loads: the row stride may be any value >= Sk); rows past the plane read zeros,
-    // keys past the end are masked
-    float bz[XB ? 32 : 1];
+    // bias of this lane's query row for its keys of the tile, issued before the products;
+    // rows past the plane read zeros, keys past the end are masked.  The lane's keys come in
+    // runs of four consecutive ones (registers 4u .. 4u+3 of a block), one 8-byte load each
+    // where the bias rows are 8-byte aligned and Sk is a multiple of 4 (no run straddles the
+    // plane end); otherwise one 2-byte load per key.
+    // bz[8kb + r/2] holds the bf16 bias of registers r (low half) and r+1 (high half), r even
+    unsigned bz[XB ? 16 : 1];
     if constexpr (XB) {
       const __amdgpu_buffer_rsrc_t rb =
           buffer_rsrc(p.bias + (int64_t)b * p.bias_s[0] + (int64_t)h * p.bias_s[1], p.bias_plane_bytes);
       const int rowoff = row * (int)p.bias_s[2];
+      if (bias_runs8) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const unsigned short x = __builtin_amdgcn_raw_buffer_load_b16(
-              rb, (rowoff + (int)kt0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3)) * 2, 0, 0);
-          bz[16 * kb + r] = __uint_as_float((unsigned)x << 16);
-        }
+          for (int u = 0; u < 4; ++u) {
+            const u32x2 w = __builtin_bit_cast(
+                u32x2, __builtin_amdgcn_raw_buffer_load_b64(rb, (rowoff + (int)kt0 + 32 * kb + 8 * u + 4 * hi) * 2, 0, 0));
+            bz[8 * kb + 2 * u] = w[0];
+            bz[8 * kb + 2 * u + 1] = w[1];
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) {
+            const int k = rowoff + (int)kt0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
+            const unsigned x0 = __builtin_amdgcn_raw_buffer_load_b16(rb, k * 2, 0, 0);
+            const unsigned x1 = __builtin_amdgcn_raw_buffer_load_b16(rb, (k + 1) * 2, 0, 0);
+            bz[8 * kb + r / 2] = x0 | (x1 << 16);
+          }
+      }
     }
     // S^T for the tile's two 32-key blocks: register r of block kb holds key
     // kt0 + 32kb + 8(r/4) + 4hi + r%4 of this lane's query
@@ -1434,7 +1453,10 @@ __global__ __launch_bounds__(256, DQK <= 128 && X != 3 ? 2 : 1) void k_fwd(const
       for (int r = 0; r < 16; ++r) {
         const int ko = 32 * kb + 8 * (r >> 2) + (r & 3);
         float x = s[kb][r] * p.scale_log2;
-        if constexpr (XB) x = __builtin_fmaf(bz[16 * kb + r], kLog2e, x);
+        if constexpr (XB) {
+          const unsigned w = bz[8 * kb + r / 2];
+          x = __builtin_fmaf(__uint_as_float((r & 1) ? (w & 0xFFFF0000u) : (w << 16)), kLog2e, x);
+        }
         s[kb][r] = (unsigned)(t0 + ko) <= span ? x : -__builtin_inff();
         mt = fmaxf(mt, s[kb][r]);
       }
