@@ -1659,6 +1659,8 @@ hipError_t launch_reduce(const Plan& plan, const KParams& kp, hipStream_t stream
   if (plan.d_qk == 64) {
     if (plan.tile_m == 128) {
       launch_reduce_t<64, 128>(plan, kp, stream);
+    } else if (plan.tile_m == 32) {
+      launch_reduce_t<64, 32>(plan, kp, stream);  // the wide layout
     } else {
       launch_reduce_t<64, 64>(plan, kp, stream);
     }

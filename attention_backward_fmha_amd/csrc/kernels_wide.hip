@@ -1,5 +1,5 @@
 // kernels_wide.hip -- the main backward kernel in its wide layout (gfx950): eight waves per
-// work group, two per SIMD, 256-key tiles, 32-row query blocks.  Serves d_qk = d_v = 128
+// work group, two per SIMD, 256-key tiles, 32-row query blocks.  Serves d_qk = d_v = 128 or 64
 // without bias or dropout; kernels.hip holds the four-wave layout for the other cases and the
 // other stages.
 #include "device.h"
@@ -10,7 +10,7 @@ namespace fmha {
 namespace {
 
 // ------------------------------------------------------------------------------------------
-// Stage 2, wide layout (d_qk = d_v = 128, no bias, no dropout).  512 threads = 8 waves, two
+// Stage 2, wide layout (d_qk = d_v = D = 128 or 64, no bias, no dropout).  512 threads = 8 waves, two
 // per SIMD, so that one wave's matrix products overlap the other's LDS reads and exponentials
 // (one wave per SIMD cannot keep more than about a quarter of the CU's LDS bandwidth busy).
 // A key tile has 256 keys; wave w owns keys 32w .. 32w+31 (lane l32 holds key 32w +
@@ -41,7 +41,9 @@ namespace {
 //     permuted inside each 32-key block (krow below) so that 4 consecutive keys land on 4
 //     rows spaced by 2, while the 16 keys one row read of S takes (every other key, see
 //     kmap) land on 16 distinct rows.
-constexpr int kRowQ = 136;   // Q, dO and K rows: 128 bf16 + 8 of padding (see below)
+// Q, dO and K rows hold D bf16 + 8 of padding (kRowQ = D + 8 in the kernel): 272 bytes at
+// D = 128, 144 at D = 64, 68 or 36 dwords, both 4 modulo 32, so the bank arguments above
+// hold for either.
 constexpr int kRowT = 36;    // dS^T rows (one per key): 32 bf16 + 4
 
 // LDS row of key k of the tile.  32-key blocks stay in place; inside a block the key's bits
@@ -70,9 +72,10 @@ __device__ __forceinline__ void write_dst(uint16_t* dst, const float (&d)[16], i
     *(u32x2*)&dst[key * kRowT + 8 * u + 4 * hi] = u32x2{pack_bf16(d[4 * u], d[4 * u + 1]), pack_bf16(d[4 * u + 2], d[4 * u + 3])};
 }
 
-template <int DQM>
+template <int D, int DQM>
 __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
-  constexpr int D = 128, TN = 256, TM = 32;
+  static_assert(D == 128 || D == 64, "head dims of the wide layout");
+  constexpr int TN = 256, TM = 32, kRowQ = D + 8, NB = D / 32;  // NB: 32-column blocks
   constexpr bool DET = DQM == 1;
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[TN * kRowQ];          // K tile
   __shared__ __attribute__((aligned(16))) uint16_t qo_lds[2][2][TM * kRowQ];   // [buffer][Q, dO]
@@ -152,15 +155,15 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
     const int hi_d = (int)min(hi64, sg.lk);
     const unsigned span = (unsigned)(hi_d - lo_d);
 
-    // K tile -> LDS (8 chunks per thread), the wave's V rows -> registers (B operand of dP)
+    // K tile -> LDS (D / 16 chunks per thread), the wave's V rows -> registers (B operand of dP)
     {
       const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(
           p.k + elem_off(p.k_s, group, b, sg.k_row0 + key0, g), (uint32_t)((nk - 1) * (int)p.k_s[1] + D) * 2u);
       const int ks1 = (int)p.k_s[1];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < D / 16; ++i) {
         const int id = tid + 512 * i;
-        const int kr = id >> 4, c = id & 15;
+        const int kr = id / (D / 8), c = id % (D / 8);
         const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rk, (kr * ks1 + c * 8) * 2, 0, 0);
         *(u32x4*)&k_lds[krow(kr) * kRowQ + c * 8] = x;
       }
@@ -230,19 +233,29 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
     };
     head_rsrc(pc.h);
 
-    // ---- staging: thread t loads 16 bytes of Q and of dO (row t/16, chunk t%16); wave 0
-    // loads L (lanes 0..31) and D (lanes 32..63) ----
+    // ---- staging.  D = 128: thread t loads 16 bytes of Q and of dO (row t/16, chunk t%16);
+    // D = 64: waves 0-3 load Q and waves 4-7 dO, 16 bytes per thread (row (t%256)/8, chunk
+    // t%8).  Wave 0 loads L (lanes 0..31) and D (lanes 32..63) ----
     u32x4 q_pre, o_pre;
     float l_pre = 0.f, d_pre = 0.f;  // wave 0: L (lanes 0..31) and D (lanes 32..63) loads in flight
     int nq_pre = 0;
-    const int st_row = tid >> 4, st_c = tid & 15;
-    const int q_lane = (st_row * qs1 + st_c * 8) * 2, o_lane = (st_row * os1 + st_c * 8) * 2;
+    const bool st_o = D == 64 && wave_s >= 4;  // D = 64: this wave stages dO
+    const int st_row = D == 128 ? tid >> 4 : (tid & 255) >> 3, st_c = tid & (D / 8 - 1);
+    const int q_lane = (st_row * (st_o ? os1 : qs1) + st_c * 8) * 2, o_lane = (st_row * os1 + st_c * 8) * 2;
     auto load_step = [&]() {  // the prefetch cursor's step, then advance it
       const bool valid = pc.n < n1;
       const __amdgpu_buffer_rsrc_t none = buffer_rsrc(p.q, 0u);
       nq_pre = valid ? min(TM, lq - pc.r) : 0;
-      q_pre = __builtin_amdgcn_raw_buffer_load_b128(valid ? rq : none, q_lane + pc.r * qs1 * 2, 0, 0);
-      o_pre = __builtin_amdgcn_raw_buffer_load_b128(valid ? ro : none, o_lane + pc.r * os1 * 2, 0, 0);
+      if constexpr (D == 128) {
+        q_pre = __builtin_amdgcn_raw_buffer_load_b128(valid ? rq : none, q_lane + pc.r * qs1 * 2, 0, 0);
+        o_pre = __builtin_amdgcn_raw_buffer_load_b128(valid ? ro : none, o_lane + pc.r * os1 * 2, 0, 0);
+      } else {
+        // a branch on the wave-uniform flag, so that each load takes one scalar resource
+        if (st_o)
+          q_pre = __builtin_amdgcn_raw_buffer_load_b128(valid ? ro : none, q_lane + pc.r * os1 * 2, 0, 0);
+        else
+          q_pre = __builtin_amdgcn_raw_buffer_load_b128(valid ? rq : none, q_lane + pc.r * qs1 * 2, 0, 0);
+      }
       if (wave == 0) {  // two loads with wave-uniform resources
         const float lv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(valid ? rl : none, (pc.r + l32) * 4, 0, 0));
         const float dv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(valid ? rd : none, (pc.r + l32) * 4, 0, 0));
@@ -254,8 +267,12 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
       if (pc.h != h_old && pc.n < n1) head_rsrc(pc.h);
     };
     auto store_step = [&](int buf) {
-      *(u32x4*)&qo_lds[buf][0][st_row * kRowQ + st_c * 8] = q_pre;
-      *(u32x4*)&qo_lds[buf][1][st_row * kRowQ + st_c * 8] = o_pre;
+      if constexpr (D == 128) {
+        *(u32x4*)&qo_lds[buf][0][st_row * kRowQ + st_c * 8] = q_pre;
+        *(u32x4*)&qo_lds[buf][1][st_row * kRowQ + st_c * 8] = o_pre;
+      } else {
+        *(u32x4*)&qo_lds[buf][st_o ? 1 : 0][st_row * kRowQ + st_c * 8] = q_pre;
+      }
       // the padding columns of Q row r carry -L2[r]/c, those of dO row r carry -D[r] (three
       // bf16 parts each); a row past the segment end gets -1e30, so its P is exactly 0
       if (wave == 0) {
@@ -275,7 +292,11 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
                            (uint32_t)(row_hi + TM) * D * 2u);
       return buffer_rsrc(p.dq_acc + (int64_t)hh * p.head_stride + sg.acc_row0 * D, (uint32_t)lq * D * 4u);
     };
-    const int nd = wave & 3;
+    const int nd = wave & (NB - 1);  // this wave's 32 dQ columns
+    // the waves that compute the dQ of the work group's step s: D = 128, the four waves of
+    // half s % 2 (one 32-column tile each); D = 64, the two waves of pair s % 4, so that each
+    // SIMD (waves w and w + 4) takes its share every other step in either case
+    auto dq_turn = [&](int s) { return D == 128 ? (wave >> 2) == (s & 1) : (wave >> 1) == (s & 3); };
     auto dq_step = [&](int buf, const __amdgpu_buffer_rsrc_t& rdq, int r) {
       // deterministic mode: the partial an earlier tile of the item left for this block is
       // read back first, so the products below hide the load latency
@@ -356,7 +377,7 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
     for (int n = n0; n < n1; ++n) {
       const int buf = (n - n0) & 1;
       // the pending dQ of step n-1, by the half whose turn it is
-      if (n > n0 && (wave >> 2) == ((n - 1 - n0) & 1)) dq_step(buf ^ 1, rdq, dc.r);
+      if (n > n0 && dq_turn(n - 1 - n0)) dq_step(buf ^ 1, rdq, dc.r);
       const int q0 = cc.r;
       // ---- S, dP, P, dS, dV, dK of step n ----
       {
@@ -433,7 +454,7 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
         const uint16_t* obl = &ob[tq_row * kRowQ + tr_col];
         const uint16_t* qbl = &qb[tq_row * kRowQ + tr_col];
         auto ldv = [&](int i) {
-          const int t = i >> 2, n2 = i & 3;
+          const int t = i / NB, n2 = i % NB;
           const int off = 16 * t * kRowQ + 32 * n2;
           bo[i & 1] = tr_read(obl + off, obl + off + kRowQ);
           bq[i & 1] = tr_read(qbl + off, qbl + off + kRowQ);
@@ -441,11 +462,11 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
         ldv(0);
         ldv(1);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          dv_acc[i & 3] = mfma(pa[i >> 2], bo[i & 1], dv_acc[i & 3]);
-          dk_acc[i & 3] = mfma(sa[i >> 2], bq[i & 1], dk_acc[i & 3]);
+        for (int i = 0; i < 2 * NB; ++i) {
+          dv_acc[i % NB] = mfma(pa[i / NB], bo[i & 1], dv_acc[i % NB]);
+          dk_acc[i % NB] = mfma(sa[i / NB], bq[i & 1], dk_acc[i % NB]);
           __builtin_amdgcn_sched_barrier(0);
-          if (i + 2 < 8) ldv(i + 2);
+          if (i + 2 < 2 * NB) ldv(i + 2);
           if (i == 0) write_dst(ds_lds[buf], ds32, key_w, hi);
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -459,7 +480,7 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
       load_step();
     }
     // the last step's dQ
-    if (n1 > n0 && (wave >> 2) == ((n1 - 1 - n0) & 1)) dq_step((n1 - 1 - n0) & 1, rdq, dc.r);
+    if (n1 > n0 && dq_turn(n1 - 1 - n0)) dq_step((n1 - 1 - n0) & 1, rdq, dc.r);
 
     // ---- epilogue: dK = scale * dK_acc, dV = dV_acc as bf16, or this part's fp32 partials ----
 #pragma unroll
@@ -496,9 +517,15 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
 
 hipError_t launch_main_wide(const Plan& plan, const KParams& kp, dim3 grid, hipStream_t stream) {
   const int mode = plan.deterministic ? 1 : (plan.dq_bf16 ? 2 : 0);
-  if (mode == 1) hipLaunchKernelGGL((k_bwd_wide<1>), grid, dim3(512), 0, stream, kp);
-  else if (mode == 2) hipLaunchKernelGGL((k_bwd_wide<2>), grid, dim3(512), 0, stream, kp);
-  else hipLaunchKernelGGL((k_bwd_wide<0>), grid, dim3(512), 0, stream, kp);
+  if (plan.d_qk == 64) {
+    if (mode == 1) hipLaunchKernelGGL((k_bwd_wide<64, 1>), grid, dim3(512), 0, stream, kp);
+    else if (mode == 2) hipLaunchKernelGGL((k_bwd_wide<64, 2>), grid, dim3(512), 0, stream, kp);
+    else hipLaunchKernelGGL((k_bwd_wide<64, 0>), grid, dim3(512), 0, stream, kp);
+  } else {
+    if (mode == 1) hipLaunchKernelGGL((k_bwd_wide<128, 1>), grid, dim3(512), 0, stream, kp);
+    else if (mode == 2) hipLaunchKernelGGL((k_bwd_wide<128, 2>), grid, dim3(512), 0, stream, kp);
+    else hipLaunchKernelGGL((k_bwd_wide<128, 0>), grid, dim3(512), 0, stream, kp);
+  }
   return hipGetLastError();
 }
 

@@ -386,22 +386,26 @@ def test_plan_reads_only_its_arguments(monkeypatch):
 
 
 def test_wide_kernel_plan():
-    """d_qk = d_v = 128 without bias or dropout runs the eight-wave kernel: 256-key tiles and
-    32-row query blocks; the deterministic and bf16 accumulators follow that block height."""
-    for det, acc in ((1, _lib.DQ_ACC_FP32), (0, _lib.DQ_ACC_FP32), (0, _lib.DQ_ACC_BF16)):
-        a = batch_args(B=2, Hq=4, Hkv=2, Sq=200, Sk=333, deterministic=det, kernel=_lib.KERNEL_AUTO)
-        a.dq_acc_dtype = acc
-        info = _lib.plan_query(a)
-        assert (info.kernel, info.tile_m, info.tile_n) == (_lib.KERNEL_WIDE, 32, 256)
-        assert info.n_kv_tiles == 2 and info.n_q_blocks == 7
-        assert _lib.workspace_size(a) == info.workspace_bytes
-        if det:
-            assert info.acc_rows == 2 * 200 + 2 * 32 and info.nsplits == 2
-        elif acc == _lib.DQ_ACC_BF16:
-            assert info.acc_rows == 224  # 200 rounded up to 32
+    """d_qk = d_v = 128 or 64 without bias or dropout runs the eight-wave kernel: 256-key tiles
+    and 32-row query blocks; the deterministic and bf16 accumulators follow that block height."""
+    for d in (128, 64):
+        for det, acc in ((1, _lib.DQ_ACC_FP32), (0, _lib.DQ_ACC_FP32), (0, _lib.DQ_ACC_BF16)):
+            a = batch_args(B=2, Hq=4, Hkv=2, Sq=200, Sk=333, d_qk=d, d_v=d, deterministic=det,
+                           kernel=_lib.KERNEL_AUTO)
+            a.dq_acc_dtype = acc
+            info = _lib.plan_query(a)
+            assert (info.kernel, info.tile_m, info.tile_n) == (_lib.KERNEL_WIDE, 32, 256)
+            assert info.n_kv_tiles == 2 and info.n_q_blocks == 7
+            assert _lib.workspace_size(a) == info.workspace_bytes
+            if det:
+                assert info.acc_rows == 2 * 200 + 2 * 32 and info.nsplits == 2
+                assert info.dq_acc_bytes == 2 * 4 * info.acc_rows * d * 4
+            elif acc == _lib.DQ_ACC_BF16:
+                assert info.acc_rows == 224  # 200 rounded up to 32
     # other head dims, a bias, dropout, or an explicit request keep the four-wave kernel
-    for d_qk, d_v in ((64, 64), (192, 128)):
-        assert _lib.plan_query(batch_args(d_qk=d_qk, d_v=d_v, kernel=_lib.KERNEL_AUTO)).kernel == _lib.KERNEL_FOUR_WAVE
+    assert _lib.plan_query(batch_args(d_qk=192, d_v=128, kernel=_lib.KERNEL_AUTO)).kernel == _lib.KERNEL_FOUR_WAVE
+    four = batch_args(d_qk=64, d_v=64, kernel=_lib.KERNEL_FOUR_WAVE)
+    assert (_lib.plan_query(four).kernel, _lib.plan_query(four).tile_m) == (_lib.KERNEL_FOUR_WAVE, 128)
     drop = batch_args(kernel=_lib.KERNEL_AUTO)
     drop.p_drop = 0.1
     assert _lib.plan_query(drop).kernel == _lib.KERNEL_FOUR_WAVE
@@ -415,7 +419,7 @@ def test_wide_kernel_plan():
     long_q.tune_kernel = _lib.KERNEL_WIDE
     assert status_of(long_q) == _lib.ERR_INVALID_ARG
     # the wide kernel cannot be forced where it does not apply; its block height is fixed
-    bad = batch_args(d_qk=64, d_v=64, kernel=_lib.KERNEL_WIDE)
+    bad = batch_args(d_qk=192, d_v=128, kernel=_lib.KERNEL_WIDE)
     assert status_of(bad) == _lib.ERR_INVALID_ARG
     bad = batch_args(kernel=_lib.KERNEL_WIDE)
     bad.tune_tile_m = 64

@@ -34,8 +34,8 @@ def _inputs(case, seed):
     return x, sq, sk, 1.0 / np.sqrt(dqk), mask, window
 
 
-# (case, kernel): both layouts where d = 128 selects the wide one by default
-CASE_KERNELS = [(c, k) for c in CASES for k in ([F.KERNEL_AUTO, F.KERNEL_FOUR_WAVE] if c[3] == (128, 128)
+# (case, kernel): both layouts where d = 128 or 64 selects the wide one by default
+CASE_KERNELS = [(c, k) for c in CASES for k in ([F.KERNEL_AUTO, F.KERNEL_FOUR_WAVE] if c[3] in ((128, 128), (64, 64))
                                                  else [F.KERNEL_AUTO])]
 CK_IDS = ["%s-%s" % (c[0], {F.KERNEL_AUTO: "auto", F.KERNEL_FOUR_WAVE: "four_wave"}[k]) for c, k in CASE_KERNELS]
 

@@ -22,7 +22,8 @@ def _segments():
         return json.load(f)
 
 
-# main-kernel layouts at d = 128: the default (eight waves, 256-key tiles) and the four-wave one
+# main-kernel layouts at d = 128 and 64: the default (eight waves, 256-key tiles) and the
+# four-wave one
 KERNELS = [F.KERNEL_AUTO, F.KERNEL_FOUR_WAVE]
 KERNEL_IDS = ["wide", "four_wave"]
 
@@ -65,10 +66,12 @@ def test_batch_masks_d128(mask, window, deterministic, kernel):
     _run_batch(2001, 2, 200, 333, 4, 2, 128, 128, mask, window, deterministic, kernel=kernel)
 
 
-@pytest.mark.parametrize("d_qk,d_v", [(64, 64), (192, 128)])
+@pytest.mark.parametrize("d_qk,d_v,kernel", [(64, 64, F.KERNEL_AUTO), (64, 64, F.KERNEL_FOUR_WAVE),
+                                             (192, 128, F.KERNEL_AUTO)],
+                         ids=["d64_wide", "d64_four_wave", "d192"])
 @pytest.mark.parametrize("mask", [NONE, BR])
-def test_batch_head_dims(d_qk, d_v, mask):
-    _run_batch(2002, 2, 150, 290, 2, 1, d_qk, d_v, mask, sigmas=(1, 1, 0.5, 0.5))
+def test_batch_head_dims(d_qk, d_v, kernel, mask):
+    _run_batch(2002, 2, 150, 290, 2, 1, d_qk, d_v, mask, sigmas=(1, 1, 0.5, 0.5), kernel=kernel)
 
 
 @pytest.mark.parametrize("name", ["split_100_80_76", "split_200_56", "split_103_77_61",
@@ -92,14 +95,17 @@ def test_bottom_right_rows_without_keys():
     _run_batch(2003, 1, 300, 100, 2, 2, 64, 64, BR)
 
 
+@pytest.mark.parametrize("kernel", KERNELS, ids=KERNEL_IDS)
 @pytest.mark.parametrize("mode", ["det", "atomic", "atomic16"])
 @pytest.mark.parametrize("mask,window", [(TL, (-1, -1)), (BR, (-1, -1)), (WIN, (90, 7)), (NONE, (-1, -1))],
                          ids=["tl", "br", "win90_7", "none"])
-def test_group_d64_block_heights(mask, window, mode):
-    """d = 64 takes 128-row query blocks in the deterministic and bf16-accumulator modes and 64-row
-    blocks with fp32 atomics: ragged segments around 64/128-row boundaries (2, 63..65, 127..129,
-    255, 300 queries), GQA 6/2, every mode.  Every segment has rows with two or more allowed keys
-    under each mask (where no row does, the exact dQ is 0 and a relative bar cannot hold)."""
+def test_group_d64_block_heights(mask, window, mode, kernel):
+    """d = 64 in both layouts: the wide one (32-row query blocks, the default) and the four-wave
+    one, which takes 128-row blocks in the deterministic and bf16-accumulator modes and 64-row
+    blocks with fp32 atomics: ragged segments around 32/64/128-row boundaries (2, 63..65,
+    127..129, 255, 300 queries), GQA 6/2, every mode.  Every segment has rows with two or more
+    allowed keys under each mask (where no row does, the exact dQ is 0 and a relative bar cannot
+    hold)."""
     lens_q = [2, 63, 64, 65, 127, 128, 129, 255, 300]
     lens_k = [7, 65, 64, 200, 128, 3, 129, 255, 290]
     sq, sk = seq_offsets(lens_q), seq_offsets(lens_k)
@@ -109,5 +115,5 @@ def test_group_d64_block_heights(mask, window, mode):
     ref = oracle_backward(x, scale=scale, mask=mask, window=window, sq=sq, sk=sk)
     det, acc = {"det": (True, "fp32"), "atomic": (False, "fp32"), "atomic16": (False, "bf16")}[mode]
     got = run_gpu(x, o, lse, scale=scale, mask=mask, window=window, sq=sq, sk=sk,
-                  deterministic=det, dq_acc_dtype=acc)
+                  deterministic=det, dq_acc_dtype=acc, tune=dict(kernel=kernel))
     assert_grads_close(got, ref, sq=sq, sk=sk)
