@@ -185,43 +185,6 @@ __device__ __forceinline__ int tpos(int q) {
 __device__ __forceinline__ int qrow(int r) { return r ^ ((r >> 4) & 3); }
 __device__ __forceinline__ int dsrow(int r) { return r ^ ((r & 8) >> 1); }
 
-// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3",
-// SC 2011) of counter c under key (k0, k1), in place.  The dropout keep mask of element
-// (b, h, i, j) is byte (j % 4) of output word (i % 4) for counter (j/4, i/4, b*Hq + h, offset).
-__device__ __forceinline__ void philox4x32_10(unsigned (&c)[4], unsigned k0, unsigned k1) {
-#pragma unroll
-  for (int r = 0; r < 10; ++r) {
-    if (r) {
-      k0 += 0x9E3779B9u;
-      k1 += 0xBB67AE85u;
-    }
-    const uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
-    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c[2];
-    const unsigned n0 = (unsigned)(p1 >> 32) ^ c[1] ^ k0;
-    const unsigned n2 = (unsigned)(p0 >> 32) ^ c[3] ^ k1;
-    c[0] = n0;
-    c[1] = (unsigned)p1;
-    c[2] = n2;
-    c[3] = (unsigned)p0;
-  }
-}
-
-// 4x4 byte transpose: t[k] holds byte k of w[0], w[1], w[2], w[3] in its bytes 0..3.
-__device__ __forceinline__ void byte_transpose4(const unsigned (&w)[4], unsigned (&t)[4]) {
-  const unsigned a0 = __builtin_amdgcn_perm(w[1], w[0], 0x05010400u);  // w0.0 w1.0 w0.1 w1.1
-  const unsigned a1 = __builtin_amdgcn_perm(w[1], w[0], 0x07030602u);  // w0.2 w1.2 w0.3 w1.3
-  const unsigned b0 = __builtin_amdgcn_perm(w[3], w[2], 0x05010400u);  // w2.0 w3.0 w2.1 w3.1
-  const unsigned b1 = __builtin_amdgcn_perm(w[3], w[2], 0x07030602u);  // w2.2 w3.2 w2.3 w3.3
-  t[0] = __builtin_amdgcn_perm(b0, a0, 0x05040100u);
-  t[1] = __builtin_amdgcn_perm(b0, a0, 0x07060302u);
-  t[2] = __builtin_amdgcn_perm(b1, a1, 0x05040100u);
-  t[3] = __builtin_amdgcn_perm(b1, a1, 0x07060302u);
-}
-
-__device__ __forceinline__ unsigned sel4(const unsigned (&v)[4], unsigned i) {
-  return (i & 2u) ? ((i & 1u) ? v[3] : v[2]) : ((i & 1u) ? v[1] : v[0]);
-}
-
 // dS of one 32-query tile to LDS, one row per query.  On entry d[4c + e] is dS(query
 // 8c + 4*hi + e of the tile, this lane's key).  Three exchanges move key bits into registers
 // and query bits into lanes: lane bit 4 <-> e bit 0 (permlane16 swap, on fp32 values), then

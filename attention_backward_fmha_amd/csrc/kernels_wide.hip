@@ -1,7 +1,7 @@
 // kernels_wide.hip -- the main backward kernel in its wide layout (gfx950): eight waves per
 // work group, two per SIMD, 256-key tiles, 32-row query blocks.  Serves d_qk = d_v = 128 or 64
-// without bias or dropout; kernels.hip holds the four-wave layout for the other cases and the
-// other stages.
+// without a bias, with or without dropout; kernels.hip holds the four-wave layout for the other
+// cases and the other stages.
 #include "device.h"
 #include "kernels.h"
 #include "tiling.h"
@@ -10,7 +10,7 @@ namespace fmha {
 namespace {
 
 // ------------------------------------------------------------------------------------------
-// Stage 2, wide layout (d_qk = d_v = D = 128 or 64, no bias, no dropout).  512 threads = 8 waves, two
+// Stage 2, wide layout (d_qk = d_v = D = 128 or 64, no bias).  512 threads = 8 waves, two
 // per SIMD, so that one wave's matrix products overlap the other's LDS reads and exponentials
 // (one wave per SIMD cannot keep more than about a quarter of the CU's LDS bandwidth busy).
 // A key tile has 256 keys; wave w owns keys 32w .. 32w+31 (lane l32 holds key 32w +
@@ -72,7 +72,7 @@ __device__ __forceinline__ void write_dst(uint16_t* dst, const float (&d)[16], i
     *(u32x2*)&dst[key * kRowT + 8 * u + 4 * hi] = u32x2{pack_bf16(d[4 * u], d[4 * u + 1]), pack_bf16(d[4 * u + 2], d[4 * u + 3])};
 }
 
-template <int D, int DQM>
+template <int D, int DQM, bool XD>
 __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
   static_assert(D == 128 || D == 64, "head dims of the wide layout");
   constexpr int TN = 256, TM = 32, kRowQ = D + 8, NB = D / 32;  // NB: 32-column blocks
@@ -80,6 +80,8 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[TN * kRowQ];          // K tile
   __shared__ __attribute__((aligned(16))) uint16_t qo_lds[2][2][TM * kRowQ];   // [buffer][Q, dO]
   __shared__ __attribute__((aligned(16))) uint16_t ds_lds[2][TN * kRowT];      // [buffer] dS^T
+  // dropout: D of the step's rows per buffer (with dropout D is not folded into dP)
+  __shared__ __attribute__((aligned(16))) float dd_lds[XD ? 2 * TM : 4];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -274,10 +276,12 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
         *(u32x4*)&qo_lds[buf][st_o ? 1 : 0][st_row * kRowQ + st_c * 8] = q_pre;
       }
       // the padding columns of Q row r carry -L2[r]/c, those of dO row r carry -D[r] (three
-      // bf16 parts each); a row past the segment end gets -1e30, so its P is exactly 0
+      // bf16 parts each); a row past the segment end gets -1e30, so its P is exactly 0.  With
+      // dropout the dO padding is 0 and D goes to dd_lds: dS = P (Z dP - D) needs dP alone
       if (wave == 0) {
-        const float x = lane < 32 ? (l32 < nq_pre ? -l_pre * inv_c : -1e30f) : -d_pre;
+        const float x = lane < 32 ? (l32 < nq_pre ? -l_pre * inv_c : -1e30f) : (XD ? 0.f : -d_pre);
         *(u32x4*)&qo_lds[buf][hi][l32 * kRowQ + D] = split3(x);
+        if (XD && lane >= 32) dd_lds[buf * TM + l32] = d_pre;
       }
     };
 
@@ -418,6 +422,37 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
         // (key, query) pair of the wave's 32 x 32 block is outside it (the block straddles
         // the mask's edge or the tile's last key): a wave-uniform test per step
         bf16x8 pa[2], sa[2];
+        // dropout: row group c (rows 8c + 4hi + e) of the lane's key takes byte (key % 4) of
+        // word e of the Philox output for (key / 4, row / 4).  The four lanes of a key quad
+        // (l, l^1, l^16, l^17: key bits 0-1 are lane bits 4 and 0) need the same four outputs;
+        // each computes the one of its position t in the quad, transposes it to per-key words
+        // of 4 row bytes, and the quad trades them
+        unsigned zw[4] = {0u, 0u, 0u, 0u};
+        if constexpr (XD) {
+          const unsigned kpos = (unsigned)(key0 + key_w);
+          const unsigned t = (unsigned)(lane & 1) | ((unsigned)(lane >> 4) & 1u) << 1;
+          unsigned w[4] = {kpos >> 2, (unsigned)(q0 + 8 * (int)t + 4 * hi) >> 2,
+                           (unsigned)(b * p.Hq + cc.h), p.offset_lo};
+          philox4x32_10(w, p.seed_lo, p.seed_hi);
+          unsigned tw[4];
+          byte_transpose4(w, tw);  // tw[k]: the 4 row bytes of key k % 4
+          unsigned rr[4];
+          rr[0] = sel4(tw, ((t >> 1) & 1u) | ((t & 1u) << 1));
+          {
+            const unsigned pu = t ^ 1u;
+            rr[1] = xor1(sel4(tw, ((pu >> 1) & 1u) | ((pu & 1u) << 1)));
+          }
+          {
+            const unsigned pu = t ^ 2u;
+            rr[2] = xor16(sel4(tw, ((pu >> 1) & 1u) | ((pu & 1u) << 1)), lane);
+          }
+          {
+            const unsigned pu = t ^ 3u;
+            rr[3] = xor16(xor1(sel4(tw, ((pu >> 1) & 1u) | ((pu & 1u) << 1))), lane);
+          }
+#pragma unroll
+          for (int c = 0; c < 4; ++c) zw[c] = sel4(rr, t ^ (unsigned)c);
+        }
         {
 #pragma unroll
           for (int r = 0; r < 16; ++r) ds32[r] = __builtin_amdgcn_exp2f(s_acc[r] * p.scale_log2);
@@ -433,14 +468,18 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
           }
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
+            f32x4 d4 = f32x4{0.f, 0.f, 0.f, 0.f};
+            if constexpr (XD) d4 = *(const f32x4*)&dd_lds[buf * TM + 8 * c + 4 * hi];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int r = 4 * c + e;
               const float pv = ds32[r];
-              const float dsv = pv * dp_acc[r];
+              // with dropout Z = 256/k where the element's byte is below k, else 0
+              const float zf = XD ? (((zw[c] >> (8 * e)) & 0xFFu) < (unsigned)p.drop_k ? p.drop_scale : 0.f) : 1.f;
+              const float dsv = XD ? pv * (dp_acc[r] * zf - d4[e]) : pv * dp_acc[r];
               // reduction slot of (c, e) in step c/2: the Q/dO rows the transposing reads give
               const int slot = 2 * (c & 1) + (e >> 1) + 4 * (e & 1);
-              pa[c >> 1][slot] = (__bf16)pv;
+              pa[c >> 1][slot] = (__bf16)(XD ? pv * zf : pv);
               sa[c >> 1][slot] = (__bf16)dsv;
               ds32[r] = dsv;
             }
@@ -513,18 +552,24 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
   }  // tiles of the item
 }
 
+template <int D, bool XD>
+void launch_wide_t(int mode, const KParams& kp, dim3 grid, hipStream_t stream) {
+  if (mode == 1) hipLaunchKernelGGL((k_bwd_wide<D, 1, XD>), grid, dim3(512), 0, stream, kp);
+  else if (mode == 2) hipLaunchKernelGGL((k_bwd_wide<D, 2, XD>), grid, dim3(512), 0, stream, kp);
+  else hipLaunchKernelGGL((k_bwd_wide<D, 0, XD>), grid, dim3(512), 0, stream, kp);
+}
+
 }  // namespace
 
 hipError_t launch_main_wide(const Plan& plan, const KParams& kp, dim3 grid, hipStream_t stream) {
   const int mode = plan.deterministic ? 1 : (plan.dq_bf16 ? 2 : 0);
+  const bool drop = plan.drop_k < 256;
   if (plan.d_qk == 64) {
-    if (mode == 1) hipLaunchKernelGGL((k_bwd_wide<64, 1>), grid, dim3(512), 0, stream, kp);
-    else if (mode == 2) hipLaunchKernelGGL((k_bwd_wide<64, 2>), grid, dim3(512), 0, stream, kp);
-    else hipLaunchKernelGGL((k_bwd_wide<64, 0>), grid, dim3(512), 0, stream, kp);
+    if (drop) launch_wide_t<64, true>(mode, kp, grid, stream);
+    else launch_wide_t<64, false>(mode, kp, grid, stream);
   } else {
-    if (mode == 1) hipLaunchKernelGGL((k_bwd_wide<128, 1>), grid, dim3(512), 0, stream, kp);
-    else if (mode == 2) hipLaunchKernelGGL((k_bwd_wide<128, 2>), grid, dim3(512), 0, stream, kp);
-    else hipLaunchKernelGGL((k_bwd_wide<128, 0>), grid, dim3(512), 0, stream, kp);
+    if (drop) launch_wide_t<128, true>(mode, kp, grid, stream);
+    else launch_wide_t<128, false>(mode, kp, grid, stream);
   }
   return hipGetLastError();
 }

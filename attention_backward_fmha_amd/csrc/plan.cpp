@@ -132,20 +132,19 @@ int make_plan(const fmha_bwd_args* a, Plan* p, char* err, size_t el, bool forwar
   if (a->tune_kv_parts < 0 || a->tune_kv_parts > 8)
     return fail(FMHA_ERR_INVALID_ARG, err, el, "tune_kv_parts must be in 0 .. 8");
   const bool with_bias = a->bias != nullptr;
-  const bool with_dropout = p->drop_k < 256;
-  // The wide kernel (eight waves, 256-key tiles) serves d_qk = d_v = 128 or 64 without bias
-  // or dropout.  It addresses 256-row key tiles, and a query head's Q and dO rows of a whole
+  // The wide kernel (eight waves, 256-key tiles) serves d_qk = d_v = 128 or 64 without a
+  // bias (with or without dropout).  It addresses 256-row key tiles, and a query head's Q and dO rows of a whole
   // segment, with 32-bit byte offsets: sequence strides below 2^22 elements, and Sq rows (plus
   // a block) times the Q and dO sequence strides below 2^30 elements.
   const bool wide_ok = ((a->d_qk == 128 && a->d_v == 128) || (a->d_qk == 64 && a->d_v == 64)) &&
-                       !with_bias && !with_dropout &&
+                       !with_bias &&
                        a->q_stride[1] < (int64_t(1) << 22) && a->k_stride[1] < (int64_t(1) << 22) &&
                        a->v_stride[1] < (int64_t(1) << 22) && a->do_stride[1] < (int64_t(1) << 22) &&
                        ((int64_t)a->Sq + 32) * a->q_stride[1] < (int64_t(1) << 30) &&
                        ((int64_t)a->Sq + 32) * a->do_stride[1] < (int64_t(1) << 30);
   if (a->tune_kernel == FMHA_KERNEL_WIDE && !wide_ok)
     return fail(FMHA_ERR_INVALID_ARG, err, el,
-                "tune_kernel = FMHA_KERNEL_WIDE needs d_qk = d_v = 128 or 64, no bias, no dropout, "
+                "tune_kernel = FMHA_KERNEL_WIDE needs d_qk = d_v = 128 or 64, no bias, "
                 "sequence strides below 2^22 and (Sq + 32) times the q and dout sequence strides "
                 "below 2^30");
   p->kernel = (a->tune_kernel == FMHA_KERNEL_FOUR_WAVE || !wide_ok) ? FMHA_KERNEL_FOUR_WAVE

@@ -205,7 +205,8 @@ enum fmha_kernel {
   FMHA_KERNEL_FOUR_WAVE = 1, /* 256 threads, 128-key tiles, 32-128-row query blocks; every
                                 head dim, bias and dropout */
   FMHA_KERNEL_WIDE = 2   /* 512 threads (two waves per SIMD), 256-key tiles, 32-row query
-                            blocks; d_qk = d_v = 128 or 64 without bias or dropout */
+                            blocks; d_qk = d_v = 128 or 64 without a bias (dropout is
+                            allowed) */
 };
 
 /* Workspace bytes that prepare/run need for these arguments.  Host only: no GPU call, no

@@ -402,13 +402,13 @@ def test_wide_kernel_plan():
                 assert info.dq_acc_bytes == 2 * 4 * info.acc_rows * d * 4
             elif acc == _lib.DQ_ACC_BF16:
                 assert info.acc_rows == 224  # 200 rounded up to 32
-    # other head dims, a bias, dropout, or an explicit request keep the four-wave kernel
+    # d_qk = 192, a bias, or an explicit request keep the four-wave kernel
     assert _lib.plan_query(batch_args(d_qk=192, d_v=128, kernel=_lib.KERNEL_AUTO)).kernel == _lib.KERNEL_FOUR_WAVE
     four = batch_args(d_qk=64, d_v=64, kernel=_lib.KERNEL_FOUR_WAVE)
     assert (_lib.plan_query(four).kernel, _lib.plan_query(four).tile_m) == (_lib.KERNEL_FOUR_WAVE, 128)
-    drop = batch_args(kernel=_lib.KERNEL_AUTO)
+    drop = batch_args(kernel=_lib.KERNEL_AUTO)  # dropout runs in the wide kernel too
     drop.p_drop = 0.1
-    assert _lib.plan_query(drop).kernel == _lib.KERNEL_FOUR_WAVE
+    assert _lib.plan_query(drop).kernel == _lib.KERNEL_WIDE
     assert _lib.plan_query(batch_args()).kernel == _lib.KERNEL_FOUR_WAVE
     # a query head's rows of a whole segment must stay inside 32-bit offsets for the wide
     # kernel: (Sq + 32) * 4096 elements of sequence stride reaches 2^30 at Sq = 262112

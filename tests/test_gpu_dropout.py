@@ -24,8 +24,9 @@ def _oracle_keep(p, seed, offset, b, h, hq, lq, lk):
     return A.dropout_keep(seed, offset, b, h, hq, np.arange(lq), np.arange(lk), k)
 
 
+@pytest.mark.parametrize("kernel", ["wide", "four_wave"])
 @pytest.mark.parametrize("p,seed,offset", [(0.5, 1234, 0), (0.1, 2**40 + 17, 77), (0.9, 5, 2**31 + 3)])
-def test_keep_mask_is_the_oracles_bit_for_bit(p, seed, offset):
+def test_keep_mask_is_the_oracles_bit_for_bit(p, seed, offset, kernel):
     import torch
     import attention_backward_fmha_amd as F
     B, L, hq, d = 2, 100, 2, 128  # L <= d: one column of V (row of dO) per key (query)
@@ -37,7 +38,8 @@ def test_keep_mask_is_the_oracles_bit_for_bit(p, seed, offset):
     kw = dict(scale=0.125, dropout_p=p, philox_seed=seed, philox_offset=offset)
     o, lse = F.fwd(q, k, v, **kw)
     do = eye[None, :, None, :].expand(B, L, hq, d).contiguous()
-    _, _, dv = F.bwd(q, k, v, o, lse, do, **kw)
+    tune = dict(kernel=F.KERNEL_WIDE if kernel == "wide" else F.KERNEL_FOUR_WAVE)
+    _, _, dv = F.bwd(q, k, v, o, lse, do, tune=tune, **kw)
     torch.cuda.synchronize()
     o = o.float().cpu().numpy()
     dv = dv.float().cpu().numpy()
@@ -53,7 +55,7 @@ def test_keep_mask_is_the_oracles_bit_for_bit(p, seed, offset):
 
 
 def _run(x, o, lse, *, scale, mask, window=(-1, -1), sq=None, sk=None, deterministic=True,
-         dq_acc_dtype="fp32", drop=(0.2, 42, 7), bias=None):
+         dq_acc_dtype="fp32", drop=(0.2, 42, 7), bias=None, tune=None):
     import torch
     import attention_backward_fmha_amd as F
     q, k, v, do = (to_dev_bf16(x[n]) for n in ("q", "k", "v", "do"))
@@ -67,7 +69,7 @@ def _run(x, o, lse, *, scale, mask, window=(-1, -1), sq=None, sk=None, determini
         kw.update(bias=to_dev_bf16(bias), bias_grad=True)
     out = F.bwd(q, k, v, od, ld, do, scale=scale, mask_type=mask, window=window,
                 deterministic=deterministic, dq_acc_dtype=dq_acc_dtype, dropout_p=drop[0],
-                philox_seed=drop[1], philox_offset=drop[2], **kw)
+                philox_seed=drop[1], philox_offset=drop[2], tune=tune, **kw)
     torch.cuda.synchronize()
     return tuple(t.float().cpu().numpy().astype(np.float64) for t in out)
 
@@ -96,9 +98,13 @@ def _inputs(case, seed):
     return x, sq, sk, 1.0 / np.sqrt(dqk), mask, window
 
 
+# d = 128 and 64 run the wide layout by default; the four-wave one is checked there as well
+CASE_KERNELS = [(c, k) for c in CASES for k in (["auto", "four_wave"] if c[3][0] in (64, 128) else ["auto"])]
+
+
 @pytest.mark.parametrize("mode", ["det", "atomic", "atomic16"])
-@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
-def test_backward_with_dropout_matches_oracle(case, mode):
+@pytest.mark.parametrize("case,kernel", CASE_KERNELS, ids=["%s-%s" % (c[0], k) for c, k in CASE_KERNELS])
+def test_backward_with_dropout_matches_oracle(case, kernel, mode):
     import oracle
     x, sq, sk, scale, mask, window = _inputs(case, 9101)
     drop = (0.2, 42, 7)
@@ -107,8 +113,10 @@ def test_backward_with_dropout_matches_oracle(case, mode):
     o, lse = oracle.forward(x["q"], x["k"], x["v"], **kw)
     ref = oracle.backward(x["q"], x["k"], x["v"], x["do"], **kw)
     det, acc = {"det": (True, "fp32"), "atomic": (False, "fp32"), "atomic16": (False, "bf16")}[mode]
+    import attention_backward_fmha_amd as F
     got = _run(x, o, lse, scale=scale, mask=mask, window=window, sq=sq, sk=sk, deterministic=det,
-               dq_acc_dtype=acc, drop=drop)
+               dq_acc_dtype=acc, drop=drop,
+               tune=dict(kernel=F.KERNEL_FOUR_WAVE) if kernel == "four_wave" else None)
     assert_grads_close(got, ref, sq, sk)
 
 
