@@ -433,7 +433,12 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
           const unsigned t = (unsigned)(lane & 1) | ((unsigned)(lane >> 4) & 1u) << 1;
           unsigned w[4] = {kpos >> 2, (unsigned)(q0 + 8 * (int)t + 4 * hi) >> 2,
                            (unsigned)(b * p.Hq + cc.h), p.offset_lo};
-          philox4x32_10(w, p.seed_lo, p.seed_hi);
+          // the key enters each step through an empty asm statement, so that the compiler
+          // derives the round keys in the step (two scalar adds per round) instead of keeping
+          // all twenty live across the loop, which spilled scalar registers
+          unsigned k0 = p.seed_lo, k1 = p.seed_hi;
+          asm volatile("" : "+s"(k0), "+s"(k1));
+          philox4x32_10(w, k0, k1);
           unsigned tw[4];
           byte_transpose4(w, tw);  // tw[k]: the 4 row bytes of key k % 4
           unsigned rr[4];
