@@ -30,28 +30,44 @@ namespace {
 // the tile's last key (a wave-uniform test), and the L/D loads of the next step are selected
 // where they are stored, so no wave waits on a global load inside a step.
 //
-// LDS tiles are row-major with rows padded by 16 bytes, so that consecutive rows start 4
-// banks apart and every LDS offset of the unrolled loops is a per-lane base plus a constant:
-//   - 16-byte row reads (16 lanes read 16 consecutive rows at one column) touch 64 distinct
-//     banks;
-//   - a transposing 8-byte read takes 4 rows of 32 bytes per 16-lane group, and is free of
-//     conflicts when its 4 rows are spaced by 2 (2 row offsets = 8 banks): the dV/dK products
-//     read query rows {0, 2, 8, 10} (+1) of a 16-row group, i.e. their reduction slots take
-//     the S/dP result registers in that order, and the K tile is stored with its keys
-//     permuted inside each 32-key block (krow below) so that 4 consecutive keys land on 4
-//     rows spaced by 2, while the 16 keys one row read of S takes (every other key, see
-//     kmap) land on 16 distinct rows.
-// Q, dO and K rows hold D bf16 + 8 of padding (kRowQ = D + 8 in the kernel): 272 bytes at
-// D = 128, 144 at D = 64, 68 or 36 dwords, both 4 modulo 32, so the bank arguments above
-// hold for either.
+// LDS banks: 64 of 4 bytes.  8-byte reads (plain or transposing) are served 32 lanes per
+// cycle: the bank-conflict counter is zero for every transposing read below, each of whose
+// half-waves touches every bank once, and was not for rows chosen to suit 16-lane groups.  Q,
+// dO and K rows hold D bf16 + 8 of padding (kRowQ = D + 8 in the kernel: 68 dwords at D =
+// 128, 36 at D = 64; either is 4 times an odd number, so row r starts at bank 4r (D = 128) or
+// 4 * (9r mod 16) (D = 64) modulo 64).
+//   - a transposing 8-byte read (two 16-lane groups reading the two 32-byte halves of the
+//     same 4 rows) needs its 4 rows to start 16 banks apart: rows r, r + 4, r + 8, r + 12
+//     modulo 16;
+//   - 16-byte row reads need at least 16 rows distinct modulo 16 in each 16-lane group; the
+//     row orders below were also measured free of conflicts (an order meeting only that
+//     condition was not).
+// Rows are therefore stored permuted inside each 32-row block by one bit permutation (qrow:
+// one-to-one, linear over GF(2)) for the query rows of Q and dO and for the keys of the K
+// tile.  The bits a read's lanes vary and the bits its unrolled steps vary map to disjoint row
+// bits, so every LDS offset of the unrolled loops is a per-lane base plus a constant.  The
+// key-major dS tile (dslot) has 72-byte rows (18 dwords): the 4 keys of a transposing read
+// (key bits 0-1) go to row bits 3-4, 8 rows = 16 banks apart.  Its 8-byte writes (four per
+// lane and step) still show conflicts, about 5% of the step's LDS cycles.
 constexpr int kRowT = 36;    // dS^T rows (one per key): 32 bf16 + 4
 
-// LDS row of key k of the tile.  32-key blocks stay in place; inside a block the key's bits
-// k0..k4 go to row bits r0 = k3, r1 = k0 ^ k2, r2 = k1, r3 = k4, r4 = k2 (one-to-one, and
-// linear over GF(2)).
-__device__ __forceinline__ int krow(int k) {
-  return (k & ~31) | ((k >> 3) & 1) | (((k ^ (k >> 2)) & 1) << 1) | (((k >> 1) & 1) << 2) |
-         (((k >> 4) & 1) << 3) | (((k >> 2) & 1) << 4);
+__device__ __forceinline__ int bit_of(int x, int i) { return (x >> i) & 1; }
+
+// LDS row of query row (or key) m of a step: bits m0..m4 go to r0 = m3, r1 = m2, r2 = m0,
+// r3 = m1, r4 = m4.  The dV/dK products' transposing reads of lane half hi, reduction step t
+// and read h take query rows 16t + 8h + 4hi + {0..3}, i.e. rows 16t + h + 2hi + 4 * {0..3};
+// dQ's transposing reads take keys 16kk + 8hi + 4h + {0..3}, i.e. rows 16kk + 2h + hi +
+// 4 * {0..3}.  (Row reads of S through kmap's key order also measured free of conflicts,
+// where an order built only for a 16-consecutive-lane bank model was not.)
+__device__ __forceinline__ int qrow(int m) {
+  return (m & ~31) | bit_of(m, 3) | bit_of(m, 2) << 1 | bit_of(m, 0) << 2 | bit_of(m, 1) << 3 | bit_of(m, 4) << 4;
+}
+
+// Row of key k in the key-major dS tile: s0 = k3, s1 = k2, s2 = k4, s3 = k0, s4 = k1.  dQ's
+// transposing reads take keys 16kk + 8hi + 4h + {0..3} onto rows dslot(8hi + {0..3}) +
+// 32(kk / 2) + 4(kk % 2) + 2h.
+__device__ __forceinline__ int dslot(int k) {
+  return (k & ~31) | bit_of(k, 3) | bit_of(k, 2) << 1 | bit_of(k, 4) << 2 | bit_of(k, 0) << 3 | bit_of(k, 1) << 4;
 }
 
 // x as three bf16 parts (x = p1 + p2 + p3 to within fp32 rounding) followed by five zeros.
@@ -63,13 +79,13 @@ __device__ __forceinline__ u32x4 split3(float x) {
   return u32x4{__builtin_bit_cast(unsigned, bf16x2{p1, p2}), (unsigned)__builtin_bit_cast(uint16_t, p3), 0u, 0u};
 }
 
-// dS of the lane's key for the step's 32 queries into the key-major tile: register 4u + e
-// holds query 8u + 4hi + e, so each u is one 8-byte write of four consecutive queries.  With
-// 72-byte rows the 16 even (or odd) keys one 16-lane pass writes land on distinct bank pairs.
-__device__ __forceinline__ void write_dst(uint16_t* dst, const float (&d)[16], int key, int hi) {
+// dS of the lane's key for the step's 32 queries into the key-major tile (row `row` =
+// dslot(key)): register 4u + e holds query 8u + 4hi + e, so each u is one 8-byte write of
+// four consecutive queries.
+__device__ __forceinline__ void write_dst(uint16_t* dst, const float (&d)[16], int row, int hi) {
 #pragma unroll
   for (int u = 0; u < 4; ++u)
-    *(u32x2*)&dst[key * kRowT + 8 * u + 4 * hi] = u32x2{pack_bf16(d[4 * u], d[4 * u + 1]), pack_bf16(d[4 * u + 2], d[4 * u + 3])};
+    *(u32x2*)&dst[row * kRowT + 8 * u + 4 * hi] = u32x2{pack_bf16(d[4 * u], d[4 * u + 1]), pack_bf16(d[4 * u + 2], d[4 * u + 3])};
 }
 
 template <int D, int DQM, bool XD>
@@ -126,12 +142,12 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
   const int tr_row = i16 >> 2;                        // row inside a 4-row transposing read
   const int tr_col = 16 * (g16 & 1) + 4 * (i16 & 3);  // its columns inside a 32-column tile
   const int key_w = 32 * wave + kmap(l32);            // the lane's key inside the tile
-  // query rows of the lane's transposing reads of Q and dO (reduction step 0; +16 for step 1,
-  // +1 for the second read): 4hi + {0, 2, 8, 10}
-  const int tq_row = 4 * hi + 2 * (tr_row & 1) + 8 * (tr_row >> 1);
-  // K rows of the lane's transposing reads for dQ (key group 0; + 32*(kk/2) + 8*(kk%2) for
-  // reduction step kk): keys 8hi + tr_row and 8hi + 4 + tr_row
-  const int tk_row0 = krow(8 * hi + tr_row), tk_row1 = krow(8 * hi + 4 + tr_row);
+  // LDS row of the lane's transposing reads of Q and dO (reduction step 0; +16 for step 1,
+  // +1 for the second read): query row 4hi + tr_row
+  const int tq_row = qrow(4 * hi + tr_row);
+  // K and dS rows of the lane's transposing reads for dQ: key 8hi + tr_row of reduction step 0
+  const int tk_row = qrow(8 * hi + tr_row), td_row = dslot(8 * hi + tr_row);
+  const int q_row = qrow(l32);                        // LDS row of the lane's query (S, dP)
   const float inv_c = 1.f / p.scale_log2;
   // B operand of ones in reduction slots 0..2 of lane half 0 (bf16 1.0 = 0x3F80), zeros in
   // half 1: the product with a padding chunk adds its three parts
@@ -167,7 +183,7 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
         const int id = tid + 512 * i;
         const int kr = id / (D / 8), c = id % (D / 8);
         const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rk, (kr * ks1 + c * 8) * 2, 0, 0);
-        *(u32x4*)&k_lds[krow(kr) * kRowQ + c * 8] = x;
+        *(u32x4*)&k_lds[qrow(kr) * kRowQ + c * 8] = x;
       }
     }
     bf16x8 vw[D / 16];
@@ -243,6 +259,7 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
     int nq_pre = 0;
     const bool st_o = D == 64 && wave_s >= 4;  // D = 64: this wave stages dO
     const int st_row = D == 128 ? tid >> 4 : (tid & 255) >> 3, st_c = tid & (D / 8 - 1);
+    const int st_lds = qrow(st_row) * kRowQ + st_c * 8;
     const int q_lane = (st_row * (st_o ? os1 : qs1) + st_c * 8) * 2, o_lane = (st_row * os1 + st_c * 8) * 2;
     auto load_step = [&]() {  // the prefetch cursor's step, then advance it
       const bool valid = pc.n < n1;
@@ -270,17 +287,17 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
     };
     auto store_step = [&](int buf) {
       if constexpr (D == 128) {
-        *(u32x4*)&qo_lds[buf][0][st_row * kRowQ + st_c * 8] = q_pre;
-        *(u32x4*)&qo_lds[buf][1][st_row * kRowQ + st_c * 8] = o_pre;
+        *(u32x4*)&qo_lds[buf][0][st_lds] = q_pre;
+        *(u32x4*)&qo_lds[buf][1][st_lds] = o_pre;
       } else {
-        *(u32x4*)&qo_lds[buf][st_o ? 1 : 0][st_row * kRowQ + st_c * 8] = q_pre;
+        *(u32x4*)&qo_lds[buf][st_o ? 1 : 0][st_lds] = q_pre;
       }
       // the padding columns of Q row r carry -L2[r]/c, those of dO row r carry -D[r] (three
       // bf16 parts each); a row past the segment end gets -1e30, so its P is exactly 0.  With
       // dropout the dO padding is 0 and D goes to dd_lds: dS = P (Z dP - D) needs dP alone
       if (wave == 0) {
         const float x = lane < 32 ? (l32 < nq_pre ? -l_pre * inv_c : -1e30f) : (XD ? 0.f : -d_pre);
-        *(u32x4*)&qo_lds[buf][hi][l32 * kRowQ + D] = split3(x);
+        *(u32x4*)&qo_lds[buf][hi][q_row * kRowQ + D] = split3(x);
         if (XD && lane >= 32) dd_lds[buf * TM + l32] = d_pre;
       }
     };
@@ -313,17 +330,18 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
           prev[u] = __builtin_amdgcn_raw_buffer_load_b128(rprev, (r * D + nd * 1024 + u * 256 + lane * 4) * 4, 0, kPartialPolicy);
       }
       f32x16 acc = f32x16{};
-      // A operand: keys 16kk + 8hi .. +7 of query l32, two transposing reads of the key-major dS
-      const uint16_t* dsb = &ds_lds[buf][(8 * hi + tr_row) * kRowT + tr_col];
-      const uint16_t* kt0 = &k_lds[tk_row0 * kRowQ + 32 * nd + tr_col];
-      const uint16_t* kt1 = &k_lds[tk_row1 * kRowQ + 32 * nd + tr_col];
+      // A operand: keys 16kk + 8hi + {0..3, 4..7} of query l32, two transposing reads of the
+      // key-major dS; B operand: the same keys' rows of K, columns 32nd .. 32nd + 31
+      const uint16_t* dsb = &ds_lds[buf][td_row * kRowT + tr_col];
+      const uint16_t* kt = &k_lds[tk_row * kRowQ + 32 * nd + tr_col];
       // operands of reduction step kk: dS row chunk and the transposed K block; loaded two
       // steps ahead of their product (the fences keep that order)
       bf16x8 da[2], bk[2];
       auto ld = [&](int kk) {
-        const int kb = (32 * (kk >> 1) + 8 * (kk & 1)) * kRowQ;
-        da[kk & 1] = tr_read(&dsb[16 * kk * kRowT], &dsb[(16 * kk + 4) * kRowT]);
-        bk[kk & 1] = tr_read(&kt0[kb], &kt1[kb]);
+        const int db = (32 * (kk >> 1) + 4 * (kk & 1)) * kRowT;
+        const int kb = 16 * kk * kRowQ;
+        da[kk & 1] = tr_read(&dsb[db], &dsb[db + 2 * kRowT]);
+        bk[kk & 1] = tr_read(&kt[kb], &kt[kb + 2 * kRowQ]);
       };
       ld(0);
       ld(1);
@@ -391,21 +409,21 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
         // S and dP, interleaved; the scheduling groups keep the LDS reads two reduction steps
         // ahead of the products that use them
         f32x16 s_acc = f32x16{}, dp_acc = f32x16{};
-        const uint16_t* qrow = &qb[l32 * kRowQ + 8 * hi];
-        const uint16_t* orow = &ob[l32 * kRowQ + 8 * hi];
-        const uint16_t* krw = &k_lds[krow(key_w) * kRowQ + 8 * hi];
+        const uint16_t* qrw = &qb[q_row * kRowQ + 8 * hi];
+        const uint16_t* orw = &ob[q_row * kRowQ + 8 * hi];
+        const uint16_t* krw = &k_lds[qrow(key_w) * kRowQ + 8 * hi];
         // S and dP interleaved; operands loaded two reduction steps ahead of their products.
         // A ninth step multiplies the padding chunk of the Q and dO rows by ones3, which adds
         // -L2/c to S and -D to dP: then P = exp2(c S) and dS = P dP directly.
         bf16x8 qa[2], kb2[2], oa[2];
         auto ld = [&](int kk) {
           if (kk < D / 16) {
-            qa[kk & 1] = *(const bf16x8*)&qrow[16 * kk];
+            qa[kk & 1] = *(const bf16x8*)&qrw[16 * kk];
             kb2[kk & 1] = *(const bf16x8*)&krw[16 * kk];
-            oa[kk & 1] = *(const bf16x8*)&orow[16 * kk];
+            oa[kk & 1] = *(const bf16x8*)&orw[16 * kk];
           } else {
-            qa[kk & 1] = *(const bf16x8*)&qb[l32 * kRowQ + D];
-            oa[kk & 1] = *(const bf16x8*)&ob[l32 * kRowQ + D];
+            qa[kk & 1] = *(const bf16x8*)&qb[q_row * kRowQ + D];
+            oa[kk & 1] = *(const bf16x8*)&ob[q_row * kRowQ + D];
           }
         };
         ld(0);
@@ -482,8 +500,8 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
               // with dropout Z = 256/k where the element's byte is below k, else 0
               const float zf = XD ? (((zw[c] >> (8 * e)) & 0xFFu) < (unsigned)p.drop_k ? p.drop_scale : 0.f) : 1.f;
               const float dsv = XD ? pv * (dp_acc[r] * zf - d4[e]) : pv * dp_acc[r];
-              // reduction slot of (c, e) in step c/2: the Q/dO rows the transposing reads give
-              const int slot = 2 * (c & 1) + (e >> 1) + 4 * (e & 1);
+              // reduction slot of (c, e) in step c/2: read c % 2, row e of the transposing reads
+              const int slot = 4 * (c & 1) + e;
               pa[c >> 1][slot] = (__bf16)(XD ? pv * zf : pv);
               sa[c >> 1][slot] = (__bf16)dsv;
               ds32[r] = dsv;
@@ -491,8 +509,8 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
           }
         }
         // dV += P^T dO, dK += dS^T Q: reduction step t covers queries 16t .. 16t + 15; lane
-        // half hi takes rows 16t + 4hi + {0, 2, 8, 10} and then + 1.  Operand pairs are loaded
-        // two products ahead; the dS exchange runs under the first products.
+        // half hi takes query rows 16t + 4hi + {0..3} and then + 8.  Operand pairs are loaded
+        // two products ahead; the dS write runs under the first products.
         bf16x8 bo[2], bq[2];
         // per-lane bases; each read adds a constant, which becomes the instruction's offset
         const uint16_t* obl = &ob[tq_row * kRowQ + tr_col];
@@ -511,7 +529,7 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
           dk_acc[i % NB] = mfma(sa[i / NB], bq[i & 1], dk_acc[i % NB]);
           __builtin_amdgcn_sched_barrier(0);
           if (i + 2 < 2 * NB) ldv(i + 2);
-          if (i == 0) write_dst(ds_lds[buf], ds32, key_w, hi);
+          if (i == 0) write_dst(ds_lds[buf], ds32, dslot(key_w), hi);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -526,27 +544,76 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
     // the last step's dQ
     if (n1 > n0 && dq_turn(n1 - 1 - n0)) dq_step((n1 - 1 - n0) & 1, rdq, dc.r);
 
-    // ---- epilogue: dK = scale * dK_acc, dV = dV_acc as bf16, or this part's fp32 partials ----
+    // ---- epilogue: dK = scale * dK_acc, dV = dV_acc as bf16, or this part's fp32 partials.
+    // Each lane holds one column of 16 keys, so the values go through LDS: the wave writes a
+    // pass (2D bytes per key: all of dK or dV in bf16, or D/2 fp32 columns of a partial) into
+    // its 32 rows of the K tile, row m for the key of M index m, and reads it back in 16-byte
+    // chunks, 16 lanes per row, so that each buffer store covers four keys' contiguous runs.
+    // The stores' resources span the tile's nk rows, so the range check drops keys past the
+    // tile end.
+    __syncthreads();  // the last dQ products have read the K tile
+    {
+      constexpr int kChunks = D / 8;  // 16-byte chunks per row and pass
+      // the lane index again, from mbcnt: per-lane values derived here are not merged with the
+      // ones computed before the step loop, so they do not stay live (and spill) across it
+      const int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+      uint16_t* ep = &k_lds[32 * wave_s * kRowQ];
+      // write: lane (l32, hi) holds M indices 8c + 4hi + e; read: lane l takes row 4i + l / 16
+      // (i = 0 .. 32 * kChunks / 64 - 1), chunk l % 16 (D = 128) or rows 8i + l / 8, chunk l % 8
+      uint16_t* ep_w = ep + 4 * (ln >> 5) * kRowQ + (ln & 31);
+      constexpr int kRowsPerRead = 64 / kChunks;
+      const int rd_row = ln / kChunks, rd_c = ln % kChunks;
+      const uint16_t* ep_r = ep + rd_row * kRowQ + 8 * rd_c;
+      // key of read row kRowsPerRead * i + rd_row: kmap is linear, key = kmap(rd_row) + kmap(kRowsPerRead * i)
+      const int kl_lane = wave_s * 32 + kmap(rd_row);
+      const auto pass = [&](const int ps, const bool part_out) {
+        const bool is_v = part_out ? ps >= 2 : ps == 1;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int kl = wave * 32 + kmap(8 * (r >> 2) + 4 * hi + (r & 3));
-      if (kl < nk) {
-        const int64_t krow = sg.k_row0 + key0 + kl;
-        if (p.kv_parts == 1) {
-          uint16_t* dkp = p.dk + elem_off(p.dk_s, group, b, krow, g) + l32;
-          uint16_t* dvp = p.dv + elem_off(p.dv_s, group, b, krow, g) + l32;
+        for (int r = 0; r < 16; ++r) {
+          const int mo = (8 * (r >> 2) + (r & 3)) * kRowQ;
+          if (!part_out) {
 #pragma unroll
-          for (int n = 0; n < D / 32; ++n) dkp[32 * n] = to_bf16_bits(dk_acc[n][r] * p.scale);
+            for (int n = 0; n < NB; ++n) ep_w[mo + 32 * n] = to_bf16_bits(is_v ? dv_acc[n][r] : dk_acc[n][r] * p.scale);
+          } else {
 #pragma unroll
-          for (int n = 0; n < D / 32; ++n) dvp[32 * n] = to_bf16_bits(dv_acc[n][r]);
-        } else {
-          const int64_t prow = sg.kws_row0 + key0 + kl;
-          float* pp = p.dkv_acc + (((int64_t)part * p.Hkv + g) * p.rows_k + prow) * (2 * D) + l32;
-#pragma unroll
-          for (int n = 0; n < D / 32; ++n) __builtin_nontemporal_store(dk_acc[n][r], &pp[32 * n]);
-#pragma unroll
-          for (int n = 0; n < D / 32; ++n) __builtin_nontemporal_store(dv_acc[n][r], &pp[D + 32 * n]);
+            for (int n2 = 0; n2 < NB / 2; ++n2) {
+              const int n = (ps & 1) * (NB / 2) + n2;
+              *(float*)&ep[(4 * (ln >> 5) * kRowQ + mo) + 2 * (32 * n2 + (ln & 31))] = is_v ? dv_acc[n][r] : dk_acc[n][r];
+            }
+          }
         }
+        __amdgpu_buffer_rsrc_t rs;
+        int row_bytes, col_bytes;
+        if (!part_out) {
+          const int64_t* st = is_v ? p.dv_s : p.dk_s;
+          uint16_t* base = (is_v ? p.dv : p.dk) + elem_off(st, group, b, sg.k_row0 + key0, g);
+          row_bytes = (int)st[1] * 2;
+          col_bytes = 0;
+          rs = buffer_rsrc(base, (uint32_t)((nk - 1) * (int)st[1] + D) * 2u);
+        } else {
+          float* base = p.dkv_acc + (((int64_t)part * p.Hkv + g) * p.rows_k + sg.kws_row0 + key0) * (2 * D);
+          row_bytes = 2 * D * 4;
+          col_bytes = ((is_v ? D : 0) + (ps & 1) * (D / 2)) * 4;
+          rs = buffer_rsrc(base, (uint32_t)nk * (uint32_t)row_bytes);
+        }
+        const int voff = kl_lane * row_bytes + col_bytes + 16 * rd_c;
+#pragma unroll
+        for (int i = 0; i < 32 * kChunks / 64; ++i) {
+          const u32x4 x = *(const u32x4*)&ep_r[kRowsPerRead * i * kRowQ];
+          if (part_out)
+            __builtin_amdgcn_raw_buffer_store_b128(x, rs, voff + kmap(kRowsPerRead * i) * row_bytes, 0, kPartialPolicy);
+          else
+            __builtin_amdgcn_raw_buffer_store_b128(x, rs, voff + kmap(kRowsPerRead * i) * row_bytes, 0, 0);
+        }
+      };
+      if (p.kv_parts == 1) {
+        pass(0, false);
+        pass(1, false);
+      } else {
+        pass(0, true);
+        pass(1, true);
+        pass(2, true);
+        pass(3, true);
       }
     }
     if (nblk > 0) {
