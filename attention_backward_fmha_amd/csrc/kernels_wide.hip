@@ -53,6 +53,15 @@ constexpr int kRowT = 36;    // dS^T rows (one per key): 32 bf16 + 4
 
 __device__ __forceinline__ int bit_of(int x, int i) { return (x >> i) & 1; }
 
+// The lane index, read again where it is used: a volatile asm statement is not hoisted out of
+// the key-tile loop, so per-lane addresses derived from it are computed per tile instead of
+// being kept live (and spilled) across the step loop.
+__device__ __forceinline__ int lane_here() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 // LDS row of query row (or key) m of a step: bits m0..m4 go to r0 = m3, r1 = m2, r2 = m0,
 // r3 = m1, r4 = m4.  The dV/dK products' transposing reads of lane half hi, reduction step t
 // and read h take query rows 16t + 8h + 4hi + {0..3}, i.e. rows 16t + h + 2hi + 4 * {0..3};
@@ -173,28 +182,43 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
     const int hi_d = (int)min(hi64, sg.lk);
     const unsigned span = (unsigned)(hi_d - lo_d);
 
-    // K tile -> LDS (D / 16 chunks per thread), the wave's V rows -> registers (B operand of dP)
+    // ---- prologue.  The tile's loads are all issued before the first wait: the K tile (D / 16
+    // chunks per thread, into registers), then step n0's Q and dO rows (below), then the wave's
+    // V rows (the B operand of dP, kept in registers); the K chunks and the first step's rows
+    // then go to LDS.  (Loads and LDS writes taken one chunk at a time cost one HBM round trip
+    // per chunk, about 25k cycles per tile.)
+    const int ln_t = lane_here();
+    const int tid_t = 64 * wave_s + ln_t;
+    u32x4 kx[D / 16];
     {
       const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(
           p.k + elem_off(p.k_s, group, b, sg.k_row0 + key0, g), (uint32_t)((nk - 1) * (int)p.k_s[1] + D) * 2u);
       const int ks1 = (int)p.k_s[1];
 #pragma unroll
       for (int i = 0; i < D / 16; ++i) {
-        const int id = tid + 512 * i;
+        const int id = tid_t + 512 * i;
         const int kr = id / (D / 8), c = id % (D / 8);
-        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rk, (kr * ks1 + c * 8) * 2, 0, 0);
-        *(u32x4*)&k_lds[qrow(kr) * kRowQ + c * 8] = x;
+        kx[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, (kr * ks1 + c * 8) * 2, 0, 0);
       }
     }
     bf16x8 vw[D / 16];
-    {
+    const auto load_v = [&]() {
       const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(
           p.v + elem_off(p.v_s, group, b, sg.k_row0 + key0, g), (uint32_t)((nk - 1) * (int)p.v_s[1] + D) * 2u);
       const int vs1 = (int)p.v_s[1];
+      const int kv = 32 * wave_s + kmap(ln_t & 31);
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk)
-        vw[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, (key_w * vs1 + 16 * kk + 8 * hi) * 2, 0, 0));
-    }
+        vw[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, (kv * vs1 + 16 * kk + 8 * (ln_t >> 5)) * 2, 0, 0));
+    };
+    const auto store_k = [&]() {
+#pragma unroll
+      for (int i = 0; i < D / 16; ++i) {
+        const int id = tid_t + 512 * i;
+        const int kr = id / (D / 8), c = id % (D / 8);
+        *(u32x4*)&k_lds[qrow(kr) * kRowQ + c * 8] = kx[i];
+      }
+    };
     f32x16 dk_acc[D / 32], dv_acc[D / 32];
 #pragma unroll
     for (int n = 0; n < D / 32; ++n) {
@@ -388,8 +412,10 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
     };
 
     Cur cc = pc;  // the step being computed
+    if (n1 > n0) load_step();
+    load_v();
+    store_k();
     if (n1 > n0) {
-      load_step();
       store_step(0);
       load_step();
     }
