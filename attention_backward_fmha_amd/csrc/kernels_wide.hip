@@ -160,7 +160,9 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
   const float inv_c = 1.f / p.scale_log2;
   // B operand of ones in reduction slots 0..2 of lane half 0 (bf16 1.0 = 0x3F80), zeros in
   // half 1: the product with a padding chunk adds its three parts
-  const bf16x8 ones3 = __builtin_bit_cast(bf16x8, u32x4{hi ? 0u : 0x3F803F80u, hi ? 0u : 0x3F80u, 0u, 0u});
+  // (at D = 128 it is built where it is used instead, from a lane index read there, so that
+  // it does not take four registers across the step loop)
+  const bf16x8 ones3_kept = __builtin_bit_cast(bf16x8, u32x4{hi ? 0u : 0x3F803F80u, hi ? 0u : 0x3F80u, 0u, 0u});
   const int qs1 = (int)p.q_s[1];
   const int os1 = (int)p.do_s[1];
 
@@ -455,8 +457,13 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
         };
         ld(0);
         ld(1);
+        bf16x8 ones3 = ones3_kept;
 #pragma unroll
         for (int kk = 0; kk <= D / 16; ++kk) {
+          if (D == 128 && kk == D / 16) {
+            const bool h0 = lane_here() < 32;
+            ones3 = __builtin_bit_cast(bf16x8, u32x4{h0 ? 0x3F803F80u : 0u, h0 ? 0x3F80u : 0u, 0u, 0u});
+          }
           s_acc = mfma(qa[kk & 1], kk < D / 16 ? kb2[kk & 1] : ones3, s_acc);
           dp_acc = mfma(oa[kk & 1], kk < D / 16 ? vw[kk] : ones3, dp_acc);
           __builtin_amdgcn_sched_barrier(0);
@@ -474,9 +481,12 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
         // of 4 row bytes, and the quad trades them
         unsigned zw[4] = {0u, 0u, 0u, 0u};
         if constexpr (XD) {
-          const unsigned kpos = (unsigned)(key0 + key_w);
-          const unsigned t = (unsigned)(lane & 1) | ((unsigned)(lane >> 4) & 1u) << 1;
-          unsigned w[4] = {kpos >> 2, (unsigned)(q0 + 8 * (int)t + 4 * hi) >> 2,
+          // at D = 128 the lane values come from a lane index read here, so that they do not
+          // stay live across the step loop (which spilled registers reloaded in every step)
+          const int ln = D == 128 ? lane_here() : lane;
+          const unsigned kpos = (unsigned)(key0 + 32 * wave_s + kmap(ln & 31));
+          const unsigned t = (unsigned)(ln & 1) | ((unsigned)(ln >> 4) & 1u) << 1;
+          unsigned w[4] = {kpos >> 2, (unsigned)(q0 + 8 * (int)t + 4 * (ln >> 5)) >> 2,
                            (unsigned)(b * p.Hq + cc.h), p.offset_lo};
           // the key enters each step through an empty asm statement, so that the compiler
           // derives the round keys in the step (two scalar adds per round) instead of keeping
@@ -494,11 +504,11 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
           }
           {
             const unsigned pu = t ^ 2u;
-            rr[2] = xor16(sel4(tw, ((pu >> 1) & 1u) | ((pu & 1u) << 1)), lane);
+            rr[2] = xor16(sel4(tw, ((pu >> 1) & 1u) | ((pu & 1u) << 1)), ln);
           }
           {
             const unsigned pu = t ^ 3u;
-            rr[3] = xor16(xor1(sel4(tw, ((pu >> 1) & 1u) | ((pu & 1u) << 1))), lane);
+            rr[3] = xor16(xor1(sel4(tw, ((pu >> 1) & 1u) | ((pu & 1u) << 1))), ln);
           }
 #pragma unroll
           for (int c = 0; c < 4; ++c) zw[c] = sel4(rr, t ^ (unsigned)c);
