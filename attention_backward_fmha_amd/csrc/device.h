@@ -83,6 +83,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 // 8192-token ragged GQA one 0.556 -> 0.506 ms.
 constexpr int kPartialPolicy = 2;
 
+// The lane index, read again where it is used: a volatile asm statement is not hoisted out of
+// a loop, so per-lane values derived from it are computed where they are needed instead of
+// being kept live (and spilled) across the main kernels' step loops.
+__device__ __forceinline__ int lane_here() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }

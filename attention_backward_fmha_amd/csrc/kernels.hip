@@ -838,28 +838,69 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(const KParams p) {
   }
 
   // ---- epilogue: dK = scale * dK_acc, dV = dV_acc as bf16 (one part), or this part's fp32
-  // partials (row kws_row0 + key of [part][g][rows_k][d_qk + d_v], unscaled) ----
-  // result row i of dK/dV is the key of lane i, 32*wave + kmap(i)
+  // partials (row kws_row0 + key of [part][g][rows_k][d_qk + d_v], unscaled).  Each lane holds
+  // one column of 16 keys (result row i is the key 32*wave + kmap(i)), so the values go through
+  // LDS: the wave writes a pass (one tensor in bf16, or half of its columns in fp32: at most
+  // 2*d_qk bytes per key) into its 32 rows of the K tile and reads it back in 16-byte chunks,
+  // which the buffer stores write as contiguous runs of each key's row; the stores' resources
+  // span the tile's nk rows, so the range check drops keys past the tile end.  (2-byte stores
+  // from the accumulator layout took about 35 cycles each.) ----
+  __syncthreads();  // the last dQ products have read the K tile
+  {
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    const int ln = lane_here();
+    uint16_t* ep = &k_lds[32 * wave_s * KS];
+    const auto pass = [&](const int which, const int half, const bool part_out) {
+      const int nbt = which == 0 ? DQK / 32 : DV / 32;  // 32-column blocks of the tensor
+      const int ncol = part_out ? nbt / 2 : nbt;        // ... in this pass
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int kl = wave * 32 + kmap(8 * (r >> 2) + 4 * hi + (r & 3));
-    if (kl < nk) {
-      const int64_t krow = sg.k_row0 + key0 + kl;
-      if (p.kv_parts == 1) {
-        uint16_t* dkp = p.dk + elem_off(p.dk_s, group, b, krow, g) + l32;
-        uint16_t* dvp = p.dv + elem_off(p.dv_s, group, b, krow, g) + l32;
+      for (int r = 0; r < 16; ++r) {
+        const int m = 8 * (r >> 2) + 4 * (ln >> 5) + (r & 3);
 #pragma unroll
-        for (int n = 0; n < DQK / 32; ++n) dkp[32 * n] = to_bf16_bits(dk_acc[n][r] * p.scale);
-#pragma unroll
-        for (int n = 0; n < DV / 32; ++n) dvp[32 * n] = to_bf16_bits(dv_acc[n][r]);
-      } else {
-        const int64_t prow = sg.kws_row0 + key0 + kl;
-        float* pp = p.dkv_acc + (((int64_t)part * p.Hkv + g) * p.rows_k + prow) * (DQK + DV) + l32;
-#pragma unroll
-        for (int n = 0; n < DQK / 32; ++n) __builtin_nontemporal_store(dk_acc[n][r], &pp[32 * n]);
-#pragma unroll
-        for (int n = 0; n < DV / 32; ++n) __builtin_nontemporal_store(dv_acc[n][r], &pp[DQK + 32 * n]);
+        for (int n2 = 0; n2 < ncol; ++n2) {
+          const int n = half * ncol + n2;
+          const float v = which == 0 ? dk_acc[n][r] : dv_acc[n][r];
+          if (!part_out)
+            ep[m * KS + 32 * n2 + (ln & 31)] = to_bf16_bits(which == 0 ? v * p.scale : v);
+          else
+            *(float*)&ep[m * KS + 2 * (32 * n2 + (ln & 31))] = v;
+        }
       }
+      __amdgpu_buffer_rsrc_t rs;
+      int row_bytes, col_bytes;
+      if (!part_out) {
+        const int64_t* st = which == 0 ? p.dk_s : p.dv_s;
+        uint16_t* base = (which == 0 ? p.dk : p.dv) + elem_off(st, group, b, sg.k_row0 + key0, g);
+        row_bytes = (int)st[1] * 2;
+        col_bytes = 0;
+        rs = buffer_rsrc(base, (uint32_t)((nk - 1) * (int)st[1] + (which == 0 ? DQK : DV)) * 2u);
+      } else {
+        float* base = p.dkv_acc + (((int64_t)part * p.Hkv + g) * p.rows_k + sg.kws_row0 + key0) * (DQK + DV);
+        row_bytes = (DQK + DV) * 4;
+        col_bytes = ((which == 0 ? 0 : DQK) + half * ncol * 32) * 4;
+        rs = buffer_rsrc(base, (uint32_t)nk * (uint32_t)row_bytes);
+      }
+      const int nch = part_out ? 8 * ncol : 4 * nbt;  // 16-byte chunks per row in this pass
+#pragma unroll
+      for (int i = 0; i < nch / 2; ++i) {  // 32 rows * nch chunks over 64 lanes
+        const int id = ln + 64 * i;
+        const int row = id / nch, c = id - row * nch;
+        const u32x4 x = *(const u32x4*)&ep[row * KS + 8 * c];
+        const int voff = (32 * wave_s + kmap(row)) * row_bytes + col_bytes + 16 * c;
+        if (part_out)
+          __builtin_amdgcn_raw_buffer_store_b128(x, rs, voff, 0, kPartialPolicy);
+        else
+          __builtin_amdgcn_raw_buffer_store_b128(x, rs, voff, 0, 0);
+      }
+    };
+    if (p.kv_parts == 1) {
+      pass(0, 0, false);
+      pass(1, 0, false);
+    } else {
+      pass(0, 0, true);
+      pass(0, 1, true);
+      pass(1, 0, true);
+      pass(1, 1, true);
     }
   }
   if (nblk > 0) {

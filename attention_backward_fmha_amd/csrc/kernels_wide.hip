@@ -53,15 +53,6 @@ constexpr int kRowT = 36;    // dS^T rows (one per key): 32 bf16 + 4
 
 __device__ __forceinline__ int bit_of(int x, int i) { return (x >> i) & 1; }
 
-// The lane index, read again where it is used: a volatile asm statement is not hoisted out of
-// the key-tile loop, so per-lane addresses derived from it are computed per tile instead of
-// being kept live (and spilled) across the step loop.
-__device__ __forceinline__ int lane_here() {
-  int l;
-  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
-  return l;
-}
-
 // LDS row of query row (or key) m of a step: bits m0..m4 go to r0 = m3, r1 = m2, r2 = m0,
 // r3 = m1, r4 = m4.  The dV/dK products' transposing reads of lane half hi, reduction step t
 // and read h take query rows 16t + 8h + 4hi + {0..3}, i.e. rows 16t + h + 2hi + 4 * {0..3};
