@@ -88,7 +88,7 @@ __device__ __forceinline__ void write_dst(uint16_t* dst, const float (&d)[16], i
     *(u32x2*)&dst[row * kRowT + 8 * u + 4 * hi] = u32x2{pack_bf16(d[4 * u], d[4 * u + 1]), pack_bf16(d[4 * u + 2], d[4 * u + 3])};
 }
 
-template <int D, int DQM, bool XD>
+template <int D, int DQM, bool XD, bool RB>
 __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
   static_assert(D == 128 || D == 64, "head dims of the wide layout");
   constexpr int TN = 256, TM = 32, kRowQ = D + 8, NB = D / 32;  // NB: 32-column blocks
@@ -98,6 +98,13 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t ds_lds[2][TN * kRowT];      // [buffer] dS^T
   // dropout: D of the step's rows per buffer (with dropout D is not folded into dP)
   __shared__ __attribute__((aligned(16))) float dd_lds[XD ? 2 * TM : 4];
+  // deterministic mode with items of several key tiles (RB): the item's earlier partial of the
+  // block whose dQ a wave computes next, loaded straight into LDS one step ahead (a 4 KB slot
+  // for each of waves 0-3; it does not fit beside the dropout arrays at D = 128, which then load
+  // it at the start of the products).  Items of one tile have nothing to read back.
+  static_assert(DET || !RB, "read-back is a deterministic-mode matter");
+  constexpr bool PV = RB && (D == 64 || !XD);
+  __shared__ __attribute__((aligned(16))) float pv_lds[PV ? 4 * 1024 : 4];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -337,10 +344,14 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
     // all four (one 32-column tile each); D = 64, waves 0-1 and 2-3 taking turns
     auto dq_turn = [&](int s) { return D == 128 ? wave_s < 4 : (wave_s >> 1) == (s & 1); };
     auto dq_step = [&](int buf, const __amdgpu_buffer_rsrc_t& rdq, int r) {
-      // deterministic mode: the partial an earlier tile of the item left for this block is
-      // read back first, so the products below hide the load latency
-      u32x4 prev[4];
-      if (DET) {
+      // deterministic mode: the partial an earlier tile of the item left for this block, from
+      // the wave's LDS slot (loaded a step ahead, below) or read back first, so that the
+      // products below hide the load latency
+      u32x4 prev[4] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
+      if constexpr (PV) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) prev[u] = *(const u32x4*)&pv_lds[(wave_s & 3) * 1024 + u * 256 + lane * 4];
+      } else if constexpr (RB) {
         const int qbn = r / TM;
         const __amdgpu_buffer_rsrc_t rprev = qbn >= w_lo && qbn <= w_hi ? rdq : buffer_rsrc(p.dq_acc, 0u);
 #pragma unroll
@@ -420,6 +431,23 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
       const int buf = (n - n0) & 1;
       // the pending dQ of step n-1, by the half whose turn it is
       if (n > n0 && dq_turn(n - 1 - n0)) dq_step(buf ^ 1, rdq, dc.r);
+      // the wave that computes step n's dQ (in the next iteration) loads the item's earlier
+      // partial of step n's block into its slot now: direct-to-LDS loads, 16 bytes per lane,
+      // lane l's at 16l of each kilobyte (a block the item has not written reads as zeros)
+      if constexpr (PV) {
+        if (dq_turn(n - n0)) {
+          // (a copy of the cursor's row: with the cursor field itself in the offset operand, the
+          // host pass of this compiler left the kernel's launch stub undefined)
+          const int r_pv = cc.r;
+          const int qbn = r_pv / TM;
+          const __amdgpu_buffer_rsrc_t rpv = qbn >= w_lo && qbn <= w_hi ? dq_rsrc(cc.h) : buffer_rsrc(p.dq_acc, 0u);
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rpv, (__attribute__((address_space(3))) void*)&pv_lds[(wave_s & 3) * 1024 + u * 256], 16,
+                (r_pv * D + nd * 1024 + u * 256) * 4 + lane * 16, 0, 0, kPartialPolicy);
+        }
+      }
       const int q0 = cc.r;
       // ---- S, dP, P, dS, dV, dK of step n ----
       {
@@ -653,10 +681,11 @@ __global__ __launch_bounds__(512) void k_bwd_wide(const KParams p) {
 }
 
 template <int D, bool XD>
-void launch_wide_t(int mode, const KParams& kp, dim3 grid, hipStream_t stream) {
-  if (mode == 1) hipLaunchKernelGGL((k_bwd_wide<D, 1, XD>), grid, dim3(512), 0, stream, kp);
-  else if (mode == 2) hipLaunchKernelGGL((k_bwd_wide<D, 2, XD>), grid, dim3(512), 0, stream, kp);
-  else hipLaunchKernelGGL((k_bwd_wide<D, 0, XD>), grid, dim3(512), 0, stream, kp);
+void launch_wide_t(int mode, bool read_back, const KParams& kp, dim3 grid, hipStream_t stream) {
+  if (mode == 1 && read_back) hipLaunchKernelGGL((k_bwd_wide<D, 1, XD, true>), grid, dim3(512), 0, stream, kp);
+  else if (mode == 1) hipLaunchKernelGGL((k_bwd_wide<D, 1, XD, false>), grid, dim3(512), 0, stream, kp);
+  else if (mode == 2) hipLaunchKernelGGL((k_bwd_wide<D, 2, XD, false>), grid, dim3(512), 0, stream, kp);
+  else hipLaunchKernelGGL((k_bwd_wide<D, 0, XD, false>), grid, dim3(512), 0, stream, kp);
 }
 
 }  // namespace
@@ -664,12 +693,13 @@ void launch_wide_t(int mode, const KParams& kp, dim3 grid, hipStream_t stream) {
 hipError_t launch_main_wide(const Plan& plan, const KParams& kp, dim3 grid, hipStream_t stream) {
   const int mode = plan.deterministic ? 1 : (plan.dq_bf16 ? 2 : 0);
   const bool drop = plan.drop_k < 256;
+  const bool rb = plan.tiles_per_item > 1;  // an item's later tiles add to its earlier partials
   if (plan.d_qk == 64) {
-    if (drop) launch_wide_t<64, true>(mode, kp, grid, stream);
-    else launch_wide_t<64, false>(mode, kp, grid, stream);
+    if (drop) launch_wide_t<64, true>(mode, rb, kp, grid, stream);
+    else launch_wide_t<64, false>(mode, rb, kp, grid, stream);
   } else {
-    if (drop) launch_wide_t<128, true>(mode, kp, grid, stream);
-    else launch_wide_t<128, false>(mode, kp, grid, stream);
+    if (drop) launch_wide_t<128, true>(mode, rb, kp, grid, stream);
+    else launch_wide_t<128, false>(mode, rb, kp, grid, stream);
   }
   return hipGetLastError();
 }
