@@ -120,6 +120,27 @@ def test_backward_with_dropout_matches_oracle(case, kernel, mode):
     assert_grads_close(got, ref, sq, sk)
 
 
+WIDE_CASES = [c for c in CASES if c[3][0] in (64, 128)]
+
+
+@pytest.mark.parametrize("case", WIDE_CASES, ids=[c[0] for c in WIDE_CASES])
+def test_dropout_items_of_two_tiles_deterministic(case):
+    """Deterministic items of two key tiles with dropout, wide layout: the second tile reads
+    back the first one's dQ partial (a register load at d = 128, where the LDS slots of the
+    read-back do not fit beside the dropout arrays; an LDS slot at d = 64)."""
+    import oracle
+    import attention_backward_fmha_amd as F
+    x, sq, sk, scale, mask, window = _inputs(case, 9103)
+    drop = (0.15, 7, 3)
+    kw = dict(scale=scale, mask_type=mask, window_left=window[0], window_right=window[1],
+              seqstart_q=sq, seqstart_k=sk, dropout=drop)
+    o, lse = oracle.forward(x["q"], x["k"], x["v"], **kw)
+    ref = oracle.backward(x["q"], x["k"], x["v"], x["do"], **kw)
+    got = _run(x, o, lse, scale=scale, mask=mask, window=window, sq=sq, sk=sk, deterministic=True,
+               dq_acc_dtype="fp32", drop=drop, tune=dict(kernel=F.KERNEL_WIDE, tiles_per_item=2))
+    assert_grads_close(got, ref, sq, sk)
+
+
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_forward_with_dropout_matches_oracle(case):
     import torch
