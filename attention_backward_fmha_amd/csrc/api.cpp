@@ -167,16 +167,13 @@ int fmha_bwd_prepare_workspace(const fmha_bwd_args* args, void* ws, size_t bytes
   st = check_ws(p, ws, bytes, "prepare_workspace");
   if (st != FMHA_OK) return st;
   log_plan(p, "prepare_workspace");
-  st = hip_status(fmha::launch_header((uint64_t*)ws, fmha::kWorkspaceMagic, p.fingerprint, (hipStream_t)stream),
-                  "prepare_workspace");
-  if (st != FMHA_OK) return st;
-  if (p.needs_zero) {
-    st = hip_status(fmha::launch_zero((float*)((char*)ws + p.dq_acc_offset), p.dq_acc_bytes / 4,
-                                      (hipStream_t)stream),
+  if (p.needs_zero)
+    return hip_status(fmha::launch_zero_header((float*)((char*)ws + p.dq_acc_offset), p.dq_acc_bytes / 4,
+                                               (uint64_t*)ws, fmha::kWorkspaceMagic, p.fingerprint,
+                                               (hipStream_t)stream),
+                      "prepare_workspace");
+  return hip_status(fmha::launch_header((uint64_t*)ws, fmha::kWorkspaceMagic, p.fingerprint, (hipStream_t)stream),
                     "prepare_workspace");
-    if (st != FMHA_OK) return st;
-  }
-  return FMHA_OK;
 }
 
 int fmha_bwd_run_stages(const fmha_bwd_args* args, void* ws, size_t bytes, int stages, void* stream) {

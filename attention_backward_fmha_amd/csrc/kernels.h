@@ -72,7 +72,9 @@ hipError_t launch_main_wide(const Plan& plan, const KParams& kp, dim3 grid, hipS
 hipError_t launch_reduce(const Plan& plan, const KParams& kp, hipStream_t stream);
 hipError_t launch_dbias(const Plan& plan, const KParams& kp, hipStream_t stream);
 hipError_t launch_dkv_reduce(const Plan& plan, const KParams& kp, hipStream_t stream);
-hipError_t launch_zero(float* ptr, int64_t count, hipStream_t stream);
+// Zeroes count floats at ptr and writes the workspace header (as launch_header) in one launch.
+hipError_t launch_zero_header(float* ptr, int64_t count, uint64_t* ws, uint64_t magic, uint64_t fingerprint,
+                              hipStream_t stream);
 // Workspace header: magic value and plan fingerprint at ws[0], ws[1] (one vector store each).
 hipError_t launch_header(uint64_t* ws, uint64_t magic, uint64_t fingerprint, hipStream_t stream);
 constexpr uint64_t kWorkspaceMagic = 0x31445742414d4846ull;  // bytes "FHMABWD1"

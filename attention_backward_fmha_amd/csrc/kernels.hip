@@ -1558,10 +1558,21 @@ __global__ __launch_bounds__(64) void k_header(uint64_t* ws, uint64_t magic, uin
   }
 }
 
-__global__ __launch_bounds__(256) void k_zero(float* ptr, int64_t n4) {
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride)
-    ((f32x4*)ptr)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+// Zeroes n4 16-byte chunks (four per thread, each store instruction one contiguous 4 KiB run
+// of the work group) and writes the workspace header from one lane, so the atomic modes'
+// prepare step is a single launch.
+__global__ __launch_bounds__(256) void k_zero(float* ptr, int64_t n4, uint64_t* ws, uint64_t magic,
+                                              uint64_t fingerprint) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    ws[0] = magic;
+    ws[1] = fingerprint;
+  }
+  const int64_t stride = (int64_t)gridDim.x * 1024;
+  for (int64_t i0 = (int64_t)blockIdx.x * 1024 + threadIdx.x; i0 < n4; i0 += stride) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (i0 + 256 * j < n4) ((f32x4*)ptr)[i0 + 256 * j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 }
 
 }  // namespace
@@ -1707,12 +1718,13 @@ hipError_t launch_header(uint64_t* ws, uint64_t magic, uint64_t fingerprint, hip
   return hipGetLastError();
 }
 
-hipError_t launch_zero(float* ptr, int64_t count, hipStream_t stream) {
-  if (count == 0) return hipSuccess;
+hipError_t launch_zero_header(float* ptr, int64_t count, uint64_t* ws, uint64_t magic, uint64_t fingerprint,
+                              hipStream_t stream) {
   const int64_t n4 = count / 4;  // the accumulator is a multiple of 4 floats (d_qk % 4 == 0)
-  int64_t blocks = (n4 + 255) / 256;
+  int64_t blocks = (n4 + 1023) / 1024;
+  if (blocks < 1) blocks = 1;
   if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(k_zero, dim3((unsigned)blocks), dim3(256), 0, stream, ptr, n4);
+  hipLaunchKernelGGL(k_zero, dim3((unsigned)blocks), dim3(256), 0, stream, ptr, n4, ws, magic, fingerprint);
   return hipGetLastError();
 }
 
