@@ -85,6 +85,8 @@ __device__ void order_work_groups(const KParams& p, int* key) {
   for (int r = threadIdx.x; r < n; r += blockDim.x) p.order[r] = key[r] & 2047;
 }
 
+constexpr int kDotRows = 64;  // rows of one query head per work group of k_dot
+
 template <int DV>
 __global__ __launch_bounds__(256) void k_dot(const KParams p) {
   // with a cost order, work group 0 builds it (dispatched first, it overlaps the others)
@@ -94,38 +96,52 @@ __global__ __launch_bounds__(256) void k_dot(const KParams p) {
     order_work_groups(p, key);
     return;
   }
+  // Work group = 64 consecutive rows of one query head, so the LSE reads and the D / scaled-LSE
+  // writes are contiguous runs; LPR lanes share a row, each pass covers RPP rows, and the
+  // loads of all passes are issued before the products.
   constexpr int LPR = DV / 8;
-  constexpr int RPB = 256 / LPR;
+  constexpr int RPP = 256 / LPR;
+  constexpr int NP = kDotRows / RPP;
   const int tid = threadIdx.x;
-  const int64_t r = (int64_t)blk * RPB + tid / LPR;  // r = row*Hq + h
   const int c8 = tid % LPR;
+  const int h = blk % p.Hq;
+  const int64_t row0 = (int64_t)(blk / p.Hq) * kDotRows + tid / LPR;
   const bool group = p.seqstart_q != nullptr;
-  const bool valid = r < p.rows_q * p.Hq;
-  float acc = 0.f;
-  float l2 = 0.f;
-  int64_t row = 0;
-  int h = 0;
-  if (valid) {
-    row = r / p.Hq;
-    h = (int)(r - row * p.Hq);
+  bf16x8 a[NP], o[NP];
+  int bs[NP];
+  int64_t trs[NP];
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    const int64_t row = row0 + j * RPP;
     int b = 0;
     int64_t trow = row;
     if (!group) {
       b = (int)(row / p.Sq);
       trow = row - (int64_t)b * p.Sq;
     }
-    if (c8 == 0)
-      l2 = p.lse[(group ? 0 : (int64_t)b * p.lse_s[0]) + (int64_t)h * p.lse_s[1] + trow] * kLog2e;
-    const bf16x8 a = *(const bf16x8*)(p.dout + elem_off(p.do_s, group, b, trow, h) + c8 * 8);
-    const bf16x8 o = *(const bf16x8*)(p.o + elem_off(p.o_s, group, b, trow, h) + c8 * 8);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc += (float)a[e] * (float)o[e];
+    bs[j] = b;
+    trs[j] = trow;
+    if (row < p.rows_q) {
+      a[j] = *(const bf16x8*)(p.dout + elem_off(p.do_s, group, b, trow, h) + c8 * 8);
+      o[j] = *(const bf16x8*)(p.o + elem_off(p.o_s, group, b, trow, h) + c8 * 8);
+    }
   }
 #pragma unroll
-  for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, LPR);
-  if (valid && c8 == 0) {
-    p.dsum[(int64_t)h * p.rows_q + row] = acc;
-    p.lse2[(int64_t)h * p.rows_q + row] = l2;
+  for (int j = 0; j < NP; ++j) {
+    const int64_t row = row0 + j * RPP;
+    const bool valid = row < p.rows_q;
+    float acc = 0.f;
+    if (valid) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc += (float)a[j][e] * (float)o[j][e];
+    }
+#pragma unroll
+    for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, LPR);
+    if (valid && c8 == 0) {
+      const float l2 = p.lse[(group ? 0 : (int64_t)bs[j] * p.lse_s[0]) + (int64_t)h * p.lse_s[1] + trs[j]] * kLog2e;
+      p.dsum[(int64_t)h * p.rows_q + row] = acc;
+      p.lse2[(int64_t)h * p.rows_q + row] = l2;
+    }
   }
 }
 
@@ -1580,10 +1596,9 @@ __global__ __launch_bounds__(256) void k_zero(float* ptr, int64_t n4, uint64_t* 
 hipError_t launch_dot(const Plan& plan, const KParams& kp, hipStream_t stream) {
   const int64_t rows = plan.rows_q * plan.Hq;
   if (rows == 0) return hipSuccess;
-  const int rpb = 256 / (plan.d_v / 8);
   // one more work group ranks the wide kernel's work groups when the plan orders them
   if (plan.order_n > 2048 || (plan.order_n > 0 && kp.order == nullptr)) return hipErrorInvalidValue;
-  const int64_t blocks = (rows + rpb - 1) / rpb + (plan.order_n > 0 ? 1 : 0);
+  const int64_t blocks = (plan.rows_q + kDotRows - 1) / kDotRows * plan.Hq + (plan.order_n > 0 ? 1 : 0);
   if (plan.d_v == 64) {
     hipLaunchKernelGGL(k_dot<64>, dim3((unsigned)blocks), dim3(256), 0, stream, kp);
   } else {
