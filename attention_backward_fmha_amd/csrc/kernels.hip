@@ -37,14 +37,14 @@ namespace {
 // tiles): the (query head, query block) pairs of its item's tiles, shared evenly by the
 // item's parts, plus a constant for the tile loads and the epilogue; 0 for a work group
 // whose segment has no such tile.
-__device__ int wide_steps(const KParams& p, int w) {
+__device__ int wide_steps(const KParams& p, const int* seqstart_q, const int* seqstart_k, int w) {
   const int nbh = p.Hkv * p.B;
   const int ip = w / nbh;
   const int item = ip / p.kv_parts;
   const int part = ip - item * p.kv_parts;
   const int b = (w - ip * nbh) / p.Hkv;
-  const int lq = p.seqstart_q[b + 1] - p.seqstart_q[b];
-  const int lk = p.seqstart_k[b + 1] - p.seqstart_k[b];
+  const int lq = seqstart_q[b + 1] - seqstart_q[b];
+  const int lk = seqstart_k[b + 1] - seqstart_k[b];
   const MaskGeom mg = mask_geom(p.mask_type, p.window_left, p.window_right, lq, lk);
   int steps = 0;
   for (int tsub = 0; tsub < p.tiles_per_item; ++tsub) {
@@ -58,25 +58,54 @@ __device__ int wide_steps(const KParams& p, int w) {
   return steps * (part + 1) / p.kv_parts - steps * part / p.kv_parts + 6;
 }
 
+constexpr int kOrderSegs = 1025;  // segment offsets staged in LDS for up to 1024 segments
+
 // The wide kernel's work groups (at most 2048) sorted by the key
 // (65535 - steps) * 2048 + w, i.e. most steps first and ties in grid order, with a bitonic
 // network in LDS; order[i] is the work group of rank i.  Run by the first work group of the D
 // stage, so it costs no launch of its own and overlaps that stage's memory traffic.
-__device__ void order_work_groups(const KParams& p, int* key) {
+__device__ void order_work_groups(const KParams& p, int* key, int* seg) {
   const int n = p.order_n;
   int N = 2;
   while (N < n) N <<= 1;
+  // the segment offsets come to LDS in one round of loads, not eight dependent ones per
+  // thread that would wait behind the stage's HBM stream
+  const int* sq = p.seqstart_q;
+  const int* sk = p.seqstart_k;
+  if (p.B < kOrderSegs) {
+    for (int i = threadIdx.x; i <= p.B; i += blockDim.x) {
+      seg[i] = sq[i];
+      seg[kOrderSegs + i] = sk[i];
+    }
+    __syncthreads();
+    sq = seg;
+    sk = seg + kOrderSegs;
+  }
   for (int w = threadIdx.x; w < N; w += blockDim.x)
-    key[w] = w < n ? ((65535 - min(wide_steps(p, w), 65535)) << 11) | w : 0x7fffffff;
+    key[w] = w < n ? ((65535 - min(wide_steps(p, sq, sk, w), 65535)) << 11) | w : 0x7fffffff;
   __syncthreads();
+  // 256 threads, at most 1024 pairs per stage: the loads of a thread's four pairs are issued
+  // before any comparison, so a stage costs one LDS round trip rather than four
+  constexpr int PT = 4;
   for (int k = 2; k <= N; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int t = threadIdx.x; t < N / 2; t += blockDim.x) {
+      int a[PT], c[PT];
+#pragma unroll
+      for (int u = 0; u < PT; ++u) {
+        const int t = threadIdx.x + 256 * u;
         const int i = 2 * t - (t & (j - 1));  // 2j * (t / j) + t % j, j a power of two
-        const int a = key[i], c = key[i + j];
-        if ((a > c) == ((i & k) == 0)) {
-          key[i] = c;
-          key[i + j] = a;
+        if (t < N / 2) {
+          a[u] = key[i];
+          c[u] = key[i + j];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < PT; ++u) {
+        const int t = threadIdx.x + 256 * u;
+        const int i = 2 * t - (t & (j - 1));
+        if (t < N / 2 && (a[u] > c[u]) == ((i & k) == 0)) {
+          key[i] = c[u];
+          key[i + j] = a[u];
         }
       }
       __syncthreads();
@@ -93,7 +122,8 @@ __global__ __launch_bounds__(256) void k_dot(const KParams p) {
   const int blk = (int)blockIdx.x - (p.order_n > 0 ? 1 : 0);
   if (blk < 0) {
     __shared__ int key[2048];
-    order_work_groups(p, key);
+    __shared__ int seg[2 * kOrderSegs];
+    order_work_groups(p, key, seg);
     return;
   }
   // Work group = 64 consecutive rows of one query head, so the LSE reads and the D / scaled-LSE
