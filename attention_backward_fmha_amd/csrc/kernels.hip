@@ -1624,11 +1624,11 @@ __global__ __launch_bounds__(256) void k_zero(float* ptr, int64_t n4, uint64_t* 
 }  // namespace
 
 hipError_t launch_dot(const Plan& plan, const KParams& kp, hipStream_t stream) {
-  const int64_t rows = plan.rows_q * plan.Hq;
-  if (rows == 0) return hipSuccess;
-  // one more work group ranks the wide kernel's work groups when the plan orders them
+  // one more work group ranks the wide kernel's work groups when the plan orders them; it runs
+  // even without query rows (keys only), since the main kernel still reads the list then
   if (plan.order_n > 2048 || (plan.order_n > 0 && kp.order == nullptr)) return hipErrorInvalidValue;
   const int64_t blocks = (plan.rows_q + kDotRows - 1) / kDotRows * plan.Hq + (plan.order_n > 0 ? 1 : 0);
+  if (blocks == 0) return hipSuccess;
   if (plan.d_v == 64) {
     hipLaunchKernelGGL(k_dot<64>, dim3((unsigned)blocks), dim3(256), 0, stream, kp);
   } else {

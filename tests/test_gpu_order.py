@@ -74,3 +74,40 @@ def test_work_group_order_is_a_ranked_permutation(case):
     keys = [(-c, int(w)) for c, w in zip(cost, order)]
     assert all(a < b for a, b in zip(keys, keys[1:]))
     assert cost[0] > 0
+
+
+def test_keys_without_queries_still_get_their_list():
+    """Every query segment empty: the D stage has no rows, yet the main kernel's work groups
+    still take their items from the list, so the ranking work group runs on its own. The
+    workspace starts zeroed (a stale list whose entries are all in range, which would run item 0
+    everywhere) and dK/dV start as NaN: every key must come back with dK = dV = 0."""
+    import torch
+    import attention_backward_fmha_amd as F
+    lens_q, lens_k = [0, 0, 0], [300, 700, 50]
+    sq, sk = I.seqstart(lens_q), I.seqstart(lens_k)
+    tk = int(sk[-1])
+    g = torch.Generator(device="cpu").manual_seed(11)
+    kv = lambda: torch.randn((tk, 2, 128), generator=g).to(torch.bfloat16).cuda()
+    z = lambda *s: torch.zeros(s, dtype=torch.bfloat16, device="cuda")
+    q, o, do = z(0, 4, 128), z(0, 4, 128), z(0, 4, 128)
+    k, v = kv(), kv()
+    lse = torch.zeros((4, 0), dtype=torch.float32, device="cuda")
+    dq = torch.empty_like(q)
+    dk = torch.full_like(k, float("nan"))
+    dv = torch.full_like(v, float("nan"))
+    c = F.make_call(q, k, v, o, lse, do, dq, dk, dv, mask_type=0, deterministic=True,
+                    cu_seqlens_q=torch.from_numpy(sq).cuda(), cu_seqlens_k=torch.from_numpy(sk).cuda(),
+                    cu_seqlens_q_host=sq, cu_seqlens_k_host=sk, tune=dict(kernel=F.KERNEL_WIDE))
+    info = c.plan()
+    n = info.ordered_groups
+    assert info.rows_q == 0 and n > 1
+    ws = torch.zeros(c.workspace_size(), dtype=torch.uint8, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    c.prepare(ws, s)
+    c.run(ws, s)
+    torch.cuda.synchronize()
+    off = (info.dkv_acc_offset + info.dkv_acc_bytes + 255) // 256 * 256
+    order = ws[off:off + 4 * n].cpu().numpy().view(np.int32)
+    assert np.array_equal(np.sort(order), np.arange(n))
+    assert torch.equal(dk.float().cpu(), torch.zeros(dk.shape))
+    assert torch.equal(dv.float().cpu(), torch.zeros(dv.shape))
